@@ -1,0 +1,154 @@
+"""CPU oracle for the temperature-T BCJR soft quantizer (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It loads ``liboracle.so``, built from
+``oracle.c`` with gcc (``-O2``, no fast-math, no FMA contraction, OpenMP over
+sequences), and shares no code with the GPU path.
+
+What the oracle computes follows "BCJR-QAT: A Differentiable Relaxation of
+Trellis-Coded Weight Quantization" (arXiv 2605.10655): the Boltzmann path
+measure at temperature T, the soft codeword as the expectation of c(s_t)
+(gist.science Technical Summary, "Core Mechanism"), its exact gradient in the
+weights, and the Viterbi hard code as the T -> 0 limit (abstract).  The
+readings the pages leave open are stated in ``oracle.c``'s header.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+             "-fexcess-precision=standard"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc; returns its path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Handle:
+    """ctypes handle on one build of the oracle library."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        lib.oracle_soft.argtypes = [f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p, f64p]
+        lib.oracle_soft.restype = ci
+        lib.oracle_grad.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p]
+        lib.oracle_grad.restype = ci
+        lib.oracle_viterbi.argtypes = [f32p, f32p, i64, i64, ci, ci, i32p, i32p, f32p, f32p]
+        lib.oracle_viterbi.restype = ci
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ci
+        self.lib = lib
+
+
+_handle = None
+
+
+def _load():
+    global _handle
+    if _handle is None:
+        build(force=False)
+        _handle = _Handle(_LIB)
+    return _handle.lib
+
+
+def use_library(path: str) -> None:
+    """Point this module at another build of oracle.c (the mutation tests plant mistakes in copies)."""
+    global _handle
+    _handle = _Handle(path)
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a, ctype):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _check_shapes(w, c, L):
+    if w.ndim != 2:
+        raise ValueError("w must be [B, n]")
+    if c.shape != (1 << L,):
+        raise ValueError(f"codebook must have 2^L = {1 << L} entries")
+
+
+def soft(w, c, L: int, k: int, T: float, sigma=None, with_check: bool = False):
+    """Soft codeword w_soft [B, n] (float64) and ln Z [B] for float32 inputs.
+
+    With ``with_check`` also returns max_t |logsumexp_s(alpha_t + beta_t) - ln Z| per sequence.
+    """
+    w = _f32(w)
+    c = _f32(c)
+    _check_shapes(w, c, L)
+    B, n = w.shape
+    sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
+    out = np.empty((B, n), np.float64)
+    lz = np.empty(B, np.float64)
+    dev = np.empty(B, np.float64)
+    rc = _load().oracle_soft(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k, float(T),
+                             _ptr(sg, ctypes.c_int32), _ptr(out, ctypes.c_double), _ptr(lz, ctypes.c_double),
+                             _ptr(dev, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError(f"oracle_soft failed ({rc})")
+    return (out, lz, dev) if with_check else (out, lz)
+
+
+def grad(w, c, g, L: int, k: int, T: float, sigma=None):
+    """dL/dw [B, n] (float64) for upstream g = dL/dw_soft, plus w_soft [B, n]."""
+    w = _f32(w)
+    c = _f32(c)
+    g = _f32(g)
+    _check_shapes(w, c, L)
+    if g.shape != w.shape:
+        raise ValueError("g must match w")
+    B, n = w.shape
+    sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
+    out = np.empty((B, n), np.float64)
+    ws = np.empty((B, n), np.float64)
+    rc = _load().oracle_grad(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(g, ctypes.c_float), B, n,
+                             L, k, float(T), _ptr(sg, ctypes.c_int32), _ptr(out, ctypes.c_double),
+                             _ptr(ws, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError(f"oracle_grad failed ({rc})")
+    return out, ws
+
+
+def viterbi(w, c, L: int, k: int, sigma=None):
+    """Viterbi states [B, n] int32 (s_1..s_n), c(states) [B, n] float32 and path cost [B] float32."""
+    w = _f32(w)
+    c = _f32(c)
+    _check_shapes(w, c, L)
+    B, n = w.shape
+    sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
+    st = np.empty((B, n), np.int32)
+    wh = np.empty((B, n), np.float32)
+    cost = np.empty(B, np.float32)
+    rc = _load().oracle_viterbi(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k,
+                                _ptr(sg, ctypes.c_int32), _ptr(st, ctypes.c_int32), _ptr(wh, ctypes.c_float),
+                                _ptr(cost, ctypes.c_float))
+    if rc != 0:
+        raise RuntimeError(f"oracle_viterbi failed ({rc})")
+    return st, wh, cost
+
+
+def num_threads() -> int:
+    """OpenMP threads one oracle call uses."""
+    return int(_load().oracle_num_threads())
