@@ -1,0 +1,127 @@
+"""differentiable_bcjr_amd -- the temperature-T BCJR soft quantizer of BCJR-QAT on MI355X (gfx950).
+
+Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/bcjr.h``:
+
+* ``soft_codeword``      -- w_soft[b, t] = E_p[c(s_t)], the Boltzmann expectation of the codebook value over all
+  bitshift-trellis paths at temperature T, and ln Z (BCJR-QAT, arXiv 2605.10655; gist.science Technical Summary,
+  "Core Mechanism");
+* ``soft_codeword_grad`` -- dL/dw from an upstream dL/dw_soft, the exact derivative of the soft codeword;
+* ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32.
+
+These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
+torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
+in the library's kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import abi
+
+__all__ = ["soft_codeword", "soft_codeword_grad", "viterbi_hard_code", "workspace_bytes", "BCJRError", "abi"]
+
+
+class BCJRError(RuntimeError):
+    """A non-zero status from libbcjr.so."""
+
+    def __init__(self, status: int):
+        super().__init__(abi.bcjr_status_string(status))
+        self.status = status
+
+
+def _check(rc: int) -> None:
+    if rc != abi.BCJR_OK:
+        raise BCJRError(rc)
+
+
+def _f32(x: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if x.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    return x.contiguous()
+
+
+def _sigma(s, B: int, device) -> torch.Tensor | None:
+    if s is None:
+        return None
+    if not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype != torch.int32 or s.numel() != B:
+        raise TypeError("boundary_state must be an int32 CUDA tensor with one entry per sequence")
+    return s.contiguous()
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2) -> int:
+    """Device workspace bytes the library needs for op (abi.BCJR_OP_SOFT / _GRAD / _VITERBI)."""
+    return abi.bcjr_workspace_bytes(op, B, n, L, k)
+
+
+def _workspace(op, B, n, L, k, device, workspace):
+    need = workspace_bytes(op, B, n, L, k)
+    if workspace is None:
+        # torch's allocator hands out 512-byte aligned blocks; the library checks 256-byte alignment itself
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
+                  boundary_state: torch.Tensor | None = None, *, return_log_z: bool = False,
+                  workspace: torch.Tensor | None = None):
+    """Soft codeword [B, n] (and ln Z [B] if ``return_log_z``) for weights w [B, n] and codebook [2^L]."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    if w.dim() != 2:
+        raise ValueError("w must be [B, n]")
+    B, n = w.shape
+    sig = _sigma(boundary_state, B, w.device)
+    out = torch.empty_like(w)
+    lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
+    ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace)
+    _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                  out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    return (out, lz) if return_log_z else out
+
+
+def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int, k: int = 2,
+                       T: float = 1.0, boundary_state: torch.Tensor | None = None, *, return_w_soft: bool = False,
+                       workspace: torch.Tensor | None = None):
+    """dL/dw [B, n] given dL/dw_soft [B, n] (and the soft codeword if ``return_w_soft``)."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    g = _f32(grad_w_soft, "grad_w_soft")
+    if w.dim() != 2 or g.shape != w.shape:
+        raise ValueError("w and grad_w_soft must both be [B, n]")
+    B, n = w.shape
+    sig = _sigma(boundary_state, B, w.device)
+    grad = torch.empty_like(w)
+    ws_out = torch.empty_like(w) if return_w_soft else None
+    ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace)
+    _check(abi.bcjr_soft_codeword_grad(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                       g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
+                                       _stream(w.device)))
+    return (grad, ws_out) if return_w_soft else grad
+
+
+def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2,
+                      boundary_state: torch.Tensor | None = None, *, workspace: torch.Tensor | None = None):
+    """(states [B, n] int32, w_hard [B, n] float32, cost [B] float32) of the minimum-energy paths."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    if w.dim() != 2:
+        raise ValueError("w must be [B, n]")
+    B, n = w.shape
+    sig = _sigma(boundary_state, B, w.device)
+    states = torch.empty((B, n), dtype=torch.int32, device=w.device)
+    w_hard = torch.empty_like(w)
+    cost = torch.empty(B, dtype=torch.float32, device=w.device)
+    ws, need = _workspace(abi.BCJR_OP_VITERBI, B, n, L, k, w.device, workspace)
+    _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
+                                 w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    return states, w_hard, cost

@@ -1,0 +1,170 @@
+// bcjr_abi.cpp -- the C-ABI of libbcjr.so (declared in include/bcjr.h): argument checks, workspace planning and
+// kernel dispatch.  Every check runs on the host before any HIP call, so all error paths are testable without a GPU.
+#include "bcjr.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "trellis.hpp"
+
+namespace bcjr {
+
+struct SoftArgs;
+struct GradArgs;
+struct ViterbiArgs;
+hipError_t launch_soft(int L, const SoftArgs& a, int grid, hipStream_t st);
+hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st);
+hipError_t launch_viterbi(int L, const ViterbiArgs& a, int grid, hipStream_t st);
+
+}  // namespace bcjr
+
+#include "kernel_args.hpp"
+
+namespace {
+
+using namespace bcjr;
+
+constexpr int64_t kMaxN = 8192;   // keeps every per-block workspace offset within 32 bits
+constexpr int64_t kMaxB = 2147483647LL;
+constexpr float kMinT = 1e-12f;
+
+struct Plan {
+    int grid;
+    int slots;
+    size_t slot_bytes;
+    size_t total;
+};
+
+int check_shape(int64_t B, int64_t n, int32_t L, int32_t k) {
+    if (B < 1 || B > kMaxB || n < 1 || n > kMaxN || k < 1 || L < 2 * k || L > 16) return BCJR_ERR_SHAPE;
+    if (k != 2) return BCJR_ERR_UNSUPPORTED;
+    return BCJR_OK;
+}
+
+int check_temp(float T) {
+    if (!std::isfinite(T) || !(T >= kMinT)) return BCJR_ERR_TEMP;
+    return BCJR_OK;
+}
+
+// Grid, slot count and per-slot workspace bytes of one entry point.  One slot per in-flight sequence.
+Plan make_plan(int op, int64_t B, int64_t n, int L) {
+    const GeoRT g = geo_rt(L);
+    const int64_t groups = (B + g.SPB - 1) / g.SPB;
+    const int64_t cap = (int64_t)kNumCU * blocks_per_cu(L);
+    Plan p{};
+    p.grid = (int)(groups < cap ? groups : cap);
+    p.slots = p.grid * g.SPB;
+    const size_t msgs = (size_t)(n + 1) * (size_t)g.G * 4;   // one float per group per step (+1 spare row)
+    const size_t nrm = (size_t)n * 4;                         // one normaliser per step
+    switch (op) {
+        case BCJR_OP_SOFT: p.slot_bytes = align256(msgs) + align256(nrm); break;
+        case BCJR_OP_GRAD: p.slot_bytes = 2 * align256(msgs) + align256(nrm); break;
+        default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
+    }
+    p.total = (size_t)p.slots * p.slot_bytes;
+    return p;
+}
+
+int check_workspace(const void* ws, size_t bytes, const Plan& p) {
+    if (ws == nullptr || bytes < p.total) return BCJR_ERR_WORKSPACE;
+    if (((uintptr_t)ws & 255u) != 0) return BCJR_ERR_WORKSPACE;
+    return BCJR_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? BCJR_OK : BCJR_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
+    if (op < BCJR_OP_SOFT || op > BCJR_OP_VITERBI) return 0;
+    if (check_shape(B, n, L, k) != BCJR_OK) return 0;
+    return make_plan(op, B, n, L).total;
+}
+
+const char* bcjr_status_string(int32_t status) {
+    switch (status) {
+        case BCJR_OK: return "BCJR_OK: success";
+        case BCJR_ERR_NULL: return "BCJR_ERR_NULL: a required pointer is NULL";
+        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 8192, k >= 1, 2k <= L <= 16";
+        case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
+        case BCJR_ERR_UNSUPPORTED: return "BCJR_ERR_UNSUPPORTED: only k = 2 has kernels";
+        case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
+        case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
+        default: return "BCJR: unknown status";
+    }
+}
+
+int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, float T,
+                       const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    const Plan p = make_plan(BCJR_OP_SOFT, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    SoftArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B;
+    a.n = (int)n;
+    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.sigma = boundary_state;
+    a.w_soft = w_soft;
+    a.log_z = log_z;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_soft(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                            float T, const int32_t* boundary_state, const float* grad_w_soft, float* grad_w,
+                            float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !grad_w_soft || !grad_w) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    const Plan p = make_plan(BCJR_OP_GRAD, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    GradArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.g = grad_w_soft;
+    a.B = B;
+    a.n = (int)n;
+    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.two_over_T = (float)(2.0 / (double)T);
+    a.sigma = boundary_state;
+    a.grad = grad_w;
+    a.w_soft = w_soft;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_grad(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                      const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !states) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    const Plan p = make_plan(BCJR_OP_VITERBI, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    ViterbiArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B;
+    a.n = (int)n;
+    a.sigma = boundary_state;
+    a.states = states;
+    a.w_hard = w_hard;
+    a.cost = cost;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,376 @@
+// grad.hip -- exact gradient of the soft codeword with respect to the weights, on gfx950.
+//
+// The soft codeword is exactly differentiable in the weight pre-image (BCJR-QAT, arXiv 2605.10655: gist.science
+// Technical Summary, "Core Mechanism"; "Key Technical Innovations").  Differentiating w_soft_t = E_p[c(s_t)] under
+// p(path) ~ exp(-sum_t (w_t - c(s_t))^2 / T) gives d w_soft_t / d w_u = (2/T) Cov_p(c(s_t), c(s_u)), so for an
+// upstream gradient g
+//     grad_u = (2/T) Cov_p( c(s_u), F ),   F = sum_t g_t (c(s_t) - w_t)
+// (subtracting the constant sum_t g_t w_t from F changes no covariance and keeps F small).  E[F | s_u] splits at u
+// because the posterior is a Markov chain, and both halves are carried as one extra message per group alongside the
+// log-sum-exp messages of the soft pass, weighted by the same softmax weights (the expectation semiring):
+//   forward   Q_{t+1}(v) = sum_a pi_a  [ g_t (c(s_a) - w_t) + Q_t(v >> 2 | a << (L-4)) ],  pi = softmax over a
+//   backward  P_{t-1}(u) = sum_b rho_b [ g_t (c(s_b) - w_t) + P_t((4u + b) & (G-1)) ],   rho = softmax over b
+//   at step t, for state s: E[F | s_t = s] = g_t (c(s) - w_t) + Q_t(s >> 2) + P_t(s & (G-1))
+// The covariance is reduced over the block per step from the posterior weights of the soft pass, with E[F] (from the
+// end of the forward pass) subtracted first so that the two-moment formula does not cancel.
+//
+// LDS holds the log-sum-exp message and the expectation message of one direction (2 x 64 KiB at L = 16) in a single
+// buffer: each step loads its inputs into registers, barriers, then writes its outputs.  Both forward messages go to
+// the workspace tape.  At L = 16 the codebook is read through L1/L2 each step (a thread has no registers left for it);
+// at smaller L it stays in registers.
+#include "kernel_args.hpp"
+#include "trellis.hpp"
+
+namespace bcjr {
+
+// Scaled codebook row c'(a << (L-2) | j << 2 | 0..3) of quad m: from registers, or through L1/L2.
+template <int L, int TPS, bool CB_REG, int M>
+__device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs, uint32_t v_cb, float scale, int m,
+                                         int a) {
+    if constexpr (CB_REG) {
+        return make_float4(cbr[m][a][0], cbr[m][a][1], cbr[m][a][2], cbr[m][a][3]);
+    } else {
+        const float4 v = buf_ld4(cbs, v_cb, 4u * ((uint32_t)a << (L - 2)) + 16u * TPS * m);
+        return make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+    }
+}
+
+template <int L>
+__global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
+    using Gm = Geo<L>;
+    constexpr int G = Gm::G, Q = Gm::Q, QPT = Gm::QPT, TPS = Gm::TPS, SPB = Gm::SPB, WPS = Gm::WPS;
+    constexpr int SEG = Gm::SEG;
+    constexpr bool CB_REG = QPT <= 2;
+    __shared__ float4 lds_r4[SPB][G / 4];
+    __shared__ float4 lds_q4[SPB][G / 4];
+    __shared__ float redmax[2][SPB][WPS];
+    __shared__ float4 redsum[2][SPB][WPS];
+
+    const int tid = threadIdx.x;
+    const int sq = tid / TPS;
+    const int tau = tid % TPS;
+    const int lane = tid & 63;
+    const int wv = tau >> 6;
+    float* mr = reinterpret_cast<float*>(&lds_r4[sq][0]);
+    float* mq = reinterpret_cast<float*>(&lds_q4[sq][0]);
+
+    const int n = args.n;
+    const float scale = args.scale;
+    const float inv_scale = 1.0f / scale;
+
+    const rsrc_t cbs = make_rsrc(args.cb, 4u << L);
+    const uint32_t v_cb = 16u * tau;
+    float cbr[CB_REG ? QPT : 1][4][4];
+    if constexpr (CB_REG) {
+#pragma unroll
+        for (int m = 0; m < QPT; ++m)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const float4 v = buf_ld4(cbs, v_cb, 4u * ((uint32_t)a << (L - 2)) + 16u * TPS * m);
+                cbr[m][a][0] = v.x * scale;
+                cbr[m][a][1] = v.y * scale;
+                cbr[m][a][2] = v.z * scale;
+                cbr[m][a][3] = v.w * scale;
+            }
+    }
+
+    // tape of this block's sequences: slot sq at sq * slot_bytes; [n+1][G] R~, [n+1][G] Q, [n] normalisers
+    const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
+    const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * SPB * args.slot_bytes, SPB * slot_bytes);
+    const uint32_t v_quad = sq * slot_bytes + 16u * tau;
+    const uint32_t v_grp = sq * slot_bytes + 4u * tau;
+    const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const uint32_t nrm_base = 2u * q_base;
+
+    const int64_t ngroups = (args.B + SPB - 1) / SPB;
+    for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
+        const int64_t b = gi * SPB + sq;
+        const bool active = b < args.B;
+        const int64_t bb = active ? b : args.B - 1;
+        const float* wb = args.w + bb * n;
+        const float* gb = args.g + bb * n;
+        const bool has_sigma = args.sigma != nullptr;
+        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[bb] & (uint32_t)(Gm::S - 1)) : 0u;
+
+        // ------------------------------------------------------------------ forward: R~ and Q
+#pragma unroll
+        for (int m = 0; m < QPT; ++m) {
+            const int j = tau + TPS * m;
+            float4 r;
+            r.x = (!has_sigma || (uint32_t)(4 * j + 0) == (sig & (G - 1))) ? 0.f : kNeg;
+            r.y = (!has_sigma || (uint32_t)(4 * j + 1) == (sig & (G - 1))) ? 0.f : kNeg;
+            r.z = (!has_sigma || (uint32_t)(4 * j + 2) == (sig & (G - 1))) ? 0.f : kNeg;
+            r.w = (!has_sigma || (uint32_t)(4 * j + 3) == (sig & (G - 1))) ? 0.f : kNeg;
+            const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4*>(mr + 4 * j) = r;
+            *reinterpret_cast<float4*>(mq + 4 * j) = z;
+            buf_st4(r, tape, v_quad, 16u * TPS * m);
+            buf_st4(z, tape, v_quad, q_base + 16u * TPS * m);
+        }
+        lds_barrier();
+
+        float N = 0.f;
+        double A = 0.0;
+        float N_last = 0.f;
+        for (int t = 0; t < n; ++t) {
+            float rin[QPT][4], qin[QPT][4];
+#pragma unroll
+            for (int m = 0; m < QPT; ++m)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    rin[m][a] = mr[tau + TPS * m + Q * a];
+                    qin[m][a] = mq[tau + TPS * m + Q * a];
+                }
+            lds_barrier();   // every input read before any output overwrites it
+            const float wt = wb[t] * scale;
+            const float gt = gb[t] * inv_scale;
+            float lmax = -3.0e38f;
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                const float4 c0 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 0);
+                const float4 c1 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 1);
+                const float4 c2 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 2);
+                const float4 c3 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 3);
+                const float cv[4][4] = {{c0.x, c0.y, c0.z, c0.w}, {c1.x, c1.y, c1.z, c1.w},
+                                        {c2.x, c2.y, c2.z, c2.w}, {c3.x, c3.y, c3.z, c3.w}};
+                float ro[4], qo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float x[4], z[4];
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float d = cv[a][i] - wt;
+                        x[a] = fmaf(-d, d, rin[m][a]);
+                        z[a] = fmaf(gt, d, qin[m][a]);
+                    }
+                    const float mx = max4(x[0], x[1], x[2], x[3]);
+                    const float e0 = ex2(x[0] - mx), e1 = ex2(x[1] - mx), e2 = ex2(x[2] - mx), e3 = ex2(x[3] - mx);
+                    const float s = (e0 + e1) + (e2 + e3);
+                    ro[i] = (mx - N) + lg2(s);
+                    qo[i] = fmaf(e0, z[0], fmaf(e1, z[1], fmaf(e2, z[2], e3 * z[3]))) * rcp(s);
+                    pin_order(ro[i], qo[i]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                lmax = fmaxf(lmax, max4(ro[0], ro[1], ro[2], ro[3]));
+                const float4 r4 = make_float4(ro[0], ro[1], ro[2], ro[3]);
+                const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
+                *reinterpret_cast<float4*>(mr + 4 * j) = r4;
+                *reinterpret_cast<float4*>(mq + 4 * j) = q4;
+                buf_st4(r4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
+                buf_st4(q4, tape, v_quad, q_base + (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
+            }
+            if (tau == 0) buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
+            lmax = seg_max_fast<SEG>(lmax);
+            if constexpr (WPS > 1) {
+                if (lane == 0) redmax[t & 1][sq][wv] = lmax;
+            }
+            lds_barrier();
+            if constexpr (WPS > 1) {
+#pragma unroll
+                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+            }
+            if constexpr (SPB == 1) lmax = uniform_f(lmax);
+            A += (double)N;
+            N_last = N;
+            N = lmax;
+        }
+        // rz = log2 Z - A_n and E[F] (which centres the covariance of the backward pass)
+        float rz, EF;
+        if (!has_sigma) {
+            float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                const float4 o = *reinterpret_cast<const float4*>(mr + 4 * j);
+                const float4 q = *reinterpret_cast<const float4*>(mq + 4 * j);
+                const float p0 = ex2(o.x - N), p1 = ex2(o.y - N), p2 = ex2(o.z - N), p3 = ex2(o.w - N);
+                z0 += (p0 + p1) + (p2 + p3);
+                z1 += fmaf(p0, q.x, fmaf(p1, q.y, fmaf(p2, q.z, p3 * q.w)));
+            }
+            z0 = seg_sum_fast<SEG>(z0);
+            z1 = seg_sum_fast<SEG>(z1);
+            if constexpr (WPS > 1) {
+                if (lane == 0) redsum[n & 1][sq][wv] = make_float4(z0, z1, 0.f, 0.f);
+            }
+            lds_barrier();
+            if constexpr (WPS > 1) {
+                z0 = 0.f;
+                z1 = 0.f;
+#pragma unroll
+                for (int q = 0; q < WPS; ++q) {
+                    z0 += redsum[n & 1][sq][q].x;
+                    z1 += redsum[n & 1][sq][q].y;
+                }
+            }
+            rz = N + lg2(z0);
+            EF = z1 / z0;
+            __syncthreads();   // tape writes of the forward pass visible to every thread of the block
+        } else {
+            // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
+            __syncthreads();
+            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            const float r = buf_ld(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
+            const float q = buf_ld(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
+            rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
+            EF = fmaf(gb[n - 1] * inv_scale, d, q);
+        }
+        const bool valid = rz > 0.5f * kNeg;
+
+        // ------------------------------------------------------------------ backward: B~ and P, covariance
+        float Nb = 0.f;
+        float C = 0.f;
+        float D = 0.f;
+        int t = n - 1;
+        if (!has_sigma) {
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                *reinterpret_cast<float4*>(mr + 4 * j) = z;
+                *reinterpret_cast<float4*>(mq + 4 * j) = z;
+            }
+        } else {
+            // s_n = sigma: posterior at n-1 is the indicator of sigma (so grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
+            // the messages left are B_{n-2}(sigma >> 2) = theta_{n-1}(sigma), P_{n-2}(sigma >> 2) = g (c(sigma) - w)
+            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            const float th = -d * d;
+            const float pz = gb[n - 1] * inv_scale * d;
+#pragma unroll
+            for (int m = 0; m < QPT; ++m)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
+                    mr[u] = (u == (sig >> 2)) ? th : kNeg;
+                    mq[u] = (u == (sig >> 2)) ? pz : 0.f;
+                }
+            if (tau == 0 && active) {
+                args.grad[b * n + n - 1] = valid ? 0.f : __builtin_nanf("");
+                if (args.w_soft) args.w_soft[b * n + n - 1] = valid ? args.cb[sig] : __builtin_nanf("");
+            }
+            D = N_last;
+            Nb = th;
+            t = n - 2;
+        }
+        lds_barrier();
+
+        for (; t >= 0; --t) {
+            float bin[QPT][4], pin[QPT][4];
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const float4 v = *reinterpret_cast<const float4*>(mr + 4 * (tau + TPS * m));
+                const float4 p = *reinterpret_cast<const float4*>(mq + 4 * (tau + TPS * m));
+                bin[m][0] = v.x; bin[m][1] = v.y; bin[m][2] = v.z; bin[m][3] = v.w;
+                pin[m][0] = p.x; pin[m][1] = p.y; pin[m][2] = p.z; pin[m][3] = p.w;
+            }
+            lds_barrier();
+            const float wt = wb[t] * scale;
+            const float gt = gb[t] * inv_scale;
+            float Nt = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
+            if constexpr (SPB == 1) Nt = uniform_f(Nt);
+            D += Nt;
+            const float ref = (rz + D) - C;
+            float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
+                    const float rt = buf_ld(tape, v_grp, so);
+                    const float qt = buf_ld(tape, v_grp, q_base + so) - EF;
+                    const float4 cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, a);
+                    const float d0 = cr.x - wt, d1 = cr.y - wt, d2 = cr.z - wt, d3 = cr.w - wt;
+                    const float y0 = fmaf(-d0, d0, bin[m][0]), y1 = fmaf(-d1, d1, bin[m][1]);
+                    const float y2 = fmaf(-d2, d2, bin[m][2]), y3 = fmaf(-d3, d3, bin[m][3]);
+                    const float z0 = fmaf(gt, d0, pin[m][0]), z1 = fmaf(gt, d1, pin[m][1]);
+                    const float z2 = fmaf(gt, d2, pin[m][2]), z3 = fmaf(gt, d3, pin[m][3]);
+                    const float mx = max4(y0, y1, y2, y3);
+                    const float e0 = ex2(y0 - mx), e1 = ex2(y1 - mx), e2 = ex2(y2 - mx), e3 = ex2(y3 - mx);
+                    const float s = (e0 + e1) + (e2 + e3);
+                    const float ez = fmaf(e0, z0, fmaf(e1, z1, fmaf(e2, z2, e3 * z3)));
+                    const float ed0 = e0 * d0, ed1 = e1 * d1, ed2 = e2 * d2, ed3 = e3 * d3;
+                    const float ed = (ed0 + ed1) + (ed2 + ed3);
+                    const float edz = fmaf(ed0, z0, fmaf(ed1, z1, fmaf(ed2, z2, ed3 * z3)));
+                    const float out = (mx - Nb) + lg2(s);
+                    const float f = ex2((mx + rt) - ref);
+                    S0 = fmaf(f, s, S0);
+                    S1 = fmaf(f, ed, S1);
+                    S2 = fmaf(f, fmaf(qt, s, ez), S2);
+                    S3 = fmaf(f, fmaf(qt, ed, edz), S3);
+                    lmax = fmaxf(lmax, out);
+                    const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
+                    mr[u] = out;            // at t = 0 these land in buffers nobody reads
+                    mq[u] = ez * rcp(s);
+                    pin_order(S0, S1, lmax);
+                    pin_order(S2, S3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            lmax = seg_max_fast<SEG>(lmax);
+            S0 = seg_sum_fast<SEG>(S0);
+            S1 = seg_sum_fast<SEG>(S1);
+            S2 = seg_sum_fast<SEG>(S2);
+            S3 = seg_sum_fast<SEG>(S3);
+            if constexpr (WPS > 1) {
+                if (lane == 0) {
+                    redsum[t & 1][sq][wv] = make_float4(S0, S1, S2, S3);
+                    redmax[t & 1][sq][wv] = lmax;
+                }
+            }
+            lds_barrier();
+            if constexpr (WPS > 1) {
+#pragma unroll
+                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+                if (tau == 0) {
+                    S0 = S1 = S2 = S3 = 0.f;
+#pragma unroll
+                    for (int q = 0; q < WPS; ++q) {
+                        const float4 p = redsum[t & 1][sq][q];
+                        S0 += p.x;
+                        S1 += p.y;
+                        S2 += p.z;
+                        S3 += p.w;
+                    }
+                }
+            }
+            if constexpr (SPB == 1) lmax = uniform_f(lmax);
+            if (tau == 0 && active) {
+                const float i0 = 1.0f / S0;
+                const float m1 = S1 * i0, m2 = S2 * i0;
+                const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' in scaled units
+                args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
+            }
+            C += Nb;
+            Nb = lmax;
+        }
+        __syncthreads();
+    }
+}
+
+template <int L>
+static hipError_t launch_grad_L(const GradArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL(grad_kernel<L>, dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st) {
+    switch (L) {
+        case 4: return launch_grad_L<4>(a, grid, st);
+        case 5: return launch_grad_L<5>(a, grid, st);
+        case 6: return launch_grad_L<6>(a, grid, st);
+        case 7: return launch_grad_L<7>(a, grid, st);
+        case 8: return launch_grad_L<8>(a, grid, st);
+        case 9: return launch_grad_L<9>(a, grid, st);
+        case 10: return launch_grad_L<10>(a, grid, st);
+        case 11: return launch_grad_L<11>(a, grid, st);
+        case 12: return launch_grad_L<12>(a, grid, st);
+        case 13: return launch_grad_L<13>(a, grid, st);
+        case 14: return launch_grad_L<14>(a, grid, st);
+        case 15: return launch_grad_L<15>(a, grid, st);
+        case 16: return launch_grad_L<16>(a, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace bcjr

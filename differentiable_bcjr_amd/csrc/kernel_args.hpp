@@ -1,0 +1,49 @@
+// kernel_args.hpp -- argument blocks passed by value from the C-ABI to the three kernels.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bcjr {
+
+struct SoftArgs {
+    const float* w;        // [B, n]
+    const float* cb;       // [2^L]
+    int64_t B;
+    int n;
+    float scale;           // sqrt(log2(e) / T)
+    const int32_t* sigma;  // [B] or nullptr
+    float* w_soft;         // [B, n]
+    float* log_z;          // [B] or nullptr
+    unsigned char* ws;
+    size_t slot_bytes;
+};
+
+struct GradArgs {
+    const float* w;        // [B, n]
+    const float* cb;       // [2^L]
+    const float* g;        // [B, n] upstream dL/dw_soft
+    int64_t B;
+    int n;
+    float scale;           // sqrt(log2(e) / T)
+    float two_over_T;
+    const int32_t* sigma;  // [B] or nullptr
+    float* grad;           // [B, n]
+    float* w_soft;         // [B, n] or nullptr
+    unsigned char* ws;
+    size_t slot_bytes;
+};
+
+struct ViterbiArgs {
+    const float* w;        // [B, n]
+    const float* cb;       // [2^L]
+    int64_t B;
+    int n;
+    const int32_t* sigma;  // [B] or nullptr
+    int32_t* states;       // [B, n]
+    float* w_hard;         // [B, n] or nullptr
+    float* cost;           // [B] or nullptr
+    unsigned char* ws;
+    size_t slot_bytes;
+};
+
+}  // namespace bcjr

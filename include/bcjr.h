@@ -1,0 +1,106 @@
+/*
+ * bcjr.h -- C-ABI of libbcjr.so: the temperature-T BCJR forward-backward soft quantizer on a bitshift trellis,
+ * its exact gradient, and the Viterbi hard code, as hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The method is "BCJR-QAT: A Differentiable Relaxation of Trellis-Coded Weight Quantization" (arXiv 2605.10655):
+ * the hard Viterbi decision of trellis-coded quantization is replaced by the BCJR sum-product pass at temperature
+ * T, whose output, the soft codeword, is the Boltzmann expectation of the emitted codebook value over all trellis
+ * paths (abstract; gist.science Technical Summary, "Core Mechanism").  The soft codeword is exactly differentiable
+ * in the weight pre-image, and T -> 0 gives back the hard code (same passages).
+ *
+ * Trellis and energy (readings of the pages, stated once here for every entry point):
+ *   - state s_t: an L-bit integer, 0 <= s_t < 2^L; each step shifts in k = 2 new bits at the low end:
+ *       s_{t+1} = ((s_t << k) & (2^L - 1)) | b,  b in [0, 2^k).   One weight per step (2 bits per weight).
+ *   - a path s_1..s_n emits codebook[s_t] at step t; its energy is E = sum_t (w_t - codebook[s_t])^2 and its
+ *     weight exp(-E / T).  Transitions carry no cost.
+ *   - boundary_state == NULL: free start and free end (s_1 and s_n unconstrained).
+ *     boundary_state != NULL: sequence b starts from a non-emitting s_0 = sigma_b (so s_1 is a successor of
+ *     sigma_b) and ends in s_n = sigma_b (tail-biting with a given state).  sigma_b is masked to its low L bits.
+ *     If no path satisfies the constraint (possible only when n < L/k), that sequence's outputs are NaN
+ *     (soft and gradient), log_z is -inf, and the Viterbi cost is +inf.
+ *
+ * Memory and execution, for every entry point:
+ *   - every tensor pointer is a DEVICE pointer to contiguous row-major memory owned by the caller: w, w_soft,
+ *     grad_w_soft, grad_w, w_hard are float32 [B, n]; codebook is float32 [2^L]; boundary_state, log_z and cost
+ *     are [B]; states is int32 [B, n].  Outputs must not alias inputs or each other.
+ *   - workspace is device scratch memory owned by the caller, at least bcjr_workspace_bytes(...) bytes, aligned
+ *     to 256 bytes; its contents on entry do not matter and are clobbered.  The library allocates nothing,
+ *     frees nothing, keeps no state between calls and never synchronizes: the work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
+ *     Calls on different streams need different workspaces.
+ *   - supported shapes: k == 2, 4 <= L <= 16, 1 <= n <= 8192, 1 <= B <= 2^31 - 1.
+ *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
+ *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
+ *     into that sequence's outputs.
+ */
+#ifndef BCJR_H
+#define BCJR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    BCJR_OK = 0,
+    BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
+    BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 8192, k < 1, L < 2k or L > 16 */
+    BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2 */
+    BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
+    BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+};
+
+enum { BCJR_OP_SOFT = 0, BCJR_OP_GRAD = 1, BCJR_OP_VITERBI = 2 };
+
+/*
+ * Soft codeword (gist.science Technical Summary, "Core Mechanism"):
+ *   w_soft[b, t] = sum_s codebook[s] * p_T(s_t = s | w_b),  p_T(path) proportional to exp(-E(path) / T),
+ * computed exactly by the log-domain BCJR forward-backward recursion (abstract; "Key Technical Innovations").
+ * log_z[b] = ln Z_b = ln sum_paths exp(-E / T) over the emitting states (optional output, may be NULL).
+ * Returns BCJR_OK or a negative status.
+ */
+int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, float T,
+                       const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Gradient of the soft codeword with respect to the weight pre-image w ("exactly differentiable with respect to
+ * the weight pre-image", gist.science Technical Summary, "Core Mechanism"):
+ *   grad_w[b, u] = sum_t grad_w_soft[b, t] * d w_soft[b, t] / d w[b, u]
+ *               = (2 / T) * Cov_p( codebook[s_u], sum_t grad_w_soft[b, t] * codebook[s_t] ),
+ * the covariance taken under the same Boltzmann path measure.  grad_w_soft is the upstream dL/dw_soft (required).
+ * w_soft (optional, may be NULL) receives the soft codeword of the same pass.
+ */
+int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                            float T, const int32_t* boundary_state, const float* grad_w_soft, float* grad_w,
+                            float* w_soft, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Viterbi hard code, the T -> 0 limit of the soft codeword (abstract): the path of minimum energy.  Arithmetic is
+ * IEEE float32 in a fixed order, without fused multiply-add:
+ *   M_1(s) = fl(d*d), d = fl(w_1 - codebook[s]);  M_t(s) = fl(fl(d*d) + min over predecessors p of M_{t-1}(p)),
+ * ties between predecessors go to the one with the smallest index, ties between end states to the smallest state.
+ * states[b, t] = s_t (int32, t = 1..n); w_hard[b, t] = codebook[s_t] (optional); cost[b] = M_n(s_n) (optional).
+ * T plays no part.
+ */
+int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                      const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace the entry point `op` (BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI) needs for
+ * these shapes; 0 when the shapes are invalid or unsupported.  Pure host function; no HIP call.
+ */
+size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);
+
+/* Static, NUL-terminated description of a status code. */
+const char* bcjr_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCJR_H */

@@ -1,0 +1,172 @@
+"""Host-side checks of the C-ABI (no GPU needed): the library loads, exports every symbol include/bcjr.h declares,
+reports status strings and workspace sizes, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from differentiable_bcjr_amd import abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bcjr.h")
+
+FAKE = 0x100000   # a non-NULL pointer value; every call below fails a host check before it could be used
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "if", "extern"})
+
+
+def test_header_declares_the_three_ops():
+    fns = declared_functions()
+    for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "viterbi_hard_code", "bcjr_workspace_bytes",
+                 "bcjr_status_string"]:
+        assert name in fns
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(abi.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in bcjr.h but not exported"
+    assert set(declared_functions()) == set(abi.EXPORTS)
+
+
+def test_status_strings():
+    for code in [abi.BCJR_OK, abi.BCJR_ERR_NULL, abi.BCJR_ERR_SHAPE, abi.BCJR_ERR_TEMP, abi.BCJR_ERR_UNSUPPORTED,
+                 abi.BCJR_ERR_WORKSPACE, abi.BCJR_ERR_HIP]:
+        s = abi.bcjr_status_string(code)
+        assert s.startswith("BCJR")
+    assert "unknown" in abi.bcjr_status_string(-99)
+
+
+def _geo(L):
+    G, Q = 1 << (L - 2), 1 << (L - 4)
+    QPT = (1 << (L - 14)) if L >= 14 else 1
+    TPS = Q // QPT
+    NT = max(TPS, 64)
+    return G, TPS, NT // TPS
+
+
+def _a256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("L", [4, 5, 8, 12, 14, 15, 16])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (4096, 256), (1000, 7)])
+def test_workspace_bytes_formula(L, B, n):
+    G, TPS, SPB = _geo(L)
+    bpc = 1 if L >= 15 else (2 if L == 14 else 8)
+    grid = min((B + SPB - 1) // SPB, 256 * bpc)
+    slots = grid * SPB
+    msgs = _a256((n + 1) * G * 4)
+    nrm = _a256(n * 4)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + nrm)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, B, n, L, 2) == slots * _a256(2 * n * TPS * 4)
+
+
+def test_workspace_bytes_for_the_headline_workload():
+    # 4096 sequences of 256 weights on a 2^16-state trellis: one 16 MiB forward tape per CU
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4096, 256, 16, 2) == 256 * (257 * 65536 + 1024)
+
+
+@pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 8193, 8, 2), (1, 4, 3, 2),
+                                  (1, 4, 17, 2), (1, 4, 8, 0), (1 << 31, 4, 8, 2)])
+def test_workspace_bytes_invalid_shapes_are_zero(args):
+    for op in (0, 1, 2):
+        assert abi.bcjr_workspace_bytes(op, *args) == 0
+    assert abi.bcjr_workspace_bytes(7, 1, 4, 8, 2) == 0
+
+
+def test_unsupported_k_has_no_workspace():
+    assert abi.bcjr_workspace_bytes(0, 4, 8, 8, 1) == 0
+    assert abi.bcjr_workspace_bytes(0, 4, 8, 9, 3) == 0
+
+
+def _soft(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, boundary_state=None, w_soft=FAKE, log_z=None,
+             workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword(*a.values())
+
+
+def _grad(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, boundary_state=None, grad_w_soft=FAKE,
+             grad_w=FAKE, w_soft=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_grad(*a.values())
+
+
+def _vit(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, boundary_state=None, states=FAKE, w_hard=None, cost=None,
+             workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.viterbi_hard_code(*a.values())
+
+
+def test_null_pointers_rejected():
+    assert _soft(w=None) == abi.BCJR_ERR_NULL
+    assert _soft(codebook=None) == abi.BCJR_ERR_NULL
+    assert _soft(w_soft=None) == abi.BCJR_ERR_NULL
+    assert _grad(grad_w_soft=None) == abi.BCJR_ERR_NULL
+    assert _grad(grad_w=None) == abi.BCJR_ERR_NULL
+    assert _vit(states=None) == abi.BCJR_ERR_NULL
+    assert _vit(codebook=None) == abi.BCJR_ERR_NULL
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=8193), dict(L=3), dict(L=17), dict(k=0), dict(L=4, k=3)])
+def test_bad_shapes_rejected(kw):
+    assert _soft(**kw) == abi.BCJR_ERR_SHAPE
+    assert _grad(**kw) == abi.BCJR_ERR_SHAPE
+    assert _vit(**kw) == abi.BCJR_ERR_SHAPE
+
+
+def test_unsupported_k_rejected():
+    assert _soft(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert _grad(L=9, k=3) == abi.BCJR_ERR_UNSUPPORTED
+    assert _vit(k=1) == abi.BCJR_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T", [0.0, -1.0, float("nan"), float("inf"), 1e-13])
+def test_bad_temperature_rejected(T):
+    assert _soft(T=T) == abi.BCJR_ERR_TEMP
+    assert _grad(T=T) == abi.BCJR_ERR_TEMP
+
+
+def test_viterbi_ignores_temperature_and_checks_workspace():
+    need = abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, 4, 8, 8, 2)
+    assert _vit(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
+    assert _vit(workspace=None, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+    assert _vit(workspace=FAKE + 16, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+
+
+def test_workspace_too_small_or_misaligned_rejected():
+    need = abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4, 8, 8, 2)
+    assert _soft(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
+    assert _soft(workspace=None, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+    assert _soft(workspace=FAKE + 64, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+    needg = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 8, 2)
+    assert _grad(workspace_bytes=needg - 1) == abi.BCJR_ERR_WORKSPACE
+
+
+def test_checks_precede_each_other_in_documented_order():
+    # NULL before shape before temperature before workspace
+    assert _soft(w=None, B=0, T=-1.0) == abi.BCJR_ERR_NULL
+    assert _soft(B=0, T=-1.0) == abi.BCJR_ERR_SHAPE
+    assert _soft(T=-1.0, workspace=None) == abi.BCJR_ERR_TEMP
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+
+    import differentiable_bcjr_amd as dba
+
+    w = torch.zeros(2, 4)
+    c = torch.zeros(256)
+    with pytest.raises(TypeError):
+        dba.soft_codeword(w, c, 8)
+    with pytest.raises(TypeError):
+        dba.viterbi_hard_code(w, c, 8)
