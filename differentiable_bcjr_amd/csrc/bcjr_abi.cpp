@@ -25,7 +25,7 @@ namespace {
 
 using namespace bcjr;
 
-constexpr int64_t kMaxN = 8192;   // keeps every per-block workspace offset within 32 bits
+constexpr int64_t kMaxN = 4096;   // keeps every per-block workspace offset (two [n+1][2^14] float tapes) below 2^31
 constexpr int64_t kMaxB = 2147483647LL;
 constexpr float kMinT = 1e-12f;
 
@@ -59,7 +59,7 @@ Plan make_plan(int op, int64_t B, int64_t n, int L) {
     const size_t nrm = (size_t)n * 4;                         // one normaliser per step
     switch (op) {
         case BCJR_OP_SOFT: p.slot_bytes = align256(msgs) + align256(nrm); break;
-        case BCJR_OP_GRAD: p.slot_bytes = 2 * align256(msgs) + align256(nrm); break;
+        case BCJR_OP_GRAD: p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm); break;
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
     }
     p.total = (size_t)p.slots * p.slot_bytes;
@@ -88,7 +88,7 @@ const char* bcjr_status_string(int32_t status) {
     switch (status) {
         case BCJR_OK: return "BCJR_OK: success";
         case BCJR_ERR_NULL: return "BCJR_ERR_NULL: a required pointer is NULL";
-        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 8192, k >= 1, 2k <= L <= 16";
+        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
         case BCJR_ERR_UNSUPPORTED: return "BCJR_ERR_UNSUPPORTED: only k = 2 has kernels";
         case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";

@@ -11,8 +11,12 @@
 //   forward   Q_{t+1}(v) = sum_a pi_a  [ g_t (c(s_a) - w_t) + Q_t(v >> 2 | a << (L-4)) ],  pi = softmax over a
 //   backward  P_{t-1}(u) = sum_b rho_b [ g_t (c(s_b) - w_t) + P_t((4u + b) & (G-1)) ],   rho = softmax over b
 //   at step t, for state s: E[F | s_t = s] = g_t (c(s) - w_t) + Q_t(s >> 2) + P_t(s & (G-1))
-// The covariance is reduced over the block per step from the posterior weights of the soft pass, with E[F] (from the
-// end of the forward pass) subtracted first so that the two-moment formula does not cancel.
+// The covariance is reduced over the block per step from the posterior weights of the soft pass.  Float32 accuracy
+// needs every per-state term of that reduction to stay O(1), so both expectation messages are re-centred each step
+// by a per-step constant (Cov ignores constants): Q by its value at the forward pass's most likely group, P by
+// g_t (w_soft_t - w_t), which turns P into E[sum_{tau>t} g_tau (c(s_tau) - w_soft_tau) | s_t], a zero-mean quantity.
+// The constants are carried separately and recombined into one per-step offset, so E[F | s_t] - E[F] is formed
+// from small numbers only.
 //
 // LDS holds the log-sum-exp message and the expectation message of one direction (2 x 64 KiB at L = 16) in a single
 // buffer: each step loads its inputs into registers, barriers, then writes its outputs.  Both forward messages go to
@@ -23,15 +27,13 @@
 
 namespace bcjr {
 
-// Scaled codebook row c'(a << (L-2) | j << 2 | 0..3) of quad m: from registers, or through L1/L2.
+// Codebook row c(a << (L-2) | j << 2 | 0..3) of quad m (unscaled): from registers, or through L1/L2.
 template <int L, int TPS, bool CB_REG, int M>
-__device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs, uint32_t v_cb, float scale, int m,
-                                         int a) {
+__device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs, uint32_t v_cb, int m, int a) {
     if constexpr (CB_REG) {
         return make_float4(cbr[m][a][0], cbr[m][a][1], cbr[m][a][2], cbr[m][a][3]);
     } else {
-        const float4 v = buf_ld4(cbs, v_cb, 4u * ((uint32_t)a << (L - 2)) + 16u * TPS * m);
-        return make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale);
+        return buf_ld4(cbs, v_cb, 4u * ((uint32_t)a << (L - 2)) + 16u * TPS * m);
     }
 }
 
@@ -44,6 +46,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     __shared__ float4 lds_r4[SPB][G / 4];
     __shared__ float4 lds_q4[SPB][G / 4];
     __shared__ float redmax[2][SPB][WPS];
+    __shared__ float redq[2][SPB][WPS];
     __shared__ float4 redsum[2][SPB][WPS];
 
     const int tid = threadIdx.x;
@@ -67,20 +70,22 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
                 const float4 v = buf_ld4(cbs, v_cb, 4u * ((uint32_t)a << (L - 2)) + 16u * TPS * m);
-                cbr[m][a][0] = v.x * scale;
-                cbr[m][a][1] = v.y * scale;
-                cbr[m][a][2] = v.z * scale;
-                cbr[m][a][3] = v.w * scale;
+                cbr[m][a][0] = v.x;
+                cbr[m][a][1] = v.y;
+                cbr[m][a][2] = v.z;
+                cbr[m][a][3] = v.w;
             }
     }
 
-    // tape of this block's sequences: slot sq at sq * slot_bytes; [n+1][G] R~, [n+1][G] Q, [n] normalisers
+    // tape of this block's sequences: slot sq at sq * slot_bytes; [n+1][G] R~, [n+1][G] Q^, then per step the
+    // normaliser N_t and the offset K_{t-1} of Q^_t (true Q_t = Q^_t + K_{t-1})
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * SPB * args.slot_bytes, SPB * slot_bytes);
     const uint32_t v_quad = sq * slot_bytes + 16u * tau;
     const uint32_t v_grp = sq * slot_bytes + 4u * tau;
     const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
     const uint32_t nrm_base = 2u * q_base;
+    const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
@@ -109,9 +114,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         }
         lds_barrier();
 
-        float N = 0.f;
         double A = 0.0;
-        float N_last = 0.f;
+        float N = 0.f;
+        float kq = 0.f;       // kappa_t: Q^_t at the most likely group of R~_t, subtracted on input
+        float K = 0.f;        // K_{t-1} = sum of the kappas applied so far
+        float N_last = 0.f, K_last = 0.f;
         for (int t = 0; t < n; ++t) {
             float rin[QPT][4], qin[QPT][4];
 #pragma unroll
@@ -119,19 +126,25 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     rin[m][a] = mr[tau + TPS * m + Q * a];
-                    qin[m][a] = mq[tau + TPS * m + Q * a];
+                    qin[m][a] = mq[tau + TPS * m + Q * a] - kq;
                 }
             lds_barrier();   // every input read before any output overwrites it
+            if (tau == 0) {
+                buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
+                buf_st(K, tape, sq * slot_bytes, kq_base + 4u * t);
+            }
+            K_last = K;
+            K += kq;
             const float wt = wb[t] * scale;
             const float gt = gb[t] * inv_scale;
-            float lmax = -3.0e38f;
+            float lmax = -3.0e38f, lq = 0.f;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
                 const int j = tau + TPS * m;
-                const float4 c0 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 0);
-                const float4 c1 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 1);
-                const float4 c2 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 2);
-                const float4 c3 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, 3);
+                const float4 c0 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 0);
+                const float4 c1 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 1);
+                const float4 c2 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 2);
+                const float4 c3 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 3);
                 const float cv[4][4] = {{c0.x, c0.y, c0.z, c0.w}, {c1.x, c1.y, c1.z, c1.w},
                                         {c2.x, c2.y, c2.z, c2.w}, {c3.x, c3.y, c3.z, c3.w}};
                 float ro[4], qo[4];
@@ -140,7 +153,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     float x[4], z[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
-                        const float d = cv[a][i] - wt;
+                        const float d = fmaf(cv[a][i], scale, -wt);
                         x[a] = fmaf(-d, d, rin[m][a]);
                         z[a] = fmaf(gt, d, qin[m][a]);
                     }
@@ -149,10 +162,13 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const float s = (e0 + e1) + (e2 + e3);
                     ro[i] = (mx - N) + lg2(s);
                     qo[i] = fmaf(e0, z[0], fmaf(e1, z[1], fmaf(e2, z[2], e3 * z[3]))) * rcp(s);
+                    const bool up = ro[i] > lmax;
+                    lmax = up ? ro[i] : lmax;
+                    lq = up ? qo[i] : lq;
                     pin_order(ro[i], qo[i]);
+                    pin_order(lmax, lq);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-                lmax = fmaxf(lmax, max4(ro[0], ro[1], ro[2], ro[3]));
                 const float4 r4 = make_float4(ro[0], ro[1], ro[2], ro[3]);
                 const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
                 *reinterpret_cast<float4*>(mr + 4 * j) = r4;
@@ -160,20 +176,34 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 buf_st4(r4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
                 buf_st4(q4, tape, v_quad, q_base + (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
             }
-            if (tau == 0) buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
-            lmax = seg_max_fast<SEG>(lmax);
+            seg_argmax_payload<SEG>(lmax, lq);
             if constexpr (WPS > 1) {
-                if (lane == 0) redmax[t & 1][sq][wv] = lmax;
+                if (lane == 0) {
+                    redmax[t & 1][sq][wv] = lmax;
+                    redq[t & 1][sq][wv] = lq;
+                }
             }
             lds_barrier();
             if constexpr (WPS > 1) {
+                float bm = redmax[t & 1][sq][0], bq = redq[t & 1][sq][0];
 #pragma unroll
-                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+                for (int q = 1; q < WPS; ++q) {
+                    const float vm = redmax[t & 1][sq][q];
+                    const bool up = vm > bm;
+                    bm = up ? vm : bm;
+                    bq = up ? redq[t & 1][sq][q] : bq;
+                }
+                lmax = bm;
+                lq = bq;
             }
-            if constexpr (SPB == 1) lmax = uniform_f(lmax);
+            if constexpr (SPB == 1) {
+                lmax = uniform_f(lmax);
+                lq = uniform_f(lq);
+            }
             A += (double)N;
             N_last = N;
             N = lmax;
+            kq = lq;
         }
         // rz = log2 Z - A_n and E[F] (which centres the covariance of the backward pass)
         float rz, EF;
@@ -204,16 +234,16 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 }
             }
             rz = N + lg2(z0);
-            EF = z1 / z0;
+            EF = z1 / z0 + K;   // the final outputs Q^_n carry the offset K_{n-1}
             __syncthreads();   // tape writes of the forward pass visible to every thread of the block
         } else {
             // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
             __syncthreads();
-            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float r = buf_ld(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
             const float q = buf_ld(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
-            EF = fmaf(gb[n - 1] * inv_scale, d, q);
+            EF = fmaf(gb[n - 1] * inv_scale, d, q + K_last);   // Q^_{n-1} carries the offset K_{n-2}
         }
         const bool valid = rz > 0.5f * kNeg;
 
@@ -221,6 +251,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         float Nb = 0.f;
         float C = 0.f;
         float D = 0.f;
+        float kb = 0.f;   // kappa_{t+1} = g_{t+1} (w_soft_{t+1} - w_{t+1}), subtracted from the P^ inputs
+        float H = 0.f;    // sum of the kappas of the steps after t
         int t = n - 1;
         if (!has_sigma) {
 #pragma unroll
@@ -232,8 +264,9 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
         } else {
             // s_n = sigma: posterior at n-1 is the indicator of sigma (so grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
-            // the messages left are B_{n-2}(sigma >> 2) = theta_{n-1}(sigma), P_{n-2}(sigma >> 2) = g (c(sigma) - w)
-            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            // the messages left are B_{n-2}(sigma >> 2) = theta_{n-1}(sigma), P^_{n-2}(sigma >> 2) = g (c(sigma) - w),
+            // and kappa_{n-1} = g (c(sigma) - w) as well
+            const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float th = -d * d;
             const float pz = gb[n - 1] * inv_scale * d;
 #pragma unroll
@@ -250,6 +283,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
             D = N_last;
             Nb = th;
+            kb = pz;
+            H = pz;
             t = n - 2;
         }
         lds_barrier();
@@ -261,15 +296,21 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 const float4 v = *reinterpret_cast<const float4*>(mr + 4 * (tau + TPS * m));
                 const float4 p = *reinterpret_cast<const float4*>(mq + 4 * (tau + TPS * m));
                 bin[m][0] = v.x; bin[m][1] = v.y; bin[m][2] = v.z; bin[m][3] = v.w;
-                pin[m][0] = p.x; pin[m][1] = p.y; pin[m][2] = p.z; pin[m][3] = p.w;
+                pin[m][0] = p.x - kb; pin[m][1] = p.y - kb; pin[m][2] = p.z - kb; pin[m][3] = p.w - kb;
             }
             lds_barrier();
             const float wt = wb[t] * scale;
             const float gt = gb[t] * inv_scale;
             float Nt = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
-            if constexpr (SPB == 1) Nt = uniform_f(Nt);
+            float Kt = buf_ld(tape, sq * slot_bytes, kq_base + 4u * t);
+            if constexpr (SPB == 1) {
+                Nt = uniform_f(Nt);
+                Kt = uniform_f(Kt);
+            }
             D += Nt;
             const float ref = (rz + D) - C;
+            // E[F | s_t = s] - E[F] = Q^_t(s >> 2) + cst + g_t (c(s) - w_t) + P''_t(s & (G-1)), cst per step
+            const float cst = (Kt - EF) + H;
             float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
@@ -277,9 +318,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 for (int a = 0; a < 4; ++a) {
                     const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
                     const float rt = buf_ld(tape, v_grp, so);
-                    const float qt = buf_ld(tape, v_grp, q_base + so) - EF;
-                    const float4 cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, scale, m, a);
-                    const float d0 = cr.x - wt, d1 = cr.y - wt, d2 = cr.z - wt, d3 = cr.w - wt;
+                    const float qt = buf_ld(tape, v_grp, q_base + so) + cst;
+                    const float4 cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                    const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
+                    const float d2 = fmaf(cr.z, scale, -wt), d3 = fmaf(cr.w, scale, -wt);
                     const float y0 = fmaf(-d0, d0, bin[m][0]), y1 = fmaf(-d1, d1, bin[m][1]);
                     const float y2 = fmaf(-d2, d2, bin[m][2]), y3 = fmaf(-d3, d3, bin[m][3]);
                     const float z0 = fmaf(gt, d0, pin[m][0]), z1 = fmaf(gt, d1, pin[m][1]);
@@ -290,13 +332,17 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const float ez = fmaf(e0, z0, fmaf(e1, z1, fmaf(e2, z2, e3 * z3)));
                     const float ed0 = e0 * d0, ed1 = e1 * d1, ed2 = e2 * d2, ed3 = e3 * d3;
                     const float ed = (ed0 + ed1) + (ed2 + ed3);
-                    const float edz = fmaf(ed0, z0, fmaf(ed1, z1, fmaf(ed2, z2, ed3 * z3)));
+                    // E[F | s] - E[F] per state, formed before any product: its two parts nearly cancel at the
+                    // likely states, and multiplying them separately would keep their rounding
+                    const float r0 = z0 + qt, r1 = z1 + qt, r2 = z2 + qt, r3 = z3 + qt;
+                    const float er = fmaf(e0, r0, fmaf(e1, r1, fmaf(e2, r2, e3 * r3)));
+                    const float edr = fmaf(ed0, r0, fmaf(ed1, r1, fmaf(ed2, r2, ed3 * r3)));
                     const float out = (mx - Nb) + lg2(s);
                     const float f = ex2((mx + rt) - ref);
                     S0 = fmaf(f, s, S0);
                     S1 = fmaf(f, ed, S1);
-                    S2 = fmaf(f, fmaf(qt, s, ez), S2);
-                    S3 = fmaf(f, fmaf(qt, ed, edz), S3);
+                    S2 = fmaf(f, er, S2);
+                    S3 = fmaf(f, edr, S3);
                     lmax = fmaxf(lmax, out);
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
                     mr[u] = out;            // at t = 0 these land in buffers nobody reads
@@ -319,28 +365,31 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
             lds_barrier();
             if constexpr (WPS > 1) {
+                S0 = S1 = S2 = S3 = 0.f;
 #pragma unroll
-                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
-                if (tau == 0) {
-                    S0 = S1 = S2 = S3 = 0.f;
-#pragma unroll
-                    for (int q = 0; q < WPS; ++q) {
-                        const float4 p = redsum[t & 1][sq][q];
-                        S0 += p.x;
-                        S1 += p.y;
-                        S2 += p.z;
-                        S3 += p.w;
-                    }
+                for (int q = 0; q < WPS; ++q) {
+                    lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+                    const float4 p = redsum[t & 1][sq][q];
+                    S0 += p.x;
+                    S1 += p.y;
+                    S2 += p.z;
+                    S3 += p.w;
                 }
             }
-            if constexpr (SPB == 1) lmax = uniform_f(lmax);
+            const float i0 = 1.0f / S0;
+            const float m1 = S1 * i0;   // w_soft_t - w_t in scaled codebook units
             if (tau == 0 && active) {
-                const float i0 = 1.0f / S0;
-                const float m1 = S1 * i0, m2 = S2 * i0;
+                const float m2 = S2 * i0;
                 const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' in scaled units
                 args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
                 if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
             }
+            kb = gt * m1;
+            if constexpr (SPB == 1) {
+                lmax = uniform_f(lmax);
+                kb = uniform_f(kb);
+            }
+            H += kb;
             C += Nb;
             Nb = lmax;
         }

@@ -9,7 +9,8 @@
 //   backward  B~_{t-1}(u) = logsumexp_b[ theta_t(4u + b)         + B~_t((4u + b) & (G-1)) ] - N'_t
 //   posterior p_t(s) = 2^( theta_t(s) + R~_t(s >> 2) + B~_t(s & (G-1)) - ref_t ),  w_soft_t = sum_s c(s) p_t(s)
 //
-// All logs are base 2: theta_t(s) = -(c'(s) - w'_t)^2 with c' = c sqrt(log2 e / T), w' = w sqrt(log2 e / T).
+// All logs are base 2: theta_t(s) = -(c(s) k - w'_t)^2 with k = sqrt(log2 e / T), w' = w k, the difference formed by
+// one fused multiply-add so that each state's log-weight carries a single rounding.
 // N_t, N'_t are per-step normalisers (the max of the incoming message), so messages stay within one step's
 // emission range of 0.  With A_t = sum_{tau<t} N_tau and C_t = sum_{tau>t} N'_tau, ref_t = log2 Z - A_t - C_t makes
 // sum_s p_t(s) = 1 without a second pass; any error in ref_t cancels in the ratio that gives w_soft_t.
@@ -44,7 +45,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
     const float scale = args.scale;
     const float inv_scale = 1.0f / scale;
 
-    // codebook c'(s) for this thread's quads, s = a << (L-2) | j << 2 | i
+    // codebook c(s) for this thread's quads, s = a << (L-2) | j << 2 | i, unscaled: the scaled difference is formed
+    // as fma(c, sqrt(log2 e / T), -w'), which rounds once per state instead of rounding c' first
     float cb[QPT][4][4];
 #pragma unroll
     for (int m = 0; m < QPT; ++m) {
@@ -52,10 +54,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const float4 v = *reinterpret_cast<const float4*>(args.cb + (a << (L - 2)) + 4 * j);
-            cb[m][a][0] = v.x * scale;
-            cb[m][a][1] = v.y * scale;
-            cb[m][a][2] = v.z * scale;
-            cb[m][a][3] = v.w * scale;
+            cb[m][a][0] = v.x;
+            cb[m][a][1] = v.y;
+            cb[m][a][2] = v.z;
+            cb[m][a][3] = v.w;
         }
     }
 
@@ -110,7 +112,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     float x[4];
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
-                        const float d = cb[m][a][i] - wt;
+                        const float d = fmaf(cb[m][a][i], scale, -wt);
                         x[a] = fmaf(-d, d, r[a]);
                     }
                     const float mx = max4(x[0], x[1], x[2], x[3]);
@@ -162,7 +164,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             rz = N + lg2(part);
         } else {
             const float* ml = ((n - 1) & 1) ? msg1 : msg0;
-            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float r = ml[sig >> 2];
             lds_barrier();
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma, and the only finite message left is
             // B_{n-2}(sigma >> 2) = theta_{n-1}(sigma)
             float* mi = ((n - 2) & 1) ? msg1 : msg0;
-            const float d = args.cb[sig] * scale - wb[n - 1] * scale;
+            const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float th = -d * d;
             if (n > 1) {
 #pragma unroll
@@ -234,8 +236,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                 const float4 bq = *reinterpret_cast<const float4*>(mc + 4 * j);
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const float d0 = cb[m][a][0] - wt, d1 = cb[m][a][1] - wt;
-                    const float d2 = cb[m][a][2] - wt, d3 = cb[m][a][3] - wt;
+                    const float d0 = fmaf(cb[m][a][0], scale, -wt), d1 = fmaf(cb[m][a][1], scale, -wt);
+                    const float d2 = fmaf(cb[m][a][2], scale, -wt), d3 = fmaf(cb[m][a][3], scale, -wt);
                     const float y0 = fmaf(-d0, d0, bq.x), y1 = fmaf(-d1, d1, bq.y);
                     const float y2 = fmaf(-d2, d2, bq.z), y3 = fmaf(-d3, d3, bq.w);
                     const float mx = max4(y0, y1, y2, y3);

@@ -153,6 +153,30 @@ __device__ __forceinline__ float seg_sum_fast(float x) {
     else return seg_sum<SEG>(x);
 }
 
+// (max of v, q of the lowest lane attaining it) over the SEG lanes of one sequence inside a wave.
+template <int SEG>
+__device__ __forceinline__ void seg_argmax_payload(float& v, float& q) {
+    if constexpr (SEG == 64) {
+        const float m = wave_max64(v);
+        const uint64_t hit = __ballot(v == m);
+        const int src = __builtin_ctzll(hit);
+        q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q), src));
+        v = m;
+    } else {
+        int lane = (int)(threadIdx.x & 63);
+#pragma unroll
+        for (int o = 1; o < SEG; o <<= 1) {
+            const float v2 = __shfl_xor(v, o);
+            const float q2 = __shfl_xor(q, o);
+            const int l2 = __shfl_xor(lane, o);
+            const bool take = (v2 > v) || (v2 == v && l2 < lane);
+            v = take ? v2 : v;
+            q = take ? q2 : q;
+            lane = take ? l2 : lane;
+        }
+    }
+}
+
 // Wave-uniform value into a scalar register (only valid when every lane holds the same value).
 __device__ __forceinline__ float uniform_f(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x)));
@@ -176,9 +200,13 @@ __device__ __forceinline__ float4 buf_ld4(rsrc_t r, uint32_t voff, uint32_t soff
 __device__ __forceinline__ void buf_st(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);
 }
+// A store wider than 8 bytes reads its data VGPRs after issue, so a VALU write to them in the next cycle can reach
+// memory instead of the stored value (seen here as the first dword of a 16-byte tape store changing from run to
+// run while the store queue was full).  The compiler inserts the required wait state only for stores whose SGPR
+// offset field is not a register, so the whole offset goes through the VGPR and the SGPR offset stays literal 0.
 __device__ __forceinline__ void buf_st4(float4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
-                                           voff, soff, 0);
+                                           voff + soff, 0, 0);
 }
 
 // Per-slot workspace layout (bytes), shared by the host planner and the kernels.

@@ -28,7 +28,7 @@
  *     frees nothing, keeps no state between calls and never synchronizes: the work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
  *     Calls on different streams need different workspaces.
- *   - supported shapes: k == 2, 4 <= L <= 16, 1 <= n <= 8192, 1 <= B <= 2^31 - 1.
+ *   - supported shapes: k == 2, 4 <= L <= 16, 1 <= n <= 4096, 1 <= B <= 2^31 - 1.
  *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
  *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
  *     into that sequence's outputs.
@@ -46,7 +46,7 @@ extern "C" {
 enum {
     BCJR_OK = 0,
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
-    BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 8192, k < 1, L < 2k or L > 16 */
+    BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
     BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2 */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */

@@ -64,7 +64,7 @@ def test_workspace_bytes_formula(L, B, n):
     msgs = _a256((n + 1) * G * 4)
     nrm = _a256(n * 4)
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm)
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + nrm)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + 2 * nrm)
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, B, n, L, 2) == slots * _a256(2 * n * TPS * 4)
 
 
@@ -73,7 +73,7 @@ def test_workspace_bytes_for_the_headline_workload():
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4096, 256, 16, 2) == 256 * (257 * 65536 + 1024)
 
 
-@pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 8193, 8, 2), (1, 4, 3, 2),
+@pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 4097, 8, 2), (1, 4, 3, 2),
                                   (1, 4, 17, 2), (1, 4, 8, 0), (1 << 31, 4, 8, 2)])
 def test_workspace_bytes_invalid_shapes_are_zero(args):
     for op in (0, 1, 2):
@@ -117,7 +117,7 @@ def test_null_pointers_rejected():
     assert _vit(codebook=None) == abi.BCJR_ERR_NULL
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=8193), dict(L=3), dict(L=17), dict(k=0), dict(L=4, k=3)])
+@pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=4097), dict(L=3), dict(L=17), dict(k=0), dict(L=4, k=3)])
 def test_bad_shapes_rejected(kw):
     assert _soft(**kw) == abi.BCJR_ERR_SHAPE
     assert _grad(**kw) == abi.BCJR_ERR_SHAPE
@@ -170,3 +170,12 @@ def test_python_wrapper_refuses_cpu_tensors():
         dba.soft_codeword(w, c, 8)
     with pytest.raises(TypeError):
         dba.viterbi_hard_code(w, c, 8)
+
+
+def test_largest_shape_keeps_workspace_offsets_in_32_bits():
+    # the kernels address one block's slots with 32-bit buffer offsets
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+        for L in (8, 12, 16):
+            G, TPS, SPB = _geo(L)
+            per_block = abi.bcjr_workspace_bytes(op, SPB, 4096, L, 2)
+            assert 0 < per_block < 2 ** 31
