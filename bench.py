@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the BCJR soft-quantizer hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic weights, inputs resident in HBM:
+
+  1. bcjr_soft_codeword       temperature-T forward-backward over the bitshift trellis -> soft codeword, ln Z
+  2. bcjr_soft_codeword_grad  the exact gradient w.r.t. the weights (expectation semiring), upstream grad ~ N(0,1)
+  3. viterbi_hard_code        the T -> 0 limit: minimum-energy path, its codeword and cost
+
+(BCJR-QAT, arXiv 2605.10655: abstract; gist.science Technical Summary, "Core Mechanism" and "Key Technical
+Innovations".)  The default workload is a 1024x1024 Gaussian matrix cut into 4096 sequences of 256 weights on the
+L = 16, k = 2 trellis (65536 states), T = 0.1, free boundary.
+
+Counting.  A state-update is one trellis state at one step in one direction: the soft and gradient passes do
+2 * B * n * 2^L each (forward and backward), Viterbi B * n * 2^L (its traceback touches one state per step).
+``value`` is the step's state-updates per second; ``weights_per_s`` is B * n per step time.
+
+The roofline object covers the step's longest kernel.  Its bound is VALU issue: the work per state-step is counted in
+full-rate fp32 VALU lane slots, a transcendental (v_exp/v_log/v_rcp, quarter rate) costing 4, and the peak is
+256 CUs x 128 fp32 lanes x 2.4 GHz = 78.6e12 slots/s (the published 157.3 TFLOP/s fp32 vector rate with an FMA as
+two flops).  Kernel times come from HIP events recorded on the stream the kernels run on.
+
+``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+# fp32 VALU lane slots per state-step (one state, one step), transcendental = 4 slots.  The per-state operation
+# counts of each pass in the grouped-message form (one log-sum-exp of 4 per group of 4 states):
+#   soft    forward 5 VALU + 1.25 trans; backward 5 + 1.25; posterior 2 + 0.25        -> 12 VALU + 2.75 trans
+#   grad    forward 8 VALU + 1.5 trans (adds the Q message); backward 14.75 + 1.75    -> 22.75 VALU + 3.25 trans
+#   viterbi sub, mul, add, 0.75 min-compare + 0.75 select + 0.5 back-pointer packing  -> 5.5 VALU
+TRANS_SLOTS = 4.0
+ALU_SLOTS = {
+    "soft": 12.0 + 2.75 * TRANS_SLOTS,
+    "grad": 22.75 + 3.25 * TRANS_SLOTS,
+    "viterbi": 5.5,
+}
+DIRECTIONS = {"soft": 2, "grad": 2, "viterbi": 1}
+PEAK_SLOTS_PER_S = 256 * 128 * 2.4e9
+KERNEL_SOURCES = {
+    "soft": ["soft.hip"],
+    "grad": ["grad.hip"],
+    "viterbi": ["viterbi.hip"],
+}
+COMMON_SOURCES = ["trellis.hpp", "kernel_args.hpp"]
+KERNEL_NAMES = {"soft": "soft_kernel<16>", "grad": "grad_kernel<16>", "viterbi": "viterbi_kernel<16>"}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 4, 5],
+                    help="synthetic workload (2: 1024x1024 matrix, 3: 8192x2048, 4: 2048x2048, 5: whole layer)")
+    ap.add_argument("--temperature", type=float, default=0.1)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
+    return ap.parse_args()
+
+
+def source_digest(op: str) -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "differentiable_bcjr_amd", "csrc")
+    for f in KERNEL_SOURCES[op] + COMMON_SOURCES:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(op: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{op}_kernel_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                key, val = line[2:].split(":", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("source_sha256") != source_digest(op):
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, T, n_rows_per_thread=4):
+    """The oracle (plain fp64 C, OpenMP over sequences) on a bounded sample of the same workload and step."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    threads = oracle.num_threads()
+    rows = wl.sample_rows(max(4, n_rows_per_thread * threads))
+    c = wl.codebook()
+    w = wl.weights()[rows]
+    g = wl.upstream_grad()[rows]
+    t0 = time.perf_counter()
+    oracle.soft(w, c, wl.L, wl.k, T)
+    oracle.grad(w, c, g, wl.L, wl.k, T)
+    oracle.viterbi(w, c, wl.L, wl.k)
+    dt = time.perf_counter() - t0
+    S = 1 << wl.L
+    upd = sum(DIRECTIONS.values()) * len(rows) * wl.n * S
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(rows)} of the {wl.B} sequences (rows 0 and B-1 included, seed {4000 + wl.cfg}), "
+                      f"one full step (soft + grad + viterbi), {dt:.1f} s, weights/s {len(rows) * wl.n / dt:.3g}",
+            "weights_per_s": len(rows) * wl.n / dt}
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): sequences are "
+              "independent, so more GPUs would shard the batch with no exchange; no multi-GPU figure is produced.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from differentiable_bcjr_amd import abi
+
+    abi.load()   # fails loudly if the HIP library has not been built
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[args.workload]
+    B, n, L, k, T = wl.B, wl.n, wl.L, wl.k, float(args.temperature)
+    S = 1 << L
+
+    c = torch.from_numpy(wl.codebook()).to(dev)
+    w = torch.from_numpy(wl.weights()).to(dev)
+    g = torch.from_numpy(wl.upstream_grad()).to(dev)
+    w_soft = torch.empty((B, n), dtype=torch.float32, device=dev)
+    log_z = torch.empty((B,), dtype=torch.float32, device=dev)
+    grad = torch.empty((B, n), dtype=torch.float32, device=dev)
+    states = torch.empty((B, n), dtype=torch.int32, device=dev)
+    w_hard = torch.empty((B, n), dtype=torch.float32, device=dev)
+    cost = torch.empty((B,), dtype=torch.float32, device=dev)
+    ws_bytes = max(abi.bcjr_workspace_bytes(op, B, n, L, k) for op in (0, 1, 2))
+    ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: {abi.bcjr_status_string(rc)}")
+
+    def soft():
+        check(abi.bcjr_soft_codeword(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, w_soft.data_ptr(),
+                                     log_z.data_ptr(), ws.data_ptr(), ws_bytes, sp), "bcjr_soft_codeword")
+
+    def grad_op():
+        check(abi.bcjr_soft_codeword_grad(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, g.data_ptr(),
+                                          grad.data_ptr(), None, ws.data_ptr(), ws_bytes, sp),
+              "bcjr_soft_codeword_grad")
+
+    def viterbi():
+        check(abi.viterbi_hard_code(w.data_ptr(), c.data_ptr(), B, n, L, k, None, states.data_ptr(),
+                                    w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws_bytes, sp),
+              "viterbi_hard_code")
+
+    ops = [("soft", soft), ("grad", grad_op), ("viterbi", viterbi)]
+
+    if args.copy_calibration:
+        # a plain copy of 1 GiB: reads 2^30 bytes and writes 2^30 bytes once each
+        src = torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("copy calibration: one device copy of 1073741824 bytes", file=sys.stderr, flush=True)
+        del src, dst
+
+    for _ in range(args.warmup):
+        for _, f in ops:
+            f()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        ev = events[s]
+        ev[0].record(stream)
+        for i, (_, f) in enumerate(ops):
+            f()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    per_op = {}
+    for i, (name, _) in enumerate(ops):
+        ms = float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(K)]))
+        upd = DIRECTIONS[name] * B * n * S
+        slots = ALU_SLOTS[name] * B * n * S
+        per_op[name] = {"kernel": KERNEL_NAMES[name], "ms": round(ms, 4), "state_updates_per_s": upd / (ms * 1e-3),
+                        "weights_per_s": B * n / (ms * 1e-3),
+                        "alu_frac": slots / (ms * 1e-3) / PEAK_SLOTS_PER_S}
+    dom = max(per_op, key=lambda o: per_op[o]["ms"])
+    d = per_op[dom]
+    achieved = ALU_SLOTS[dom] * B * n * S / (d["ms"] * 1e-3) / 1e12
+    peak = PEAK_SLOTS_PER_S / 1e12
+    roofline = {"bound": "alu", "kernel": d["kernel"], "achieved": round(achieved, 3), "peak": round(peak, 3),
+                "unit": "T VALU-slots/s", "frac": round(achieved / peak, 4),
+                "traffic": recorded_traffic(dom, wl.name),
+                "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (transcendental = 4)",
+                "units_per_launch": B * n * S}
+
+    total_upd = sum(DIRECTIONS[o] for o, _ in ops) * B * n * S
+    line = {
+        "metric": "trellis state-updates/sec and weights/sec, BCJR fwd+bwd, L=16 k=2 n=256",
+        "value": total_upd / (ms_per_step * 1e-3),
+        "unit": "state-updates/s",
+        "weights_per_s": B * n / (ms_per_step * 1e-3),
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "matrix": wl.matrix, "L": L, "k": k, "B": B, "n": n, "T": T,
+                   "boundary": "free", "step": "soft + grad + viterbi"},
+        "ops": per_op,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, T)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
