@@ -58,8 +58,12 @@ Plan make_plan(int op, int64_t B, int64_t n, int L) {
     const size_t msgs = (size_t)(n + 1) * (size_t)g.G * 4;   // one float per group per step (+1 spare row)
     const size_t nrm = (size_t)n * 4;                         // one normaliser per step
     switch (op) {
-        case BCJR_OP_SOFT: p.slot_bytes = align256(msgs) + align256(nrm); break;
-        case BCJR_OP_GRAD: p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm); break;
+        case BCJR_OP_SOFT:   // + per-wave (S0, S1) of every step when a sequence spans several waves
+            p.slot_bytes = align256(msgs) + align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 8) : 0);
+            break;
+        case BCJR_OP_GRAD:   // + per-wave (S0..S3) of every step when a sequence spans several waves
+            p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0);
+            break;
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
     }
     p.total = (size_t)p.slots * p.slot_bytes;

@@ -27,6 +27,20 @@
 
 namespace bcjr {
 
+// Groups of 4 states whose work the scheduler may interleave between two scheduling barriers (forward, backward).
+#ifndef BCJR_GRAD_FWD_GROUPS
+#define BCJR_GRAD_FWD_GROUPS 1
+#endif
+#ifndef BCJR_GRAD_BWD_GROUPS
+#define BCJR_GRAD_BWD_GROUPS 1
+#endif
+constexpr int kGradFwdGroups = BCJR_GRAD_FWD_GROUPS;
+constexpr int kGradBwdGroups = BCJR_GRAD_BWD_GROUPS;
+#ifndef BCJR_GRAD_PREFETCH
+#define BCJR_GRAD_PREFETCH 1
+#endif
+constexpr bool kGradPrefetch = BCJR_GRAD_PREFETCH != 0;
+
 // Codebook row c(a << (L-2) | j << 2 | 0..3) of quad m (unscaled): from registers, or through L1/L2.
 template <int L, int TPS, bool CB_REG, int M>
 __device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs, uint32_t v_cb, int m, int a) {
@@ -48,6 +62,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     __shared__ float redmax[2][SPB][WPS];
     __shared__ float redq[2][SPB][WPS];
     __shared__ float4 redsum[2][SPB][WPS];
+    __shared__ float2 redsum2[2][SPB][WPS];
 
     const int tid = threadIdx.x;
     const int sq = tid / TPS;
@@ -86,6 +101,9 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
     const uint32_t nrm_base = 2u * q_base;
     const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
+    // with several waves per sequence, each wave's (S0, S1, S2, S3) of every step goes here and the outputs are
+    // formed after the backward pass; only (S0, S1) is reduced across waves inside the loop (for the P offset)
+    const uint32_t part_base = kq_base + (uint32_t)align256((size_t)n * 4);
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
@@ -119,6 +137,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         float kq = 0.f;       // kappa_t: Q^_t at the most likely group of R~_t, subtracted on input
         float K = 0.f;        // K_{t-1} = sum of the kappas applied so far
         float N_last = 0.f, K_last = 0.f;
+        float4 fc[4];   // codebook rows of the next quad, when they come from memory
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            fc[a] = (kGradPrefetch && !CB_REG) ? cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, a) : make_float4(0.f, 0.f, 0.f, 0.f);
         for (int t = 0; t < n; ++t) {
             float rin[QPT][4], qin[QPT][4];
 #pragma unroll
@@ -141,10 +163,18 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
                 const int j = tau + TPS * m;
-                const float4 c0 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 0);
-                const float4 c1 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 1);
-                const float4 c2 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 2);
-                const float4 c3 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 3);
+                float4 c0, c1, c2, c3;
+                if constexpr (kGradPrefetch && !CB_REG) {
+                    c0 = fc[0]; c1 = fc[1]; c2 = fc[2]; c3 = fc[3];
+                    const int m2 = (m + 1) % QPT;   // the last quad fetches the next step's first
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) fc[a] = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a);
+                } else {
+                    c0 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 0);
+                    c1 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 1);
+                    c2 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 2);
+                    c3 = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, 3);
+                }
                 const float cv[4][4] = {{c0.x, c0.y, c0.z, c0.w}, {c1.x, c1.y, c1.z, c1.w},
                                         {c2.x, c2.y, c2.z, c2.w}, {c3.x, c3.y, c3.z, c3.w}};
                 float ro[4], qo[4];
@@ -165,9 +195,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const bool up = ro[i] > lmax;
                     lmax = up ? ro[i] : lmax;
                     lq = up ? qo[i] : lq;
-                    pin_order(ro[i], qo[i]);
-                    pin_order(lmax, lq);
-                    __builtin_amdgcn_sched_barrier(0);
+                    if ((i + 1) % kGradFwdGroups == 0) {
+                        pin_order(ro[i], qo[i]);
+                        pin_order(lmax, lq);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
                 const float4 r4 = make_float4(ro[0], ro[1], ro[2], ro[3]);
                 const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
@@ -289,6 +321,22 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         }
         lds_barrier();
 
+        // loads of the next group (forward messages R~, Q^ of this step, codebook row) are issued one group ahead
+        float rt_n = 0.f, qt_n = 0.f;
+        float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (kGradPrefetch && t >= 0) {
+            rt_n = buf_ld(tape, v_grp, (uint32_t)t * (G * 4u));
+            qt_n = buf_ld(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
+            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+        }
+        const int t_out = t;   // last step whose outputs the loop below produces
+        float w_nx = 0.f, g_nx = 0.f, N_nx = 0.f, K_nx = 0.f;
+        if (t >= 0) {
+            w_nx = wb[t];
+            g_nx = gb[t];
+            N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
+            K_nx = buf_ld(tape, sq * slot_bytes, kq_base + 4u * t);
+        }
         for (; t >= 0; --t) {
             float bin[QPT][4], pin[QPT][4];
 #pragma unroll
@@ -299,10 +347,15 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 pin[m][0] = p.x - kb; pin[m][1] = p.y - kb; pin[m][2] = p.z - kb; pin[m][3] = p.w - kb;
             }
             lds_barrier();
-            const float wt = wb[t] * scale;
-            const float gt = gb[t] * inv_scale;
-            float Nt = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
-            float Kt = buf_ld(tape, sq * slot_bytes, kq_base + 4u * t);
+            const float wt = w_nx * scale;
+            const float gt = g_nx * inv_scale;
+            float Nt = N_nx, Kt = K_nx;
+            if (t > 0) {   // the next step's weight, upstream gradient and forward scalars, one step ahead
+                w_nx = wb[t - 1];
+                g_nx = gb[t - 1];
+                N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
+                K_nx = buf_ld(tape, sq * slot_bytes, kq_base + 4u * (t - 1));
+            }
             if constexpr (SPB == 1) {
                 Nt = uniform_f(Nt);
                 Kt = uniform_f(Kt);
@@ -316,10 +369,32 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             for (int m = 0; m < QPT; ++m) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
-                    const float rt = buf_ld(tape, v_grp, so);
-                    const float qt = buf_ld(tape, v_grp, q_base + so) + cst;
-                    const float4 cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                    float rt, qt;
+                    float4 cr;
+                    if constexpr (kGradPrefetch) {
+                        rt = rt_n;
+                        qt = qt_n + cst;
+                        if constexpr (CB_REG) cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                        else cr = cr_n;
+                        const bool last = (m == QPT - 1) && (a == 3);
+                        const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
+                        if (!last) {
+                            const uint32_t so2 = (uint32_t)t * (G * 4u) + 4u * (TPS * m2 + Q * a2);
+                            rt_n = buf_ld(tape, v_grp, so2);
+                            qt_n = buf_ld(tape, v_grp, q_base + so2);
+                            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
+                        } else if (t > 0) {
+                            const uint32_t so2 = (uint32_t)(t - 1) * (G * 4u);
+                            rt_n = buf_ld(tape, v_grp, so2);
+                            qt_n = buf_ld(tape, v_grp, q_base + so2);
+                            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+                        }
+                    } else {
+                        const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
+                        rt = buf_ld(tape, v_grp, so);
+                        qt = buf_ld(tape, v_grp, q_base + so) + cst;
+                        cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                    }
                     const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
                     const float d2 = fmaf(cr.z, scale, -wt), d3 = fmaf(cr.w, scale, -wt);
                     const float y0 = fmaf(-d0, d0, bin[m][0]), y1 = fmaf(-d1, d1, bin[m][1]);
@@ -347,9 +422,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
                     mr[u] = out;            // at t = 0 these land in buffers nobody reads
                     mq[u] = ez * rcp(s);
-                    pin_order(S0, S1, lmax);
-                    pin_order(S2, S3);
-                    __builtin_amdgcn_sched_barrier(0);
+                    if ((a + 1) % kGradBwdGroups == 0) {
+                        pin_order(S0, S1, lmax);
+                        pin_order(S2, S3);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
             lmax = seg_max_fast<SEG>(lmax);
@@ -359,30 +436,32 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             S3 = seg_sum_fast<SEG>(S3);
             if constexpr (WPS > 1) {
                 if (lane == 0) {
-                    redsum[t & 1][sq][wv] = make_float4(S0, S1, S2, S3);
+                    redsum2[t & 1][sq][wv] = make_float2(S0, S1);
                     redmax[t & 1][sq][wv] = lmax;
+                    buf_st4(make_float4(S0, S1, S2, S3), tape, sq * slot_bytes,
+                            part_base + 16u * (uint32_t)(t * WPS + wv));
                 }
             }
             lds_barrier();
             if constexpr (WPS > 1) {
-                S0 = S1 = S2 = S3 = 0.f;
+                S0 = S1 = 0.f;
 #pragma unroll
                 for (int q = 0; q < WPS; ++q) {
                     lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
-                    const float4 p = redsum[t & 1][sq][q];
+                    const float2 p = redsum2[t & 1][sq][q];
                     S0 += p.x;
                     S1 += p.y;
-                    S2 += p.z;
-                    S3 += p.w;
                 }
             }
             const float i0 = 1.0f / S0;
             const float m1 = S1 * i0;   // w_soft_t - w_t in scaled codebook units
-            if (tau == 0 && active) {
-                const float m2 = S2 * i0;
-                const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' in scaled units
-                args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
-                if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
+            if constexpr (WPS == 1) {
+                if (tau == 0 && active) {
+                    const float m2 = S2 * i0;
+                    const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' scaled
+                    args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
+                }
             }
             kb = gt * m1;
             if constexpr (SPB == 1) {
@@ -392,6 +471,30 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             H += kb;
             C += Nb;
             Nb = lmax;
+        }
+        if constexpr (WPS > 1) {
+            // outputs of steps 0..t_out from the per-wave partial sums, one step per thread, summed over the waves
+            // in wave order
+            __syncthreads();
+            for (int tt = tau; tt <= t_out; tt += TPS) {
+                float S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
+#pragma unroll
+                for (int q = 0; q < WPS; ++q) {
+                    const float4 p = buf_ld4(tape, sq * slot_bytes, part_base + 16u * (uint32_t)(tt * WPS + q));
+                    S0 += p.x;
+                    S1 += p.y;
+                    S2 += p.z;
+                    S3 += p.w;
+                }
+                const float i0 = 1.0f / S0;
+                const float m1 = S1 * i0;
+                const float m2 = S2 * i0;
+                const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' in scaled units
+                if (active) {
+                    args.grad[b * n + tt] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (args.w_soft) args.w_soft[b * n + tt] = valid ? wb[tt] + m1 * inv_scale : __builtin_nanf("");
+                }
+            }
         }
         __syncthreads();
     }

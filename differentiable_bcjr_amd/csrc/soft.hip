@@ -24,6 +24,16 @@
 
 namespace bcjr {
 
+// Groups of 4 states whose work the scheduler may interleave between two scheduling barriers (forward, backward).
+#ifndef BCJR_SOFT_FWD_GROUPS
+#define BCJR_SOFT_FWD_GROUPS 1
+#endif
+#ifndef BCJR_SOFT_BWD_GROUPS
+#define BCJR_SOFT_BWD_GROUPS 1
+#endif
+constexpr int kSoftFwdGroups = BCJR_SOFT_FWD_GROUPS;
+constexpr int kSoftBwdGroups = BCJR_SOFT_BWD_GROUPS;
+
 template <int L>
 __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
     using Gm = Geo<L>;
@@ -31,7 +41,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
     constexpr int SEG = Gm::SEG;
     __shared__ float4 msg4[SPB][2][G / 4];
     __shared__ float redmax[2][SPB][WPS];
-    __shared__ float2 redsum[2][SPB][WPS];
+    __shared__ float redsum[2][SPB][WPS];
 
     const int tid = threadIdx.x;
     const int sq = tid / TPS;
@@ -67,6 +77,9 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
     const uint32_t v_quad = sq * slot_bytes + 16u * tau;   // float4 at group 4j, j = tau + TPS m
     const uint32_t v_grp = sq * slot_bytes + 4u * tau;     // float at group j + Q a
     const uint32_t nrm_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    // with several waves per sequence, each wave's (S0, S1) of every step goes here and the soft codeword is formed
+    // after the backward pass, so no wave waits on a serial per-step reduction
+    const uint32_t part_base = nrm_base + (uint32_t)align256((size_t)n * 4);
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
@@ -95,10 +108,12 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
         float N = 0.f;        // normaliser subtracted at this step (max of R~_t)
         double A = 0.0;       // A_t: log2 offset of R~_t
         float N_last = 0.f;   // N_{n-1}
+        float w_nx = wb[0];   // the next step's weight, loaded one step ahead
         for (int t = 0; t < n; ++t) {
             const float* mc = (t & 1) ? msg1 : msg0;
             float* mn = (t & 1) ? msg0 : msg1;
-            const float wt = wb[t] * scale;
+            const float wt = w_nx * scale;
+            if (t + 1 < n) w_nx = wb[t + 1];
             float lmax = -3.0e38f;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
@@ -118,7 +133,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     const float mx = max4(x[0], x[1], x[2], x[3]);
                     const float s = (ex2(x[0] - mx) + ex2(x[1] - mx)) + (ex2(x[2] - mx) + ex2(x[3] - mx));
                     o[i] = (mx - N) + lg2(s);
-                    __builtin_amdgcn_sched_barrier(0);
+                    if ((i + 1) % kSoftFwdGroups == 0) __builtin_amdgcn_sched_barrier(0);
                 }
                 lmax = fmaxf(lmax, max4(o[0], o[1], o[2], o[3]));
                 const float4 o4 = make_float4(o[0], o[1], o[2], o[3]);
@@ -153,13 +168,13 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             }
             part = seg_sum_fast<SEG>(part);
             if constexpr (WPS > 1) {
-                if (lane == 0) redsum[n & 1][sq][wv] = make_float2(part, 0.f);
+                if (lane == 0) redsum[n & 1][sq][wv] = part;
             }
             lds_barrier();
             if constexpr (WPS > 1) {
                 part = 0.f;
 #pragma unroll
-                for (int q = 0; q < WPS; ++q) part += redsum[n & 1][sq][q].x;
+                for (int q = 0; q < WPS; ++q) part += redsum[n & 1][sq][q];
             }
             rz = N + lg2(part);
         } else {
@@ -212,11 +227,21 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
 #pragma unroll
             for (int a = 0; a < 4; ++a) rq[a] = buf_ld(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * Q * a);
         }
+        const int t_out = t;   // last step whose soft codeword the loop below produces
+        float N_nx = 0.f;
+        if (t >= 0) {
+            w_nx = wb[t];
+            N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
+        }
         for (; t >= 0; --t) {
             const float* mc = (t & 1) ? msg1 : msg0;
             float* mn = (t & 1) ? msg0 : msg1;
-            const float wt = wb[t] * scale;
-            float Nt = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
+            const float wt = w_nx * scale;
+            float Nt = N_nx;
+            if (t > 0) {   // the next step's weight and forward normaliser, one step ahead
+                w_nx = wb[t - 1];
+                N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
+            }
             if constexpr (SPB == 1) Nt = uniform_f(Nt);
             D += Nt;
             const float ref = (rz + D) - C;
@@ -249,8 +274,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     S1 = fmaf(f, fmaf(e0, d0, fmaf(e1, d1, fmaf(e2, d2, e3 * d3))), S1);
                     lmax = fmaxf(lmax, out);
                     mn[j + Q * a] = out;   // at t = 0 this lands in a buffer nobody reads
-                    pin_order(S0, S1, lmax);
-                    __builtin_amdgcn_sched_barrier(0);
+                    if ((a + 1) % kSoftBwdGroups == 0) {
+                        pin_order(S0, S1, lmax);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
 #pragma unroll
                 for (int a = 0; a < 4; ++a) rq[a] = rn[a];
@@ -261,29 +288,35 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             if constexpr (WPS > 1) {
                 if (lane == 0) {
                     redmax[t & 1][sq][wv] = lmax;
-                    redsum[t & 1][sq][wv] = make_float2(S0, S1);
+                    buf_st2(make_float2(S0, S1), tape, sq * slot_bytes, part_base + 8u * (uint32_t)(t * WPS + wv));
                 }
             }
             lds_barrier();
             if constexpr (WPS > 1) {
 #pragma unroll
                 for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
-                if (tau == 0) {
-                    S0 = 0.f;
-                    S1 = 0.f;
-#pragma unroll
-                    for (int q = 0; q < WPS; ++q) {
-                        const float2 p = redsum[t & 1][sq][q];
-                        S0 += p.x;
-                        S1 += p.y;
-                    }
-                }
+            } else {
+                if (tau == 0 && active)
+                    args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");
             }
             if constexpr (SPB == 1) lmax = uniform_f(lmax);
-            if (tau == 0 && active)
-                args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");
             C += Nb;
             Nb = lmax;
+        }
+        if constexpr (WPS > 1) {
+            // soft codewords of steps 0..t_out from the per-wave partial sums, one step per thread, summed over the
+            // waves in wave order
+            __syncthreads();
+            for (int tt = tau; tt <= t_out; tt += TPS) {
+                float S0 = 0.f, S1 = 0.f;
+#pragma unroll
+                for (int q = 0; q < WPS; ++q) {
+                    const float2 p = buf_ld2(tape, sq * slot_bytes, part_base + 8u * (uint32_t)(tt * WPS + q));
+                    S0 += p.x;
+                    S1 += p.y;
+                }
+                if (active) args.w_soft[b * n + tt] = valid ? wb[tt] + (S1 / S0) * inv_scale : __builtin_nanf("");
+            }
         }
         // the next sequence reuses the tape and the LDS buffers
         __syncthreads();

@@ -39,14 +39,14 @@ struct Geo {
 
 // The same numbers for a runtime L (host-side planning).
 struct GeoRT {
-    int G, Q, QPT, TPS, NT, SPB;
+    int G, Q, QPT, TPS, NT, SPB, WPS;
 };
 __host__ __device__ constexpr GeoRT geo_rt(int L) {
     const int G = 1 << (L - 2), Q = 1 << (L - 4);
     const int QPT = L >= 14 ? (1 << (L - 14)) : 1;
     const int TPS = Q / QPT;
     const int NT = TPS >= 64 ? TPS : 64;
-    return GeoRT{G, Q, QPT, TPS, NT, NT / TPS};
+    return GeoRT{G, Q, QPT, TPS, NT, NT / TPS, TPS >= 64 ? TPS / 64 : 1};
 }
 
 // Blocks per CU the launch plans for (bounds the grid, hence the workspace): one block fills a CU at L >= 15.
@@ -196,6 +196,13 @@ __device__ __forceinline__ float buf_ld(rsrc_t r, uint32_t voff, uint32_t soff) 
 }
 __device__ __forceinline__ float4 buf_ld4(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ float2 buf_ld2(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_st2(float2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned int, v), r,
+                                          voff, soff, 0);
 }
 __device__ __forceinline__ void buf_st(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, 0);

@@ -50,6 +50,11 @@ def _geo(L):
     return G, TPS, NT // TPS
 
 
+def _wps(L):
+    _, TPS, _ = _geo(L)
+    return TPS // 64 if TPS >= 64 else 1
+
+
 def _a256(x):
     return (x + 255) // 256 * 256
 
@@ -63,14 +68,16 @@ def test_workspace_bytes_formula(L, B, n):
     slots = grid * SPB
     msgs = _a256((n + 1) * G * 4)
     nrm = _a256(n * 4)
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm)
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + 2 * nrm)
+    part = _a256(n * _wps(L) * 8) if _wps(L) > 1 else 0   # per-wave partial sums of every step
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm + part)
+    part4 = _a256(n * _wps(L) * 16) if _wps(L) > 1 else 0
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + 2 * nrm + part4)
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, B, n, L, 2) == slots * _a256(2 * n * TPS * 4)
 
 
 def test_workspace_bytes_for_the_headline_workload():
-    # 4096 sequences of 256 weights on a 2^16-state trellis: one 16 MiB forward tape per CU
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4096, 256, 16, 2) == 256 * (257 * 65536 + 1024)
+    # 4096 sequences of 256 weights on a 2^16-state trellis: one 16 MiB forward tape per CU (+ 16 waves' partial sums)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4096, 256, 16, 2) == 256 * (257 * 65536 + 1024 + 256 * 16 * 8)
 
 
 @pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 4097, 8, 2), (1, 4, 3, 2),
