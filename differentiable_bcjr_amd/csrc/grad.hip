@@ -127,8 +127,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4*>(mr + 4 * j) = r;
             *reinterpret_cast<float4*>(mq + 4 * j) = z;
-            buf_st4(r, tape, v_quad, 16u * TPS * m);
-            buf_st4(z, tape, v_quad, q_base + 16u * TPS * m);
+            buf_st4_nt(r, tape, v_quad, 16u * TPS * m);
+            buf_st4_nt(z, tape, v_quad, q_base + 16u * TPS * m);
         }
         lds_barrier();
 
@@ -205,8 +205,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
                 *reinterpret_cast<float4*>(mr + 4 * j) = r4;
                 *reinterpret_cast<float4*>(mq + 4 * j) = q4;
-                buf_st4(r4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
-                buf_st4(q4, tape, v_quad, q_base + (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
+                buf_st4_nt(r4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
+                buf_st4_nt(q4, tape, v_quad, q_base + (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
             }
             seg_argmax_payload<SEG>(lmax, lq);
             if constexpr (WPS > 1) {
@@ -217,14 +217,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
             lds_barrier();
             if constexpr (WPS > 1) {
-                float bm = redmax[t & 1][sq][0], bq = redq[t & 1][sq][0];
-#pragma unroll
-                for (int q = 1; q < WPS; ++q) {
-                    const float vm = redmax[t & 1][sq][q];
-                    const bool up = vm > bm;
-                    bm = up ? vm : bm;
-                    bq = up ? redq[t & 1][sq][q] : bq;
-                }
+                static_assert(WPS <= 16, "per-wave slots are combined inside one 16-lane row");
+                const int qs = lane & 15;
+                float bm = qs < WPS ? redmax[t & 1][sq][qs] : -3.0e38f;
+                float bq = qs < WPS ? redq[t & 1][sq][qs] : 0.f;
+                row16_argmax_payload(bm, bq);   // first wave attaining the max, as a serial scan would pick
                 lmax = bm;
                 lq = bq;
             }
@@ -272,8 +269,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
             __syncthreads();
             const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
-            const float r = buf_ld(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
-            const float q = buf_ld(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
+            const float r = buf_ld_nt(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
+            const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
             EF = fmaf(gb[n - 1] * inv_scale, d, q + K_last);   // Q^_{n-1} carries the offset K_{n-2}
         }
@@ -325,8 +322,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         float rt_n = 0.f, qt_n = 0.f;
         float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
         if (kGradPrefetch && t >= 0) {
-            rt_n = buf_ld(tape, v_grp, (uint32_t)t * (G * 4u));
-            qt_n = buf_ld(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
+            rt_n = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u));
+            qt_n = buf_ld_nt(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
         }
         const int t_out = t;   // last step whose outputs the loop below produces
@@ -334,8 +331,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         if (t >= 0) {
             w_nx = wb[t];
             g_nx = gb[t];
-            N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
-            K_nx = buf_ld(tape, sq * slot_bytes, kq_base + 4u * t);
+            N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * t);
+            K_nx = buf_ld_nt(tape, sq * slot_bytes, kq_base + 4u * t);
         }
         for (; t >= 0; --t) {
             float bin[QPT][4], pin[QPT][4];
@@ -353,8 +350,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             if (t > 0) {   // the next step's weight, upstream gradient and forward scalars, one step ahead
                 w_nx = wb[t - 1];
                 g_nx = gb[t - 1];
-                N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
-                K_nx = buf_ld(tape, sq * slot_bytes, kq_base + 4u * (t - 1));
+                N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
+                K_nx = buf_ld_nt(tape, sq * slot_bytes, kq_base + 4u * (t - 1));
             }
             if constexpr (SPB == 1) {
                 Nt = uniform_f(Nt);
@@ -380,19 +377,19 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                         const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
                         if (!last) {
                             const uint32_t so2 = (uint32_t)t * (G * 4u) + 4u * (TPS * m2 + Q * a2);
-                            rt_n = buf_ld(tape, v_grp, so2);
-                            qt_n = buf_ld(tape, v_grp, q_base + so2);
+                            rt_n = buf_ld_nt(tape, v_grp, so2);
+                            qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
                             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
                         } else if (t > 0) {
                             const uint32_t so2 = (uint32_t)(t - 1) * (G * 4u);
-                            rt_n = buf_ld(tape, v_grp, so2);
-                            qt_n = buf_ld(tape, v_grp, q_base + so2);
+                            rt_n = buf_ld_nt(tape, v_grp, so2);
+                            qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
                             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
                         }
                     } else {
                         const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
-                        rt = buf_ld(tape, v_grp, so);
-                        qt = buf_ld(tape, v_grp, q_base + so) + cst;
+                        rt = buf_ld_nt(tape, v_grp, so);
+                        qt = buf_ld_nt(tape, v_grp, q_base + so) + cst;
                         cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
                     }
                     const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
@@ -443,20 +440,20 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 }
             }
             lds_barrier();
+            float m1;   // w_soft_t - w_t in scaled codebook units
             if constexpr (WPS > 1) {
-                S0 = S1 = 0.f;
-#pragma unroll
-                for (int q = 0; q < WPS; ++q) {
-                    lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
-                    const float2 p = redsum2[t & 1][sq][q];
-                    S0 += p.x;
-                    S1 += p.y;
-                }
+                const int qs = lane & 15;
+                const float2 p = qs < WPS ? redsum2[t & 1][sq][qs] : make_float2(0.f, 0.f);
+                lmax = row16_max(qs < WPS ? redmax[t & 1][sq][qs] : -3.0e38f);
+                // only the P offset uses m1 here, and any value common to the block serves: the approximate
+                // reciprocal keeps the division off the step's critical path
+                m1 = row16_sum(p.y) * rcp(row16_sum(p.x));
+            } else {
+                m1 = S1 * (1.0f / S0);
             }
-            const float i0 = 1.0f / S0;
-            const float m1 = S1 * i0;   // w_soft_t - w_t in scaled codebook units
             if constexpr (WPS == 1) {
                 if (tau == 0 && active) {
+                    const float i0 = 1.0f / S0;
                     const float m2 = S2 * i0;
                     const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' scaled
                     args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             r.z = (!has_sigma || (uint32_t)(4 * j + 2) == (sig & (G - 1))) ? 0.f : kNeg;
             r.w = (!has_sigma || (uint32_t)(4 * j + 3) == (sig & (G - 1))) ? 0.f : kNeg;
             *reinterpret_cast<float4*>(msg0 + 4 * j) = r;
-            buf_st4(r, tape, v_quad, 16u * TPS * m);
+            buf_st4_nt(r, tape, v_quad, 16u * TPS * m);
         }
         lds_barrier();
 
@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                 lmax = fmaxf(lmax, max4(o[0], o[1], o[2], o[3]));
                 const float4 o4 = make_float4(o[0], o[1], o[2], o[3]);
                 *reinterpret_cast<float4*>(mn + 4 * j) = o4;
-                buf_st4(o4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);   // row n is spare
+                buf_st4_nt(o4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);   // row n is spare
             }
             if (tau == 0) buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
             lmax = seg_max_fast<SEG>(lmax);
@@ -147,8 +147,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             }
             lds_barrier();
             if constexpr (WPS > 1) {
-#pragma unroll
-                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+                static_assert(WPS <= 16, "per-wave slots are combined inside one 16-lane row");
+                lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][sq][lane & 15] : -3.0e38f);
             }
             if constexpr (SPB == 1) lmax = uniform_f(lmax);
             A += (double)N;
@@ -225,13 +225,13 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
         float rq[4], rn[4];
         if (t >= 0) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) rq[a] = buf_ld(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * Q * a);
+            for (int a = 0; a < 4; ++a) rq[a] = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * Q * a);
         }
         const int t_out = t;   // last step whose soft codeword the loop below produces
         float N_nx = 0.f;
         if (t >= 0) {
             w_nx = wb[t];
-            N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * t);
+            N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * t);
         }
         for (; t >= 0; --t) {
             const float* mc = (t & 1) ? msg1 : msg0;
@@ -240,7 +240,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             float Nt = N_nx;
             if (t > 0) {   // the next step's weight and forward normaliser, one step ahead
                 w_nx = wb[t - 1];
-                N_nx = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
+                N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
             }
             if constexpr (SPB == 1) Nt = uniform_f(Nt);
             D += Nt;
@@ -253,10 +253,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                 if (m + 1 < QPT) {
 #pragma unroll
                     for (int a = 0; a < 4; ++a)
-                        rn[a] = buf_ld(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * (TPS * (m + 1) + Q * a));
+                        rn[a] = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * (TPS * (m + 1) + Q * a));
                 } else if (t > 0) {
 #pragma unroll
-                    for (int a = 0; a < 4; ++a) rn[a] = buf_ld(tape, v_grp, (uint32_t)(t - 1) * (G * 4u) + 4u * Q * a);
+                    for (int a = 0; a < 4; ++a) rn[a] = buf_ld_nt(tape, v_grp, (uint32_t)(t - 1) * (G * 4u) + 4u * Q * a);
                 }
                 const float4 bq = *reinterpret_cast<const float4*>(mc + 4 * j);
 #pragma unroll
@@ -293,8 +293,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             }
             lds_barrier();
             if constexpr (WPS > 1) {
-#pragma unroll
-                for (int q = 0; q < WPS; ++q) lmax = fmaxf(lmax, redmax[t & 1][sq][q]);
+                lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][sq][lane & 15] : -3.0e38f);
             } else {
                 if (tau == 0 && active)
                     args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");

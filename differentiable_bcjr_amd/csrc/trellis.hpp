@@ -153,6 +153,31 @@ __device__ __forceinline__ float seg_sum_fast(float x) {
     else return seg_sum<SEG>(x);
 }
 
+// Combine the per-wave slots of one sequence (at most 16): each lane reads slot (lane & 15), lanes past the last
+// slot hold the neutral value, and a DPP tree inside each 16-lane row leaves the result in every lane.  All four
+// rows read the same slots, so the result is wave-uniform.  Max and first-max are exact, so they match a serial
+// scan over the slots; a sum is added in tree order.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    x = fmaxf(x, dpp<0x4E>(x));
+    x = fmaxf(x, dpp<0x141>(x));
+    return fmaxf(x, dpp<0x140>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    x += dpp<0x141>(x);
+    return x + dpp<0x140>(x);
+}
+// (max of v over the row, q of the lowest lane of the row attaining it)
+__device__ __forceinline__ void row16_argmax_payload(float& v, float& q) {
+    const float m = row16_max(v);
+    const uint64_t hit = __ballot(v == m) & 0xFFFFull;
+    const int src = hit ? __builtin_ctzll(hit) : 0;
+    q = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, q), src));
+    v = m;
+}
+
 // (max of v, q of the lowest lane attaining it) over the SEG lanes of one sequence inside a wave.
 template <int SEG>
 __device__ __forceinline__ void seg_argmax_payload(float& v, float& q) {
@@ -214,6 +239,18 @@ __device__ __forceinline__ void buf_st(float v, rsrc_t r, uint32_t voff, uint32_
 __device__ __forceinline__ void buf_st4(float4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
                                            voff + soff, 0, 0);
+}
+
+// The forward tapes are written once and read once, a full pass later: their accesses carry the non-temporal
+// policy so the stream does not evict what is reused from L2 (the codebook).
+constexpr int kStreamPolicy = 2;   // nt on gfx950
+__device__ __forceinline__ float buf_ld_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy));
+}
+// Same store form as buf_st4 (whole offset in the VGPR, so the compiler adds the wait state after it).
+__device__ __forceinline__ void buf_st4_nt(float4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
+                                           voff + soff, 0, kStreamPolicy);
 }
 
 // Per-slot workspace layout (bytes), shared by the host planner and the kernels.
