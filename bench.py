@@ -16,7 +16,7 @@ Counting.  A state-update is one trellis state at one step in one direction: the
 ``value`` is the step's state-updates per second; ``weights_per_s`` is B * n per step time.
 
 The roofline object covers the step's longest kernel.  Its bound is VALU issue: the work per state-step is counted in
-full-rate fp32 VALU lane slots, a transcendental (v_exp/v_log/v_rcp, quarter rate) costing 4, and the peak is
+full-rate fp32 VALU lane slots (a half-rate max/compare/select costs 2, a quarter-rate exp2/log2/rcp 4), and the peak is
 256 CUs x 128 fp32 lanes x 2.4 GHz = 78.6e12 slots/s (the published 157.3 TFLOP/s fp32 vector rate with an FMA as
 two flops).  Kernel times come from HIP events recorded on the stream the kernels run on.
 
@@ -34,16 +34,20 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# fp32 VALU lane slots per state-step (one state, one step), transcendental = 4 slots.  The per-state operation
-# counts of each pass in the grouped-message form (one log-sum-exp of 4 per group of 4 states):
-#   soft    forward 5 VALU + 1.25 trans; backward 5 + 1.25; posterior 2 + 0.25        -> 12 VALU + 2.75 trans
-#   grad    forward 8 VALU + 1.5 trans (adds the Q message); backward 14.75 + 1.75    -> 22.75 VALU + 3.25 trans
-#   viterbi sub, mul, add, 0.75 min-compare + 0.75 select + 0.5 back-pointer packing  -> 5.5 VALU
-TRANS_SLOTS = 4.0
+# Algorithmic VALU work per state-step (one state, one step), in fp32 lane slots of a full-rate instruction
+# (add, mul, fma).  Measured on gfx950: max/min/compare/select issue at half that rate (2 slots), exp2/log2/rcp at a
+# quarter (4 slots).  Per-state counts of the grouped-message form (one log-sum-exp of 4 per group of 4 states):
+#   soft    forward 4.25 full + 1 half + 1.25 trans; backward the same; posterior 2 full + 0.25 trans
+#           -> 10.5 full + 2 half + 2.75 trans = 25.5 slots
+#   grad    forward 6.5 full + 1 half + 1.5 trans (adds the Q message); backward 13 full + 1 half + 1.75 trans
+#           (adds the P message and the four covariance sums) -> 19.5 full + 2 half + 3.25 trans = 36.5 slots
+#   viterbi sub, mul, add, 0.5 back-pointer packing (full) + 2.25 compare/select for the min of 4 with its index
+#           -> 3.5 full + 2.25 half = 8 slots
+HALF_SLOTS, TRANS_SLOTS = 2.0, 4.0
 ALU_SLOTS = {
-    "soft": 12.0 + 2.75 * TRANS_SLOTS,
-    "grad": 22.75 + 3.25 * TRANS_SLOTS,
-    "viterbi": 5.5,
+    "soft": 10.5 + 2.0 * HALF_SLOTS + 2.75 * TRANS_SLOTS,
+    "grad": 19.5 + 2.0 * HALF_SLOTS + 3.25 * TRANS_SLOTS,
+    "viterbi": 3.5 + 2.25 * HALF_SLOTS,
 }
 DIRECTIONS = {"soft": 2, "grad": 2, "viterbi": 1}
 PEAK_SLOTS_PER_S = 256 * 128 * 2.4e9
@@ -225,7 +229,7 @@ def main():
     roofline = {"bound": "alu", "kernel": d["kernel"], "achieved": round(achieved, 3), "peak": round(peak, 3),
                 "unit": "T VALU-slots/s", "frac": round(achieved / peak, 4),
                 "traffic": recorded_traffic(dom, wl.name),
-                "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (transcendental = 4)",
+                "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (half-rate op = 2, transcendental = 4)",
                 "units_per_launch": B * n * S}
 
     total_upd = sum(DIRECTIONS[o] for o, _ in ops) * B * n * S
