@@ -238,6 +238,74 @@ def test_headline_workload_sampled(oracle_mod, dev):
         assert e <= TOL and elz <= TOL
 
 
+def test_headline_workload_gradient_and_viterbi_sampled(oracle_mod, dev):
+    """The benchmark's step on the same workload: gradient at T = 0.1 and the Viterbi code."""
+    wl = workloads.WORKLOADS[2]
+    c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
+    rows = wl.sample_rows(4)
+    T = 0.1
+    wt, ct = _t(w, dev), _t(c, dev)
+    gr, ws = dba.soft_codeword_grad(wt, ct, _t(g, dev), wl.L, wl.k, T, return_w_soft=True)
+    ref, rws = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
+    got = gr.cpu().numpy()[rows]
+    e, en, ew = grad_err(got, ref, g[rows], c, T), norm_err(got, ref), rel_err(ws.cpu().numpy()[rows], rws)
+    print(f"headline grad rows={rows.tolist()}: {en:.2e} normwise, {e:.2e} elementwise; w_soft {ew:.2e}", flush=True)
+    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG and ew <= TOL
+    st, wh, cost = dba.viterbi_hard_code(wt, ct, wl.L, wl.k)
+    rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k)
+    np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
+    np.testing.assert_array_equal(wh.cpu().numpy()[rows].view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.cpu().numpy()[rows].view(np.uint32), rcost.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# shape edges: the longest sequences, one sequence, batches that leave a block partly idle or make blocks loop
+
+
+@pytest.mark.parametrize("sigma", [False, True])
+def test_longest_sequences(oracle_mod, dev, sigma):
+    """n = 4096, the largest the boundary accepts, on a 2^10-state trellis."""
+    L, B, n, T = 10, 2, 4096, 0.1
+    w, c, g, s = _inputs(L, B, n, 77, sigma)
+    wt, ct, st_ = _t(w, dev), _t(c, dev), _t(s, dev)
+    got, lz = dba.soft_codeword(wt, ct, L, 2, T, st_, return_log_z=True)
+    ref, rlz = oracle_mod.soft(w, c, L, 2, T, sigma=s)
+    assert rel_err(got.cpu().numpy(), ref) <= TOL
+    assert float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.abs(rlz))) <= TOL
+    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T, st_).cpu().numpy()
+    rgr, _ = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
+    en, e = norm_err(gr, rgr), grad_err(gr, rgr, g, c, T)
+    print(f"n=4096 sigma={sigma}: grad {en:.2e} normwise, {e:.2e} elementwise", flush=True)
+    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG
+    stt, _, cost = dba.viterbi_hard_code(wt, ct, L, 2, st_)
+    rst, _, rcost = oracle_mod.viterbi(w, c, L, 2, sigma=s)
+    np.testing.assert_array_equal(stt.cpu().numpy(), rst)
+    np.testing.assert_array_equal(cost.cpu().numpy().view(np.uint32), rcost.view(np.uint32))
+
+
+@pytest.mark.parametrize("L,B,n,rows", [
+    (16, 1, 64, [0]),                    # one sequence on the 2^16-state trellis
+    (16, 260, 8, [0, 3, 255, 256, 259]),  # blocks 0..3 take a second sequence (grid = 256)
+    (8, 8200, 4, [0, 8191, 8192, 8199]),  # 4 sequences per block, 2048 blocks: rows past 8191 come back round
+    (4, 65, 5, [0, 63, 64]),              # 64 sequences per block: the second block has one active sequence
+])
+def test_batch_edges(oracle_mod, dev, L, B, n, rows):
+    T = 0.1
+    w, c, g, _ = _inputs(L, B, n, 900 + L)
+    rows = np.asarray(rows)
+    wt, ct = _t(w, dev), _t(c, dev)
+    got = dba.soft_codeword(wt, ct, L, 2, T).cpu().numpy()[rows]
+    ref, _ = oracle_mod.soft(w[rows], c, L, 2, T)
+    assert rel_err(got, ref) <= TOL
+    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T).cpu().numpy()[rows]
+    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], L, 2, T)
+    assert grad_err(gr, rgr, g[rows], c, T) <= grad_tol(T, False)
+    st, _, cost = dba.viterbi_hard_code(wt, ct, L, 2)
+    rst, _, rcost = oracle_mod.viterbi(w[rows], c, L, 2)
+    np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
+    np.testing.assert_array_equal(cost.cpu().numpy()[rows].view(np.uint32), rcost.view(np.uint32))
+
+
 def test_mlp_layer_gradient_sampled(oracle_mod, dev):
     """65536 sequences (an 8192x2048 matrix), T = 0.05: soft codeword and gradient."""
     wl = workloads.WORKLOADS[3]
