@@ -354,6 +354,28 @@ def test_low_temperature_sweep_and_viterbi_sampled(oracle_mod, dev):
     assert np.mean(np.abs(got - hard) < 1e-3) > 0.9
 
 
+def test_low_temperature_workload_sigma_sampled(oracle_mod, dev):
+    """The same 16384 sequences with s_0 = s_n = sigma: soft codeword at T = 0.1 and 0.01, gradient at T = 0.1."""
+    wl = workloads.WORKLOADS[4]
+    c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
+    sig = wl.boundary_states()
+    rows = wl.sample_rows(4)
+    wt, ct, st_ = _t(w, dev), _t(c, dev), _t(sig, dev)
+    for T in (0.1, 0.01):
+        got, lz = dba.soft_codeword(wt, ct, wl.L, wl.k, T, st_, return_log_z=True)
+        ref, rlz = oracle_mod.soft(w[rows], c, wl.L, wl.k, T, sigma=sig[rows])
+        e = rel_err(got.cpu().numpy()[rows], ref)
+        elz = float(np.max(np.abs(lz.cpu().numpy()[rows] - rlz) / np.abs(rlz)))
+        print(f"low-T sigma T={T}: soft err {e:.2e}, log_z err {elz:.2e}", flush=True)
+        assert e <= soft_tol(T, True) and elz <= TOL
+    T = 0.1
+    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), wl.L, wl.k, T, st_).cpu().numpy()[rows]
+    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T, sigma=sig[rows])
+    en, e = norm_err(gr, rgr), grad_err(gr, rgr, g[rows], c, T)
+    print(f"low-T sigma grad T={T}: {en:.2e} normwise, {e:.2e} elementwise", flush=True)
+    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG
+
+
 @pytest.mark.slow
 def test_whole_decoder_layer_sampled(oracle_mod, dev):
     """All seven Llama-3.2-1B projection shapes as one batch of 237,568 sequences, T = 0.05."""
