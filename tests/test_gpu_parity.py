@@ -391,3 +391,38 @@ def test_whole_decoder_layer_sampled(oracle_mod, dev):
     print(f"layer rows={rows.tolist()}: grad err {en:.2e} normwise, {e:.2e} elementwise; w_soft err {ew:.2e}",
           flush=True)
     assert en <= TOL and e <= GRAD_ELEM_TOL_LONG and ew <= TOL
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# a seeded sweep over shapes, temperatures and boundary modes (every draw is checked like the fixed cases above)
+
+def _random_cases(count=36, seed=2024):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        L = int(rng.integers(4, 17))
+        n = int(rng.integers(1, 81)) if L <= 12 else int(rng.integers(1, 25))
+        B = int(rng.integers(1, 41)) if L <= 12 else int(rng.integers(1, 5))
+        T = float(rng.choice([1.0, 0.3, 0.1, 0.05]))
+        sigma = bool(rng.integers(0, 2)) and n >= (L + 1) // 2   # sigma needs L/k steps to reach every state
+        cases.append((i, L, B, n, T, sigma))
+    return cases
+
+
+@pytest.mark.parametrize("i,L,B,n,T,sigma", _random_cases())
+def test_random_configuration(oracle_mod, dev, i, L, B, n, T, sigma):
+    w, c, g, s = _inputs(L, B, n, 5000 + i, sigma)
+    wt, ct, st_ = _t(w, dev), _t(c, dev), _t(s, dev)
+    got, lz = dba.soft_codeword(wt, ct, L, 2, T, st_, return_log_z=True)
+    ref, rlz = oracle_mod.soft(w, c, L, 2, T, sigma=s)
+    assert rel_err(got.cpu().numpy(), ref) <= soft_tol(T, sigma)
+    assert float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0))) <= TOL
+    gr, ws = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T, st_, return_w_soft=True)
+    rgr, rws = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
+    assert rel_err(ws.cpu().numpy(), rws) <= soft_tol(T, sigma)
+    assert grad_err(gr.cpu().numpy(), rgr, g, c, T) <= grad_tol(T, sigma)
+    stt, wh, cost = dba.viterbi_hard_code(wt, ct, L, 2, st_)
+    rst, rwh, rcost = oracle_mod.viterbi(w, c, L, 2, sigma=s)
+    np.testing.assert_array_equal(stt.cpu().numpy(), rst)
+    np.testing.assert_array_equal(wh.cpu().numpy().view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.cpu().numpy().view(np.uint32), rcost.view(np.uint32))
