@@ -415,7 +415,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     S1 = fmaf(f, ed, S1);
                     S2 = fmaf(f, er, S2);
                     S3 = fmaf(f, edr, S3);
-                    lmax = fmaxf(lmax, out);
+                    lmax = run_max(lmax, out);
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
                     mr[u] = out;            // at t = 0 these land in buffers nobody reads
                     mq[u] = ez * rcp(s);

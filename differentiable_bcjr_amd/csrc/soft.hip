@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     o[i] = (mx - N) + lg2(s);
                     if ((i + 1) % kSoftFwdGroups == 0) __builtin_amdgcn_sched_barrier(0);
                 }
-                lmax = fmaxf(lmax, max4(o[0], o[1], o[2], o[3]));
+                lmax = run_max(lmax, max4(o[0], o[1], o[2], o[3]));
                 const float4 o4 = make_float4(o[0], o[1], o[2], o[3]);
                 *reinterpret_cast<float4*>(mn + 4 * j) = o4;
                 buf_st4_nt(o4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);   // row n is spare
@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     const float f = ex2((mx + rq[a]) - ref);
                     S0 = fmaf(f, s, S0);
                     S1 = fmaf(f, fmaf(e0, d0, fmaf(e1, d1, fmaf(e2, d2, e3 * d3))), S1);
-                    lmax = fmaxf(lmax, out);
+                    lmax = run_max(lmax, out);
                     mn[j + Q * a] = out;   // at t = 0 this lands in a buffer nobody reads
                     if ((a + 1) % kSoftBwdGroups == 0) {
                         pin_order(S0, S1, lmax);

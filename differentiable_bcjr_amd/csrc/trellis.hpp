@@ -60,6 +60,10 @@ __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x)
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float max4(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
+// Running maximum over finite values (v_maximum3_f32).  fmaxf must quiet signalling NaNs, so the compiler re-canonicalises
+// an operand it cannot prove canonical (one that left an asm ordering point) with an extra half-rate v_max per use; the
+// IEEE-2019 maximum has no such requirement, and the two agree on the finite values and sentinels used here.
+__device__ __forceinline__ float run_max(float acc, float x) { return __builtin_elementwise_maximum(acc, x); }
 
 // Keeps the compiler from deferring the accumulation of these values past this point (which would keep every
 // group's temporaries alive at once): an empty volatile asm that claims to read and rewrite them.
