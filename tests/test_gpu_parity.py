@@ -426,3 +426,75 @@ def test_random_configuration(oracle_mod, dev, i, L, B, n, T, sigma):
     np.testing.assert_array_equal(stt.cpu().numpy(), rst)
     np.testing.assert_array_equal(wh.cpu().numpy().view(np.uint32), rwh.view(np.uint32))
     np.testing.assert_array_equal(cost.cpu().numpy().view(np.uint32), rcost.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------------------------------
+# execution: the entry points allocate nothing and only launch kernels, so they can be captured in a HIP graph and
+# run concurrently on separate streams with separate workspaces
+
+
+def _raw_step(wt, ct, gt, L, n, T, ws, outs, stream):
+    B = wt.shape[0]
+    w_soft, log_z, grad, states, w_hard, cost = outs
+    sp = stream.cuda_stream
+    assert abi.bcjr_soft_codeword(wt.data_ptr(), ct.data_ptr(), B, n, L, 2, T, None, w_soft.data_ptr(),
+                                  log_z.data_ptr(), ws.data_ptr(), ws.numel(), sp) == abi.BCJR_OK
+    assert abi.bcjr_soft_codeword_grad(wt.data_ptr(), ct.data_ptr(), B, n, L, 2, T, None, gt.data_ptr(),
+                                       grad.data_ptr(), None, ws.data_ptr(), ws.numel(), sp) == abi.BCJR_OK
+    assert abi.viterbi_hard_code(wt.data_ptr(), ct.data_ptr(), B, n, L, 2, None, states.data_ptr(),
+                                 w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), sp) == abi.BCJR_OK
+
+
+def _outs(B, n, dev):
+    f = lambda *s: torch.empty(s, dtype=torch.float32, device=dev)
+    return [f(B, n), f(B), f(B, n), torch.empty((B, n), dtype=torch.int32, device=dev), f(B, n), f(B)]
+
+
+def test_graph_capture_replays_match_eager(dev):
+    L, B, n, T = 12, 40, 24, 0.2
+    w, c, g, _ = _inputs(L, B, n, 31)
+    wt, ct, gt = _t(w, dev), _t(c, dev), _t(g, dev)
+    ws = torch.empty(max(abi.bcjr_workspace_bytes(op, B, n, L, 2) for op in (0, 1, 2)), dtype=torch.uint8, device=dev)
+    eager = _outs(B, n, dev)
+    _raw_step(wt, ct, gt, L, n, T, ws, eager, torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    graph_outs = _outs(B, n, dev)
+    side = torch.cuda.Stream(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        _raw_step(wt, ct, gt, L, n, T, ws, graph_outs, side)
+    for rep in range(3):
+        for o in graph_outs:
+            o.fill_(-7)                      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(graph_outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs from the eager call"
+
+
+def test_concurrent_streams_with_separate_workspaces(dev):
+    L, B, n, T = 14, 6, 32, 0.1
+    inputs = [_inputs(L, B, n, 40 + i) for i in range(2)]
+    ref = []
+    for w, c, g, _ in inputs:
+        o = _outs(B, n, dev)
+        ws = torch.empty(max(abi.bcjr_workspace_bytes(op, B, n, L, 2) for op in (0, 1, 2)), dtype=torch.uint8,
+                         device=dev)
+        _raw_step(_t(w, dev), _t(c, dev), _t(g, dev), L, n, T, ws, o, torch.cuda.current_stream(dev))
+        ref.append(o)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev) for _ in range(2)]
+    outs = [_outs(B, n, dev) for _ in range(2)]
+    wss = [torch.empty(max(abi.bcjr_workspace_bytes(op, B, n, L, 2) for op in (0, 1, 2)), dtype=torch.uint8,
+                       device=dev) for _ in range(2)]
+    tens = [tuple(_t(a, dev) for a in inp[:3]) for inp in inputs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                _raw_step(*tens[i], L, n, T, wss[i], outs[i], streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            for a, b in zip(outs[i], ref[i]):
+                assert torch.equal(a, b)
