@@ -20,8 +20,12 @@
 //
 // LDS holds the log-sum-exp message and the expectation message of one direction (2 x 64 KiB at L = 16) in a single
 // buffer: each step loads its inputs into registers, barriers, then writes its outputs.  Both forward messages go to
-// the workspace tape.  At L = 16 the codebook is read through L1/L2 each step (a thread has no registers left for it);
-// at smaller L it stays in registers.
+// the workspace tape (non-temporal: written once, read once a pass later).  At L = 16 the codebook is read through
+// L1/L2 each step (a thread has no registers left for it); at smaller L it stays in registers.  Memory latency is
+// covered by issuing each load one group (backward tape and codebook) or one quad (forward codebook) ahead, and the
+// next step's scalars (w, g, normaliser, Q offset) one step ahead.  With several waves per sequence only (S0, S1) is
+// combined across waves inside the step loop; every wave's (S0..S3) goes to the workspace and the outputs are formed
+// after the backward pass.
 #include "kernel_args.hpp"
 #include "trellis.hpp"
 
@@ -36,10 +40,6 @@ namespace bcjr {
 #endif
 constexpr int kGradFwdGroups = BCJR_GRAD_FWD_GROUPS;
 constexpr int kGradBwdGroups = BCJR_GRAD_BWD_GROUPS;
-#ifndef BCJR_GRAD_PREFETCH
-#define BCJR_GRAD_PREFETCH 1
-#endif
-constexpr bool kGradPrefetch = BCJR_GRAD_PREFETCH != 0;
 
 // Codebook row c(a << (L-2) | j << 2 | 0..3) of quad m (unscaled): from registers, or through L1/L2.
 template <int L, int TPS, bool CB_REG, int M>
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         float4 fc[4];   // codebook rows of the next quad, when they come from memory
 #pragma unroll
         for (int a = 0; a < 4; ++a)
-            fc[a] = (kGradPrefetch && !CB_REG) ? cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, a) : make_float4(0.f, 0.f, 0.f, 0.f);
+            fc[a] = !CB_REG ? cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, a) : make_float4(0.f, 0.f, 0.f, 0.f);
         for (int t = 0; t < n; ++t) {
             float rin[QPT][4], qin[QPT][4];
 #pragma unroll
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             for (int m = 0; m < QPT; ++m) {
                 const int j = tau + TPS * m;
                 float4 c0, c1, c2, c3;
-                if constexpr (kGradPrefetch && !CB_REG) {
+                if constexpr (!CB_REG) {
                     c0 = fc[0]; c1 = fc[1]; c2 = fc[2]; c3 = fc[3];
                     const int m2 = (m + 1) % QPT;   // the last quad fetches the next step's first
 #pragma unroll
@@ -321,7 +321,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         // loads of the next group (forward messages R~, Q^ of this step, codebook row) are issued one group ahead
         float rt_n = 0.f, qt_n = 0.f;
         float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (kGradPrefetch && t >= 0) {
+        if (t >= 0) {
             rt_n = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u));
             qt_n = buf_ld_nt(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
@@ -366,31 +366,24 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             for (int m = 0; m < QPT; ++m) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    float rt, qt;
+                    const float rt = rt_n;
+                    const float qt = qt_n + cst;
                     float4 cr;
-                    if constexpr (kGradPrefetch) {
-                        rt = rt_n;
-                        qt = qt_n + cst;
-                        if constexpr (CB_REG) cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
-                        else cr = cr_n;
-                        const bool last = (m == QPT - 1) && (a == 3);
-                        const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
-                        if (!last) {
-                            const uint32_t so2 = (uint32_t)t * (G * 4u) + 4u * (TPS * m2 + Q * a2);
-                            rt_n = buf_ld_nt(tape, v_grp, so2);
-                            qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
-                            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
-                        } else if (t > 0) {
-                            const uint32_t so2 = (uint32_t)(t - 1) * (G * 4u);
-                            rt_n = buf_ld_nt(tape, v_grp, so2);
-                            qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
-                            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
-                        }
-                    } else {
-                        const uint32_t so = (uint32_t)t * (G * 4u) + 4u * (TPS * m + Q * a);
-                        rt = buf_ld_nt(tape, v_grp, so);
-                        qt = buf_ld_nt(tape, v_grp, q_base + so) + cst;
-                        cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                    if constexpr (CB_REG) cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
+                    else cr = cr_n;
+                    // issue the next group's loads (or the next step's first group's) before this group's math
+                    const bool last = (m == QPT - 1) && (a == 3);
+                    const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
+                    if (!last) {
+                        const uint32_t so2 = (uint32_t)t * (G * 4u) + 4u * (TPS * m2 + Q * a2);
+                        rt_n = buf_ld_nt(tape, v_grp, so2);
+                        qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
+                        if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
+                    } else if (t > 0) {
+                        const uint32_t so2 = (uint32_t)(t - 1) * (G * 4u);
+                        rt_n = buf_ld_nt(tape, v_grp, so2);
+                        qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
+                        if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
                     }
                     const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
                     const float d2 = fmaf(cr.z, scale, -wt), d3 = fmaf(cr.w, scale, -wt);

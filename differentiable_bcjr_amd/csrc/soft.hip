@@ -18,7 +18,10 @@
 // Layout: 1024 threads per sequence at L = 16 (4 quads = 64 states per thread, their codebook values in VGPRs),
 // messages double-buffered in LDS (2 x 64 KiB), one block per CU.  The forward messages R~_t of every step go to a
 // per-block tape in the workspace ([n+1][G] float32 written as float4, then the per-step normalisers N_t) and are read
-// back by the backward pass one quad ahead, through raw buffer instructions (SGPR base + one VGPR lane offset).
+// back by the backward pass one quad ahead, through raw buffer instructions (SGPR base + one VGPR lane offset) with
+// the non-temporal policy (written once, read once a pass later).  The next step's weight and normaliser are loaded
+// one step ahead.  With several waves per sequence each wave's (S0, S1) of every step goes to the workspace and the
+// soft codewords are formed after the backward pass, so the step loop carries no serial output reduction.
 #include "kernel_args.hpp"
 #include "trellis.hpp"
 
