@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -75,11 +76,15 @@ def parse_args():
 
 
 def source_digest(op: str) -> str:
+    """Digest of a kernel's sources with comments and whitespace removed (comment edits keep counters valid)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "differentiable_bcjr_amd", "csrc")
     for f in KERNEL_SOURCES[op] + COMMON_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
