@@ -8,6 +8,10 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 * ``soft_codeword_grad`` -- dL/dw from an upstream dL/dw_soft, the exact derivative of the soft codeword;
 * ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32.
 
+``soft_quantize`` ties the first two together for autograd: its forward is ``soft_codeword`` and its backward
+``soft_codeword_grad``, the weights' gradient of the soft codeword being exact ("exactly differentiable with respect
+to the weight pre-image", Technical Summary, "Core Mechanism").
+
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
 in the library's kernels.
@@ -18,7 +22,8 @@ import torch
 
 from . import abi
 
-__all__ = ["soft_codeword", "soft_codeword_grad", "viterbi_hard_code", "workspace_bytes", "BCJRError", "abi"]
+__all__ = ["soft_codeword", "soft_codeword_grad", "viterbi_hard_code", "soft_quantize", "workspace_bytes", "BCJRError",
+           "abi"]
 
 
 class BCJRError(RuntimeError):
@@ -125,3 +130,30 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
     _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
                                  w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), _stream(w.device)))
     return states, w_hard, cost
+
+
+class _SoftQuantize(torch.autograd.Function):
+    """w_soft = soft_codeword(w); dL/dw = soft_codeword_grad(w, dL/dw_soft).  The codebook is a constant."""
+
+    @staticmethod
+    def forward(ctx, w, codebook, L, k, T, boundary_state):
+        ctx.save_for_backward(w, codebook, boundary_state)
+        ctx.params = (L, k, T)
+        return soft_codeword(w, codebook, L, k, T, boundary_state)
+
+    @staticmethod
+    def backward(ctx, grad_w_soft):
+        if ctx.needs_input_grad[1]:
+            raise NotImplementedError("soft_quantize has no gradient with respect to the codebook")
+        w, codebook, boundary_state = ctx.saved_tensors
+        L, k, T = ctx.params
+        grad_w = None
+        if ctx.needs_input_grad[0]:
+            grad_w = soft_codeword_grad(w, codebook, grad_w_soft.contiguous(), L, k, T, boundary_state)
+        return grad_w, None, None, None, None, None
+
+
+def soft_quantize(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
+                  boundary_state: torch.Tensor | None = None) -> torch.Tensor:
+    """The soft codeword of w [B, n] as a differentiable function of w (autograd runs the exact gradient kernel)."""
+    return _SoftQuantize.apply(w, codebook, L, k, T, boundary_state)

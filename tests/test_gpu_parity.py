@@ -498,3 +498,20 @@ def test_concurrent_streams_with_separate_workspaces(dev):
         for i in range(2):
             for a, b in zip(outs[i], ref[i]):
                 assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("sigma", [False, True])
+def test_soft_quantize_autograd(oracle_mod, dev, sigma):
+    """Autograd through soft_quantize gives the soft codeword forward and the exact weights' gradient backward."""
+    L, B, n, T = 10, 6, 24, 0.1
+    w, c, g, s = _inputs(L, B, n, 61, sigma)
+    wt = _t(w, dev).requires_grad_(True)
+    out = dba.soft_quantize(wt, _t(c, dev), L, 2, T, _t(s, dev))
+    (out * _t(g, dev)).sum().backward()
+    ref, _ = oracle_mod.soft(w, c, L, 2, T, sigma=s)
+    rgr, _ = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
+    assert rel_err(out.detach().cpu().numpy(), ref) <= TOL
+    assert grad_err(wt.grad.cpu().numpy(), rgr, g, c, T) <= grad_tol(T, sigma)
+    cb = _t(c, dev).requires_grad_(True)
+    with pytest.raises(NotImplementedError):
+        dba.soft_quantize(_t(w, dev), cb, L, 2, T).sum().backward()
