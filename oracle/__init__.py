@@ -51,6 +51,9 @@ class _Handle:
         lib.oracle_soft.restype = ci
         lib.oracle_grad.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p]
         lib.oracle_grad.restype = ci
+        lib.oracle_grad_codebook.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p,
+                                             f64p]
+        lib.oracle_grad_codebook.restype = ci
         lib.oracle_viterbi.argtypes = [f32p, f32p, i64, i64, ci, ci, i32p, i32p, f32p, f32p]
         lib.oracle_viterbi.restype = ci
         lib.oracle_num_threads.argtypes = []
@@ -129,6 +132,31 @@ def grad(w, c, g, L: int, k: int, T: float, sigma=None):
     if rc != 0:
         raise RuntimeError(f"oracle_grad failed ({rc})")
     return out, ws
+
+
+def grad_codebook(w, c, g, L: int, k: int, T: float, sigma=None, per_sequence: bool = False):
+    """dL/dc [2^L] summed over the batch (float64), dL/dw [B, n] and w_soft [B, n], for upstream g = dL/dw_soft.
+
+    With ``per_sequence`` the first result is [B, 2^L], one row per sequence.  A sequence with no admissible path
+    (sigma mode, n < L/k) has a NaN row, so the batch sum is NaN.
+    """
+    w = _f32(w)
+    c = _f32(c)
+    g = _f32(g)
+    _check_shapes(w, c, L)
+    if g.shape != w.shape:
+        raise ValueError("g must match w")
+    B, n = w.shape
+    sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
+    gw = np.empty((B, n), np.float64)
+    ws = np.empty((B, n), np.float64)
+    gc = np.empty((B, 1 << L), np.float64)
+    rc = _load().oracle_grad_codebook(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(g, ctypes.c_float), B,
+                                      n, L, k, float(T), _ptr(sg, ctypes.c_int32), _ptr(gw, ctypes.c_double),
+                                      _ptr(ws, ctypes.c_double), _ptr(gc, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError(f"oracle_grad_codebook failed ({rc})")
+    return (gc if per_sequence else gc.sum(axis=0)), gw, ws
 
 
 def viterbi(w, c, L: int, k: int, sigma=None):

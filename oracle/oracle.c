@@ -198,6 +198,14 @@ int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int
  *           = sum_b P(s_{u+1} = Succ_b(s) | s_u = s) [g_{u+1} c(Succ_b(s)) + rb_{u+1}(Succ_b(s))],
  *     where P(s_{u+1} = Succ_b(s) | s_u = s) = softmax_b [theta_{u+1}(Succ_b(s)) + beta_{u+1}(Succ_b(s))].
  * States of zero posterior weight contribute nothing.
+ *
+ * Codebook gradient (the soft codeword is differentiable in the trellis parameters as well, gist.science Technical
+ * Summary, "Core Mechanism"; the parameters of a bitshift trellis with a table codebook are the values c(s)).
+ * d(-E/T)/d c(v) = (2/T) sum_u (w_u - c(v)) [s_u = v], and w_soft_t depends on c(v) directly through c(s_t) as well
+ * as through the path measure, so
+ *   dL/dc(v) = sum_t g_t P(s_t = v) + Cov_p(F, (2/T) sum_u (w_u - c(v)) [s_u = v])
+ *            = sum_u P(s_u = v) [ g_u + (2/T) (w_u - c(v)) (E[F | s_u = v] - E[F]) ],
+ * summed here per sequence (the caller adds sequences up).
  */
 static void softmax_weights(const double* x, int m, double* pw) {
     double mx = -INFINITY;
@@ -213,10 +221,12 @@ static void softmax_weights(const double* x, int m, double* pw) {
 }
 
 static void grad_one(const float* w, const float* c, const float* g, int64_t n, int L, int k, double T,
-                     int has_sigma, uint32_t sigma, double* grad, double* w_soft, double* alpha,
+                     int has_sigma, uint32_t sigma, double* grad, double* w_soft, double* gc, double* alpha,
                      double* ra, double* b0, double* b1, double* rb0, double* rb1, double* tmp) {
     const uint32_t S = 1u << L, P = 1u << k;
     double x[64], pw[64];
+    if (gc)
+        for (uint32_t s = 0; s < S; ++s) gc[s] = 0.0;
     forward(w, c, n, L, k, T, has_sigma, sigma, alpha);
     /* ra: forward expectation pass */
     for (uint32_t s = 0; s < S; ++s) ra[s] = (double)g[0] * (double)c[s];
@@ -276,6 +286,10 @@ static void grad_one(const float* w, const float* c, const float* g, int64_t n, 
         double cov = 0.0;
         for (uint32_t s = 0; s < S; ++s)
             if (tmp[s] != 0.0) cov += tmp[s] * ((double)c[s] - m0) * (rt[s] + rbcur[s] - mr);
+        if (gc && isfinite(lnz))
+            for (uint32_t s = 0; s < S; ++s)
+                if (tmp[s] != 0.0)
+                    gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));
         if (isfinite(lnz)) {
             grad[t] = (2.0 / T) * cov;
             if (w_soft) w_soft[t] = m0;
@@ -284,10 +298,12 @@ static void grad_one(const float* w, const float* c, const float* g, int64_t n, 
             if (w_soft) w_soft[t] = NAN;
         }
     }
+    if (gc && !isfinite(lnz))   /* no path satisfies the boundary: the loss, hence its gradient, is undefined */
+        for (uint32_t s = 0; s < S; ++s) gc[s] = NAN;
 }
 
-int oracle_grad(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, double T,
-                const int32_t* sigma, double* grad, double* w_soft) {
+static int grad_all(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, double T,
+                    const int32_t* sigma, double* grad, double* w_soft, double* gc) {
     if (check_args(B, n, L, k) != ORACLE_OK || k > 6 || !(T > 0.0) || !w || !c || !g || !grad)
         return ORACLE_ERR_ARG;
     const size_t S = (size_t)1 << L;
@@ -309,12 +325,26 @@ int oracle_grad(const float* w, const float* c, const float* g, int64_t B, int64
             for (int64_t b = 0; b < B; ++b) {
                 uint32_t sg = sigma ? ((uint32_t)sigma[b] & (uint32_t)(S - 1)) : 0u;
                 grad_one(w + b * n, c, g + b * n, n, L, k, T, sigma != NULL, sg, grad + b * n,
-                         w_soft ? w_soft + b * n : NULL, alpha, ra, b0, b1, rb0, rb1, tmp);
+                         w_soft ? w_soft + b * n : NULL, gc ? gc + (size_t)b * S : NULL, alpha, ra, b0, b1, rb0,
+                         rb1, tmp);
             }
         }
         free(alpha); free(ra); free(b0); free(b1); free(rb0); free(rb1); free(tmp);
     }
     return err;
+}
+
+/* grad [B, n]: dL/dw for upstream g = dL/dw_soft; w_soft [B, n] optional. */
+int oracle_grad(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, double T,
+                const int32_t* sigma, double* grad, double* w_soft) {
+    return grad_all(w, c, g, B, n, L, k, T, sigma, grad, w_soft, NULL);
+}
+
+/* The same, plus gc [B, 2^L]: dL/dc of each sequence on its own (NaN for a sequence with no admissible path). */
+int oracle_grad_codebook(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k,
+                         double T, const int32_t* sigma, double* grad, double* w_soft, double* gc) {
+    if (!gc) return ORACLE_ERR_ARG;
+    return grad_all(w, c, g, B, n, L, k, T, sigma, grad, w_soft, gc);
 }
 
 /* ------------------------------------------------------------------------------------------------ */

@@ -72,6 +72,25 @@ def brute_jacobian(paths, w, c, T):
     return (2.0 / T) * (cc * p[:, None]).T @ cc
 
 
+def brute_codebook_jacobian(paths, w, c, T):
+    """K_tv = d w_soft_t / d c(v) over all paths.
+
+    c(v) enters w_soft_t = sum_path p(path) c(s_t) twice: directly (the emitted value, weight P(s_t = v)) and
+    through the path measure, where d log p / d c(v) = h_v - E[h_v] with h_v = (2/T) sum_u (w_u - c(v)) [s_u = v].
+    """
+    _, _, p = brute_soft(paths, w, c, T)
+    S = c.shape[0]
+    n = paths.shape[1]
+    cv = c.astype(np.float64)[paths]
+    onehot = (paths[:, :, None] == np.arange(S)[None, None, :]).astype(np.float64)      # [P, n, S]
+    direct = np.einsum("p,pts->ts", p, onehot)                                            # P(s_t = v)
+    dw = w.astype(np.float64)[:, None] - c.astype(np.float64)[None, :]                   # [n, S]
+    h = (2.0 / T) * np.einsum("pus,us->ps", onehot, dw)                                   # [P, S]
+    hc = h - (p[:, None] * h).sum(axis=0)[None, :]
+    cc = cv - (p[:, None] * cv).sum(axis=0)[None, :]
+    return direct + np.einsum("p,pt,ps->ts", p, cc, hc)
+
+
 def brute_viterbi_fp32(paths, w, c):
     """Per-path float32 cost accumulated in step order, ((e_1 + e_2) + e_3) + ..., and the argmin set."""
     w32 = w.astype(np.float32)

@@ -30,6 +30,14 @@ MUTANTS = [
      "acc += pw[b] * ((double)g[t] * (double)c[u] + rbnext[u]);"),
     ("grad_uncentred_codeword", "cov += tmp[s] * ((double)c[s] - m0) * (rt[s] + rbcur[s] - mr);",
      "cov += tmp[s] * ((double)c[s]) * (rt[s] + rbcur[s] - mr) * 0.5;"),
+    ("codebook_drops_direct_term", "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));",
+     "gc[s] += tmp[s] * ((2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));"),
+    ("codebook_residual_sign", "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));",
+     "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)c[s] - (double)w[t]) * (rt[s] + rbcur[s] - mr));"),
+    ("codebook_uncentred", "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));",
+     "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s]));"),
+    ("codebook_factor", "gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));",
+     "gc[s] += tmp[s] * ((double)g[t] + (1.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));"),
     ("viterbi_tie_rule", "if (v < best) { best = v; arg = a; }", "if (v <= best) { best = v; arg = a; }"),
     ("viterbi_end_tie_rule", "if (mcur[s] < mcur[s_end]) s_end = s;", "if (mcur[s] <= mcur[s_end]) s_end = s;"),
     ("viterbi_fma_order", "mcur[s] = e + best;", "mcur[s] = fmaf(d, d, best);"),

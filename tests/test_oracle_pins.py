@@ -362,3 +362,86 @@ def test_tiny_workload_sigma_and_free_self_consistent(oracle_mod):
         ws, lz, dev = oracle_mod.soft(w, c, wl.L, wl.k, T, with_check=True)
         assert np.isfinite(ws).all() and np.isfinite(lz).all()
         assert dev.max() < 1e-8 * max(1.0, np.abs(lz).max())
+
+
+# ------------------------------------------------------------------------------ P9 gradient in the codebook values
+
+
+@pytest.mark.parametrize("L,k,n", TRELLISES)
+@pytest.mark.parametrize("T", [1.0, 0.2])
+def test_codebook_grad_matches_brute_force(oracle_mod, L, k, n, T):
+    w, c, g = _inputs(L, n, 13 * L + 7 * k + n)
+    gc, gw, ws = oracle_mod.grad_codebook(w, c, g, L, k, T, per_sequence=True)
+    paths = pins.free_paths(L, k, n)
+    for b in range(w.shape[0]):
+        ref = g[b].astype(np.float64) @ pins.brute_codebook_jacobian(paths, w[b], c, T)
+        np.testing.assert_allclose(gc[b], ref, rtol=0, atol=1e-11 * max(1.0, np.abs(ref).max()))
+        Jw = pins.brute_jacobian(paths, w[b], c, T)
+        np.testing.assert_allclose(gw[b], Jw @ g[b].astype(np.float64), rtol=0, atol=1e-11 * max(1.0, np.abs(gw[b]).max()))
+    total, _, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
+    np.testing.assert_allclose(total, gc.sum(axis=0), rtol=0, atol=1e-13 * max(1.0, np.abs(total).max()))
+
+
+@pytest.mark.parametrize("L,k,n", [(4, 2, 6), (5, 2, 5), (4, 1, 8)])
+def test_codebook_grad_matches_brute_force_sigma(oracle_mod, L, k, n):
+    T = 0.6
+    w, c, g = _inputs(L, n, 321 + L)
+    sig = np.array([2, 9, (1 << L) - 3], np.int32)
+    gc, _, _ = oracle_mod.grad_codebook(w, c, g, L, k, T, sigma=sig, per_sequence=True)
+    for b in range(w.shape[0]):
+        paths = pins.sigma_paths(L, k, n, int(sig[b]))
+        ref = g[b].astype(np.float64) @ pins.brute_codebook_jacobian(paths, w[b], c, T)
+        np.testing.assert_allclose(gc[b], ref, rtol=0, atol=1e-11 * max(1.0, np.abs(ref).max()))
+
+
+def test_brute_codebook_jacobian_is_the_derivative():
+    """The covariance form of the codebook Jacobian equals finite differences of the brute-force soft codeword."""
+    L, k, n, T = 4, 2, 5, 0.7
+    w, c, _ = _inputs(L, n, 4321, B=1)
+    paths = pins.free_paths(L, k, n)
+    K = pins.brute_codebook_jacobian(paths, w[0], c, T)
+    h = 1e-4
+    c0 = c.astype(np.float64)
+    for v in range(1 << L):
+        e = np.zeros(1 << L)
+        e[v] = h
+        fp, _, _ = pins.brute_soft(paths, w[0], c0 + e, T)
+        fm, _, _ = pins.brute_soft(paths, w[0], c0 - e, T)
+        np.testing.assert_allclose((fp - fm) / (2 * h), K[:, v], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("sigma", [None, 77])
+def test_codebook_and_weight_grads_sum_to_upstream_total(oracle_mod, sigma):
+    """Moving every codebook value and every weight by the same amount leaves the path measure alone and moves each
+    w_soft_t by that amount, so sum_v dL/dc(v) + sum_u dL/dw_u = sum_t g_t exactly."""
+    L, k, n, T = 8, 2, 40, 0.3
+    w, c, g = _inputs(L, n, 555, B=3)
+    sig = None if sigma is None else np.full(3, sigma, np.int32)
+    gc, gw, _ = oracle_mod.grad_codebook(w, c, g, L, k, T, sigma=sig, per_sequence=True)
+    for b in range(3):
+        lhs = gc[b].sum() + gw[b].sum()
+        rhs = g[b].astype(np.float64).sum()
+        assert abs(lhs - rhs) <= 1e-10 * (np.abs(gc[b]).sum() + np.abs(gw[b]).sum() + np.abs(rhs))
+
+
+def test_codebook_grad_low_temperature_is_viterbi_histogram(oracle_mod):
+    """T -> 0: the measure sits on the best path s*, the covariance term dies as exp(-gap/T)/T, and dL/dc(v) tends to
+    sum_t g_t [s*_t = v]."""
+    L, k, n = 5, 2, 6
+    w, c, g = _inputs(L, n, 777, B=3)
+    paths = pins.free_paths(L, k, n)
+    for b in range(3):
+        E = pins.path_energies(paths, w[b], c)
+        order = np.argsort(E)
+        T = (E[order[1]] - E[order[0]]) / 60.0
+        gc, _, _ = oracle_mod.grad_codebook(w[b:b + 1], c, g[b:b + 1], L, k, T)
+        ref = np.zeros(1 << L)
+        np.add.at(ref, paths[order[0]], g[b].astype(np.float64))
+        np.testing.assert_allclose(gc, ref, rtol=0, atol=1e-9 * max(1.0, np.abs(ref).max()))
+
+
+def test_codebook_grad_nan_when_no_path(oracle_mod):
+    L, k, n = 6, 2, 2   # sigma mode needs n >= L/k
+    w, c, g = _inputs(L, n, 9, B=2)
+    gc, gw, _ = oracle_mod.grad_codebook(w, c, g, L, k, 0.5, sigma=np.array([5, 40], np.int32), per_sequence=True)
+    assert np.isnan(gc).all() and np.isnan(gw).all()
