@@ -6,11 +6,14 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
   bitshift-trellis paths at temperature T, and ln Z (BCJR-QAT, arXiv 2605.10655; gist.science Technical Summary,
   "Core Mechanism");
 * ``soft_codeword_grad`` -- dL/dw from an upstream dL/dw_soft, the exact derivative of the soft codeword;
+* ``soft_codeword_grad_codebook`` -- dL/dc [2^L], the exact derivative in the codebook values (the trellis
+  parameters), summed over the batch, together with dL/dw;
 * ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32.
 
-``soft_quantize`` ties the first two together for autograd: its forward is ``soft_codeword`` and its backward
-``soft_codeword_grad``, the weights' gradient of the soft codeword being exact ("exactly differentiable with respect
-to the weight pre-image", Technical Summary, "Core Mechanism").
+``soft_quantize`` ties them together for autograd: its forward is ``soft_codeword``; its backward is
+``soft_codeword_grad``, or ``soft_codeword_grad_codebook`` when the codebook needs a gradient too.  Both gradients
+are exact ("exactly differentiable with respect to the weight pre-image and trellis parameters", Technical Summary,
+"Core Mechanism").
 
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
@@ -22,8 +25,8 @@ import torch
 
 from . import abi
 
-__all__ = ["soft_codeword", "soft_codeword_grad", "viterbi_hard_code", "soft_quantize", "workspace_bytes", "BCJRError",
-           "abi"]
+__all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code", "soft_quantize",
+           "workspace_bytes", "BCJRError", "abi"]
 
 
 class BCJRError(RuntimeError):
@@ -64,7 +67,7 @@ def _stream(device) -> int:
 
 
 def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2) -> int:
-    """Device workspace bytes the library needs for op (abi.BCJR_OP_SOFT / _GRAD / _VITERBI)."""
+    """Device workspace bytes the library needs for op (abi.BCJR_OP_SOFT / _GRAD / _VITERBI / _GRAD_CODEBOOK)."""
     return abi.bcjr_workspace_bytes(op, B, n, L, k)
 
 
@@ -114,6 +117,30 @@ def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: tor
     return (grad, ws_out) if return_w_soft else grad
 
 
+def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int,
+                                k: int = 2, T: float = 1.0, boundary_state: torch.Tensor | None = None, *,
+                                return_grad_w: bool = True, return_w_soft: bool = False,
+                                workspace: torch.Tensor | None = None):
+    """dL/dc [2^L] (summed over the batch) given dL/dw_soft [B, n]; then dL/dw [B, n] if ``return_grad_w`` and the
+    soft codeword if ``return_w_soft``.  Returns a tuple when either is asked for."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    g = _f32(grad_w_soft, "grad_w_soft")
+    if w.dim() != 2 or g.shape != w.shape:
+        raise ValueError("w and grad_w_soft must both be [B, n]")
+    B, n = w.shape
+    sig = _sigma(boundary_state, B, w.device)
+    gc = torch.empty(1 << L, dtype=torch.float32, device=w.device)
+    grad = torch.empty_like(w) if return_grad_w else None
+    ws_out = torch.empty_like(w) if return_w_soft else None
+    ws, need = _workspace(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, k, w.device, workspace)
+    _check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                                g.data_ptr(), gc.data_ptr(), _ptr(grad), _ptr(ws_out), ws.data_ptr(),
+                                                ws.numel(), _stream(w.device)))
+    extra = tuple(x for x in (grad, ws_out) if x is not None)
+    return (gc, *extra) if extra else gc
+
+
 def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2,
                       boundary_state: torch.Tensor | None = None, *, workspace: torch.Tensor | None = None):
     """(states [B, n] int32, w_hard [B, n] float32, cost [B] float32) of the minimum-energy paths."""
@@ -133,7 +160,7 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
 
 
 class _SoftQuantize(torch.autograd.Function):
-    """w_soft = soft_codeword(w); dL/dw = soft_codeword_grad(w, dL/dw_soft).  The codebook is a constant."""
+    """w_soft = soft_codeword(w, c); dL/dw and dL/dc from the exact gradient kernels."""
 
     @staticmethod
     def forward(ctx, w, codebook, L, k, T, boundary_state):
@@ -143,17 +170,23 @@ class _SoftQuantize(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_w_soft):
-        if ctx.needs_input_grad[1]:
-            raise NotImplementedError("soft_quantize has no gradient with respect to the codebook")
         w, codebook, boundary_state = ctx.saved_tensors
         L, k, T = ctx.params
-        grad_w = None
-        if ctx.needs_input_grad[0]:
-            grad_w = soft_codeword_grad(w, codebook, grad_w_soft.contiguous(), L, k, T, boundary_state)
-        return grad_w, None, None, None, None, None
+        g = grad_w_soft.contiguous()
+        grad_w = grad_c = None
+        if ctx.needs_input_grad[1]:
+            if ctx.needs_input_grad[0]:
+                grad_c, grad_w = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state)
+            else:
+                grad_c = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state, return_grad_w=False)
+            grad_c = grad_c.to(codebook.dtype)
+        elif ctx.needs_input_grad[0]:
+            grad_w = soft_codeword_grad(w, codebook, g, L, k, T, boundary_state)
+        return grad_w, grad_c, None, None, None, None
 
 
 def soft_quantize(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
                   boundary_state: torch.Tensor | None = None) -> torch.Tensor:
-    """The soft codeword of w [B, n] as a differentiable function of w (autograd runs the exact gradient kernel)."""
+    """The soft codeword of w [B, n] as a differentiable function of w and of the codebook [2^L] (autograd runs the
+    exact gradient kernels)."""
     return _SoftQuantize.apply(w, codebook, L, k, T, boundary_state)

@@ -22,9 +22,10 @@ BCJR_ERR_HIP = -6
 BCJR_OP_SOFT = 0
 BCJR_OP_GRAD = 1
 BCJR_OP_VITERBI = 2
+BCJR_OP_GRAD_CODEBOOK = 3
 
-EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "viterbi_hard_code", "bcjr_workspace_bytes",
-           "bcjr_status_string")
+EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
+           "bcjr_workspace_bytes", "bcjr_status_string")
 
 _lib = None
 
@@ -42,6 +43,8 @@ def load() -> ctypes.CDLL:
     lib.bcjr_soft_codeword.restype = ctypes.c_int
     lib.bcjr_soft_codeword_grad.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.bcjr_soft_codeword_grad.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_grad_codebook.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.bcjr_soft_codeword_grad_codebook.restype = ctypes.c_int
     lib.viterbi_hard_code.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_hard_code.restype = ctypes.c_int
     lib.bcjr_workspace_bytes.argtypes = [i32, i64, i64, i32, i32]
@@ -62,6 +65,12 @@ def bcjr_soft_codeword_grad(w, codebook, B, n, L, k, T, boundary_state, grad_w_s
                             workspace_bytes, stream) -> int:
     return load().bcjr_soft_codeword_grad(w, codebook, B, n, L, k, T, boundary_state, grad_w_soft, grad_w, w_soft,
                                           workspace, workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_grad_codebook(w, codebook, B, n, L, k, T, boundary_state, grad_w_soft, grad_codebook, grad_w,
+                                     w_soft, workspace, workspace_bytes, stream) -> int:
+    return load().bcjr_soft_codeword_grad_codebook(w, codebook, B, n, L, k, T, boundary_state, grad_w_soft,
+                                                   grad_codebook, grad_w, w_soft, workspace, workspace_bytes, stream)
 
 
 def viterbi_hard_code(w, codebook, B, n, L, k, boundary_state, states, w_hard, cost, workspace, workspace_bytes,

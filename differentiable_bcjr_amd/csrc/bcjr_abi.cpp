@@ -15,6 +15,7 @@ struct GradArgs;
 struct ViterbiArgs;
 hipError_t launch_soft(int L, const SoftArgs& a, int grid, hipStream_t st);
 hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st);
+hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook);
 hipError_t launch_viterbi(int L, const ViterbiArgs& a, int grid, hipStream_t st);
 
 }  // namespace bcjr
@@ -64,6 +65,10 @@ Plan make_plan(int op, int64_t B, int64_t n, int L) {
         case BCJR_OP_GRAD:   // + per-wave (S0..S3) of every step when a sequence spans several waves
             p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0);
             break;
+        case BCJR_OP_GRAD_CODEBOOK:   // the gradient's slot + one float accumulator per state
+            p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0) +
+                           align256(((size_t)1 << L) * 4);
+            break;
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
     }
     p.total = (size_t)p.slots * p.slot_bytes;
@@ -83,7 +88,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? BCJR_OK : BCJR_ERR_HIP; 
 extern "C" {
 
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
-    if (op < BCJR_OP_SOFT || op > BCJR_OP_VITERBI) return 0;
+    if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_CODEBOOK) return 0;
     if (check_shape(B, n, L, k) != BCJR_OK) return 0;
     return make_plan(op, B, n, L).total;
 }
@@ -147,6 +152,32 @@ int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, in
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
     return hip_status(launch_grad(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                     int32_t k, float T, const int32_t* boundary_state, const float* grad_w_soft,
+                                     float* grad_codebook, float* grad_w, float* w_soft, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !grad_w_soft || !grad_codebook) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    const Plan p = make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    GradArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.g = grad_w_soft;
+    a.B = B;
+    a.n = (int)n;
+    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.two_over_T = (float)(2.0 / (double)T);
+    a.sigma = boundary_state;
+    a.grad = grad_w;
+    a.w_soft = w_soft;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_grad_codebook(L, a, p.grid, static_cast<hipStream_t>(stream), grad_codebook));
 }
 
 int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,

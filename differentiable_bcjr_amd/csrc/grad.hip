@@ -26,6 +26,8 @@
 // next step's scalars (w, g, normaliser, Q offset) one step ahead.  With several waves per sequence only (S0, S1) is
 // combined across waves inside the step loop; every wave's (S0..S3) goes to the workspace and the outputs are formed
 // after the backward pass.
+#include <type_traits>
+
 #include "kernel_args.hpp"
 #include "trellis.hpp"
 
@@ -51,7 +53,10 @@ __device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs
     }
 }
 
-template <int L>
+// GC: also accumulate dL/dc per state of the trellis into this slot's accumulator (read-modify-write of
+// [2^L] floats at the end of the slot, one float4 per group and step), normalising each step's posterior by the
+// previous step's exact total, with the running normaliser sums in double.
+template <int L, bool GC>
 __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     using Gm = Geo<L>;
     constexpr int G = Gm::G, Q = Gm::Q, QPT = Gm::QPT, TPS = Gm::TPS, SPB = Gm::SPB, WPS = Gm::WPS;
@@ -104,6 +109,18 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     // with several waves per sequence, each wave's (S0, S1, S2, S3) of every step goes here and the outputs are
     // formed after the backward pass; only (S0, S1) is reduced across waves inside the loop (for the P offset)
     const uint32_t part_base = kq_base + (uint32_t)align256((size_t)n * 4);
+    // the codebook-gradient accumulator of the slot: state s at acc_base + 4 s, so the 4 states of group (m, a)
+    // are the float4 at acc_base + 16 (a Q + j)
+    const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * 16) : 0u);
+    using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
+    const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
+    if constexpr (GC) {
+#pragma unroll
+        for (int m = 0; m < QPT; ++m)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+    }
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
@@ -236,6 +253,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         }
         // rz = log2 Z - A_n and E[F] (which centres the covariance of the backward pass)
         float rz, EF;
+        RT rzr;   // rz in the precision of the running sums
         if (!has_sigma) {
             float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -263,6 +281,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 }
             }
             rz = N + lg2(z0);
+            rzr = (RT)N + (RT)lg2(z0);
             EF = z1 / z0 + K;   // the final outputs Q^_n carry the offset K_{n-1}
             __syncthreads();   // tape writes of the forward pass visible to every thread of the block
         } else {
@@ -272,14 +291,16 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             const float r = buf_ld_nt(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
             const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
+            rzr = (r < 0.5f * kNeg) ? (RT)kNeg : (RT)fmaf(-d, d, r) - (RT)N_last;
             EF = fmaf(gb[n - 1] * inv_scale, d, q + K_last);   // Q^_{n-1} carries the offset K_{n-2}
         }
         const bool valid = rz > 0.5f * kNeg;
 
         // ------------------------------------------------------------------ backward: B~ and P, covariance
         float Nb = 0.f;
-        float C = 0.f;
-        float D = 0.f;
+        RT C = 0;
+        RT D = 0;
+        float lam = 1.f;   // 1 / (posterior total of the previous step), GC only
         float kb = 0.f;   // kappa_{t+1} = g_{t+1} (w_soft_{t+1} - w_{t+1}), subtracted from the P^ inputs
         float H = 0.f;    // sum of the kappas of the steps after t
         int t = n - 1;
@@ -307,7 +328,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     mq[u] = (u == (sig >> 2)) ? pz : 0.f;
                 }
             if (tau == 0 && active) {
-                args.grad[b * n + n - 1] = valid ? 0.f : __builtin_nanf("");
+                if (!GC || args.grad) args.grad[b * n + n - 1] = valid ? 0.f : __builtin_nanf("");
                 if (args.w_soft) args.w_soft[b * n + n - 1] = valid ? args.cb[sig] : __builtin_nanf("");
             }
             D = N_last;
@@ -315,16 +336,25 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             kb = pz;
             H = pz;
             t = n - 2;
+            if constexpr (GC) {   // p_{n-1} is the indicator of sigma and E[F | s_{n-1}] = E[F]: dL/dc(sigma) += g_{n-1}
+                const uint32_t js = (sig >> 2) & (uint32_t)(Q - 1);
+                if (active && valid && (uint32_t)tau == js % (uint32_t)TPS) {
+                    const float acc = buf_ld(tape, sq * slot_bytes, acc_base + 4u * sig);
+                    buf_st(acc + gb[n - 1], tape, sq * slot_bytes, acc_base + 4u * sig);
+                }
+            }
         }
         lds_barrier();
 
         // loads of the next group (forward messages R~, Q^ of this step, codebook row) are issued one group ahead
         float rt_n = 0.f, qt_n = 0.f;
         float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 ac_n = make_float4(0.f, 0.f, 0.f, 0.f);   // the next group's accumulator (GC)
         if (t >= 0) {
             rt_n = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u));
             qt_n = buf_ld_nt(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+            if constexpr (GC) ac_n = buf_ld4(tape, v_quad, acc_base);
         }
         const int t_out = t;   // last step whose outputs the loop below produces
         float w_nx = 0.f, g_nx = 0.f, N_nx = 0.f, K_nx = 0.f;
@@ -346,6 +376,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             lds_barrier();
             const float wt = w_nx * scale;
             const float gt = g_nx * inv_scale;
+            const float gnat = g_nx;
             float Nt = N_nx, Kt = K_nx;
             if (t > 0) {   // the next step's weight, upstream gradient and forward scalars, one step ahead
                 w_nx = wb[t - 1];
@@ -358,7 +389,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 Kt = uniform_f(Kt);
             }
             D += Nt;
-            const float ref = (rz + D) - C;
+            const float ref = (float)((rzr + D) - C);
             // E[F | s_t = s] - E[F] = Q^_t(s >> 2) + cst + g_t (c(s) - w_t) + P''_t(s & (G-1)), cst per step
             const float cst = (Kt - EF) + H;
             float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
@@ -385,6 +416,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                         qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
                         if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
                     }
+                    float4 ac = ac_n;
+                    if constexpr (GC) {
+                        if (!last) ac_n = buf_ld4(tape, v_quad, acc_base + 16u * (TPS * m2 + Q * a2));
+                        else if (t > 0) ac_n = buf_ld4(tape, v_quad, acc_base);
+                    }
                     const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
                     const float d2 = fmaf(cr.z, scale, -wt), d3 = fmaf(cr.w, scale, -wt);
                     const float y0 = fmaf(-d0, d0, bin[m][0]), y1 = fmaf(-d1, d1, bin[m][1]);
@@ -409,6 +445,16 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     S2 = fmaf(f, er, S2);
                     S3 = fmaf(f, edr, S3);
                     lmax = run_max(lmax, out);
+                    if constexpr (GC) {
+                        // p_t(s) [g_t + (2/T)(w_t - c(s))(E[F | s] - E[F])] with p_t(s) = lam f e_i
+                        const float fa = lam * f;
+                        const float ga = fa * gnat, ka = fa * kap;
+                        ac.x = fmaf(ga, e0, fmaf(-ka, ed0 * r0, ac.x));
+                        ac.y = fmaf(ga, e1, fmaf(-ka, ed1 * r1, ac.y));
+                        ac.z = fmaf(ga, e2, fmaf(-ka, ed2 * r2, ac.z));
+                        ac.w = fmaf(ga, e3, fmaf(-ka, ed3 * r3, ac.w));
+                        if (active) buf_st4(ac, tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+                    }
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
                     mr[u] = out;            // at t = 0 these land in buffers nobody reads
                     mq[u] = ez * rcp(s);
@@ -440,16 +486,20 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 lmax = row16_max(qs < WPS ? redmax[t & 1][sq][qs] : -3.0e38f);
                 // only the P offset uses m1 here, and any value common to the block serves: the approximate
                 // reciprocal keeps the division off the step's critical path
-                m1 = row16_sum(p.y) * rcp(row16_sum(p.x));
+                const float s0b = row16_sum(p.x);
+                m1 = row16_sum(p.y) * rcp(s0b);
+                if constexpr (GC) lam = rcp(s0b);
             } else {
                 m1 = S1 * (1.0f / S0);
+                if constexpr (GC) lam = 1.0f / S0;
             }
             if constexpr (WPS == 1) {
                 if (tau == 0 && active) {
                     const float i0 = 1.0f / S0;
                     const float m2 = S2 * i0;
                     const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' scaled
-                    args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (!GC || args.grad)
+                        args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
                     if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
                 }
             }
@@ -457,6 +507,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             if constexpr (SPB == 1) {
                 lmax = uniform_f(lmax);
                 kb = uniform_f(kb);
+                if constexpr (GC) lam = uniform_f(lam);
             }
             H += kb;
             C += Nb;
@@ -481,38 +532,108 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 const float m2 = S2 * i0;
                 const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' in scaled units
                 if (active) {
-                    args.grad[b * n + tt] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (!GC || args.grad)
+                        args.grad[b * n + tt] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
                     if (args.w_soft) args.w_soft[b * n + tt] = valid ? wb[tt] + m1 * inv_scale : __builtin_nanf("");
                 }
             }
         }
+        if constexpr (GC) {
+            if (active && !valid) {   // no admissible path: the loss, hence its gradient, is undefined
+                const float nan = __builtin_nanf("");
+#pragma unroll
+                for (int m = 0; m < QPT; ++m)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+                        buf_st4(make_float4(nan, nan, nan, nan), tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+            }
+        }
         __syncthreads();
+    }
+    if constexpr (GC && SPB > 1) {
+        // the block's sequence slots hold the same states: fold them into slot 0, in slot order (the __syncthreads
+        // that ends the last sequence orders every thread's accumulator stores before these loads)
+        if (sq == 0) {
+#pragma unroll
+            for (int m = 0; m < QPT; ++m)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const uint32_t o = acc_base + 16u * (TPS * m + Q * a) + 16u * tau;
+                    float4 x = buf_ld4(tape, 0u, o);
+                    for (int q = 1; q < SPB; ++q) {
+                        const float4 y = buf_ld4(tape, (uint32_t)q * slot_bytes, o);
+                        x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
+                    }
+                    buf_st4(x, tape, 0u, o);
+                }
+        }
     }
 }
 
-template <int L>
+// dL/dc = the sum of the per-block accumulators (slot 0 of every block, `count` of them, `stride` bytes apart), in
+// block order and in double.  A block of 256 threads covers W = min(2^L, 64) states with 256 / W interleaved runs of
+// blocks each; the runs are added in run order, so the result does not depend on timing.
+__global__ void __launch_bounds__(256) codebook_reduce_kernel(const unsigned char* ws, size_t stride, uint32_t acc_off,
+                                                              int count, int S, float* out) {
+    __shared__ double part[256];
+    const int W = S < 64 ? S : 64;
+    const int R = 256 / W;
+    const int r = threadIdx.x / W, v = blockIdx.x * W + threadIdx.x % W;
+    double acc = 0.0;
+    const unsigned char* base = ws + acc_off + 4 * (size_t)v;
+    for (int q = r; q < count; q += R) acc += (double)*reinterpret_cast<const float*>(base + (size_t)q * stride);
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    if (r == 0) {
+        double x = part[threadIdx.x];
+        for (int q = 1; q < R; ++q) x += part[q * W + threadIdx.x];
+        out[v] = (float)x;
+    }
+}
+
+template <int L, bool GC>
 static hipError_t launch_grad_L(const GradArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL(grad_kernel<L>, dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    hipLaunchKernelGGL((grad_kernel<L, GC>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
     return hipGetLastError();
 }
 
-hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st) {
+template <bool GC>
+static hipError_t launch_grad_any(int L, const GradArgs& a, int grid, hipStream_t st) {
     switch (L) {
-        case 4: return launch_grad_L<4>(a, grid, st);
-        case 5: return launch_grad_L<5>(a, grid, st);
-        case 6: return launch_grad_L<6>(a, grid, st);
-        case 7: return launch_grad_L<7>(a, grid, st);
-        case 8: return launch_grad_L<8>(a, grid, st);
-        case 9: return launch_grad_L<9>(a, grid, st);
-        case 10: return launch_grad_L<10>(a, grid, st);
-        case 11: return launch_grad_L<11>(a, grid, st);
-        case 12: return launch_grad_L<12>(a, grid, st);
-        case 13: return launch_grad_L<13>(a, grid, st);
-        case 14: return launch_grad_L<14>(a, grid, st);
-        case 15: return launch_grad_L<15>(a, grid, st);
-        case 16: return launch_grad_L<16>(a, grid, st);
+        case 4: return launch_grad_L<4, GC>(a, grid, st);
+        case 5: return launch_grad_L<5, GC>(a, grid, st);
+        case 6: return launch_grad_L<6, GC>(a, grid, st);
+        case 7: return launch_grad_L<7, GC>(a, grid, st);
+        case 8: return launch_grad_L<8, GC>(a, grid, st);
+        case 9: return launch_grad_L<9, GC>(a, grid, st);
+        case 10: return launch_grad_L<10, GC>(a, grid, st);
+        case 11: return launch_grad_L<11, GC>(a, grid, st);
+        case 12: return launch_grad_L<12, GC>(a, grid, st);
+        case 13: return launch_grad_L<13, GC>(a, grid, st);
+        case 14: return launch_grad_L<14, GC>(a, grid, st);
+        case 15: return launch_grad_L<15, GC>(a, grid, st);
+        case 16: return launch_grad_L<16, GC>(a, grid, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st) {
+    return launch_grad_any<false>(L, a, grid, st);
+}
+
+hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook) {
+    const hipError_t e = launch_grad_any<true>(L, a, grid, st);
+    if (e != hipSuccess) return e;
+    const GeoRT g = geo_rt(L);
+    const int S = 1 << L;
+    const int W = S < 64 ? S : 64;
+    // the accumulator sits after the tape, the two scalar tracks and (several waves per sequence) the partial sums
+    const size_t n = (size_t)a.n;
+    const size_t acc_off = 2 * align256((n + 1) * (size_t)g.G * 4) + 2 * align256(n * 4) +
+                           (g.WPS > 1 ? align256(n * (size_t)g.WPS * 16) : 0);
+    hipLaunchKernelGGL(codebook_reduce_kernel, dim3(S / W), dim3(256), 0, st, a.ws, a.slot_bytes * g.SPB,
+                       (uint32_t)acc_off, grid, S, grad_codebook);
+    return hipGetLastError();
 }
 
 }  // namespace bcjr

@@ -21,8 +21,8 @@
  *
  * Memory and execution, for every entry point:
  *   - every tensor pointer is a DEVICE pointer to contiguous row-major memory owned by the caller: w, w_soft,
- *     grad_w_soft, grad_w, w_hard are float32 [B, n]; codebook is float32 [2^L]; boundary_state, log_z and cost
- *     are [B]; states is int32 [B, n].  Outputs must not alias inputs or each other.
+ *     grad_w_soft, grad_w, w_hard are float32 [B, n]; codebook and grad_codebook are float32 [2^L];
+ *     boundary_state, log_z and cost are [B]; states is int32 [B, n].  Outputs must not alias inputs or each other.
  *   - workspace is device scratch memory owned by the caller, at least bcjr_workspace_bytes(...) bytes, aligned
  *     to 256 bytes; its contents on entry do not matter and are clobbered.  The library allocates nothing,
  *     frees nothing, keeps no state between calls and never synchronizes: the work is enqueued on `stream`
@@ -53,7 +53,7 @@ enum {
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
 
-enum { BCJR_OP_SOFT = 0, BCJR_OP_GRAD = 1, BCJR_OP_VITERBI = 2 };
+enum { BCJR_OP_SOFT = 0, BCJR_OP_GRAD = 1, BCJR_OP_VITERBI = 2, BCJR_OP_GRAD_CODEBOOK = 3 };
 
 /*
  * Soft codeword (gist.science Technical Summary, "Core Mechanism"):
@@ -79,6 +79,25 @@ int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, in
                             float* w_soft, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Gradient of the soft codeword with respect to the codebook values, the trellis parameters in which the soft
+ * codeword is also exactly differentiable (gist.science Technical Summary, "Core Mechanism"), summed over the batch
+ * because every sequence reads the same codebook:
+ *   grad_codebook[v] = sum_b sum_t grad_w_soft[b, t] * d w_soft[b, t] / d codebook[v]
+ *                    = sum_b sum_u p(s_u = v) * ( grad_w_soft[b, u]
+ *                                                 + (2 / T) (w[b, u] - codebook[v]) (E[F_b | s_u = v] - E[F_b]) ),
+ * with F_b = sum_t grad_w_soft[b, t] * codebook[s_t] and p the Boltzmann path measure of sequence b.  codebook[v]
+ * enters w_soft both as the emitted value and through the path energies.  grad_codebook is float32 [2^L], written
+ * in full (required).  grad_w (float32 [B, n]) and w_soft receive the same values as bcjr_soft_codeword_grad would
+ * give, up to rounding; each may be NULL.  One sequence with no admissible path (see above) makes every entry of
+ * grad_codebook NaN.  The result is deterministic: the per-slot partial sums are added in a fixed order.
+ * The workspace holds, besides what bcjr_soft_codeword_grad needs, one float accumulator per state per slot.
+ */
+int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                     int32_t k, float T, const int32_t* boundary_state, const float* grad_w_soft,
+                                     float* grad_codebook, float* grad_w, float* w_soft, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * Viterbi hard code, the T -> 0 limit of the soft codeword (abstract): the path of minimum energy.  Arithmetic is
  * IEEE float32 in a fixed order, without fused multiply-add:
  *   M_1(s) = fl(d*d), d = fl(w_1 - codebook[s]);  M_t(s) = fl(fl(d*d) + min over predecessors p of M_{t-1}(p)),
@@ -91,7 +110,8 @@ int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t 
                       size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace the entry point `op` (BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI) needs for
+ * Bytes of device workspace the entry point `op` (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_VITERBI or
+ * BCJR_OP_GRAD_CODEBOOK) needs for
  * these shapes; 0 when the shapes are invalid or unsupported.  Pure host function; no HIP call.
  */
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);

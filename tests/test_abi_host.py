@@ -20,10 +20,10 @@ def declared_functions():
     return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"defined", "if", "extern"})
 
 
-def test_header_declares_the_three_ops():
+def test_header_declares_every_op():
     fns = declared_functions()
-    for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "viterbi_hard_code", "bcjr_workspace_bytes",
-                 "bcjr_status_string"]:
+    for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
+                 "viterbi_hard_code", "bcjr_workspace_bytes", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -72,6 +72,8 @@ def test_workspace_bytes_formula(L, B, n):
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm + part)
     part4 = _a256(n * _wps(L) * 16) if _wps(L) > 1 else 0
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + 2 * nrm + part4)
+    acc = _a256((1 << L) * 4)   # one float accumulator per state
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, 2) == slots * (2 * msgs + 2 * nrm + part4 + acc)
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, B, n, L, 2) == slots * _a256(2 * n * TPS * 4)
 
 
@@ -83,7 +85,7 @@ def test_workspace_bytes_for_the_headline_workload():
 @pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 4097, 8, 2), (1, 4, 3, 2),
                                   (1, 4, 17, 2), (1, 4, 8, 0), (1 << 31, 4, 8, 2)])
 def test_workspace_bytes_invalid_shapes_are_zero(args):
-    for op in (0, 1, 2):
+    for op in (0, 1, 2, 3):
         assert abi.bcjr_workspace_bytes(op, *args) == 0
     assert abi.bcjr_workspace_bytes(7, 1, 4, 8, 2) == 0
 
@@ -107,6 +109,13 @@ def _grad(**kw):
     return abi.bcjr_soft_codeword_grad(*a.values())
 
 
+def _gc(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, boundary_state=None, grad_w_soft=FAKE,
+             grad_codebook=FAKE, grad_w=None, w_soft=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_grad_codebook(*a.values())
+
+
 def _vit(**kw):
     a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, boundary_state=None, states=FAKE, w_hard=None, cost=None,
              workspace=FAKE, workspace_bytes=0, stream=None)
@@ -120,6 +129,11 @@ def test_null_pointers_rejected():
     assert _soft(w_soft=None) == abi.BCJR_ERR_NULL
     assert _grad(grad_w_soft=None) == abi.BCJR_ERR_NULL
     assert _grad(grad_w=None) == abi.BCJR_ERR_NULL
+    assert _gc(grad_codebook=None) == abi.BCJR_ERR_NULL
+    assert _gc(grad_w_soft=None) == abi.BCJR_ERR_NULL
+    assert _gc(w=None) == abi.BCJR_ERR_NULL
+    # grad_w and w_soft are optional for the codebook gradient: with them NULL the next check is the workspace
+    assert _gc() == abi.BCJR_ERR_WORKSPACE
     assert _vit(states=None) == abi.BCJR_ERR_NULL
     assert _vit(codebook=None) == abi.BCJR_ERR_NULL
 
@@ -128,12 +142,14 @@ def test_null_pointers_rejected():
 def test_bad_shapes_rejected(kw):
     assert _soft(**kw) == abi.BCJR_ERR_SHAPE
     assert _grad(**kw) == abi.BCJR_ERR_SHAPE
+    assert _gc(**kw) == abi.BCJR_ERR_SHAPE
     assert _vit(**kw) == abi.BCJR_ERR_SHAPE
 
 
 def test_unsupported_k_rejected():
     assert _soft(k=1) == abi.BCJR_ERR_UNSUPPORTED
     assert _grad(L=9, k=3) == abi.BCJR_ERR_UNSUPPORTED
+    assert _gc(k=1) == abi.BCJR_ERR_UNSUPPORTED
     assert _vit(k=1) == abi.BCJR_ERR_UNSUPPORTED
 
 
@@ -141,6 +157,7 @@ def test_unsupported_k_rejected():
 def test_bad_temperature_rejected(T):
     assert _soft(T=T) == abi.BCJR_ERR_TEMP
     assert _grad(T=T) == abi.BCJR_ERR_TEMP
+    assert _gc(T=T) == abi.BCJR_ERR_TEMP
 
 
 def test_viterbi_ignores_temperature_and_checks_workspace():
@@ -157,6 +174,11 @@ def test_workspace_too_small_or_misaligned_rejected():
     assert _soft(workspace=FAKE + 64, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
     needg = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 8, 2)
     assert _grad(workspace_bytes=needg - 1) == abi.BCJR_ERR_WORKSPACE
+    needc = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 8, 2)
+    assert needc > needg
+    assert _gc(workspace_bytes=needg) == abi.BCJR_ERR_WORKSPACE   # the gradient's workspace is not enough
+    assert _gc(workspace_bytes=needc - 1) == abi.BCJR_ERR_WORKSPACE
+    assert _gc(workspace=FAKE + 128, workspace_bytes=needc) == abi.BCJR_ERR_WORKSPACE
 
 
 def test_checks_precede_each_other_in_documented_order():
@@ -177,11 +199,13 @@ def test_python_wrapper_refuses_cpu_tensors():
         dba.soft_codeword(w, c, 8)
     with pytest.raises(TypeError):
         dba.viterbi_hard_code(w, c, 8)
+    with pytest.raises(TypeError):
+        dba.soft_codeword_grad_codebook(w, c, w, 8)
 
 
 def test_largest_shape_keeps_workspace_offsets_in_32_bits():
     # the kernels address one block's slots with 32-bit buffer offsets
-    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI, abi.BCJR_OP_GRAD_CODEBOOK):
         for L in (8, 12, 16):
             G, TPS, SPB = _geo(L)
             per_block = abi.bcjr_workspace_bytes(op, SPB, 4096, L, 2)
