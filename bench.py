@@ -20,6 +20,11 @@ full-rate fp32 VALU lane slots (a half-rate max/compare/select costs 2, a quarte
 256 CUs x 128 fp32 lanes x 2.4 GHz = 78.6e12 slots/s (the published 157.3 TFLOP/s fp32 vector rate with an FMA as
 two flops).  Kernel times come from HIP events recorded on the stream the kernels run on.
 
+After the timed steps, and outside them, the codebook gradient (bcjr_soft_codeword_grad_codebook, the exact dL/dc
+summed over the batch) is timed on the same inputs and reported under ``next_rows`` with its own roofline.  Its bound
+is HBM: besides the 4 bytes of forward tape per state-step (written once, read once), every state's float32
+accumulator is read and written once per step, 12 bytes per state-step against the 8 TB/s peak.
+
 ``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
 """
 from __future__ import annotations
@@ -56,9 +61,16 @@ KERNEL_SOURCES = {
     "soft": ["soft.hip"],
     "grad": ["grad.hip"],
     "viterbi": ["viterbi.hip"],
+    "grad_codebook": ["grad.hip"],
 }
 COMMON_SOURCES = ["trellis.hpp", "kernel_args.hpp"]
-KERNEL_NAMES = {"soft": "soft_kernel<16>", "grad": "grad_kernel<16>", "viterbi": "viterbi_kernel<16>"}
+KERNEL_NAMES = {"soft": "soft_kernel<16>", "grad": "grad_kernel<16, false>", "viterbi": "viterbi_kernel<16>",
+                "grad_codebook": "grad_kernel<16, true>"}
+# HBM bytes per state-step of the codebook gradient: forward tape R~ and Q^ (one float per group each, i.e. 2 bytes
+# per state, written by the forward pass and read by the backward pass) + the per-state accumulator (4 bytes read
+# and 4 written per step)
+CODEBOOK_GRAD_BYTES = 2 * 2.0 + 8.0
+HBM_PEAK_GBS = 8000.0
 
 
 def parse_args():
@@ -70,6 +82,8 @@ def parse_args():
                     help="synthetic workload (2: 1024x1024 matrix, 3: 8192x2048, 4: 2048x2048, 5: whole layer)")
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--codebook-grad-steps", type=int, default=3,
+                    help="calls of the codebook gradient timed after the step (0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -165,7 +179,8 @@ def main():
     states = torch.empty((B, n), dtype=torch.int32, device=dev)
     w_hard = torch.empty((B, n), dtype=torch.float32, device=dev)
     cost = torch.empty((B,), dtype=torch.float32, device=dev)
-    ws_bytes = max(abi.bcjr_workspace_bytes(op, B, n, L, k) for op in (0, 1, 2))
+    ops_ws = (0, 1, 2, 3) if args.codebook_grad_steps > 0 else (0, 1, 2)
+    ws_bytes = max(abi.bcjr_workspace_bytes(op, B, n, L, k) for op in ops_ws)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
@@ -237,6 +252,37 @@ def main():
                 "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (half-rate op = 2, transcendental = 4)",
                 "units_per_launch": B * n * S}
 
+    next_rows = {}
+    if args.codebook_grad_steps > 0:
+        # the codebook gradient, timed on its own after the step (it is not part of the step)
+        grad_c = torch.empty((S,), dtype=torch.float32, device=dev)
+
+        def grad_codebook():
+            check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, g.data_ptr(),
+                                                       grad_c.data_ptr(), grad.data_ptr(), None, ws.data_ptr(),
+                                                       ws_bytes, sp), "bcjr_soft_codeword_grad_codebook")
+
+        grad_codebook()
+        torch.cuda.synchronize()
+        K2 = args.codebook_grad_steps
+        ev2 = [torch.cuda.Event(enable_timing=True) for _ in range(K2 + 1)]
+        ev2[0].record(stream)
+        for i in range(K2):
+            grad_codebook()
+            ev2[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms2 = float(np.mean([ev2[i].elapsed_time(ev2[i + 1]) for i in range(K2)]))
+        nbytes = CODEBOOK_GRAD_BYTES * B * n * S
+        gbs = nbytes / (ms2 * 1e-3) / 1e9
+        next_rows["grad_codebook"] = {
+            "entry_point": "bcjr_soft_codeword_grad_codebook", "kernel": KERNEL_NAMES["grad_codebook"],
+            "calls": K2, "ms": round(ms2, 4), "state_updates_per_s": 2 * B * n * S / (ms2 * 1e-3),
+            "weights_per_s": B * n / (ms2 * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("grad_codebook", wl.name),
+                         "per_unit": f"{CODEBOOK_GRAD_BYTES:g} B per state-step (tape 4, accumulator 8)",
+                         "units_per_launch": B * n * S}}
+
     total_upd = sum(DIRECTIONS[o] for o, _ in ops) * B * n * S
     line = {
         "metric": "trellis state-updates/sec and weights/sec, BCJR fwd+bwd, L=16 k=2 n=256",
@@ -257,6 +303,8 @@ def main():
         "ops": per_op,
         "roofline": roofline,
     }
+    if next_rows:
+        line["next_rows"] = next_rows
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, T)
     print(json.dumps(line), flush=True)
