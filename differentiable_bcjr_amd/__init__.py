@@ -15,6 +15,8 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 are exact ("exactly differentiable with respect to the weight pre-image and trellis parameters", Technical Summary,
 "Core Mechanism").
 
+``temperature_schedule`` gives the annealing sequence T0 -> T_end for a QAT run (host-side, see ``anneal``).
+
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
 in the library's kernels.
@@ -24,9 +26,10 @@ from __future__ import annotations
 import torch
 
 from . import abi
+from .anneal import temperature_schedule
 
 __all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code", "soft_quantize",
-           "workspace_bytes", "BCJRError", "abi"]
+           "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
 
 
 class BCJRError(RuntimeError):
