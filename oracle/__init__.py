@@ -177,6 +177,40 @@ def viterbi(w, c, L: int, k: int, sigma=None):
     return st, wh, cost
 
 
+TB_EXACT, TB_ROTATE = 0, 1
+
+
+def viterbi_tail_biting(w, c, L: int, k: int, mode: int = TB_EXACT):
+    """Tail-biting Viterbi with the start state chosen by the decoder: (states [B, n], c(states), cost [B], sigma [B]).
+
+    A tail-biting path has s_0 = s_n (the non-emitting start equals the last emitting state).  Both modes end with a
+    sigma-mode decode, so the result is a tail-biting path and its cost follows the fixed float32 order.
+      TB_EXACT:  sigma = the smallest state whose sigma-mode cost is the minimum over all 2^L states.
+      TB_ROTATE: decode the sequence rotated left by n // 2 with a free boundary; sigma = the state of that path at
+                 the original last weight (rotated position n - 1 - n // 2), where the cycle closes.
+    Composed from this module's Viterbi (its own pins cover it); the selection is a plain argmin.
+    """
+    w = _f32(w)
+    c = _f32(c)
+    _check_shapes(w, c, L)
+    B, n = w.shape
+    S = 1 << L
+    if mode == TB_EXACT:
+        reps = np.repeat(w, S, axis=0)
+        sig_all = np.tile(np.arange(S, dtype=np.int32), B)
+        _, _, costs = viterbi(reps, c, L, k, sigma=sig_all)
+        costs = costs.reshape(B, S)
+        sigma = np.argmin(costs, axis=1).astype(np.int32)   # first index attaining the minimum
+    elif mode == TB_ROTATE:
+        r = n // 2
+        st, _, _ = viterbi(np.roll(w, -r, axis=1), c, L, k)
+        sigma = st[:, n - 1 - r].astype(np.int32)
+    else:
+        raise ValueError("mode must be TB_EXACT or TB_ROTATE")
+    st, wh, cost = viterbi(w, c, L, k, sigma=sigma)
+    return st, wh, cost, sigma
+
+
 def num_threads() -> int:
     """OpenMP threads one oracle call uses."""
     return int(_load().oracle_num_threads())

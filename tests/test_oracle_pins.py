@@ -445,3 +445,59 @@ def test_codebook_grad_nan_when_no_path(oracle_mod):
     w, c, g = _inputs(L, n, 9, B=2)
     gc, gw, _ = oracle_mod.grad_codebook(w, c, g, L, k, 0.5, sigma=np.array([5, 40], np.int32), per_sequence=True)
     assert np.isnan(gc).all() and np.isnan(gw).all()
+
+
+# ------------------------------------------------------------------------------ P10 tail-biting with chosen sigma
+
+
+def _brute_tail_biting(L, k, n, w, c):
+    """(minimum fp32 cost over every tail-biting path, the smallest sigma attaining it, per-sigma argmin path sets)."""
+    best, arg, sets = np.float32(np.inf), -1, {}
+    for sig in range(1 << L):
+        paths = pins.sigma_paths(L, k, n, sig)
+        if paths.shape[0] == 0:
+            continue
+        acc, idx = pins.brute_viterbi_fp32(paths, w, c)
+        sets[sig] = paths[idx]
+        if acc.min() < best:
+            best, arg = acc.min(), sig
+    return best, arg, sets
+
+
+@pytest.mark.parametrize("L,k,n", [(4, 2, 5), (4, 2, 7), (5, 2, 6), (4, 1, 7)])
+def test_tail_biting_exact_matches_brute_force(oracle_mod, L, k, n):
+    w, c, _ = _inputs(L, n, 808 + L + n, B=4)
+    st, wh, cost, sig = oracle_mod.viterbi_tail_biting(w, c, L, k, oracle_mod.TB_EXACT)
+    for b in range(w.shape[0]):
+        best, arg, sets = _brute_tail_biting(L, k, n, w[b], c)
+        assert cost[b] == best and sig[b] == arg
+        assert any(np.array_equal(st[b], p) for p in sets[arg])
+        np.testing.assert_array_equal(wh[b], c[st[b]])
+
+
+def test_tail_biting_rotate_matches_brute_force_composition(oracle_mod):
+    """The heuristic's steps redone by brute force: free minimum on the rotated weights, its state at the original
+    last weight as sigma, then the sigma-constrained minimum."""
+    L, k, n = 5, 2, 8
+    w, c, _ = _inputs(L, n, 4242, B=5)
+    st, _, cost, sig = oracle_mod.viterbi_tail_biting(w, c, L, k, oracle_mod.TB_ROTATE)
+    free = pins.free_paths(L, k, n)
+    r = n // 2
+    for b in range(w.shape[0]):
+        acc, idx = pins.brute_viterbi_fp32(free, np.roll(w[b], -r), c)
+        assert sig[b] in {int(free[i][n - 1 - r]) for i in idx}
+        acc2, idx2 = pins.brute_viterbi_fp32(pins.sigma_paths(L, k, n, int(sig[b])), w[b], c)
+        assert cost[b] == acc2.min()
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_tail_biting_paths_close_the_cycle_and_exact_is_best(oracle_mod, mode):
+    L, k, n = 8, 2, 40
+    w, c, _ = _inputs(L, n, 99, B=6)
+    st, _, cost, sig = oracle_mod.viterbi_tail_biting(w, c, L, k, mode)
+    mask = (1 << (L - k)) - 1
+    assert np.array_equal(st[:, -1], sig)                       # s_n = sigma
+    assert np.array_equal(st[:, 0] >> k, sig & mask)            # s_1 is a successor of s_0 = sigma
+    assert np.array_equal(st[:, 1:] >> k, st[:, :-1] & mask)    # every step is a trellis transition
+    _, _, cost_exact, _ = oracle_mod.viterbi_tail_biting(w, c, L, k, 0)
+    assert np.all(cost >= cost_exact)
