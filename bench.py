@@ -23,7 +23,8 @@ two flops).  Kernel times come from HIP events recorded on the stream the kernel
 After the timed steps, and outside them, the codebook gradient (bcjr_soft_codeword_grad_codebook, the exact dL/dc
 summed over the batch) is timed on the same inputs and reported under ``next_rows`` with its own roofline.  Its bound
 is HBM: besides the 4 bytes of forward tape per state-step (written once, read once), every state's float32
-accumulator is read and written once per step, 12 bytes per state-step against the 8 TB/s peak.
+accumulator is read and written once per step, 12 bytes per state-step against the 8 TB/s peak.  The tail-biting
+Viterbi with rotate-and-decode start-state choice (viterbi_tail_biting, two decodes) is timed the same way.
 
 ``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
 """
@@ -83,7 +84,8 @@ def parse_args():
     ap.add_argument("--temperature", type=float, default=0.1)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--codebook-grad-steps", type=int, default=3,
-                    help="calls of the codebook gradient timed after the step (0 skips it)")
+                    help="calls of the codebook gradient (and of the tail-biting Viterbi) timed after the step "
+                         "(0 skips them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -179,7 +181,7 @@ def main():
     states = torch.empty((B, n), dtype=torch.int32, device=dev)
     w_hard = torch.empty((B, n), dtype=torch.float32, device=dev)
     cost = torch.empty((B,), dtype=torch.float32, device=dev)
-    ops_ws = (0, 1, 2, 3) if args.codebook_grad_steps > 0 else (0, 1, 2)
+    ops_ws = (0, 1, 2, 3, 5) if args.codebook_grad_steps > 0 else (0, 1, 2)
     ws_bytes = max(abi.bcjr_workspace_bytes(op, B, n, L, k) for op in ops_ws)
     ws = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -281,6 +283,34 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic("grad_codebook", wl.name),
                          "per_unit": f"{CODEBOOK_GRAD_BYTES:g} B per state-step (tape 4, accumulator 8)",
+                         "units_per_launch": B * n * S}}
+
+    if args.codebook_grad_steps > 0:
+        sigma_tb = torch.empty((B,), dtype=torch.int32, device=dev)
+
+        def tail_biting():
+            check(abi.viterbi_tail_biting(w.data_ptr(), c.data_ptr(), B, n, L, k, abi.BCJR_TB_ROTATE,
+                                          states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(), sigma_tb.data_ptr(),
+                                          ws.data_ptr(), ws_bytes, sp), "viterbi_tail_biting")
+
+        tail_biting()
+        torch.cuda.synchronize()
+        K3 = args.codebook_grad_steps
+        ev3 = [torch.cuda.Event(enable_timing=True) for _ in range(K3 + 1)]
+        ev3[0].record(stream)
+        for i in range(K3):
+            tail_biting()
+            ev3[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms3 = float(np.mean([ev3[i].elapsed_time(ev3[i + 1]) for i in range(K3)]))
+        slots3 = 2 * ALU_SLOTS["viterbi"] * B * n * S
+        next_rows["viterbi_tail_biting_rotate"] = {
+            "entry_point": "viterbi_tail_biting (BCJR_TB_ROTATE)", "kernel": "2 x viterbi_kernel<16>",
+            "calls": K3, "ms": round(ms3, 4), "weights_per_s": B * n / (ms3 * 1e-3),
+            "roofline": {"bound": "alu", "achieved": round(slots3 / (ms3 * 1e-3) / 1e12, 3),
+                         "peak": round(PEAK_SLOTS_PER_S / 1e12, 3), "unit": "T VALU-slots/s",
+                         "frac": round(slots3 / (ms3 * 1e-3) / PEAK_SLOTS_PER_S, 4),
+                         "per_unit": f"2 x {ALU_SLOTS['viterbi']} fp32 VALU slots per state-step (two decodes)",
                          "units_per_launch": B * n * S}}
 
     total_upd = sum(DIRECTIONS[o] for o, _ in ops) * B * n * S

@@ -8,7 +8,8 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 * ``soft_codeword_grad`` -- dL/dw from an upstream dL/dw_soft, the exact derivative of the soft codeword;
 * ``soft_codeword_grad_codebook`` -- dL/dc [2^L], the exact derivative in the codebook values (the trellis
   parameters), summed over the batch, together with dL/dw;
-* ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32.
+* ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32;
+* ``viterbi_tail_biting`` -- the same with s_0 = s_n and the start state chosen exactly or by rotate-and-decode.
 
 ``soft_quantize`` ties them together for autograd: its forward is ``soft_codeword``; its backward is
 ``soft_codeword_grad``, or ``soft_codeword_grad_codebook`` when the codebook needs a gradient too.  Both gradients
@@ -28,8 +29,8 @@ import torch
 from . import abi
 from .anneal import temperature_schedule
 
-__all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code", "soft_quantize",
-           "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
+__all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code",
+           "viterbi_tail_biting", "soft_quantize", "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
 
 
 class BCJRError(RuntimeError):
@@ -160,6 +161,33 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
     _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
                                  w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), _stream(w.device)))
     return states, w_hard, cost
+
+
+_TB_MODES = {"exact": (abi.BCJR_TB_EXACT, abi.BCJR_OP_VITERBI_TB_EXACT),
+             "rotate": (abi.BCJR_TB_ROTATE, abi.BCJR_OP_VITERBI_TB_ROTATE)}
+
+
+def viterbi_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, mode: str = "exact", *,
+                        workspace: torch.Tensor | None = None):
+    """(states [B, n] int32, w_hard [B, n], cost [B], sigma [B] int32) of the minimum-energy tail-biting paths
+    (s_0 = s_n), the start state chosen ``"exact"``ly (L <= 10) or by ``"rotate"``-and-decode."""
+    if mode not in _TB_MODES:
+        raise ValueError(f"mode must be one of {sorted(_TB_MODES)}")
+    tb_mode, op = _TB_MODES[mode]
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    if w.dim() != 2:
+        raise ValueError("w must be [B, n]")
+    B, n = w.shape
+    states = torch.empty((B, n), dtype=torch.int32, device=w.device)
+    w_hard = torch.empty_like(w)
+    cost = torch.empty(B, dtype=torch.float32, device=w.device)
+    sigma = torch.empty(B, dtype=torch.int32, device=w.device)
+    ws, need = _workspace(op, B, n, L, k, w.device, workspace)
+    _check(abi.viterbi_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, tb_mode, states.data_ptr(),
+                                   w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream(w.device)))
+    return states, w_hard, cost, sigma
 
 
 class _SoftQuantize(torch.autograd.Function):

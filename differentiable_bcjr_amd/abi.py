@@ -23,9 +23,14 @@ BCJR_OP_SOFT = 0
 BCJR_OP_GRAD = 1
 BCJR_OP_VITERBI = 2
 BCJR_OP_GRAD_CODEBOOK = 3
+BCJR_OP_VITERBI_TB_EXACT = 4
+BCJR_OP_VITERBI_TB_ROTATE = 5
+
+BCJR_TB_EXACT = 0
+BCJR_TB_ROTATE = 1
 
 EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
-           "bcjr_workspace_bytes", "bcjr_status_string")
+           "viterbi_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string")
 
 _lib = None
 
@@ -47,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.bcjr_soft_codeword_grad_codebook.restype = ctypes.c_int
     lib.viterbi_hard_code.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_hard_code.restype = ctypes.c_int
+    lib.viterbi_tail_biting.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.viterbi_tail_biting.restype = ctypes.c_int
     lib.bcjr_workspace_bytes.argtypes = [i32, i64, i64, i32, i32]
     lib.bcjr_workspace_bytes.restype = sz
     lib.bcjr_status_string.argtypes = [i32]
@@ -77,6 +84,12 @@ def viterbi_hard_code(w, codebook, B, n, L, k, boundary_state, states, w_hard, c
                       stream) -> int:
     return load().viterbi_hard_code(w, codebook, B, n, L, k, boundary_state, states, w_hard, cost, workspace,
                                     workspace_bytes, stream)
+
+
+def viterbi_tail_biting(w, codebook, B, n, L, k, mode, states, w_hard, cost, sigma, workspace, workspace_bytes,
+                        stream) -> int:
+    return load().viterbi_tail_biting(w, codebook, B, n, L, k, mode, states, w_hard, cost, sigma, workspace,
+                                      workspace_bytes, stream)
 
 
 def bcjr_workspace_bytes(op, B, n, L, k) -> int:

@@ -17,6 +17,10 @@ hipError_t launch_soft(int L, const SoftArgs& a, int grid, hipStream_t st);
 hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st);
 hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook);
 hipError_t launch_viterbi(int L, const ViterbiArgs& a, int grid, hipStream_t st);
+hipError_t launch_tb_select(const float* costs, int64_t rows, int S, int32_t* sigma, int32_t* sigma_out,
+                            hipStream_t st);
+hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n, int pos, int32_t* sigma,
+                                  int32_t* sigma_out, hipStream_t st);
 
 }  // namespace bcjr
 
@@ -29,6 +33,7 @@ using namespace bcjr;
 constexpr int64_t kMaxN = 4096;   // keeps every per-block workspace offset (two [n+1][2^14] float tapes) below 2^31
 constexpr int64_t kMaxB = 2147483647LL;
 constexpr float kMinT = 1e-12f;
+constexpr int32_t kMaxTailBitingExactL = 10;   // the exact choice decodes every one of the 2^L start states
 
 struct Plan {
     int grid;
@@ -83,13 +88,43 @@ int check_workspace(const void* ws, size_t bytes, const Plan& p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? BCJR_OK : BCJR_ERR_HIP; }
 
+// Tail-biting workspace: the Viterbi slots (sized for the larger of its passes), then the per-(row, sigma) costs
+// (exact) or the rotated pass's states (rotate), then the chosen sigma per row.
+struct TailBitingPlan {
+    Plan rows, first;        // the sigma-mode pass over the rows; the first pass (every sigma, or the rotated rows)
+    size_t slots_bytes, aux_off, sigma_off, total;
+};
+
+TailBitingPlan make_tb_plan(int32_t mode, int64_t B, int64_t n, int32_t L) {
+    TailBitingPlan t{};
+    t.rows = make_plan(BCJR_OP_VITERBI, B, n, L);
+    t.first = mode == BCJR_TB_EXACT ? make_plan(BCJR_OP_VITERBI, B << L, n, L) : t.rows;
+    t.slots_bytes = align256(t.first.total > t.rows.total ? t.first.total : t.rows.total);
+    t.aux_off = t.slots_bytes;
+    const size_t aux = mode == BCJR_TB_EXACT ? (size_t)(B << L) * 4 : (size_t)B * (size_t)n * 4;
+    t.sigma_off = t.aux_off + align256(aux);
+    t.total = t.sigma_off + align256((size_t)B * 4);
+    return t;
+}
+
+int check_tb_mode(int32_t mode, int32_t L) {
+    if (mode == BCJR_TB_ROTATE) return BCJR_OK;
+    if (mode == BCJR_TB_EXACT && L <= kMaxTailBitingExactL) return BCJR_OK;
+    return BCJR_ERR_UNSUPPORTED;
+}
+
 }  // namespace
 
 extern "C" {
 
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
-    if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_CODEBOOK) return 0;
+    if (op < BCJR_OP_SOFT || op > BCJR_OP_VITERBI_TB_ROTATE) return 0;
     if (check_shape(B, n, L, k) != BCJR_OK) return 0;
+    if (op == BCJR_OP_VITERBI_TB_EXACT || op == BCJR_OP_VITERBI_TB_ROTATE) {
+        const int32_t mode = op == BCJR_OP_VITERBI_TB_EXACT ? BCJR_TB_EXACT : BCJR_TB_ROTATE;
+        if (check_tb_mode(mode, L) != BCJR_OK) return 0;
+        return make_tb_plan(mode, B, n, L).total;
+    }
     return make_plan(op, B, n, L).total;
 }
 
@@ -99,7 +134,8 @@ const char* bcjr_status_string(int32_t status) {
         case BCJR_ERR_NULL: return "BCJR_ERR_NULL: a required pointer is NULL";
         case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
-        case BCJR_ERR_UNSUPPORTED: return "BCJR_ERR_UNSUPPORTED: only k = 2 has kernels";
+        case BCJR_ERR_UNSUPPORTED:
+            return "BCJR_ERR_UNSUPPORTED: only k = 2 has kernels; the exact tail-biting choice needs L <= 10";
         case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
@@ -200,6 +236,60 @@ int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t 
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
     return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                        int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !states) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_tb_mode(mode, L))) return rc;
+    const TailBitingPlan tp = make_tb_plan(mode, B, n, L);
+    if (workspace == nullptr || workspace_bytes < tp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    int32_t* sig_ws = reinterpret_cast<int32_t*>(ws + tp.sigma_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // first pass: the cost of every (row, sigma), or the free decode of the rows rotated left by n / 2
+    ViterbiArgs f{};
+    f.w = w;
+    f.cb = codebook;
+    f.n = (int)n;
+    f.ws = ws;
+    f.slot_bytes = tp.first.slot_bytes;
+    hipError_t e;
+    if (mode == BCJR_TB_EXACT) {
+        float* costs = reinterpret_cast<float*>(ws + tp.aux_off);
+        f.B = B << L;
+        f.sigma_enum = 1;
+        f.cost = costs;
+        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
+        if ((e = launch_tb_select(costs, B, 1 << L, sig_ws, sigma, st)) != hipSuccess) return hip_status(e);
+    } else {
+        int32_t* rot_states = reinterpret_cast<int32_t*>(ws + tp.aux_off);
+        const int r = (int)(n / 2);
+        f.B = B;
+        f.rot = r;
+        f.states = rot_states;
+        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
+        if ((e = launch_tb_rotate_sigma(rot_states, B, (int)n, (int)(n - 1 - r), sig_ws, sigma, st)) != hipSuccess)
+            return hip_status(e);
+    }
+    // second pass: the sigma-constrained decode of the rows with the chosen start state
+    ViterbiArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B;
+    a.n = (int)n;
+    a.sigma = sig_ws;
+    a.states = states;
+    a.w_hard = w_hard;
+    a.cost = cost;
+    a.ws = ws;
+    a.slot_bytes = tp.rows.slot_bytes;
+    return hip_status(launch_viterbi(L, a, tp.rows.grid, st));
 }
 
 }  // extern "C"

@@ -34,16 +34,18 @@ struct GradArgs {
 };
 
 struct ViterbiArgs {
-    const float* w;        // [B, n]
+    const float* w;        // [rows, n]
     const float* cb;       // [2^L]
-    int64_t B;
+    int64_t B;             // sequences decoded (rows, or rows * 2^L with sigma_enum)
     int n;
     const int32_t* sigma;  // [B] or nullptr
-    int32_t* states;       // [B, n]
+    int32_t* states;       // [B, n], or nullptr for costs only (no traceback; w_hard must be nullptr too)
     float* w_hard;         // [B, n] or nullptr
     float* cost;           // [B] or nullptr
     unsigned char* ws;
     size_t slot_bytes;
+    int32_t rot;           // sequence b emits w[b, (t + rot) mod n] at step t (0 <= rot < n)
+    int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
 };
 
 }  // namespace bcjr

@@ -69,6 +69,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
     const uint32_t buf_bytes = (uint32_t)n * TPS * 4u;
     const uint32_t v_word = sq * slot_bytes + 4u * tau;
 
+    const bool trace = args.states != nullptr;   // costs only otherwise
+    const int rot = args.rot;
     // pending traceback (run by the sequence's lane tau == 0)
     int32_t pend_b = -1;
     int pend_t = 0;
@@ -80,9 +82,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
         const int64_t b = gi * SPB + sq;
         const bool active = b < args.B;
         const int64_t bb = active ? b : args.B - 1;
-        const float* wb = args.w + bb * n;
-        const bool has_sigma = args.sigma != nullptr;
-        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[bb] & (uint32_t)(Gm::S - 1)) : 0u;
+        const float* wb = args.w + (args.sigma_enum ? (bb >> L) : bb) * n;
+        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+        const uint32_t sig = args.sigma_enum ? (uint32_t)(bb & (Gm::S - 1))
+                                             : has_sigma ? ((uint32_t)args.sigma[bb] & (uint32_t)(Gm::S - 1)) : 0u;
         const uint32_t par = (uint32_t)(iter & 1);
 
         // V_0: free start -> 0; sigma -> only the successors of sigma reachable
@@ -101,7 +104,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
         for (int t = 0; t + 1 < n; ++t) {
             const float* mc = (t & 1) ? msg1 : msg0;
             float* mn = (t & 1) ? msg0 : msg1;
-            const float wt = wb[t];
+            const float wt = wb[t + rot < n ? t + rot : t + rot - n];
             uint32_t word = 0;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
@@ -123,7 +126,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
                 *reinterpret_cast<float4*>(mn + 4 * j) = make_float4(o[0], o[1], o[2], o[3]);
             }
             // bp_{t+1}: one word per thread
-            buf_st(__builtin_bit_cast(float, word), tape, v_word, par * buf_bytes + (uint32_t)(t + 1) * (TPS * 4u));
+            if (trace) buf_st(__builtin_bit_cast(float, word), tape, v_word, par * buf_bytes + (uint32_t)(t + 1) * (TPS * 4u));
 
             // one step of the previous sequence's traceback
             if (tau == 0 && pend_b >= 0 && pend_t >= 1) {
@@ -141,7 +144,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
 
         // last step: M_{n-1}(s) for every state, then the end state
         const float* ml = ((n - 1) & 1) ? msg1 : msg0;
-        const float wl = wb[n - 1];
+        const float wl = wb[n - 1 + rot < n ? n - 1 + rot : n - 1 + rot - n];
         float best = kInf;
         uint32_t bidx = 0xffffffffu;
         if (!has_sigma) {
@@ -199,7 +202,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
                 for (int t = tau; t < n; t += TPS) args.w_hard[pb * n + t] = args.cb[args.states[pb * n + t]];
         }
         // this sequence becomes the pending traceback
-        if (tau == 0) {
+        if (tau == 0 && trace) {
             pend_b = active ? (int32_t)b : -1;
             pend_par = par;
             pend_s = bidx;
@@ -234,6 +237,50 @@ __global__ void __launch_bounds__(Geo<L>::NT) viterbi_kernel(ViterbiArgs args) {
         if (pb < args.B)
             for (int t = tau; t < n; t += TPS) args.w_hard[pb * n + t] = args.cb[args.states[pb * n + t]];
     }
+}
+
+// Tail-biting start-state choice, exact: per row, the first sigma attaining the minimum of costs[row * S + sigma]
+// (a NaN cost ranks below every number, as the first NaN is what a plain argmin returns).  One wave per row.
+__global__ void __launch_bounds__(256) tb_select_kernel(const float* costs, int64_t rows, int S, int32_t* sigma,
+                                                         int32_t* sigma_out) {
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows) return;   // the whole wave leaves together
+    float best = __builtin_huge_valf();
+    uint32_t arg = 0xffffffffu;
+    for (int s = lane; s < S; s += 64) {
+        const float v = costs[row * S + s];
+        argmin_merge(best, arg, __builtin_isnan(v) ? -__builtin_huge_valf() : v, (uint32_t)s);
+    }
+    seg_argmin<64>(best, arg);
+    if (lane == 0) {
+        sigma[row] = (int32_t)arg;
+        if (sigma_out) sigma_out[row] = (int32_t)arg;
+    }
+}
+
+// Tail-biting start-state choice, rotate-and-decode: sigma = the state of the rotated free decode at position pos.
+__global__ void __launch_bounds__(256) tb_rotate_sigma_kernel(const int32_t* states_rot, int64_t rows, int n, int pos,
+                                                               int32_t* sigma, int32_t* sigma_out) {
+    const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (row >= rows) return;
+    const int32_t s = states_rot[row * n + pos];
+    sigma[row] = s;
+    if (sigma_out) sigma_out[row] = s;
+}
+
+hipError_t launch_tb_select(const float* costs, int64_t rows, int S, int32_t* sigma, int32_t* sigma_out,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(tb_select_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, costs, rows, S, sigma,
+                       sigma_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n, int pos, int32_t* sigma,
+                                  int32_t* sigma_out, hipStream_t st) {
+    hipLaunchKernelGGL(tb_rotate_sigma_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, states_rot,
+                       rows, n, pos, sigma, sigma_out);
+    return hipGetLastError();
 }
 
 template <int L>

@@ -48,12 +48,21 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2 */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2; exact tail-biting with L > 10; unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
 
-enum { BCJR_OP_SOFT = 0, BCJR_OP_GRAD = 1, BCJR_OP_VITERBI = 2, BCJR_OP_GRAD_CODEBOOK = 3 };
+enum {
+    BCJR_OP_SOFT = 0,
+    BCJR_OP_GRAD = 1,
+    BCJR_OP_VITERBI = 2,
+    BCJR_OP_GRAD_CODEBOOK = 3,
+    BCJR_OP_VITERBI_TB_EXACT = 4,  /* viterbi_tail_biting, mode BCJR_TB_EXACT */
+    BCJR_OP_VITERBI_TB_ROTATE = 5  /* viterbi_tail_biting, mode BCJR_TB_ROTATE */
+};
+
+enum { BCJR_TB_EXACT = 0, BCJR_TB_ROTATE = 1 };
 
 /*
  * Soft codeword (gist.science Technical Summary, "Core Mechanism"):
@@ -110,8 +119,25 @@ int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t 
                       size_t workspace_bytes, void* stream);
 
 /*
- * Bytes of device workspace the entry point `op` (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_VITERBI or
- * BCJR_OP_GRAD_CODEBOOK) needs for
+ * Tail-biting Viterbi hard code with the start state chosen by the decoder: the minimum-energy path under the
+ * constraint s_0 = s_n (the non-emitting start state equals the last emitting state), the "start state = end state"
+ * variant of the hard code.  The pages fix no rule for choosing the state; two are offered:
+ *   BCJR_TB_EXACT   every sigma in [0, 2^L) is decoded as in viterbi_hard_code's sigma mode, and sigma is the
+ *                   smallest state whose path cost is the minimum (L <= 10, else BCJR_ERR_UNSUPPORTED);
+ *   BCJR_TB_ROTATE  rotate-and-decode: the sequence rotated left by n/2 (weight (t + n/2) mod n at step t) is
+ *                   decoded with a free start and end, and sigma is that path's state at the original last weight,
+ *                   where the cycle closes; any L.  A heuristic: its cost is never below the exact one.
+ * Either way the result is the sigma-mode decode with that sigma, in the same float32 order and tie rules as
+ * viterbi_hard_code: states [B, n] (required), w_hard and cost (optional), and sigma [B] int32 (optional) receives
+ * the chosen start state.  An unknown mode gives BCJR_ERR_UNSUPPORTED.  Workspace: bcjr_workspace_bytes with
+ * BCJR_OP_VITERBI_TB_EXACT or BCJR_OP_VITERBI_TB_ROTATE.
+ */
+int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                        int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace the entry point `op` (one of the BCJR_OP_* values above) needs for
  * these shapes; 0 when the shapes are invalid or unsupported.  Pure host function; no HIP call.
  */
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);

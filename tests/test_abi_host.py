@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_every_op():
     fns = declared_functions()
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
-                 "viterbi_hard_code", "bcjr_workspace_bytes", "bcjr_status_string"]:
+                 "viterbi_hard_code", "viterbi_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -85,7 +85,7 @@ def test_workspace_bytes_for_the_headline_workload():
 @pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 4097, 8, 2), (1, 4, 3, 2),
                                   (1, 4, 17, 2), (1, 4, 8, 0), (1 << 31, 4, 8, 2)])
 def test_workspace_bytes_invalid_shapes_are_zero(args):
-    for op in (0, 1, 2, 3):
+    for op in (0, 1, 2, 3, 4, 5):
         assert abi.bcjr_workspace_bytes(op, *args) == 0
     assert abi.bcjr_workspace_bytes(7, 1, 4, 8, 2) == 0
 
@@ -114,6 +114,47 @@ def _gc(**kw):
              grad_codebook=FAKE, grad_w=None, w_soft=None, workspace=FAKE, workspace_bytes=0, stream=None)
     a.update(kw)
     return abi.bcjr_soft_codeword_grad_codebook(*a.values())
+
+
+def _tb(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, mode=abi.BCJR_TB_EXACT, states=FAKE, w_hard=None, cost=None,
+             sigma=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.viterbi_tail_biting(*a.values())
+
+
+@pytest.mark.parametrize("L", [4, 8, 10, 12, 16])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (1000, 7)])
+def test_tail_biting_workspace_formula(L, B, n):
+    G, TPS, SPB = _geo(L)
+    bpc = 1 if L >= 15 else (2 if L == 14 else 8)
+
+    def slots(rows):
+        return min((rows + SPB - 1) // SPB, 256 * bpc) * SPB
+
+    vslot = _a256(2 * n * TPS * 4)
+    rot = _a256(slots(B) * vslot) + _a256(B * n * 4) + _a256(B * 4)
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI_TB_ROTATE, B, n, L, 2) == rot
+    exact = abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI_TB_EXACT, B, n, L, 2)
+    if L <= 10:
+        first = max(slots(B << L), slots(B)) * vslot
+        assert exact == _a256(first) + _a256((B << L) * 4) + _a256(B * 4)
+    else:
+        assert exact == 0   # every one of 2^L start states would be decoded: refused above L = 10
+
+
+def test_tail_biting_checks():
+    assert _tb(states=None) == abi.BCJR_ERR_NULL
+    assert _tb(w=None) == abi.BCJR_ERR_NULL
+    assert _tb(n=0) == abi.BCJR_ERR_SHAPE
+    assert _tb(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert _tb(mode=7) == abi.BCJR_ERR_UNSUPPORTED
+    assert _tb(L=12) == abi.BCJR_ERR_UNSUPPORTED                       # exact above L = 10
+    assert _tb(L=12, mode=abi.BCJR_TB_ROTATE) == abi.BCJR_ERR_WORKSPACE   # rotate has no L limit
+    need = abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI_TB_EXACT, 4, 8, 8, 2)
+    assert _tb(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
+    assert _tb(workspace=FAKE + 32, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+    assert _tb(workspace=None, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
 
 
 def _vit(**kw):
@@ -201,11 +242,16 @@ def test_python_wrapper_refuses_cpu_tensors():
         dba.viterbi_hard_code(w, c, 8)
     with pytest.raises(TypeError):
         dba.soft_codeword_grad_codebook(w, c, w, 8)
+    with pytest.raises(TypeError):
+        dba.viterbi_tail_biting(w, c, 8)
+    with pytest.raises(ValueError):
+        dba.viterbi_tail_biting(w.cuda() if torch.cuda.is_available() else w, c, 8, mode="nearest")
 
 
 def test_largest_shape_keeps_workspace_offsets_in_32_bits():
     # the kernels address one block's slots with 32-bit buffer offsets
-    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI, abi.BCJR_OP_GRAD_CODEBOOK):
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI, abi.BCJR_OP_GRAD_CODEBOOK,
+               abi.BCJR_OP_VITERBI_TB_ROTATE):
         for L in (8, 12, 16):
             G, TPS, SPB = _geo(L)
             per_block = abi.bcjr_workspace_bytes(op, SPB, 4096, L, 2)
