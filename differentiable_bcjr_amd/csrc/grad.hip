@@ -1,4 +1,4 @@
-// grad.hip -- exact gradient of the soft codeword with respect to the weights, on gfx950.
+// grad.hip -- exact gradient of the soft codeword with respect to the weights (and the codebook values), on gfx950.
 //
 // The soft codeword is exactly differentiable in the weight pre-image (BCJR-QAT, arXiv 2605.10655: gist.science
 // Technical Summary, "Core Mechanism"; "Key Technical Innovations").  Differentiating w_soft_t = E_p[c(s_t)] under
@@ -26,6 +26,11 @@
 // next step's scalars (w, g, normaliser, Q offset) one step ahead.  With several waves per sequence only (S0, S1) is
 // combined across waves inside the step loop; every wave's (S0..S3) goes to the workspace and the outputs are formed
 // after the backward pass.
+//
+// The soft codeword is exactly differentiable in the codebook values as well (the trellis parameters, same passage).
+// The GC instantiation adds, for every state s and step t of the backward pass,
+//     p_t(s) [ g_t + (2/T) (w_t - c(s)) (E[F | s_t = s] - E[F]) ]
+// to a per-slot float accumulator in the workspace; codebook_reduce_kernel then sums the slots in a fixed order.
 #include <type_traits>
 
 #include "kernel_args.hpp"

@@ -13,6 +13,10 @@
 // a per-sequence back-pointer tape).  The traceback of a sequence runs in one lane while the block decodes the next
 // sequence, one dependent load per step, so its latency hides behind the next forward pass; the tape is
 // double-buffered by sequence for that.  Codewords c(s_t) are gathered by the whole block once a path is complete.
+//
+// The tail-biting hard code with a decoder-chosen start state (s_0 = s_n) reuses this kernel: weights read rotated
+// (rotate-and-decode), one virtual sequence per (row, sigma) for the exact choice, and a costs-only mode without
+// traceback; tb_select_kernel and tb_rotate_sigma_kernel pick sigma between the passes.
 #include "kernel_args.hpp"
 #include "trellis.hpp"
 
