@@ -16,7 +16,7 @@ import torch
 import differentiable_bcjr_amd as dba
 import workloads
 from differentiable_bcjr_amd import abi
-from test_gpu_parity import _inputs, _t, grad_err, grad_tol, norm_err, rel_err, TOL
+from test_gpu_parity import _inputs, _t, grad_err, grad_norm_ok, grad_tol, norm_err, rel_err, TOL
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,7 @@ def test_codebook_grad_matches_oracle(oracle_mod, dev, L, B, n, sigma):
         print(f"L{L} B{B} n{n} T{T} sigma={sigma}: codebook grad {en:.2e} normwise, {em:.2e} of max; "
               f"weights' grad {eg:.2e}", flush=True)
         assert en <= cb_tol(sigma) and em <= CB_ELEM_TOL
-        assert eg <= grad_tol(T, sigma)
+        assert eg <= grad_tol(T, sigma) and grad_norm_ok(gw.cpu().numpy(), rgw, T, sigma)
         assert rel_err(ws.cpu().numpy(), rws) <= (3e-5 if sigma and T < 0.05 else TOL)
 
 
@@ -171,3 +171,27 @@ def test_soft_quantize_codebook_autograd(oracle_mod, dev, sigma):
     c_only = _t(c, dev).requires_grad_(True)
     (dba.soft_quantize(_t(w, dev), c_only, L, 2, T, _t(s, dev)) * _t(g, dev)).sum().backward()
     assert torch.equal(c_only.grad, ct.grad)
+
+
+def _random_cases(count=24, seed=4048):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        L = int(rng.integers(4, 17))
+        n = int(rng.integers(1, 65)) if L <= 12 else int(rng.integers(1, 17))
+        B = int(rng.integers(1, 41)) if L <= 12 else int(rng.integers(1, 4))
+        T = float(rng.choice([1.0, 0.3, 0.1, 0.05]))
+        sigma = bool(rng.integers(0, 2)) and n >= (L + 1) // 2
+        cases.append((i, L, B, n, T, sigma))
+    return cases
+
+
+@pytest.mark.parametrize("i,L,B,n,T,sigma", _random_cases())
+def test_codebook_grad_random_configuration(oracle_mod, dev, i, L, B, n, T, sigma):
+    w, c, g, s = _inputs(L, B, n, 7000 + i, sigma)
+    gc, gw = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, 2, T, _t(s, dev))
+    rgc, rgw, _ = oracle_mod.grad_codebook(w, c, g, L, 2, T, sigma=s)
+    en, em = norm_err(gc.cpu().numpy(), rgc), max_err(gc.cpu().numpy(), rgc)
+    assert en <= cb_tol(sigma) and em <= CB_ELEM_TOL, (en, em)
+    assert grad_err(gw.cpu().numpy(), rgw, g, c, T) <= grad_tol(T, sigma)
+    assert grad_norm_ok(gw.cpu().numpy(), rgw, T, sigma)

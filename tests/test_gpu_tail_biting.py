@@ -78,3 +78,23 @@ def test_tail_biting_rotate_low_temperature_workload_rows(oracle_mod, dev):
     rows = wl.sample_rows(3)
     ref = oracle_mod.viterbi_tail_biting(w[rows], c, wl.L, wl.k, oracle_mod.TB_ROTATE)
     _same([torch.from_numpy(g[rows]) for g in got], ref)
+
+
+def _random_cases(count=24, seed=5150):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        mode = "exact" if rng.integers(0, 2) else "rotate"
+        L = int(rng.integers(4, 11)) if mode == "exact" else int(rng.integers(4, 17))
+        n = int(rng.integers(1, 65)) if L <= 12 else int(rng.integers(1, 33))
+        B = int(rng.integers(1, 41)) if L <= 12 else int(rng.integers(1, 5))
+        cases.append((i, mode, L, B, n))
+    return cases
+
+
+@pytest.mark.parametrize("i,mode,L,B,n", _random_cases())
+def test_tail_biting_random_configuration(oracle_mod, dev, i, mode, L, B, n):
+    w, c, _, _ = _inputs(L, B, n, 8000 + i)
+    got = dba.viterbi_tail_biting(_t(w, dev), _t(c, dev), L, 2, mode)
+    _same(got, oracle_mod.viterbi_tail_biting(w, c, L, 2, oracle_mod.TB_EXACT if mode == "exact" else
+                                              oracle_mod.TB_ROTATE))
