@@ -211,6 +211,57 @@ def viterbi_tail_biting(w, c, L: int, k: int, mode: int = TB_EXACT):
     return st, wh, cost, sigma
 
 
+def soft_tail_biting(w, c, L: int, k: int, T: float):
+    """Soft codeword [B, n] and ln Z [B] under the tail-biting measure: every path with s_0 = s_n, whatever the state.
+
+    The measure is the mixture over sigma of the sigma-constrained measures with weights Z_sigma / sum Z, so
+    w_soft = sum_sigma pi_sigma w_soft_sigma and ln Z = logsumexp_sigma ln Z_sigma (a sigma with no admissible path
+    has Z_sigma = 0).  Composed from this module's sigma-mode soft codeword.
+    """
+    w = _f32(w)
+    B, n = w.shape
+    S = 1 << L
+    ws_all, lz_all = soft(np.repeat(w, S, axis=0), c, L, k, T, sigma=np.tile(np.arange(S, dtype=np.int32), B))
+    lz_all = lz_all.reshape(B, S)
+    ws_all = ws_all.reshape(B, S, n)
+    m = lz_all.max(axis=1, keepdims=True)
+    pz = np.exp(lz_all - m)                      # 0 where ln Z_sigma = -inf
+    lnz = m[:, 0] + np.log(pz.sum(axis=1))
+    pi = pz / pz.sum(axis=1, keepdims=True)
+    ws_all = np.where(pi[:, :, None] > 0, ws_all, 0.0)
+    return (pi[:, :, None] * ws_all).sum(axis=1), lnz
+
+
+def grad_tail_biting(w, c, g, L: int, k: int, T: float):
+    """dL/dw [B, n] for upstream g = dL/dw_soft under the tail-biting measure, plus that measure's w_soft [B, n].
+
+    With pi_sigma = Z_sigma / sum Z and d ln Z_sigma / d w_u = (2/T) (w_soft_sigma,u - w_u):
+      grad_u = sum_sigma pi_sigma grad_sigma,u
+             + (2/T) sum_sigma pi_sigma (w_soft_sigma,u - w_soft_u) (F_sigma - sum_sigma' pi_sigma' F_sigma'),
+    F_sigma = sum_t g_t w_soft_sigma,t.  Composed from this module's sigma-mode soft codeword and gradient.
+    """
+    w = _f32(w)
+    g = _f32(g)
+    B, n = w.shape
+    S = 1 << L
+    sig = np.tile(np.arange(S, dtype=np.int32), B)
+    W = np.repeat(w, S, axis=0)
+    ws_all, lz_all = soft(W, c, L, k, T, sigma=sig)
+    gr_all, _ = grad(W, c, np.repeat(g, S, axis=0), L, k, T, sigma=sig)
+    lz_all = lz_all.reshape(B, S)
+    m = lz_all.max(axis=1, keepdims=True)
+    pz = np.exp(lz_all - m)
+    pi = pz / pz.sum(axis=1, keepdims=True)
+    live = pi[:, :, None] > 0
+    ws_all = np.where(live, ws_all.reshape(B, S, n), 0.0)
+    gr_all = np.where(live, gr_all.reshape(B, S, n), 0.0)
+    ws = (pi[:, :, None] * ws_all).sum(axis=1)
+    F = (ws_all * g.astype(np.float64)[:, None, :]).sum(axis=2)        # [B, S]
+    Fbar = (pi * F).sum(axis=1, keepdims=True)
+    mix = (2.0 / T) * (pi[:, :, None] * (ws_all - ws[:, None, :]) * (F - Fbar)[:, :, None]).sum(axis=1)
+    return (pi[:, :, None] * gr_all).sum(axis=1) + mix, ws
+
+
 def num_threads() -> int:
     """OpenMP threads one oracle call uses."""
     return int(_load().oracle_num_threads())

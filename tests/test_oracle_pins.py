@@ -501,3 +501,40 @@ def test_tail_biting_paths_close_the_cycle_and_exact_is_best(oracle_mod, mode):
     assert np.array_equal(st[:, 1:] >> k, st[:, :-1] & mask)    # every step is a trellis transition
     _, _, cost_exact, _ = oracle_mod.viterbi_tail_biting(w, c, L, k, 0)
     assert np.all(cost >= cost_exact)
+
+
+# ------------------------------------------------------------------ P11 soft codeword under the tail-biting measure
+
+
+def _tail_biting_paths(L, k, n):
+    return np.concatenate([pins.sigma_paths(L, k, n, s) for s in range(1 << L)], axis=0)
+
+
+@pytest.mark.parametrize("L,k,n", [(4, 2, 5), (4, 2, 7), (5, 2, 6), (4, 1, 7)])
+@pytest.mark.parametrize("T", [1.0, 0.3])
+def test_soft_tail_biting_matches_brute_force(oracle_mod, L, k, n, T):
+    w, c, g = _inputs(L, n, 1717 + L + n)
+    paths = _tail_biting_paths(L, k, n)
+    ws, lz = oracle_mod.soft_tail_biting(w, c, L, k, T)
+    gr, ws2 = oracle_mod.grad_tail_biting(w, c, g, L, k, T)
+    for b in range(w.shape[0]):
+        ref, lnz, _ = pins.brute_soft(paths, w[b], c, T)
+        np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ws2[b], ref, rtol=0, atol=1e-12)
+        assert abs(lz[b] - lnz) <= 1e-12 * max(1.0, abs(lnz))
+        gref = pins.brute_jacobian(paths, w[b], c, T) @ g[b].astype(np.float64)
+        np.testing.assert_allclose(gr[b], gref, rtol=0, atol=1e-11 * max(1.0, np.abs(gref).max()))
+
+
+def test_soft_tail_biting_some_sigmas_unreachable(oracle_mod):
+    """n below L/k: only the sigmas that can close the cycle carry weight."""
+    L, k, n, T = 6, 2, 2, 0.5
+    w, c, g = _inputs(L, n, 31, B=2)
+    paths = _tail_biting_paths(L, k, n)
+    ws, lz = oracle_mod.soft_tail_biting(w, c, L, k, T)
+    gr, _ = oracle_mod.grad_tail_biting(w, c, g, L, k, T)
+    for b in range(2):
+        ref, lnz, _ = pins.brute_soft(paths, w[b], c, T)
+        np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
+        gref = pins.brute_jacobian(paths, w[b], c, T) @ g[b].astype(np.float64)
+        np.testing.assert_allclose(gr[b], gref, rtol=0, atol=1e-11 * max(1.0, np.abs(gref).max()))
