@@ -9,7 +9,9 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 * ``soft_codeword_grad_codebook`` -- dL/dc [2^L], the exact derivative in the codebook values (the trellis
   parameters), summed over the batch, together with dL/dw;
 * ``viterbi_hard_code``  -- the minimum-energy path (the T -> 0 limit, abstract), bit-exact in float32;
-* ``viterbi_tail_biting`` -- the same with s_0 = s_n and the start state chosen exactly or by rotate-and-decode.
+* ``viterbi_tail_biting`` -- the same with s_0 = s_n and the start state chosen exactly or by rotate-and-decode;
+* ``soft_codeword_tail_biting``, ``soft_codeword_grad_tail_biting`` -- the soft codeword and its weights' gradient
+  under the tail-biting measure (every s_0 = s_n path, summed over the state; L <= 10).
 
 ``soft_quantize`` ties them together for autograd: its forward is ``soft_codeword``; its backward is
 ``soft_codeword_grad``, or ``soft_codeword_grad_codebook`` when the codebook needs a gradient too.  Both gradients
@@ -30,7 +32,8 @@ from . import abi
 from .anneal import temperature_schedule
 
 __all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code",
-           "viterbi_tail_biting", "soft_quantize", "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
+           "viterbi_tail_biting", "soft_codeword_tail_biting", "soft_codeword_grad_tail_biting", "soft_quantize",
+           "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
 
 
 class BCJRError(RuntimeError):
@@ -161,6 +164,41 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
     _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
                                  w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), _stream(w.device)))
     return states, w_hard, cost
+
+
+def soft_codeword_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0, *,
+                              return_log_z: bool = False, workspace: torch.Tensor | None = None):
+    """Soft codeword [B, n] (and ln Z [B]) under the tail-biting measure: every path with s_0 = s_n (L <= 10)."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    if w.dim() != 2:
+        raise ValueError("w must be [B, n]")
+    B, n = w.shape
+    out = torch.empty_like(w)
+    lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
+    ws, need = _workspace(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, w.device, workspace)
+    _check(abi.bcjr_soft_codeword_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
+                                              out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    return (out, lz) if return_log_z else out
+
+
+def soft_codeword_grad_tail_biting(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int,
+                                   k: int = 2, T: float = 1.0, *, return_w_soft: bool = False,
+                                   workspace: torch.Tensor | None = None):
+    """dL/dw [B, n] under the tail-biting measure given dL/dw_soft [B, n] (and that measure's soft codeword)."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    g = _f32(grad_w_soft, "grad_w_soft")
+    if w.dim() != 2 or g.shape != w.shape:
+        raise ValueError("w and grad_w_soft must both be [B, n]")
+    B, n = w.shape
+    grad = torch.empty_like(w)
+    ws_out = torch.empty_like(w) if return_w_soft else None
+    ws, need = _workspace(abi.BCJR_OP_GRAD_TAIL_BITING, B, n, L, k, w.device, workspace)
+    _check(abi.bcjr_soft_codeword_grad_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
+                                                   g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
+                                                   ws.numel(), _stream(w.device)))
+    return (grad, ws_out) if return_w_soft else grad
 
 
 _TB_MODES = {"exact": (abi.BCJR_TB_EXACT, abi.BCJR_OP_VITERBI_TB_EXACT),

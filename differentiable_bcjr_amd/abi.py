@@ -25,12 +25,15 @@ BCJR_OP_VITERBI = 2
 BCJR_OP_GRAD_CODEBOOK = 3
 BCJR_OP_VITERBI_TB_EXACT = 4
 BCJR_OP_VITERBI_TB_ROTATE = 5
+BCJR_OP_SOFT_TAIL_BITING = 6
+BCJR_OP_GRAD_TAIL_BITING = 7
 
 BCJR_TB_EXACT = 0
 BCJR_TB_ROTATE = 1
 
 EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
-           "viterbi_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string")
+           "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting", "bcjr_soft_codeword_grad_tail_biting",
+           "bcjr_workspace_bytes", "bcjr_status_string")
 
 _lib = None
 
@@ -52,6 +55,10 @@ def load() -> ctypes.CDLL:
     lib.bcjr_soft_codeword_grad_codebook.restype = ctypes.c_int
     lib.viterbi_hard_code.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_hard_code.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_tail_biting.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.bcjr_soft_codeword_tail_biting.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_grad_tail_biting.argtypes = [vp, vp, i64, i64, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.bcjr_soft_codeword_grad_tail_biting.restype = ctypes.c_int
     lib.viterbi_tail_biting.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_tail_biting.restype = ctypes.c_int
     lib.bcjr_workspace_bytes.argtypes = [i32, i64, i64, i32, i32]
@@ -84,6 +91,18 @@ def viterbi_hard_code(w, codebook, B, n, L, k, boundary_state, states, w_hard, c
                       stream) -> int:
     return load().viterbi_hard_code(w, codebook, B, n, L, k, boundary_state, states, w_hard, cost, workspace,
                                     workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_tail_biting(w, codebook, B, n, L, k, T, w_soft, log_z, workspace, workspace_bytes,
+                                   stream) -> int:
+    return load().bcjr_soft_codeword_tail_biting(w, codebook, B, n, L, k, T, w_soft, log_z, workspace,
+                                                 workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_grad_tail_biting(w, codebook, B, n, L, k, T, grad_w_soft, grad_w, w_soft, workspace,
+                                        workspace_bytes, stream) -> int:
+    return load().bcjr_soft_codeword_grad_tail_biting(w, codebook, B, n, L, k, T, grad_w_soft, grad_w, w_soft,
+                                                      workspace, workspace_bytes, stream)
 
 
 def viterbi_tail_biting(w, codebook, B, n, L, k, mode, states, w_hard, cost, sigma, workspace, workspace_bytes,

@@ -17,6 +17,11 @@ hipError_t launch_soft(int L, const SoftArgs& a, int grid, hipStream_t st);
 hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st);
 hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook);
 hipError_t launch_viterbi(int L, const ViterbiArgs& a, int grid, hipStream_t st);
+hipError_t launch_tb_soft_combine(const float* ws_all, const float* lz_all, int64_t rows, int n, int S,
+                                  float* w_soft, float* log_z, hipStream_t st);
+hipError_t launch_tb_grad_combine(const float* ws_all, const float* lz_all, const float* gr_all, const float* g,
+                                  int64_t rows, int n, int S, float two_over_T, float* grad, float* w_soft,
+                                  hipStream_t st);
 hipError_t launch_tb_select(const float* costs, int64_t rows, int S, int32_t* sigma, int32_t* sigma_out,
                             hipStream_t st);
 hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n, int pos, int32_t* sigma,
@@ -107,6 +112,25 @@ TailBitingPlan make_tb_plan(int32_t mode, int64_t B, int64_t n, int32_t L) {
     return t;
 }
 
+// Soft codeword / gradient under the tail-biting measure: the per-(row, sigma) passes' slots, then their outputs
+// (w_soft and ln Z of every (row, sigma); the gradient also its per-sigma gradient).
+struct MixturePlan {
+    Plan soft, grad;
+    size_t ws_off, lz_off, gr_off, total;
+};
+
+MixturePlan make_mixture_plan(bool with_grad, int64_t B, int64_t n, int32_t L) {
+    MixturePlan m{};
+    const int64_t V = B << L;
+    m.soft = make_plan(BCJR_OP_SOFT, V, n, L);
+    m.grad = with_grad ? make_plan(BCJR_OP_GRAD, V, n, L) : m.soft;
+    m.ws_off = align256(m.grad.total > m.soft.total ? m.grad.total : m.soft.total);
+    m.lz_off = m.ws_off + align256((size_t)V * (size_t)n * 4);
+    m.gr_off = m.lz_off + align256((size_t)V * 4);
+    m.total = m.gr_off + (with_grad ? align256((size_t)V * (size_t)n * 4) : 0);
+    return m;
+}
+
 int check_tb_mode(int32_t mode, int32_t L) {
     if (mode == BCJR_TB_ROTATE) return BCJR_OK;
     if (mode == BCJR_TB_EXACT && L <= kMaxTailBitingExactL) return BCJR_OK;
@@ -118,8 +142,12 @@ int check_tb_mode(int32_t mode, int32_t L) {
 extern "C" {
 
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
-    if (op < BCJR_OP_SOFT || op > BCJR_OP_VITERBI_TB_ROTATE) return 0;
+    if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
     if (check_shape(B, n, L, k) != BCJR_OK) return 0;
+    if (op == BCJR_OP_SOFT_TAIL_BITING || op == BCJR_OP_GRAD_TAIL_BITING) {
+        if (L > kMaxTailBitingExactL) return 0;
+        return make_mixture_plan(op == BCJR_OP_GRAD_TAIL_BITING, B, n, L).total;
+    }
     if (op == BCJR_OP_VITERBI_TB_EXACT || op == BCJR_OP_VITERBI_TB_ROTATE) {
         const int32_t mode = op == BCJR_OP_VITERBI_TB_EXACT ? BCJR_TB_EXACT : BCJR_TB_ROTATE;
         if (check_tb_mode(mode, L) != BCJR_OK) return 0;
@@ -236,6 +264,84 @@ int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t 
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
     return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int bcjr_soft_codeword_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                   int32_t k, float T, float* w_soft, float* log_z, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
+    const MixturePlan mp = make_mixture_plan(false, B, n, L);
+    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    SoftArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B << L;
+    a.n = (int)n;
+    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.w_soft = ws_all;
+    a.log_z = lz_all;
+    a.ws = ws;
+    a.slot_bytes = mp.soft.slot_bytes;
+    a.sigma_enum = 1;
+    hipError_t e;
+    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
+    return hip_status(launch_tb_soft_combine(ws_all, lz_all, B, (int)n, 1 << L, w_soft, log_z, st));
+}
+
+int bcjr_soft_codeword_grad_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                        int32_t k, float T, const float* grad_w_soft, float* grad_w, float* w_soft,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !grad_w_soft || !grad_w) return BCJR_ERR_NULL;
+    int rc = check_shape(B, n, L, k);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
+    const MixturePlan mp = make_mixture_plan(true, B, n, L);
+    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+    float* gr_all = reinterpret_cast<float*>(ws + mp.gr_off);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    SoftArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B << L;
+    a.n = (int)n;
+    a.scale = scale;
+    a.w_soft = ws_all;
+    a.log_z = lz_all;
+    a.ws = ws;
+    a.slot_bytes = mp.soft.slot_bytes;
+    a.sigma_enum = 1;
+    hipError_t e;
+    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
+    GradArgs ga{};
+    ga.w = w;
+    ga.cb = codebook;
+    ga.g = grad_w_soft;
+    ga.B = B << L;
+    ga.n = (int)n;
+    ga.scale = scale;
+    ga.two_over_T = (float)(2.0 / (double)T);
+    ga.grad = gr_all;
+    ga.ws = ws;
+    ga.slot_bytes = mp.grad.slot_bytes;
+    ga.sigma_enum = 1;
+    if ((e = launch_grad(L, ga, mp.grad.grid, st)) != hipSuccess) return hip_status(e);
+    return hip_status(launch_tb_grad_combine(ws_all, lz_all, gr_all, grad_w_soft, B, (int)n, 1 << L,
+                                             (float)(2.0 / (double)T), grad_w, w_soft, st));
 }
 
 int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,

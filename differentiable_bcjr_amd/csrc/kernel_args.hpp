@@ -16,6 +16,7 @@ struct SoftArgs {
     float* log_z;          // [B] or nullptr
     unsigned char* ws;
     size_t slot_bytes;
+    int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
 };
 
 struct GradArgs {
@@ -31,6 +32,7 @@ struct GradArgs {
     float* w_soft;         // [B, n] or nullptr
     unsigned char* ws;
     size_t slot_bytes;
+    int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
 };
 
 struct ViterbiArgs {

@@ -89,9 +89,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
         const int64_t b = gi * SPB + sq;
         const bool active = b < args.B;
         const int64_t bb = active ? b : args.B - 1;
-        const float* wb = args.w + bb * n;
-        const bool has_sigma = args.sigma != nullptr;
-        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[bb] & (uint32_t)(Gm::S - 1)) : 0u;
+        const int64_t row = args.sigma_enum ? (bb >> L) : bb;   // the weights' row (sigma enumeration: v >> L)
+        const float* wb = args.w + row * n;
+        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+        const uint32_t sig = args.sigma_enum ? (uint32_t)(bb & (Gm::S - 1))
+                                             : has_sigma ? ((uint32_t)args.sigma[bb] & (uint32_t)(Gm::S - 1)) : 0u;
 
         // ------------------------------------------------------------------ forward
         // R~_0: free start -> 0 everywhere; sigma -> only the successors of sigma (group sigma & (G-1)) reachable

@@ -48,7 +48,8 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2; exact tail-biting with L > 10; unknown mode */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2; exact tail-biting (choice of sigma, soft
+                                  codeword or gradient under the tail-biting measure) with L > 10; unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
@@ -59,7 +60,9 @@ enum {
     BCJR_OP_VITERBI = 2,
     BCJR_OP_GRAD_CODEBOOK = 3,
     BCJR_OP_VITERBI_TB_EXACT = 4,  /* viterbi_tail_biting, mode BCJR_TB_EXACT */
-    BCJR_OP_VITERBI_TB_ROTATE = 5  /* viterbi_tail_biting, mode BCJR_TB_ROTATE */
+    BCJR_OP_VITERBI_TB_ROTATE = 5, /* viterbi_tail_biting, mode BCJR_TB_ROTATE */
+    BCJR_OP_SOFT_TAIL_BITING = 6,  /* bcjr_soft_codeword_tail_biting */
+    BCJR_OP_GRAD_TAIL_BITING = 7   /* bcjr_soft_codeword_grad_tail_biting */
 };
 
 enum { BCJR_TB_EXACT = 0, BCJR_TB_ROTATE = 1 };
@@ -117,6 +120,30 @@ int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int6
 int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
                       const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/*
+ * Soft codeword under the tail-biting measure: every path with s_0 = s_n weighs exp(-E / T), whatever that state
+ * (the "start state = end state" variant of the soft codeword, with the state summed over rather than given).
+ * It is the mixture over sigma of the sigma-mode measures with weights Z_sigma / sum Z, so
+ *   w_soft[b, t] = sum_sigma pi_sigma w_soft_sigma[b, t],   log_z[b] = ln sum_sigma Z_sigma (optional output),
+ * computed exactly from one sigma-mode pass per (row, sigma): L <= 10, else BCJR_ERR_UNSUPPORTED.  Workspace:
+ * bcjr_workspace_bytes with BCJR_OP_SOFT_TAIL_BITING (it holds the 2^L per-sigma soft codewords of every row).
+ */
+int bcjr_soft_codeword_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                   int32_t k, float T, float* w_soft, float* log_z, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Gradient with respect to the weights of the soft codeword under the tail-biting measure, for an upstream
+ * grad_w_soft (required):  grad_w[b, u] = sum_t grad_w_soft[b, t] d w_soft[b, t] / d w[b, u].  With
+ * d ln Z_sigma / d w_u = (2/T)(w_soft_sigma,u - w_u) this is the mixture of the sigma-mode gradients plus
+ * (2/T) sum_sigma pi_sigma (w_soft_sigma,u - w_soft_u)(F_sigma - F_bar), F_sigma = sum_t grad_w_soft_t w_soft_sigma,t.
+ * w_soft (optional) receives the tail-biting soft codeword.  L <= 10, else BCJR_ERR_UNSUPPORTED.  Workspace:
+ * bcjr_workspace_bytes with BCJR_OP_GRAD_TAIL_BITING.
+ */
+int bcjr_soft_codeword_grad_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                        int32_t k, float T, const float* grad_w_soft, float* grad_w, float* w_soft,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Tail-biting Viterbi hard code with the start state chosen by the decoder: the minimum-energy path under the

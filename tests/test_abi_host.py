@@ -23,7 +23,8 @@ def declared_functions():
 def test_header_declares_every_op():
     fns = declared_functions()
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
-                 "viterbi_hard_code", "viterbi_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string"]:
+                 "viterbi_hard_code", "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting",
+                 "bcjr_soft_codeword_grad_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -85,9 +86,9 @@ def test_workspace_bytes_for_the_headline_workload():
 @pytest.mark.parametrize("args", [(0, 1, 8, 2), (-3, 1, 8, 2), (1, 0, 8, 2), (1, 4097, 8, 2), (1, 4, 3, 2),
                                   (1, 4, 17, 2), (1, 4, 8, 0), (1 << 31, 4, 8, 2)])
 def test_workspace_bytes_invalid_shapes_are_zero(args):
-    for op in (0, 1, 2, 3, 4, 5):
+    for op in (0, 1, 2, 3, 4, 5, 6, 7):
         assert abi.bcjr_workspace_bytes(op, *args) == 0
-    assert abi.bcjr_workspace_bytes(7, 1, 4, 8, 2) == 0
+    assert abi.bcjr_workspace_bytes(99, 1, 4, 8, 2) == 0
 
 
 def test_unsupported_k_has_no_workspace():
@@ -141,6 +142,51 @@ def test_tail_biting_workspace_formula(L, B, n):
         assert exact == _a256(first) + _a256((B << L) * 4) + _a256(B * 4)
     else:
         assert exact == 0   # every one of 2^L start states would be decoded: refused above L = 10
+
+
+@pytest.mark.parametrize("L", [4, 6, 8, 10, 12])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (33, 7)])
+def test_tail_biting_measure_workspace_formula(L, B, n):
+    G, TPS, SPB = _geo(L)
+    bpc = 1 if L >= 15 else (2 if L == 14 else 8)
+    V = B << L
+    slots = min((V + SPB - 1) // SPB, 256 * bpc) * SPB
+    msgs, nrm = _a256((n + 1) * G * 4), _a256(n * 4)
+    soft_slot = msgs + nrm + (_a256(n * _wps(L) * 8) if _wps(L) > 1 else 0)
+    grad_slot = 2 * msgs + 2 * nrm + (_a256(n * _wps(L) * 16) if _wps(L) > 1 else 0)
+    soft = abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, 2)
+    grad = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_TAIL_BITING, B, n, L, 2)
+    if L > 10:
+        assert soft == 0 and grad == 0
+        return
+    assert soft == _a256(slots * soft_slot) + _a256(V * n * 4) + _a256(V * 4)
+    assert grad == _a256(slots * grad_slot) + _a256(V * n * 4) + _a256(V * 4) + _a256(V * n * 4)
+
+
+def test_tail_biting_measure_checks():
+    def soft(**kw):
+        a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, w_soft=FAKE, log_z=None, workspace=FAKE,
+                 workspace_bytes=0, stream=None)
+        a.update(kw)
+        return abi.bcjr_soft_codeword_tail_biting(*a.values())
+
+    def grad(**kw):
+        a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, grad_w_soft=FAKE, grad_w=FAKE, w_soft=None,
+                 workspace=FAKE, workspace_bytes=0, stream=None)
+        a.update(kw)
+        return abi.bcjr_soft_codeword_grad_tail_biting(*a.values())
+
+    assert soft(w_soft=None) == abi.BCJR_ERR_NULL and grad(grad_w=None) == abi.BCJR_ERR_NULL
+    assert grad(grad_w_soft=None) == abi.BCJR_ERR_NULL
+    assert soft(n=0) == abi.BCJR_ERR_SHAPE and grad(B=0) == abi.BCJR_ERR_SHAPE
+    assert soft(T=0.0) == abi.BCJR_ERR_TEMP and grad(T=float("nan")) == abi.BCJR_ERR_TEMP
+    assert soft(L=12) == abi.BCJR_ERR_UNSUPPORTED and grad(L=11) == abi.BCJR_ERR_UNSUPPORTED
+    assert soft(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    need = abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT_TAIL_BITING, 4, 8, 8, 2)
+    assert soft(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
+    assert soft(workspace=FAKE + 8, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+    needg = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_TAIL_BITING, 4, 8, 8, 2)
+    assert needg > need and grad(workspace_bytes=needg - 1) == abi.BCJR_ERR_WORKSPACE
 
 
 def test_tail_biting_checks():

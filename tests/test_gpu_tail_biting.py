@@ -1,5 +1,8 @@
-"""GPU parity of viterbi_tail_biting (through the C-ABI) against the oracle: bit-exact states, codewords, float32
-costs and chosen start states, for the exact choice (every sigma decoded, L <= 10) and rotate-and-decode."""
+"""GPU parity of the tail-biting entry points (through the C-ABI) against the oracle.
+
+viterbi_tail_biting: bit-exact states, codewords, float32 costs and chosen start states, for the exact choice (every
+sigma decoded, L <= 10) and rotate-and-decode.  soft_codeword_tail_biting and soft_codeword_grad_tail_biting: the soft
+codeword, ln Z and the weights' gradient under the tail-biting measure (every s_0 = s_n path, L <= 10)."""
 import numpy as np
 import pytest
 import torch
@@ -98,3 +101,45 @@ def test_tail_biting_random_configuration(oracle_mod, dev, i, mode, L, B, n):
     got = dba.viterbi_tail_biting(_t(w, dev), _t(c, dev), L, 2, mode)
     _same(got, oracle_mod.viterbi_tail_biting(w, c, L, 2, oracle_mod.TB_EXACT if mode == "exact" else
                                               oracle_mod.TB_ROTATE))
+
+
+# ---------------------------------------------------------------- soft codeword and gradient under the measure
+# Bars: the tail-biting measure mixes the sigma-mode measures, whose forced end states carry |theta'| ~ 10/T, so the
+# sigma-mode bars apply (soft codeword 1e-5, 3e-5 below T = 0.05; gradient 5e-5 elementwise).
+
+MEASURE = [(4, 16, 6), (4, 37, 5), (5, 9, 1), (6, 5, 2), (6, 7, 33), (8, 16, 64), (9, 5, 17), (10, 3, 40)]
+
+
+def _soft_bar(T):
+    return 3e-5 if T < 0.05 else 1e-5
+
+
+@pytest.mark.parametrize("L,B,n", MEASURE)
+def test_soft_tail_biting_matches_oracle(oracle_mod, dev, L, B, n):
+    from test_gpu_parity import grad_err, rel_err
+
+    w, c, g, _ = _inputs(L, B, n, 1400 + 7 * L + n)
+    for T in [1.0, 0.1, 0.05]:
+        ws, lz = dba.soft_codeword_tail_biting(_t(w, dev), _t(c, dev), L, 2, T, return_log_z=True)
+        rws, rlz = oracle_mod.soft_tail_biting(w, c, L, 2, T)
+        assert rel_err(ws.cpu().numpy(), rws) <= _soft_bar(T)
+        assert float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0))) <= 1e-5
+        gr, ws2 = dba.soft_codeword_grad_tail_biting(_t(w, dev), _t(c, dev), _t(g, dev), L, 2, T, return_w_soft=True)
+        rgr, rws2 = oracle_mod.grad_tail_biting(w, c, g, L, 2, T)
+        e = grad_err(gr.cpu().numpy(), rgr, g, c, T)
+        print(f"tail-biting measure L{L} B{B} n{n} T{T}: soft {rel_err(ws.cpu().numpy(), rws):.2e}, grad {e:.2e}",
+              flush=True)
+        assert e <= 5e-5
+        assert rel_err(ws2.cpu().numpy(), rws2) <= _soft_bar(T)
+
+
+def test_soft_tail_biting_is_the_sigma_mixture(dev):
+    """ln Z under the measure is the log-sum over sigma of the sigma-mode ln Z (GPU path against itself)."""
+    L, B, n, T = 6, 4, 20, 0.3
+    w, c, _, _ = _inputs(L, B, n, 99)
+    _, lz = dba.soft_codeword_tail_biting(_t(w, dev), _t(c, dev), L, 2, T, return_log_z=True)
+    S = 1 << L
+    sig = torch.arange(S, dtype=torch.int32, device=dev).repeat(B)
+    _, lz_s = dba.soft_codeword(_t(np.repeat(w, S, axis=0), dev), _t(c, dev), L, 2, T, sig, return_log_z=True)
+    ref = torch.logsumexp(lz_s.double().view(B, S), dim=1)
+    assert float((lz.double() - ref).abs().max()) <= 1e-5 * float(ref.abs().max())
