@@ -11,6 +11,11 @@ measure at temperature T, the soft codeword as the expectation of c(s_t)
 (gist.science Technical Summary, "Core Mechanism"), its exact gradient in the
 weights, and the Viterbi hard code as the T -> 0 limit (abstract).  The
 readings the pages leave open are stated in ``oracle.c``'s header.
+
+Shapes: a codebook of shape [2^L] is the scalar trellis (V = 1); one of shape
+[2^L, V] emits V weights per trellis step.  Weights are [B, N] with N = n V:
+step t of a row owns its weights t V .. t V + V - 1.  Soft codewords and
+gradients have the weights' shape; Viterbi states are [B, n], one per step.
 """
 from __future__ import annotations
 
@@ -47,14 +52,14 @@ class _Handle:
         i32p = ctypes.POINTER(ctypes.c_int32)
         i64 = ctypes.c_int64
         ci = ctypes.c_int
-        lib.oracle_soft.argtypes = [f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p, f64p]
+        lib.oracle_soft.argtypes = [f32p, f32p, i64, i64, ci, ci, ci, ctypes.c_double, i32p, f64p, f64p, f64p]
         lib.oracle_soft.restype = ci
-        lib.oracle_grad.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p]
+        lib.oracle_grad.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ci, ctypes.c_double, i32p, f64p, f64p]
         lib.oracle_grad.restype = ci
-        lib.oracle_grad_codebook.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ctypes.c_double, i32p, f64p, f64p,
-                                             f64p]
+        lib.oracle_grad_codebook.argtypes = [f32p, f32p, f32p, i64, i64, ci, ci, ci, ctypes.c_double, i32p, f64p,
+                                             f64p, f64p]
         lib.oracle_grad_codebook.restype = ci
-        lib.oracle_viterbi.argtypes = [f32p, f32p, i64, i64, ci, ci, i32p, i32p, f32p, f32p]
+        lib.oracle_viterbi.argtypes = [f32p, f32p, i64, i64, ci, ci, ci, i32p, i32p, f32p, f32p]
         lib.oracle_viterbi.restype = ci
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ci
@@ -87,10 +92,15 @@ def _ptr(a, ctype):
 
 
 def _check_shapes(w, c, L):
+    """(B, n steps, V) from w [B, n V] and c [2^L] (V = 1) or [2^L, V]."""
     if w.ndim != 2:
-        raise ValueError("w must be [B, n]")
-    if c.shape != (1 << L,):
-        raise ValueError(f"codebook must have 2^L = {1 << L} entries")
+        raise ValueError("w must be [B, N]")
+    if c.ndim not in (1, 2) or c.shape[0] != 1 << L:
+        raise ValueError(f"codebook must be [2^L] or [2^L, V] with 2^L = {1 << L}")
+    V = 1 if c.ndim == 1 else c.shape[1]
+    if V < 1 or w.shape[1] % V:
+        raise ValueError("the weights per row must be a multiple of V")
+    return w.shape[0], w.shape[1] // V, V
 
 
 def soft(w, c, L: int, k: int, T: float, sigma=None, with_check: bool = False):
@@ -100,13 +110,12 @@ def soft(w, c, L: int, k: int, T: float, sigma=None, with_check: bool = False):
     """
     w = _f32(w)
     c = _f32(c)
-    _check_shapes(w, c, L)
-    B, n = w.shape
+    B, n, V = _check_shapes(w, c, L)
     sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
-    out = np.empty((B, n), np.float64)
+    out = np.empty(w.shape, np.float64)
     lz = np.empty(B, np.float64)
     dev = np.empty(B, np.float64)
-    rc = _load().oracle_soft(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k, float(T),
+    rc = _load().oracle_soft(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k, V, float(T),
                              _ptr(sg, ctypes.c_int32), _ptr(out, ctypes.c_double), _ptr(lz, ctypes.c_double),
                              _ptr(dev, ctypes.c_double))
     if rc != 0:
@@ -115,19 +124,18 @@ def soft(w, c, L: int, k: int, T: float, sigma=None, with_check: bool = False):
 
 
 def grad(w, c, g, L: int, k: int, T: float, sigma=None):
-    """dL/dw [B, n] (float64) for upstream g = dL/dw_soft, plus w_soft [B, n]."""
+    """dL/dw [B, N] (float64) for upstream g = dL/dw_soft, plus w_soft [B, N]."""
     w = _f32(w)
     c = _f32(c)
     g = _f32(g)
-    _check_shapes(w, c, L)
+    B, n, V = _check_shapes(w, c, L)
     if g.shape != w.shape:
         raise ValueError("g must match w")
-    B, n = w.shape
     sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
-    out = np.empty((B, n), np.float64)
-    ws = np.empty((B, n), np.float64)
+    out = np.empty(w.shape, np.float64)
+    ws = np.empty(w.shape, np.float64)
     rc = _load().oracle_grad(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(g, ctypes.c_float), B, n,
-                             L, k, float(T), _ptr(sg, ctypes.c_int32), _ptr(out, ctypes.c_double),
+                             L, k, V, float(T), _ptr(sg, ctypes.c_int32), _ptr(out, ctypes.c_double),
                              _ptr(ws, ctypes.c_double))
     if rc != 0:
         raise RuntimeError(f"oracle_grad failed ({rc})")
@@ -135,24 +143,24 @@ def grad(w, c, g, L: int, k: int, T: float, sigma=None):
 
 
 def grad_codebook(w, c, g, L: int, k: int, T: float, sigma=None, per_sequence: bool = False):
-    """dL/dc [2^L] summed over the batch (float64), dL/dw [B, n] and w_soft [B, n], for upstream g = dL/dw_soft.
+    """dL/dc (the codebook's shape) summed over the batch (float64), dL/dw [B, N] and w_soft [B, N], for upstream
+    g = dL/dw_soft.
 
-    With ``per_sequence`` the first result is [B, 2^L], one row per sequence.  A sequence with no admissible path
+    With ``per_sequence`` the first result has a leading batch axis, one entry per sequence.  A sequence with no admissible path
     (sigma mode, n < L/k) has a NaN row, so the batch sum is NaN.
     """
     w = _f32(w)
     c = _f32(c)
     g = _f32(g)
-    _check_shapes(w, c, L)
+    B, n, V = _check_shapes(w, c, L)
     if g.shape != w.shape:
         raise ValueError("g must match w")
-    B, n = w.shape
     sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
-    gw = np.empty((B, n), np.float64)
-    ws = np.empty((B, n), np.float64)
-    gc = np.empty((B, 1 << L), np.float64)
+    gw = np.empty(w.shape, np.float64)
+    ws = np.empty(w.shape, np.float64)
+    gc = np.empty((B,) + c.shape, np.float64)
     rc = _load().oracle_grad_codebook(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), _ptr(g, ctypes.c_float), B,
-                                      n, L, k, float(T), _ptr(sg, ctypes.c_int32), _ptr(gw, ctypes.c_double),
+                                      n, L, k, V, float(T), _ptr(sg, ctypes.c_int32), _ptr(gw, ctypes.c_double),
                                       _ptr(ws, ctypes.c_double), _ptr(gc, ctypes.c_double))
     if rc != 0:
         raise RuntimeError(f"oracle_grad_codebook failed ({rc})")
@@ -160,16 +168,15 @@ def grad_codebook(w, c, g, L: int, k: int, T: float, sigma=None, per_sequence: b
 
 
 def viterbi(w, c, L: int, k: int, sigma=None):
-    """Viterbi states [B, n] int32 (s_1..s_n), c(states) [B, n] float32 and path cost [B] float32."""
+    """Viterbi states [B, n] int32 (s_1..s_n, one per step), c(states) [B, N] float32 and path cost [B] float32."""
     w = _f32(w)
     c = _f32(c)
-    _check_shapes(w, c, L)
-    B, n = w.shape
+    B, n, V = _check_shapes(w, c, L)
     sg = None if sigma is None else np.ascontiguousarray(sigma, dtype=np.int32)
     st = np.empty((B, n), np.int32)
-    wh = np.empty((B, n), np.float32)
+    wh = np.empty(w.shape, np.float32)
     cost = np.empty(B, np.float32)
-    rc = _load().oracle_viterbi(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k,
+    rc = _load().oracle_viterbi(_ptr(w, ctypes.c_float), _ptr(c, ctypes.c_float), B, n, L, k, V,
                                 _ptr(sg, ctypes.c_int32), _ptr(st, ctypes.c_int32), _ptr(wh, ctypes.c_float),
                                 _ptr(cost, ctypes.c_float))
     if rc != 0:
@@ -192,6 +199,8 @@ def viterbi_tail_biting(w, c, L: int, k: int, mode: int = TB_EXACT):
     """
     w = _f32(w)
     c = _f32(c)
+    if c.ndim != 1:
+        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
     _check_shapes(w, c, L)
     B, n = w.shape
     S = 1 << L
@@ -219,6 +228,8 @@ def soft_tail_biting(w, c, L: int, k: int, T: float):
     has Z_sigma = 0).  Composed from this module's sigma-mode soft codeword.
     """
     w = _f32(w)
+    if np.ndim(c) != 1:
+        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
     B, n = w.shape
     S = 1 << L
     ws_all, lz_all = soft(np.repeat(w, S, axis=0), c, L, k, T, sigma=np.tile(np.arange(S, dtype=np.int32), B))
@@ -242,6 +253,8 @@ def grad_tail_biting(w, c, g, L: int, k: int, T: float):
     """
     w = _f32(w)
     g = _f32(g)
+    if np.ndim(c) != 1:
+        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
     B, n = w.shape
     S = 1 << L
     sig = np.tile(np.arange(S, dtype=np.int32), B)

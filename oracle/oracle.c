@@ -15,7 +15,10 @@
  * Readings where the pages are silent (each one is listed in the design notes):
  *   - trellis: bitshift, L state bits, k new bits per step entering at the low end:
  *       Succ_b(s) = ((s << k) & (2^L - 1)) | b,   Pred_a(s') = (s' >> k) | (a << (L - k)).
- *   - path energy E = sum_t (w_t - c(s_t))^2, path weight exp(-E / T); transitions carry no cost.
+ *   - V weights per step: each state emits a V-vector c(s) = (c(s, 0), .., c(s, V-1)), a sequence of n steps holds
+ *     n V weights (step t owns w[t V .. t V + V - 1]), and c is stored [2^L][V].  V = 1 is the scalar trellis.
+ *   - path energy E = sum_t |w_t - c(s_t)|^2 (squared Euclidean distance over the V components), path weight
+ *     exp(-E / T); transitions carry no cost.
  *   - free mode: s_1 is any state, s_n any state.  sigma mode: a non-emitting start s_0 = sigma, the first
  *     emitting state is a successor of sigma, and the last emitting state s_n = sigma (sigma masked to L bits).
  *   - log_z = ln Z over the emitting states only (no factor for the non-emitting start).
@@ -60,26 +63,37 @@ static double log_sum_exp(const double* x, int m) {
     return mx + log(s);
 }
 
-/* theta_t(s) = -(w_t - c(s))^2 / T : the log Boltzmann weight of emitting c(s) at step t. */
-static inline double log_weight(double wt, double cs, double T) {
-    double d = wt - cs;
-    return -(d * d) / T;
+/* theta_t(s) = -|w_t - c(s)|^2 / T : the log Boltzmann weight of emitting c(s) at step t (V components). */
+static inline double log_weight(const float* wt, const float* cs, int V, double T) {
+    double e = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double d = (double)wt[v] - (double)cs[v];
+        e += d * d;
+    }
+    return -e / T;
 }
 
-static int check_args(int64_t B, int64_t n, int L, int k) {
-    if (B < 0 || n < 1 || k < 1 || L <= k || L > 24) return ORACLE_ERR_ARG;
+/* <g_t, c(s)> over the V components */
+static inline double dot_v(const float* gt, const float* cs, int V) {
+    double e = 0.0;
+    for (int v = 0; v < V; ++v) e += (double)gt[v] * (double)cs[v];
+    return e;
+}
+
+static int check_args(int64_t B, int64_t n, int L, int k, int V) {
+    if (B < 0 || n < 1 || k < 1 || L <= k || L > 24 || V < 1 || V > 16) return ORACLE_ERR_ARG;
     return ORACLE_OK;
 }
 
 /* ------------------------------------------------------------------------------------------------ */
 /* forward pass: alpha_t(s) = theta_t(s) + logsumexp_a alpha_{t-1}(Pred_a(s)), stored for every t.     */
 
-static void forward(const float* w, const float* c, int64_t n, int L, int k, double T, int has_sigma,
+static void forward(const float* w, const float* c, int64_t n, int L, int k, int V, double T, int has_sigma,
                     uint32_t sigma, double* alpha /* [n][S] */) {
     const uint32_t S = 1u << L, P = 1u << k, gmask = (1u << (L - k)) - 1u;
     double x[64];
     for (uint32_t s = 0; s < S; ++s) {
-        double th = log_weight(w[0], c[s], T);
+        double th = log_weight(w, c + (size_t)s * V, V, T);
         /* sigma mode: s_1 must be a successor of sigma, i.e. share its top L-k bits with sigma's low ones */
         alpha[s] = (!has_sigma || (s >> k) == (sigma & gmask)) ? th : -INFINITY;
     }
@@ -88,20 +102,20 @@ static void forward(const float* w, const float* c, int64_t n, int L, int k, dou
         double* at = alpha + (size_t)t * S;
         for (uint32_t s = 0; s < S; ++s) {
             for (uint32_t a = 0; a < P; ++a) x[a] = ap[pred(s, a, L, k)];
-            at[s] = log_weight(w[t], c[s], T) + log_sum_exp(x, (int)P);
+            at[s] = log_weight(w + t * V, c + (size_t)s * V, V, T) + log_sum_exp(x, (int)P);
         }
     }
 }
 
 /* beta_t(s) from beta_{t+1}: logsumexp_b [theta_{t+1}(Succ_b(s)) + beta_{t+1}(Succ_b(s))]. */
-static void backward_step(const float* w, const float* c, int64_t t, int L, int k, double T,
+static void backward_step(const float* w, const float* c, int64_t t, int L, int k, int V, double T,
                           const double* bnext, double* bcur) {
     const uint32_t S = 1u << L, P = 1u << k;
     double x[64];
     for (uint32_t s = 0; s < S; ++s) {
         for (uint32_t b = 0; b < P; ++b) {
             uint32_t u = succ(s, b, L, k);
-            x[b] = log_weight(w[t + 1], c[u], T) + bnext[u];
+            x[b] = log_weight(w + (t + 1) * V, c + (size_t)u * V, V, T) + bnext[u];
         }
         bcur[s] = log_sum_exp(x, (int)P);
     }
@@ -117,14 +131,14 @@ static void backward_init(int L, int has_sigma, uint32_t sigma, double* b) {
 
 /*
  * For one sequence: alpha by the forward pass, beta by the backward pass, ln Z = logsumexp_s(alpha_t + beta_t)
- * (the same for every t), p_t(s) = exp(alpha_t(s) + beta_t(s) - ln Z), w_soft_t = sum_s c(s) p_t(s).
+ * (the same for every t), p_t(s) = exp(alpha_t(s) + beta_t(s) - ln Z), w_soft_t = sum_s c(s) p_t(s) (per component).
  * lnz_dev receives max_t |logsumexp_s(alpha_t + beta_t) - ln Z|, a self-check of the two passes.
  */
-static void soft_one(const float* w, const float* c, int64_t n, int L, int k, double T, int has_sigma,
+static void soft_one(const float* w, const float* c, int64_t n, int L, int k, int V, double T, int has_sigma,
                      uint32_t sigma, double* w_soft, double* log_z, double* lnz_dev, double* alpha,
                      double* b0, double* b1, double* tmp) {
     const uint32_t S = 1u << L;
-    forward(w, c, n, L, k, T, has_sigma, sigma, alpha);
+    forward(w, c, n, L, k, V, T, has_sigma, sigma, alpha);
     double* bcur = b0;
     double* bnext = b1;
     backward_init(L, has_sigma, sigma, bcur);
@@ -135,7 +149,7 @@ static void soft_one(const float* w, const float* c, int64_t n, int L, int k, do
     for (int64_t t = n - 1; t >= 0; --t) {
         if (t < n - 1) {
             double* sw = bcur; bcur = bnext; bnext = sw;   /* bnext now holds beta_{t+1} */
-            backward_step(w, c, t, L, k, T, bnext, bcur);
+            backward_step(w, c, t, L, k, V, T, bnext, bcur);
         }
         const double* at = alpha + (size_t)t * S;
         for (uint32_t s = 0; s < S; ++s) tmp[s] = at[s] + bcur[s];
@@ -144,20 +158,23 @@ static void soft_one(const float* w, const float* c, int64_t n, int L, int k, do
             double e = fabs(lz_t - lnz);
             if (e > dev) dev = e;
         }
-        double acc = 0.0;
-        for (uint32_t s = 0; s < S; ++s) {
-            if (tmp[s] == -INFINITY) continue;
-            acc += (double)c[s] * exp(tmp[s] - lnz);
+        for (int v = 0; v < V; ++v) {
+            double acc = 0.0;
+            for (uint32_t s = 0; s < S; ++s) {
+                if (tmp[s] == -INFINITY) continue;
+                acc += (double)c[(size_t)s * V + v] * exp(tmp[s] - lnz);
+            }
+            w_soft[t * V + v] = isfinite(lnz) ? acc : NAN;
         }
-        w_soft[t] = isfinite(lnz) ? acc : NAN;
     }
     if (log_z) *log_z = lnz;
     if (lnz_dev) *lnz_dev = dev;
 }
 
-int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int k, double T,
+/* w [B, n V], c [2^L, V], w_soft [B, n V], log_z [B] and lnz_dev [B] optional; n counts trellis steps. */
+int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int k, int V, double T,
                 const int32_t* sigma, double* w_soft, double* log_z, double* lnz_dev) {
-    if (check_args(B, n, L, k) != ORACLE_OK || k > 6 || !(T > 0.0) || !w || !c || !w_soft) return ORACLE_ERR_ARG;
+    if (check_args(B, n, L, k, V) != ORACLE_OK || k > 6 || !(T > 0.0) || !w || !c || !w_soft) return ORACLE_ERR_ARG;
     const size_t S = (size_t)1 << L;
     int err = ORACLE_OK;
 #pragma omp parallel
@@ -173,7 +190,7 @@ int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int
 #pragma omp for schedule(dynamic, 1)
             for (int64_t b = 0; b < B; ++b) {
                 uint32_t sg = sigma ? ((uint32_t)sigma[b] & (uint32_t)(S - 1)) : 0u;
-                soft_one(w + b * n, c, n, L, k, T, sigma != NULL, sg, w_soft + b * n,
+                soft_one(w + b * n * V, c, n, L, k, V, T, sigma != NULL, sg, w_soft + b * n * V,
                          log_z ? log_z + b : NULL, lnz_dev ? lnz_dev + b : NULL, alpha, b0, b1, tmp);
             }
         }
@@ -189,13 +206,15 @@ int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int
  * d w_soft_t / d w_u = (2/T) Cov_p(c(s_t), c(s_u)), since d(-E/T)/d w_u = -(2/T)(w_u - c(s_u)).
  * So for an upstream gradient g, grad_u = sum_t g_t dw_soft_t/dw_u = (2/T) Cov_p(c(s_u), F) with
  * F = sum_t g_t c(s_t).  Cov_p(c(s_u), F) = sum_s p_u(s) (c(s) - w_soft_u)(E[F | s_u = s] - E[F]).
+ * With V components per step the same holds per component: d w_soft_{t,v} / d w_{u,v'} =
+ * (2/T) Cov_p(c(s_t, v), c(s_u, v')), F = sum_t <g_t, c(s_t)>, and grad_{u,v} = (2/T) Cov_p(c(s_u, v), F).
  *
  * E[F | s_u = s] splits at u because the posterior is a Markov chain:
- *   ra_u(s) = E[sum_{t<=u} g_t c(s_t) | s_u = s]
- *           = g_u c(s) + sum_a P(s_{u-1} = Pred_a(s) | s_u = s) ra_{u-1}(Pred_a(s)),
+ *   ra_u(s) = E[sum_{t<=u} <g_t, c(s_t)> | s_u = s]
+ *           = <g_u, c(s)> + sum_a P(s_{u-1} = Pred_a(s) | s_u = s) ra_{u-1}(Pred_a(s)),
  *     where P(s_{u-1} = Pred_a(s) | s_u = s) = softmax_a alpha_{u-1}(Pred_a(s));
- *   rb_u(s) = E[sum_{t>u} g_t c(s_t) | s_u = s]
- *           = sum_b P(s_{u+1} = Succ_b(s) | s_u = s) [g_{u+1} c(Succ_b(s)) + rb_{u+1}(Succ_b(s))],
+ *   rb_u(s) = E[sum_{t>u} <g_t, c(s_t)> | s_u = s]
+ *           = sum_b P(s_{u+1} = Succ_b(s) | s_u = s) [<g_{u+1}, c(Succ_b(s))> + rb_{u+1}(Succ_b(s))],
  *     where P(s_{u+1} = Succ_b(s) | s_u = s) = softmax_b [theta_{u+1}(Succ_b(s)) + beta_{u+1}(Succ_b(s))].
  * States of zero posterior weight contribute nothing.
  *
@@ -205,7 +224,7 @@ int oracle_soft(const float* w, const float* c, int64_t B, int64_t n, int L, int
  * as through the path measure, so
  *   dL/dc(v) = sum_t g_t P(s_t = v) + Cov_p(F, (2/T) sum_u (w_u - c(v)) [s_u = v])
  *            = sum_u P(s_u = v) [ g_u + (2/T) (w_u - c(v)) (E[F | s_u = v] - E[F]) ],
- * summed here per sequence (the caller adds sequences up).
+ * summed here per sequence (the caller adds sequences up); with V components, per component of c(v), g_u and w_u.
  */
 static void softmax_weights(const double* x, int m, double* pw) {
     double mx = -INFINITY;
@@ -220,16 +239,16 @@ static void softmax_weights(const double* x, int m, double* pw) {
     for (int i = 0; i < m; ++i) pw[i] /= s;
 }
 
-static void grad_one(const float* w, const float* c, const float* g, int64_t n, int L, int k, double T,
+static void grad_one(const float* w, const float* c, const float* g, int64_t n, int L, int k, int V, double T,
                      int has_sigma, uint32_t sigma, double* grad, double* w_soft, double* gc, double* alpha,
                      double* ra, double* b0, double* b1, double* rb0, double* rb1, double* tmp) {
     const uint32_t S = 1u << L, P = 1u << k;
-    double x[64], pw[64];
+    double x[64], pw[64], m0[16], cov[16];
     if (gc)
-        for (uint32_t s = 0; s < S; ++s) gc[s] = 0.0;
-    forward(w, c, n, L, k, T, has_sigma, sigma, alpha);
+        for (size_t i = 0; i < (size_t)S * V; ++i) gc[i] = 0.0;
+    forward(w, c, n, L, k, V, T, has_sigma, sigma, alpha);
     /* ra: forward expectation pass */
-    for (uint32_t s = 0; s < S; ++s) ra[s] = (double)g[0] * (double)c[s];
+    for (uint32_t s = 0; s < S; ++s) ra[s] = dot_v(g, c + (size_t)s * V, V);
     for (int64_t t = 1; t < n; ++t) {
         const double* ap = alpha + (size_t)(t - 1) * S;
         const double* rp = ra + (size_t)(t - 1) * S;
@@ -240,7 +259,7 @@ static void grad_one(const float* w, const float* c, const float* g, int64_t n, 
             double acc = 0.0;
             for (uint32_t a = 0; a < P; ++a)
                 if (pw[a] != 0.0) acc += pw[a] * rp[pred(s, a, L, k)];
-            rt[s] = (double)g[t] * (double)c[s] + acc;
+            rt[s] = dot_v(g + t * V, c + (size_t)s * V, V) + acc;
         }
     }
     /* ln Z */
@@ -254,18 +273,18 @@ static void grad_one(const float* w, const float* c, const float* g, int64_t n, 
         if (t < n - 1) {
             double* sw = bcur; bcur = bnext; bnext = sw;
             sw = rbcur; rbcur = rbnext; rbnext = sw;
-            backward_step(w, c, t, L, k, T, bnext, bcur);
+            backward_step(w, c, t, L, k, V, T, bnext, bcur);
             for (uint32_t s = 0; s < S; ++s) {
                 for (uint32_t b = 0; b < P; ++b) {
                     uint32_t u = succ(s, b, L, k);
-                    x[b] = log_weight(w[t + 1], c[u], T) + bnext[u];
+                    x[b] = log_weight(w + (t + 1) * V, c + (size_t)u * V, V, T) + bnext[u];
                 }
                 softmax_weights(x, (int)P, pw);
                 double acc = 0.0;
                 for (uint32_t b = 0; b < P; ++b) {
                     if (pw[b] == 0.0) continue;
                     uint32_t u = succ(s, b, L, k);
-                    acc += pw[b] * ((double)g[t + 1] * (double)c[u] + rbnext[u]);
+                    acc += pw[b] * (dot_v(g + (t + 1) * V, c + (size_t)u * V, V) + rbnext[u]);
                 }
                 rbcur[s] = acc;
             }
@@ -273,38 +292,46 @@ static void grad_one(const float* w, const float* c, const float* g, int64_t n, 
         /* posterior at step t, mean codeword and mean of E[F | s_t] */
         const double* at = alpha + (size_t)t * S;
         const double* rt = ra + (size_t)t * S;
-        double m0 = 0.0, mr = 0.0;
+        double mr = 0.0;
+        for (int v = 0; v < V; ++v) m0[v] = 0.0;
         for (uint32_t s = 0; s < S; ++s) {
             double lp = at[s] + bcur[s];
             tmp[s] = (lp == -INFINITY) ? 0.0 : exp(lp - lnz);
             if (tmp[s] != 0.0) {
-                m0 += tmp[s] * (double)c[s];
+                for (int v = 0; v < V; ++v) m0[v] += tmp[s] * (double)c[(size_t)s * V + v];
                 mr += tmp[s] * (rt[s] + rbcur[s]);
             }
         }
-        /* centred two-pass covariance */
-        double cov = 0.0;
-        for (uint32_t s = 0; s < S; ++s)
-            if (tmp[s] != 0.0) cov += tmp[s] * ((double)c[s] - m0) * (rt[s] + rbcur[s] - mr);
+        /* centred two-pass covariance, per component */
+        for (int v = 0; v < V; ++v) {
+            cov[v] = 0.0;
+            for (uint32_t s = 0; s < S; ++s)
+                if (tmp[s] != 0.0) cov[v] += tmp[s] * ((double)c[(size_t)s * V + v] - m0[v]) * (rt[s] + rbcur[s] - mr);
+        }
         if (gc && isfinite(lnz))
             for (uint32_t s = 0; s < S; ++s)
                 if (tmp[s] != 0.0)
-                    gc[s] += tmp[s] * ((double)g[t] + (2.0 / T) * ((double)w[t] - (double)c[s]) * (rt[s] + rbcur[s] - mr));
-        if (isfinite(lnz)) {
-            grad[t] = (2.0 / T) * cov;
-            if (w_soft) w_soft[t] = m0;
-        } else {
-            grad[t] = NAN;
-            if (w_soft) w_soft[t] = NAN;
+                    for (int v = 0; v < V; ++v) {
+                        const double wv = (double)w[t * V + v], cv = (double)c[(size_t)s * V + v];
+                        gc[(size_t)s * V + v] += tmp[s] * ((double)g[t * V + v] + (2.0 / T) * (wv - cv) * (rt[s] + rbcur[s] - mr));
+                    }
+        for (int v = 0; v < V; ++v) {
+            if (isfinite(lnz)) {
+                grad[t * V + v] = (2.0 / T) * cov[v];
+                if (w_soft) w_soft[t * V + v] = m0[v];
+            } else {
+                grad[t * V + v] = NAN;
+                if (w_soft) w_soft[t * V + v] = NAN;
+            }
         }
     }
     if (gc && !isfinite(lnz))   /* no path satisfies the boundary: the loss, hence its gradient, is undefined */
-        for (uint32_t s = 0; s < S; ++s) gc[s] = NAN;
+        for (size_t i = 0; i < (size_t)S * V; ++i) gc[i] = NAN;
 }
 
-static int grad_all(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, double T,
-                    const int32_t* sigma, double* grad, double* w_soft, double* gc) {
-    if (check_args(B, n, L, k) != ORACLE_OK || k > 6 || !(T > 0.0) || !w || !c || !g || !grad)
+static int grad_all(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, int V,
+                    double T, const int32_t* sigma, double* grad, double* w_soft, double* gc) {
+    if (check_args(B, n, L, k, V) != ORACLE_OK || k > 6 || !(T > 0.0) || !w || !c || !g || !grad)
         return ORACLE_ERR_ARG;
     const size_t S = (size_t)1 << L;
     int err = ORACLE_OK;
@@ -324,9 +351,9 @@ static int grad_all(const float* w, const float* c, const float* g, int64_t B, i
 #pragma omp for schedule(dynamic, 1)
             for (int64_t b = 0; b < B; ++b) {
                 uint32_t sg = sigma ? ((uint32_t)sigma[b] & (uint32_t)(S - 1)) : 0u;
-                grad_one(w + b * n, c, g + b * n, n, L, k, T, sigma != NULL, sg, grad + b * n,
-                         w_soft ? w_soft + b * n : NULL, gc ? gc + (size_t)b * S : NULL, alpha, ra, b0, b1, rb0,
-                         rb1, tmp);
+                grad_one(w + b * n * V, c, g + b * n * V, n, L, k, V, T, sigma != NULL, sg, grad + b * n * V,
+                         w_soft ? w_soft + b * n * V : NULL, gc ? gc + (size_t)b * S * V : NULL, alpha, ra, b0, b1,
+                         rb0, rb1, tmp);
             }
         }
         free(alpha); free(ra); free(b0); free(b1); free(rb0); free(rb1); free(tmp);
@@ -334,36 +361,49 @@ static int grad_all(const float* w, const float* c, const float* g, int64_t B, i
     return err;
 }
 
-/* grad [B, n]: dL/dw for upstream g = dL/dw_soft; w_soft [B, n] optional. */
-int oracle_grad(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, double T,
+/* grad [B, n V]: dL/dw for upstream g = dL/dw_soft [B, n V]; w_soft [B, n V] optional. */
+int oracle_grad(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, int V, double T,
                 const int32_t* sigma, double* grad, double* w_soft) {
-    return grad_all(w, c, g, B, n, L, k, T, sigma, grad, w_soft, NULL);
+    return grad_all(w, c, g, B, n, L, k, V, T, sigma, grad, w_soft, NULL);
 }
 
-/* The same, plus gc [B, 2^L]: dL/dc of each sequence on its own (NaN for a sequence with no admissible path). */
-int oracle_grad_codebook(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k,
+/* The same, plus gc [B, 2^L, V]: dL/dc of each sequence on its own (NaN for a sequence with no admissible path). */
+int oracle_grad_codebook(const float* w, const float* c, const float* g, int64_t B, int64_t n, int L, int k, int V,
                          double T, const int32_t* sigma, double* grad, double* w_soft, double* gc) {
     if (!gc) return ORACLE_ERR_ARG;
-    return grad_all(w, c, g, B, n, L, k, T, sigma, grad, w_soft, gc);
+    return grad_all(w, c, g, B, n, L, k, V, T, sigma, grad, w_soft, gc);
 }
 
 /* ------------------------------------------------------------------------------------------------ */
 /* Viterbi hard code (the T -> 0 limit), IEEE float32 with a fixed operation order                  */
 
 /*
- * M_1(s) = fl(d*d) with d = fl(w_1 - c(s));   M_t(s) = fl(fl(d*d) + min_a M_{t-1}(Pred_a(s))).
+ * M_1(s) = e_1(s);   M_t(s) = fl(e_t(s) + min_a M_{t-1}(Pred_a(s))),  where e_t(s) = fl(d_0 * d_0) with
+ * d_v = fl(w_{t,v} - c(s, v)), and for V > 1 the components are added in order, e = fl(e + fl(d_v * d_v)).
  * The back pointer of s at step t is the smallest a attaining the min (scan a = 0, 1, ... with a strict <),
  * the end state is the smallest s attaining min_s M_n(s) (sigma mode: s_n = sigma), and the path is traced
  * back through the back pointers.  cost = M_n(s_n).  No normalisation and no fused multiply-add.
  */
-static void viterbi_one(const float* w, const float* c, int64_t n, int L, int k, int has_sigma, uint32_t sigma,
-                        int32_t* states, float* w_hard, float* cost, float* m0, float* m1, uint8_t* bp) {
+/* fl32 squared distance |w_t - c(s)|^2, components added in index order */
+static inline float sq_dist32(const float* wt, const float* cs, int V) {
+    float d = wt[0] - cs[0];
+    float e = d * d;
+    for (int v = 1; v < V; ++v) {
+        float dv = wt[v] - cs[v];
+        float ev = dv * dv;
+        e = e + ev;
+    }
+    return e;
+}
+
+static void viterbi_one(const float* w, const float* c, int64_t n, int L, int k, int V, int has_sigma,
+                        uint32_t sigma, int32_t* states, float* w_hard, float* cost, float* m0, float* m1,
+                        uint8_t* bp) {
     const uint32_t S = 1u << L, P = 1u << k, gmask = (1u << (L - k)) - 1u;
     float* mcur = m0;
     float* mprev = m1;
     for (uint32_t s = 0; s < S; ++s) {
-        float d = w[0] - c[s];
-        float e = d * d;
+        float e = sq_dist32(w, c + (size_t)s * V, V);
         mcur[s] = (!has_sigma || (s >> k) == (sigma & gmask)) ? e : INFINITY;
     }
     for (int64_t t = 1; t < n; ++t) {
@@ -376,8 +416,7 @@ static void viterbi_one(const float* w, const float* c, int64_t n, int L, int k,
                 float v = mprev[pred(s, a, L, k)];
                 if (v < best) { best = v; arg = a; }
             }
-            float d = w[t] - c[s];
-            float e = d * d;
+            float e = sq_dist32(w + t * V, c + (size_t)s * V, V);
             mcur[s] = e + best;
             bpt[s] = (uint8_t)arg;
         }
@@ -394,14 +433,16 @@ static void viterbi_one(const float* w, const float* c, int64_t n, int L, int k,
     uint32_t s = s_end;
     for (int64_t t = n - 1; t >= 0; --t) {
         states[t] = (int32_t)s;
-        if (w_hard) w_hard[t] = c[s];
+        if (w_hard)
+            for (int v = 0; v < V; ++v) w_hard[t * V + v] = c[(size_t)s * V + v];
         if (t > 0) s = pred(s, bp[(size_t)t * S + s], L, k);
     }
 }
 
-int oracle_viterbi(const float* w, const float* c, int64_t B, int64_t n, int L, int k, const int32_t* sigma,
+/* states [B, n] (one per step), w_hard [B, n V] optional, cost [B] optional. */
+int oracle_viterbi(const float* w, const float* c, int64_t B, int64_t n, int L, int k, int V, const int32_t* sigma,
                    int32_t* states, float* w_hard, float* cost) {
-    if (check_args(B, n, L, k) != ORACLE_OK || k > 8 || !w || !c || !states) return ORACLE_ERR_ARG;
+    if (check_args(B, n, L, k, V) != ORACLE_OK || k > 8 || !w || !c || !states) return ORACLE_ERR_ARG;
     const size_t S = (size_t)1 << L;
     int err = ORACLE_OK;
 #pragma omp parallel
@@ -416,8 +457,8 @@ int oracle_viterbi(const float* w, const float* c, int64_t B, int64_t n, int L, 
 #pragma omp for schedule(dynamic, 1)
             for (int64_t b = 0; b < B; ++b) {
                 uint32_t sg = sigma ? ((uint32_t)sigma[b] & (uint32_t)(S - 1)) : 0u;
-                viterbi_one(w + b * n, c, n, L, k, sigma != NULL, sg, states + b * n,
-                            w_hard ? w_hard + b * n : NULL, cost ? cost + b : NULL, m0, m1, bp);
+                viterbi_one(w + b * n * V, c, n, L, k, V, sigma != NULL, sg, states + b * n,
+                            w_hard ? w_hard + b * n * V : NULL, cost ? cost + b : NULL, m0, m1, bp);
             }
         }
         free(m0); free(m1); free(bp);

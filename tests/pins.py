@@ -11,6 +11,10 @@ Sources: the path measure p_T(path) proportional to exp(-E/T) and the soft
 codeword sum_s c(s) p_T(s_t = s) (gist.science Technical Summary, "Core
 Mechanism"); the equality with a 1-D Ising transfer-matrix product and the
 T -> 0 limit (arXiv abstract).
+
+A codebook [2^L] emits one weight per step; a codebook [2^L, V] emits a
+V-vector, and the weights of a sequence are then read as n rows of V.  The
+helpers return per-weight quantities flattened in that order.
 """
 from __future__ import annotations
 
@@ -42,10 +46,17 @@ def sigma_paths(L: int, k: int, n: int, sigma: int) -> np.ndarray:
     return p[p[:, -1] == sigma]
 
 
+def _cw(c, w):
+    """Codebook as [S, V] and weights as [n, V] (float64)."""
+    c2 = np.asarray(c, np.float64).reshape(np.shape(c)[0], -1)
+    return c2, np.asarray(w, np.float64).reshape(-1, c2.shape[1])
+
+
 def path_energies(paths: np.ndarray, w: np.ndarray, c: np.ndarray) -> np.ndarray:
-    """E(path) = sum_t (w_t - c(s_t))^2 in float64."""
-    d = w.astype(np.float64)[None, :] - c.astype(np.float64)[paths]
-    return (d * d).sum(axis=1)
+    """E(path) = sum_t |w_t - c(s_t)|^2 in float64 (V components per step)."""
+    c2, w2 = _cw(c, w)
+    d = w2[None, :, :] - c2[paths]
+    return (d * d).sum(axis=(1, 2))
 
 
 def _lse(x):
@@ -53,52 +64,68 @@ def _lse(x):
     return m + np.log(np.sum(np.exp(x - m)))
 
 
+def _emitted(paths, c):
+    """c(s_t) of every path, flattened per weight: [P, n V]."""
+    c2 = np.asarray(c, np.float64).reshape(np.shape(c)[0], -1)
+    return c2[paths].reshape(paths.shape[0], -1)
+
+
 def brute_soft(paths, w, c, T):
-    """(w_soft [n], ln Z, probabilities [P]) by summing over every path."""
+    """(w_soft [n V], ln Z, probabilities [P]) by summing over every path."""
     E = path_energies(paths, w, c)
     lw = -E / T
     lnz = _lse(lw)
     p = np.exp(lw - lnz)
-    cv = c.astype(np.float64)[paths]
+    cv = _emitted(paths, c)
     return (p[:, None] * cv).sum(axis=0), lnz, p
 
 
 def brute_jacobian(paths, w, c, T):
-    """J_tu = d w_soft_t / d w_u = (2/T) Cov_p(c(s_t), c(s_u)) over all paths."""
+    """J_tu = d w_soft_t / d w_u = (2/T) Cov_p(c(s_t), c(s_u)) over all paths (t, u index weights)."""
     _, _, p = brute_soft(paths, w, c, T)
-    cv = c.astype(np.float64)[paths]
+    cv = _emitted(paths, c)
     mu = (p[:, None] * cv).sum(axis=0)
     cc = cv - mu[None, :]
     return (2.0 / T) * (cc * p[:, None]).T @ cc
 
 
 def brute_codebook_jacobian(paths, w, c, T):
-    """K_tv = d w_soft_t / d c(v) over all paths.
+    """K_tv = d w_soft_t / d c(v) over all paths ([n, S] for a scalar codebook, [n V, S V] for a [S, V] one).
 
     c(v) enters w_soft_t = sum_path p(path) c(s_t) twice: directly (the emitted value, weight P(s_t = v)) and
-    through the path measure, where d log p / d c(v) = h_v - E[h_v] with h_v = (2/T) sum_u (w_u - c(v)) [s_u = v].
+    through the path measure, where d log p / d c(v) = h_v - E[h_v] with h_v = (2/T) sum_u (w_u - c(v)) [s_u = v]
+    (per component when V > 1: the direct term only links equal components).
     """
     _, _, p = brute_soft(paths, w, c, T)
-    S = c.shape[0]
+    c2, w2 = _cw(c, w)
+    S, V = c2.shape
     n = paths.shape[1]
-    cv = c.astype(np.float64)[paths]
     onehot = (paths[:, :, None] == np.arange(S)[None, None, :]).astype(np.float64)      # [P, n, S]
-    direct = np.einsum("p,pts->ts", p, onehot)                                            # P(s_t = v)
-    dw = w.astype(np.float64)[:, None] - c.astype(np.float64)[None, :]                   # [n, S]
-    h = (2.0 / T) * np.einsum("pus,us->ps", onehot, dw)                                   # [P, S]
+    occ = np.einsum("p,pts->ts", p, onehot)                                               # P(s_t = v)
+    direct = np.einsum("ts,ab->tasb", occ, np.eye(V)).reshape(n * V, S * V)
+    dw = w2[:, None, :] - c2[None, :, :]                                                  # [n, S, V]
+    h = (2.0 / T) * np.einsum("pus,usb->psb", onehot, dw).reshape(-1, S * V)              # [P, S V]
     hc = h - (p[:, None] * h).sum(axis=0)[None, :]
+    cv = _emitted(paths, c)
     cc = cv - (p[:, None] * cv).sum(axis=0)[None, :]
-    return direct + np.einsum("p,pt,ps->ts", p, cc, hc)
+    K = direct + np.einsum("p,pt,ps->ts", p, cc, hc)
+    return K if np.ndim(c) == 2 else K.reshape(n, S)
 
 
 def brute_viterbi_fp32(paths, w, c):
-    """Per-path float32 cost accumulated in step order, ((e_1 + e_2) + e_3) + ..., and the argmin set."""
-    w32 = w.astype(np.float32)
-    c32 = c.astype(np.float32)
+    """Per-path float32 cost accumulated in step order, ((e_1 + e_2) + e_3) + ..., and the argmin set.
+
+    e_t = |w_t - c(s_t)|^2 in float32 with the V components added in index order."""
+    c32 = np.asarray(c, np.float32).reshape(np.shape(c)[0], -1)
+    V = c32.shape[1]
+    w32 = np.asarray(w, np.float32).reshape(-1, V)
     acc = np.zeros(paths.shape[0], np.float32)
     for t in range(paths.shape[1]):
-        d = (w32[t] - c32[paths[:, t]]).astype(np.float32)
-        e = (d * d).astype(np.float32)
+        e = None
+        for v in range(V):
+            d = (w32[t, v] - c32[paths[:, t], v]).astype(np.float32)
+            dd = (d * d).astype(np.float32)
+            e = dd if e is None else (e + dd).astype(np.float32)
         acc = (e + acc).astype(np.float32) if t else e
     best = acc.min()
     return acc, np.flatnonzero(acc == best)
@@ -122,9 +149,9 @@ def transfer_product_log(w, c, T, L, k):
     A = shift_matrix(L, k)
     M = np.eye(1 << L)
     logscale = 0.0
-    c64 = c.astype(np.float64)
-    for t in range(len(w)):
-        D = np.exp(-((float(w[t]) - c64) ** 2) / T)
+    c2, w2 = _cw(c, w)
+    for t in range(w2.shape[0]):
+        D = np.exp(-((w2[t][None, :] - c2) ** 2).sum(axis=1) / T)
         M = (M @ A) * D[None, :]
         s = M.max()
         M = M / s

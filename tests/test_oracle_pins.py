@@ -538,3 +538,134 @@ def test_soft_tail_biting_some_sigmas_unreachable(oracle_mod):
         np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
         gref = pins.brute_jacobian(paths, w[b], c, T) @ g[b].astype(np.float64)
         np.testing.assert_allclose(gr[b], gref, rtol=0, atol=1e-11 * max(1.0, np.abs(gref).max()))
+
+
+# ----------------------------------------------------------- P12 vector trellis (V weights per step) and k = 4
+# A codebook [2^L, V] emits V weights per step; the path energy sums the squared distance over the components.
+
+VEC_TRELLISES = [(4, 2, 5, 2), (4, 1, 6, 2), (6, 3, 3, 2), (4, 2, 4, 3), (8, 4, 2, 2)]
+
+
+def _vec_inputs(L, n, V, seed, B=3):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = rng.standard_normal((1 << L, V)).astype(np.float32)
+    w = rng.standard_normal((B, n * V)).astype(np.float32)
+    g = rng.standard_normal((B, n * V)).astype(np.float32)
+    return w, c, g
+
+
+@pytest.mark.parametrize("L,k,n,V", VEC_TRELLISES)
+@pytest.mark.parametrize("T", [1.0, 0.3, 0.05])
+def test_vector_soft_matches_brute_force(oracle_mod, L, k, n, V, T):
+    w, c, _ = _vec_inputs(L, n, V, 31 * L + 7 * k + V)
+    ws, lz, dev = oracle_mod.soft(w, c, L, k, T, with_check=True)
+    assert ws.shape == w.shape
+    paths = pins.free_paths(L, k, n)
+    for b in range(w.shape[0]):
+        ref, lnz, _ = pins.brute_soft(paths, w[b], c, T)
+        np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
+        assert abs(lz[b] - lnz) <= 1e-12 * max(1.0, abs(lnz))
+    assert dev.max() < 1e-10
+    sig = np.array([0, (1 << L) - 1, 5], np.int32)
+    ws, lz = oracle_mod.soft(w, c, L, k, T, sigma=sig)
+    for b in range(w.shape[0]):
+        ref, lnz, _ = pins.brute_soft(pins.sigma_paths(L, k, n, int(sig[b])), w[b], c, T)
+        np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
+        assert abs(lz[b] - lnz) <= 1e-12 * max(1.0, abs(lnz))
+
+
+@pytest.mark.parametrize("L,k,n,V", VEC_TRELLISES)
+@pytest.mark.parametrize("sigma", [False, True])
+def test_vector_grads_match_brute_force(oracle_mod, L, k, n, V, sigma):
+    T = 0.5
+    w, c, g = _vec_inputs(L, n, V, 7 * L + 3 * k + V + 1)
+    sig = np.array([1, 6, (1 << L) - 2], np.int32) if sigma else None
+    gc, gw, ws = oracle_mod.grad_codebook(w, c, g, L, k, T, sigma=sig, per_sequence=True)
+    assert gc.shape == (w.shape[0], 1 << L, V) and gw.shape == w.shape
+    for b in range(w.shape[0]):
+        paths = pins.sigma_paths(L, k, n, int(sig[b])) if sigma else pins.free_paths(L, k, n)
+        J = pins.brute_jacobian(paths, w[b], c, T)
+        ref = J @ g[b].astype(np.float64)
+        np.testing.assert_allclose(gw[b], ref, rtol=0, atol=1e-11 * max(1.0, np.abs(ref).max()))
+        K = pins.brute_codebook_jacobian(paths, w[b], c, T)
+        refc = (g[b].astype(np.float64) @ K).reshape(1 << L, V)
+        np.testing.assert_allclose(gc[b], refc, rtol=0, atol=1e-11 * max(1.0, np.abs(refc).max()))
+    gr, _ = oracle_mod.grad(w, c, g, L, k, T, sigma=sig)
+    np.testing.assert_array_equal(gr, gw)
+
+
+def test_vector_brute_jacobians_are_derivatives():
+    """The covariance forms used above equal central differences of the brute-force soft codeword (V = 2)."""
+    L, k, n, V, T = 4, 2, 3, 2, 0.6
+    w, c, _ = _vec_inputs(L, n, V, 77, B=1)
+    paths = pins.free_paths(L, k, n)
+    w0, c0 = w[0].astype(np.float64), c.astype(np.float64)
+    J = pins.brute_jacobian(paths, w0, c0, T)
+    K = pins.brute_codebook_jacobian(paths, w0, c0, T)
+    h = 1e-4
+    for u in range(n * V):
+        e = np.zeros(n * V)
+        e[u] = h
+        fp, _, _ = pins.brute_soft(paths, w0 + e, c0, T)
+        fm, _, _ = pins.brute_soft(paths, w0 - e, c0, T)
+        np.testing.assert_allclose((fp - fm) / (2 * h), J[:, u], rtol=0, atol=1e-6)
+    for j in range(0, (1 << L) * V, 5):
+        e = np.zeros((1 << L) * V)
+        e[j] = h
+        fp, _, _ = pins.brute_soft(paths, w0, c0 + e.reshape(c0.shape), T)
+        fm, _, _ = pins.brute_soft(paths, w0, c0 - e.reshape(c0.shape), T)
+        np.testing.assert_allclose((fp - fm) / (2 * h), K[:, j], rtol=0, atol=1e-6)
+
+
+@pytest.mark.parametrize("L,k,n,V", VEC_TRELLISES)
+def test_vector_viterbi_matches_brute_force(oracle_mod, L, k, n, V):
+    w, c, _ = _vec_inputs(L, n, V, 5 * L + n + V, B=6)
+    st, wh, cost = oracle_mod.viterbi(w, c, L, k)
+    assert st.shape == (w.shape[0], n) and wh.shape == w.shape
+    paths = pins.free_paths(L, k, n)
+    for b in range(w.shape[0]):
+        acc, argset = pins.brute_viterbi_fp32(paths, w[b], c)
+        assert cost[b] == acc[argset[0]]
+        assert any(np.array_equal(st[b], paths[i]) for i in argset)
+        np.testing.assert_array_equal(wh[b], c[st[b]].reshape(-1))
+    sig = np.array([0, 3, (1 << L) - 1, 10 % (1 << L), 1, 2], np.int32)
+    st, _, cost = oracle_mod.viterbi(w, c, L, k, sigma=sig)
+    for b in range(w.shape[0]):
+        acc, argset = pins.brute_viterbi_fp32(pins.sigma_paths(L, k, n, int(sig[b])), w[b], c)
+        assert cost[b] == acc[argset[0]] and st[b, -1] == sig[b]
+
+
+@pytest.mark.parametrize("L,k,n,V,T", [(6, 2, 8, 2, 0.5), (8, 4, 5, 2, 0.3), (6, 1, 10, 3, 1.0)])
+def test_vector_log_z_equals_ising_transfer_product(oracle_mod, L, k, n, V, T):
+    w, c, _ = _vec_inputs(L, n, V, 900 + L + V)
+    _, lz = oracle_mod.soft(w, c, L, k, T)
+    sig = np.array([1, 21, (1 << L) - 1], np.int32)
+    _, lzs = oracle_mod.soft(w, c, L, k, T, sigma=sig)
+    for b in range(w.shape[0]):
+        ref = pins.transfer_lnz_free(w[b].astype(np.float64), c, T, L, k)
+        assert abs(lz[b] - ref) <= 1e-10 * max(1.0, abs(ref))
+        refs = pins.transfer_lnz_sigma(w[b].astype(np.float64), c, T, L, k, int(sig[b]))
+        assert abs(lzs[b] - refs) <= 1e-10 * max(1.0, abs(refs))
+
+
+def test_vector_trellis_with_a_silent_component_is_the_scalar_trellis(oracle_mod):
+    """V = 2 with the second codebook column and the second weight of every step at 0 is the V = 1 trellis on the
+    first column: same ln Z, same first component, a zero second component, the same Viterbi path and cost."""
+    L, k, n, T = 8, 2, 24, 0.2
+    w1, c1, g1 = _inputs(L, n, 4242)
+    c2 = np.stack([c1, np.zeros_like(c1)], axis=1)
+    w2 = np.stack([w1, np.zeros_like(w1)], axis=2).reshape(w1.shape[0], 2 * n)
+    g2 = np.stack([g1, np.zeros_like(g1)], axis=2).reshape(w1.shape[0], 2 * n)
+    a, la = oracle_mod.soft(w1, c1, L, k, T)
+    b, lb = oracle_mod.soft(w2, c2, L, k, T)
+    np.testing.assert_array_equal(b[:, 0::2], a)
+    np.testing.assert_array_equal(b[:, 1::2], 0.0)
+    np.testing.assert_array_equal(lb, la)
+    ga, _ = oracle_mod.grad(w1, c1, g1, L, k, T)
+    gb, _ = oracle_mod.grad(w2, c2, g2, L, k, T)
+    np.testing.assert_allclose(gb[:, 0::2], ga, rtol=0, atol=1e-12 * np.abs(ga).max())
+    np.testing.assert_array_equal(gb[:, 1::2], 0.0)
+    sa, _, ca = oracle_mod.viterbi(w1, c1, L, k)
+    sb, _, cb = oracle_mod.viterbi(w2, c2, L, k)
+    np.testing.assert_array_equal(sa, sb)
+    np.testing.assert_array_equal(ca, cb)
