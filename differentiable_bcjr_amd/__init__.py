@@ -20,6 +20,11 @@ are exact ("exactly differentiable with respect to the weight pre-image and trel
 
 ``temperature_schedule`` gives the annealing sequence T0 -> T_end for a QAT run (host-side, see ``anneal``).
 
+Trellis variants: ``k`` (bits shifted in per step) may be 1 to 4 for the soft codeword, its weights' gradient and
+Viterbi.  A codebook of shape [2^L, V] emits V weights per step (V = 1 or 2): the weights are then [B, n V], step t
+of a row owning its weights t V .. t V + V - 1, and Viterbi returns one state per step.  The codebook gradient and
+the tail-biting operations take k = 2 and a codebook [2^L].
+
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
 in the library's kernels.
@@ -73,54 +78,78 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2) -> int:
-    """Device workspace bytes the library needs for op (abi.BCJR_OP_SOFT / _GRAD / _VITERBI / _GRAD_CODEBOOK)."""
-    return abi.bcjr_workspace_bytes(op, B, n, L, k)
+def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2, V: int = 1) -> int:
+    """Device workspace bytes the library needs for op (abi.BCJR_OP_SOFT / _GRAD / _VITERBI / _GRAD_CODEBOOK ...) on
+    B sequences of n trellis steps."""
+    return abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
 
 
-def _workspace(op, B, n, L, k, device, workspace):
-    need = workspace_bytes(op, B, n, L, k)
+def _workspace(op, B, n, L, k, device, workspace, V=1):
+    need = workspace_bytes(op, B, n, L, k, V)
     if workspace is None:
         # torch's allocator hands out 512-byte aligned blocks; the library checks 256-byte alignment itself
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, need
 
 
+def _steps(w: torch.Tensor, codebook: torch.Tensor, L: int):
+    """(B, trellis steps n, V) for w [B, n V] and a codebook [2^L] (V = 1) or [2^L, V]."""
+    if w.dim() != 2:
+        raise ValueError("w must be [B, n] (or [B, n V] with a codebook [2^L, V])")
+    if codebook.dim() == 1:
+        V = 1
+    elif codebook.dim() == 2:
+        V = codebook.shape[1]
+    else:
+        raise ValueError("codebook must be [2^L] or [2^L, V]")
+    if codebook.shape[0] != 1 << L or V < 1 or w.shape[1] % V:
+        raise ValueError(f"codebook must have 2^L = {1 << L} rows and the weights per row must be a multiple of V")
+    return w.shape[0], w.shape[1] // V, V
+
+
 def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
                   boundary_state: torch.Tensor | None = None, *, return_log_z: bool = False,
                   workspace: torch.Tensor | None = None):
-    """Soft codeword [B, n] (and ln Z [B] if ``return_log_z``) for weights w [B, n] and codebook [2^L]."""
+    """Soft codeword with w's shape (and ln Z [B] if ``return_log_z``) for weights w [B, n] and codebook [2^L], or
+    w [B, n V] and codebook [2^L, V]."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
-    if w.dim() != 2:
-        raise ValueError("w must be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
     sig = _sigma(boundary_state, B, w.device)
     out = torch.empty_like(w)
     lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
-    ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace)
-    _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
-                                  out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                      out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    else:
+        _check(abi.bcjr_soft_codeword_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T), _ptr(sig),
+                                        out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
     return (out, lz) if return_log_z else out
 
 
 def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int, k: int = 2,
                        T: float = 1.0, boundary_state: torch.Tensor | None = None, *, return_w_soft: bool = False,
                        workspace: torch.Tensor | None = None):
-    """dL/dw [B, n] given dL/dw_soft [B, n] (and the soft codeword if ``return_w_soft``)."""
+    """dL/dw given dL/dw_soft, both with w's shape (and the soft codeword if ``return_w_soft``)."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     g = _f32(grad_w_soft, "grad_w_soft")
-    if w.dim() != 2 or g.shape != w.shape:
-        raise ValueError("w and grad_w_soft must both be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
+    if g.shape != w.shape:
+        raise ValueError("grad_w_soft must have w's shape")
     sig = _sigma(boundary_state, B, w.device)
     grad = torch.empty_like(w)
     ws_out = torch.empty_like(w) if return_w_soft else None
-    ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace)
-    _check(abi.bcjr_soft_codeword_grad(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
-                                       g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
-                                       _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.bcjr_soft_codeword_grad(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                           g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
+                                           _stream(w.device)))
+    else:
+        _check(abi.bcjr_soft_codeword_grad_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T), _ptr(sig),
+                                             g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
+                                             _stream(w.device)))
     return (grad, ws_out) if return_w_soft else grad
 
 
@@ -133,6 +162,8 @@ def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     g = _f32(grad_w_soft, "grad_w_soft")
+    if codebook.dim() != 1:
+        raise ValueError("the codebook gradient takes a codebook [2^L] (one weight per step)")
     if w.dim() != 2 or g.shape != w.shape:
         raise ValueError("w and grad_w_soft must both be [B, n]")
     B, n = w.shape
@@ -150,19 +181,23 @@ def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_
 
 def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2,
                       boundary_state: torch.Tensor | None = None, *, workspace: torch.Tensor | None = None):
-    """(states [B, n] int32, w_hard [B, n] float32, cost [B] float32) of the minimum-energy paths."""
+    """(states [B, n] int32, one per step, w_hard with w's shape, cost [B] float32) of the minimum-energy paths."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
-    if w.dim() != 2:
-        raise ValueError("w must be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
     sig = _sigma(boundary_state, B, w.device)
     states = torch.empty((B, n), dtype=torch.int32, device=w.device)
     w_hard = torch.empty_like(w)
     cost = torch.empty(B, dtype=torch.float32, device=w.device)
-    ws, need = _workspace(abi.BCJR_OP_VITERBI, B, n, L, k, w.device, workspace)
-    _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
-                                 w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_VITERBI, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
+                                     w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream(w.device)))
+    else:
+        _check(abi.viterbi_hard_code_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, _ptr(sig),
+                                       states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(),
+                                       ws.numel(), _stream(w.device)))
     return states, w_hard, cost
 
 
@@ -171,6 +206,8 @@ def soft_codeword_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k
     """Soft codeword [B, n] (and ln Z [B]) under the tail-biting measure: every path with s_0 = s_n (L <= 10)."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
+    if codebook.dim() != 1:
+        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
     if w.dim() != 2:
         raise ValueError("w must be [B, n]")
     B, n = w.shape
@@ -188,6 +225,8 @@ def soft_codeword_grad_tail_biting(w: torch.Tensor, codebook: torch.Tensor, grad
     """dL/dw [B, n] under the tail-biting measure given dL/dw_soft [B, n] (and that measure's soft codeword)."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
+    if codebook.dim() != 1:
+        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
     g = _f32(grad_w_soft, "grad_w_soft")
     if w.dim() != 2 or g.shape != w.shape:
         raise ValueError("w and grad_w_soft must both be [B, n]")
@@ -214,6 +253,8 @@ def viterbi_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int 
     tb_mode, op = _TB_MODES[mode]
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
+    if codebook.dim() != 1:
+        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
     if w.dim() != 2:
         raise ValueError("w must be [B, n]")
     B, n = w.shape

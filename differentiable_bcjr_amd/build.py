@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbcjr.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["soft.hip", "grad.hip", "viterbi.hip", "tail_biting.hip", "bcjr_abi.cpp"]
+SOURCES = ["soft.hip", "grad.hip", "viterbi.hip", "tail_biting.hip", "general.hip", "bcjr_abi.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

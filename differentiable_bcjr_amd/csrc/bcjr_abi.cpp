@@ -26,6 +26,9 @@ hipError_t launch_tb_select(const float* costs, int64_t rows, int S, int32_t* si
                             hipStream_t st);
 hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n, int pos, int32_t* sigma,
                                   int32_t* sigma_out, hipStream_t st);
+struct GenArgs;
+hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
+                          hipStream_t st);
 
 }  // namespace bcjr
 
@@ -47,11 +50,31 @@ struct Plan {
     size_t total;
 };
 
+constexpr int32_t kMaxGenK = 4;   // the general trellis kernels: 1 <= k <= 4
+constexpr int32_t kMaxGenV = 2;   // and V = 1 or 2 weights per step
+
+int check_dims(int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    if (B < 1 || B > kMaxB || n < 1 || n > kMaxN || k < 1 || L < 2 * k || L > 16 || V < 1) return BCJR_ERR_SHAPE;
+    return BCJR_OK;
+}
+
+// The entry points that exist for k = 2, V = 1 only (codebook gradient, tail-biting).
 int check_shape(int64_t B, int64_t n, int32_t L, int32_t k) {
-    if (B < 1 || B > kMaxB || n < 1 || n > kMaxN || k < 1 || L < 2 * k || L > 16) return BCJR_ERR_SHAPE;
+    const int rc = check_dims(B, n, L, k, 1);
+    if (rc) return rc;
     if (k != 2) return BCJR_ERR_UNSUPPORTED;
     return BCJR_OK;
 }
+
+// Soft codeword, gradient and Viterbi: the k = 2, V = 1 kernels, or the general ones.
+int check_shape_v(int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    const int rc = check_dims(B, n, L, k, V);
+    if (rc) return rc;
+    if (k > kMaxGenK || V > kMaxGenV) return BCJR_ERR_UNSUPPORTED;
+    return BCJR_OK;
+}
+
+bool tuned(int32_t k, int32_t V) { return k == 2 && V == 1; }
 
 int check_temp(float T) {
     if (!std::isfinite(T) || !(T >= kMinT)) return BCJR_ERR_TEMP;
@@ -82,6 +105,60 @@ Plan make_plan(int op, int64_t B, int64_t n, int L) {
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
     }
     p.total = (size_t)p.slots * p.slot_bytes;
+    return p;
+}
+
+// General trellis kernels: one sequence per workgroup of 2^L / SPT threads (SPT = 64 states per thread, all 2^L
+// below L = 6), G = 2^(L-k) message floats per LDS buffer.
+constexpr size_t kLdsBytes = 160 * 1024;
+constexpr size_t kLdsStatic = 2048;   // the kernels' own reduction slots
+
+struct GenPlan {
+    bool ok;          // false: no kernel for these shapes (the gradient's two message arrays exceed LDS)
+    int grid, threads, dbl;
+    size_t lds, slot_bytes, total;
+};
+
+// op: BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI.
+GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    GenPlan p{};
+    const int S = 1 << L;
+    const int spt = S < 64 ? S : 64;
+    const int tps = S / spt;
+    const int wps = tps >= 64 ? tps / 64 : 1;
+    const size_t G = (size_t)S >> k;
+    const size_t msg = G * 4;
+    if (op == BCJR_OP_GRAD) {   // R and Q, one buffer each
+        p.dbl = 0;
+        p.lds = 2 * msg;
+    } else {
+        p.dbl = 2 * msg + kLdsStatic <= kLdsBytes;
+        p.lds = p.dbl ? 2 * msg : msg;
+    }
+    p.ok = p.lds + kLdsStatic <= kLdsBytes;
+    p.threads = tps;
+    // blocks per CU: 16 waves of at most 128 VGPRs, and the LDS
+    const int waves = tps >= 64 ? tps / 64 : 1;
+    int bpc = 16 / waves;
+    const int bpc_lds = (int)(kLdsBytes / (p.lds + kLdsStatic));
+    if (bpc_lds < bpc) bpc = bpc_lds;
+    if (bpc < 1) bpc = 1;
+    const int64_t cap = (int64_t)kNumCU * bpc;
+    p.grid = (int)(B < cap ? B : cap);
+    const size_t tapes = align256((size_t)(n + 1) * G * 4);
+    const size_t nrm = align256((size_t)n * 4);
+    switch (op) {
+        case BCJR_OP_SOFT:   // R~ tape, normalisers, per-wave (S0, S1[V]) of every step
+            p.slot_bytes = tapes + nrm + (wps > 1 ? align256((size_t)n * wps * (1 + V) * 4) : 0);
+            break;
+        case BCJR_OP_GRAD:   // R~ and Q^ tapes, normalisers and Q offsets, per-wave (S0, S1[V], S2, S3[V])
+            p.slot_bytes = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
+            break;
+        default:   // two back-pointer buffers of [n][threads] words
+            p.slot_bytes = align256(2 * (size_t)n * (size_t)tps * 4);
+            break;
+    }
+    p.total = (size_t)p.grid * p.slot_bytes;
     return p;
 }
 
@@ -141,8 +218,21 @@ int check_tb_mode(int32_t mode, int32_t L) {
 
 extern "C" {
 
+size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI) {
+        if (check_shape_v(B, n, L, k, V) != BCJR_OK) return 0;
+        if (tuned(k, V)) return make_plan(op, B, n, L).total;
+        const GenPlan p = make_gen_plan(op, B, n, L, k, V);
+        return p.ok ? p.total : 0;
+    }
+    if (V != 1) return 0;
+    return bcjr_workspace_bytes(op, B, n, L, k);
+}
+
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
     if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
+    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI)
+        return bcjr_workspace_bytes_v(op, B, n, L, k, 1);
     if (check_shape(B, n, L, k) != BCJR_OK) return 0;
     if (op == BCJR_OP_SOFT_TAIL_BITING || op == BCJR_OP_GRAD_TAIL_BITING) {
         if (L > kMaxTailBitingExactL) return 0;
@@ -160,23 +250,53 @@ const char* bcjr_status_string(int32_t status) {
     switch (status) {
         case BCJR_OK: return "BCJR_OK: success";
         case BCJR_ERR_NULL: return "BCJR_ERR_NULL: a required pointer is NULL";
-        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16";
+        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16, V >= 1";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
         case BCJR_ERR_UNSUPPORTED:
-            return "BCJR_ERR_UNSUPPORTED: only k = 2 has kernels; the exact tail-biting choice needs L <= 10";
+            return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2 (k = 2, V = 1 only for the codebook "
+                   "gradient and tail-biting; the gradient at k = 1 needs L <= 15); exact tail-biting needs L <= 10";
         case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
     }
 }
 
-int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, float T,
-                       const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int gen_workspace(void* workspace, size_t bytes, const GenPlan& p) {
+    if (!p.ok) return BCJR_ERR_UNSUPPORTED;
+    if (workspace == nullptr || bytes < p.total || ((uintptr_t)workspace & 255u) != 0) return BCJR_ERR_WORKSPACE;
+    return BCJR_OK;
+}
+
+int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V, float T,
+              const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace, size_t workspace_bytes,
+              void* stream) {
     if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
+    int rc = check_shape_v(B, n, L, k, V);
     if (rc) return rc;
     if ((rc = check_temp(T))) return rc;
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    if (!tuned(k, V)) {
+        const GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V);
+        if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.B = B;
+        a.n = (int)n;
+        a.L = L;
+        a.scale = scale;
+        a.sigma = boundary_state;
+        a.w_soft = w_soft;
+        a.log_z = log_z;
+        a.ws = static_cast<unsigned char*>(workspace);
+        a.slot_bytes = p.slot_bytes;
+        a.dbl = p.dbl;
+        return hip_status(launch_general(0, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
+    }
     const Plan p = make_plan(BCJR_OP_SOFT, B, n, L);
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     SoftArgs a{};
@@ -184,7 +304,7 @@ int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t
     a.cb = codebook;
     a.B = B;
     a.n = (int)n;
-    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.scale = scale;
     a.sigma = boundary_state;
     a.w_soft = w_soft;
     a.log_z = log_z;
@@ -193,13 +313,34 @@ int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t
     return hip_status(launch_soft(L, a, p.grid, static_cast<hipStream_t>(stream)));
 }
 
-int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
-                            float T, const int32_t* boundary_state, const float* grad_w_soft, float* grad_w,
-                            float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V, float T,
+              const int32_t* boundary_state, const float* grad_w_soft, float* grad_w, float* w_soft, void* workspace,
+              size_t workspace_bytes, void* stream) {
     if (!w || !codebook || !grad_w_soft || !grad_w) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
+    int rc = check_shape_v(B, n, L, k, V);
     if (rc) return rc;
     if ((rc = check_temp(T))) return rc;
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    if (!tuned(k, V)) {
+        const GenPlan p = make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V);
+        if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.g = grad_w_soft;
+        a.B = B;
+        a.n = (int)n;
+        a.L = L;
+        a.scale = scale;
+        a.two_over_T = (float)(2.0 / (double)T);
+        a.sigma = boundary_state;
+        a.grad = grad_w;
+        a.w_soft = w_soft;
+        a.ws = static_cast<unsigned char*>(workspace);
+        a.slot_bytes = p.slot_bytes;
+        a.dbl = p.dbl;
+        return hip_status(launch_general(1, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
+    }
     const Plan p = make_plan(BCJR_OP_GRAD, B, n, L);
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     GradArgs a{};
@@ -208,7 +349,7 @@ int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, in
     a.g = grad_w_soft;
     a.B = B;
     a.n = (int)n;
-    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    a.scale = scale;
     a.two_over_T = (float)(2.0 / (double)T);
     a.sigma = boundary_state;
     a.grad = grad_w;
@@ -216,6 +357,78 @@ int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, in
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
     return hip_status(launch_grad(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+int viterbi_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
+                 const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !states) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, V);
+    if (rc) return rc;
+    if (!tuned(k, V)) {
+        const GenPlan p = make_gen_plan(BCJR_OP_VITERBI, B, n, L, k, V);
+        if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.B = B;
+        a.n = (int)n;
+        a.L = L;
+        a.sigma = boundary_state;
+        a.states = states;
+        a.w_hard = w_hard;
+        a.cost = cost;
+        a.ws = static_cast<unsigned char*>(workspace);
+        a.slot_bytes = p.slot_bytes;
+        a.dbl = p.dbl;
+        return hip_status(launch_general(2, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
+    }
+    const Plan p = make_plan(BCJR_OP_VITERBI, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    ViterbiArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B;
+    a.n = (int)n;
+    a.sigma = boundary_state;
+    a.states = states;
+    a.w_hard = w_hard;
+    a.cost = cost;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, float T,
+                       const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    return soft_impl(w, codebook, B, n, L, k, 1, T, boundary_state, w_soft, log_z, workspace, workspace_bytes,
+                     stream);
+}
+
+int bcjr_soft_codeword_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                         int32_t V, float T, const int32_t* boundary_state, float* w_soft, float* log_z,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return soft_impl(w, codebook, B, n, L, k, V, T, boundary_state, w_soft, log_z, workspace, workspace_bytes,
+                     stream);
+}
+
+int bcjr_soft_codeword_grad(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                            float T, const int32_t* boundary_state, const float* grad_w_soft, float* grad_w,
+                            float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+    return grad_impl(w, codebook, B, n, L, k, 1, T, boundary_state, grad_w_soft, grad_w, w_soft, workspace,
+                     workspace_bytes, stream);
+}
+
+int bcjr_soft_codeword_grad_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                              int32_t V, float T, const int32_t* boundary_state, const float* grad_w_soft,
+                              float* grad_w, float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+    return grad_impl(w, codebook, B, n, L, k, V, T, boundary_state, grad_w_soft, grad_w, w_soft, workspace,
+                     workspace_bytes, stream);
 }
 
 int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
@@ -247,23 +460,15 @@ int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int6
 int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
                       const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
                       size_t workspace_bytes, void* stream) {
-    if (!w || !codebook || !states) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
-    if (rc) return rc;
-    const Plan p = make_plan(BCJR_OP_VITERBI, B, n, L);
-    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
-    ViterbiArgs a{};
-    a.w = w;
-    a.cb = codebook;
-    a.B = B;
-    a.n = (int)n;
-    a.sigma = boundary_state;
-    a.states = states;
-    a.w_hard = w_hard;
-    a.cost = cost;
-    a.ws = static_cast<unsigned char*>(workspace);
-    a.slot_bytes = p.slot_bytes;
-    return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
+    return viterbi_impl(w, codebook, B, n, L, k, 1, boundary_state, states, w_hard, cost, workspace,
+                        workspace_bytes, stream);
+}
+
+int viterbi_hard_code_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                        int32_t V, const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    return viterbi_impl(w, codebook, B, n, L, k, V, boundary_state, states, w_hard, cost, workspace,
+                        workspace_bytes, stream);
 }
 
 int bcjr_soft_codeword_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,

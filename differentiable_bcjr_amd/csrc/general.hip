@@ -1,0 +1,1378 @@
+// general.hip -- soft codeword, exact gradient and Viterbi hard code for a general bitshift trellis on gfx950:
+// k bits shifted in per step (2^k predecessors and 2^k successors per state), V weights emitted per step.
+//
+// The method is that of the k = 2 kernels (BCJR-QAT, arXiv 2605.10655: gist.science Technical Summary, "Core
+// Mechanism" and "Key Technical Innovations"; the abstract for the T -> 0 limit).  The pages fix neither k nor V.
+// Here a state emits a V-vector c(s) (codebook [2^L][V]), step t consumes the weights w[t V .. t V + V - 1], and the
+// log weight of a state is -|w_t - c(s)|^2 / T.
+//
+// Grouped messages.  All states with the same u = s >> k share their 2^k predecessors u | a << (L-k), so the forward
+// pass carries one value per group, R_t(u) = logsumexp_a alpha_{t-1}(u | a << (L-k)).  All states with the same
+// s & (G-1) share their successors, so the backward pass carries B_t(s & (G-1)).  That is G = 2^(L-k) values per step
+// in each direction.
+//
+// Blocks.  With P = 2^k and J = 2^(L-2k), block j (0 <= j < J) holds the P^2 states s(j, a, i) = a << (L-k) | j << k | i
+// for a, i < P.  These are the predecessor sets of the forward groups u = j P + i, which read R_t(j + J a).  They are
+// also the successor sets of the backward groups v = j + J a, which read B_{t+1}(j P + i).  So a thread that owns the
+// states of a block serves both directions from the same codebook values.
+//
+// A thread owns SPT = 64 states (SPT = 2^L below L = 6):
+//   * k <= 3: 64 / P^2 whole blocks;
+//   * k = 4:  4 forward groups of one block, and the 4 lanes of a quad share the block's backward groups, combining
+//             them with DPP.
+// The 2^k-way log-sum-exps run over tiles of at most 4 x 4 states.  A tile's terms are exponentiated against the tile's
+// own maximum, and tiles merge with one exponential, so registers stay bounded at every k.
+//
+// Codebook: in VGPRs when a thread's SPT V values fit in 64 registers, else read through L1/L2 at each use; a tile row
+// is contiguous, 4 V floats.
+//
+// LDS holds the messages: G floats per buffer, double-buffered when two buffers fit.  Otherwise one buffer is used,
+// and each step reads its inputs into registers and passes a barrier before it writes its outputs.  The gradient
+// always keeps R and its expectation message Q in one buffer each.
+//
+// L is a run-time argument: one sequence per workgroup of 2^L / SPT threads, persistent over the batch.  k, V and SPT
+// are compile-time.  The forward tapes, normalisers and per-wave partial sums use the workspace layout of the k = 2
+// kernels.
+#include "kernel_args.hpp"
+#include "trellis.hpp"
+
+#ifndef GEN_NO_SCHED
+#define GEN_SCHED_BARRIER() __builtin_amdgcn_sched_barrier(0)
+#else
+#define GEN_SCHED_BARRIER() ((void)0)
+#endif
+
+namespace bcjr {
+
+namespace {
+
+template <int K_, int V_, int SPT_>
+struct GG {
+    static constexpr int K = K_, V = V_, SPT = SPT_;
+    static constexpr int P = 1 << K;
+    static constexpr int P2 = P * P;
+    static constexpr int C = P2 > SPT ? P2 / SPT : 1;      // threads sharing one block
+    static constexpr int I = P / C;                         // forward groups of a block per thread
+    static constexpr int BPT = P2 > SPT ? 1 : SPT / P2;     // blocks per thread
+    static constexpr int TA = P < 4 ? P : 4;                // predecessor rows per tile
+    static constexpr int TI = I < 4 ? I : 4;                // groups per tile
+    static constexpr int NA = P / TA, NI = I / TI;
+    static constexpr int ROW = TI * V;                      // codebook floats of one tile row
+    static_assert(C == 1 || C == 4, "a block is shared by at most the 4 lanes of a quad");
+    static_assert(C == 1 || NI == 1, "a shared block gives each lane one tile of groups");
+    static_assert(V >= 1 && V <= 2, "V = 1 or 2");
+};
+
+// N floats from a raw buffer at a byte offset aligned to the load width.
+template <int N>
+__device__ __forceinline__ void ld_floats(rsrc_t r, uint32_t off, float* out) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 v = buf_ld4(r, off + 4u * i, 0);
+            out[i] = v.x;
+            out[i + 1] = v.y;
+            out[i + 2] = v.z;
+            out[i + 3] = v.w;
+        }
+    } else if constexpr (N == 2) {
+        const float2 v = buf_ld2(r, off, 0);
+        out[0] = v.x;
+        out[1] = v.y;
+    } else {
+        static_assert(N == 1, "1, 2 or a multiple of 4 floats");
+        out[0] = buf_ld(r, off, 0);
+    }
+}
+
+// N floats to LDS and to the tape at one element offset (N = 1, 2 or 4, aligned to N floats).
+template <int N>
+__device__ __forceinline__ void st_floats(const float* v, float* lds, int idx, rsrc_t tape, uint32_t voff,
+                                          uint32_t soff) {
+    if constexpr (N == 4) {
+        const float4 x = make_float4(v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<float4*>(lds + idx) = x;
+        buf_st4_nt(x, tape, voff, soff);
+    } else if constexpr (N == 2) {
+        const float2 x = make_float2(v[0], v[1]);
+        *reinterpret_cast<float2*>(lds + idx) = x;
+        buf_st2(x, tape, voff, soff);
+    } else {
+        lds[idx] = v[0];
+        buf_st(v[0], tape, voff, soff);
+    }
+}
+
+// Maximum and sum over the SEG lanes of one sequence (SEG = 64, or the whole sub-wave block).
+__device__ __forceinline__ float gseq_max(float x, int seg) {
+    if (seg == 64) return wave_max64(x);
+    for (int o = 1; o < seg; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float gseq_sum(float x, int seg) {
+    if (seg == 64) return wave_sum64(x);
+    for (int o = 1; o < seg; o <<= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ void gseq_argmin(float& v, uint32_t& i, int seg) {
+    for (int o = 1; o < seg; o <<= 1) {
+        const float v2 = __shfl_xor(v, o);
+        const uint32_t i2 = (uint32_t)__shfl_xor((int)i, o);
+        argmin_merge(v, i, v2, i2);
+    }
+}
+// (max of v, q of the lowest lane attaining it) over the SEG lanes of one sequence.
+__device__ __forceinline__ void gseq_argmax_payload(float& v, float& q, int seg) {
+    if (seg == 64) {
+        seg_argmax_payload<64>(v, q);
+        return;
+    }
+    int lane = (int)(threadIdx.x & 63);
+    for (int o = 1; o < seg; o <<= 1) {
+        const float v2 = __shfl_xor(v, o);
+        const float q2 = __shfl_xor(q, o);
+        const int l2 = __shfl_xor(lane, o);
+        const bool take = (v2 > v) || (v2 == v && l2 < lane);
+        v = take ? v2 : v;
+        q = take ? q2 : q;
+        lane = take ? l2 : lane;
+    }
+}
+
+__device__ __forceinline__ void pin_one(float& a) { asm volatile("" : "+v"(a)); }
+
+// Quad reductions (the 4 lanes sharing a block at k = 4).
+__device__ __forceinline__ float quad_max(float x) {
+    x = fmaxf(x, dpp<0xB1>(x));
+    return fmaxf(x, dpp<0x4E>(x));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+    x += dpp<0xB1>(x);
+    return x + dpp<0x4E>(x);
+}
+
+// Merge the log-sum-exp of one tile (maximum cm, sum of 2^(x - cm) cs, and optionally sum of 2^(x - cm) z, cz) into a
+// running one (mx, s, sz): the side with the smaller maximum is scaled by 2^(-|mx - cm|), one exponential.
+__device__ __forceinline__ void lse_merge(float& mx, float& s, float cm, float cs) {
+    const bool keep = mx >= cm;
+    const float e = ex2(fminf(mx, cm) - fmaxf(mx, cm));
+    s = keep ? fmaf(cs, e, s) : fmaf(s, e, cs);
+    mx = keep ? mx : cm;
+}
+__device__ __forceinline__ void lse_merge(float& mx, float& s, float& sz, float cm, float cs, float cz) {
+    const bool keep = mx >= cm;
+    const float e = ex2(fminf(mx, cm) - fmaxf(mx, cm));
+    s = keep ? fmaf(cs, e, s) : fmaf(s, e, cs);
+    sz = keep ? fmaf(cz, e, sz) : fmaf(sz, e, cz);
+    mx = keep ? mx : cm;
+}
+
+// IEEE float32 squared distance plus the incoming metric, in a fixed order without fused multiply-add:
+// e = fl(d_0 d_0), e = fl(e + fl(d_v d_v)) for v = 1.., then fl(e + vin), d_v = fl(w_v - c_v).
+template <int V>
+__device__ __forceinline__ float vmetric(const float* wt, const float* c, float vin) {
+#pragma clang fp contract(off)
+    const float d0 = wt[0] - c[0];
+    float e = d0 * d0;
+#pragma unroll
+    for (int v = 1; v < V; ++v) {
+        const float dv = wt[v] - c[v];
+        const float ev = dv * dv;
+        e = e + ev;
+    }
+    return e + vin;
+}
+
+// Per-thread view of the trellis: which blocks and groups it owns, and its codebook values.
+template <int K, int V, int SPT, bool REG>
+struct Owner {
+    using Gm = GG<K, V, SPT>;
+    static constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TI = Gm::TI, NI = Gm::NI, ROW = Gm::ROW;
+    int L, tau, TPS, cl, i0;
+    rsrc_t cbs;
+    float cbr[REG ? BPT : 1][REG ? P : 1][REG ? I * V : 1];
+
+    __device__ __forceinline__ int j(int m) const { return C == 1 ? tau + TPS * m : tau / C; }
+    // first forward group of tile q of block m
+    __device__ __forceinline__ int fgroup(int m, int q) const { return (j(m) << K) + i0 + TI * q; }
+    // state of (block m, row a, group i0 + TI q + ii)
+    __device__ __forceinline__ uint32_t state(int m, int a, int q, int ii) const {
+        return ((uint32_t)a << (L - K)) | (uint32_t)fgroup(m, q) + (uint32_t)ii;
+    }
+    __device__ __forceinline__ uint32_t row_bytes(int m, int a, int q) const {
+        return 4u * (uint32_t)V * state(m, a, q, 0);
+    }
+
+    __device__ __forceinline__ void init(const float* cb, int L_, int TPS_) {
+        L = L_;
+        TPS = TPS_;
+        tau = threadIdx.x;
+        cl = C == 1 ? 0 : (tau & (C - 1));
+        i0 = cl * I;
+        cbs = make_rsrc(cb, (uint32_t)V * (4u << L));
+        if constexpr (REG) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a)
+#pragma unroll
+                    for (int q = 0; q < NI; ++q) ld_floats<ROW>(cbs, row_bytes(m, a, q), &cbr[m][a][ROW * q]);
+        }
+    }
+    // codebook values of tile row (m, a, q): ROW floats, group-major then component
+    __device__ __forceinline__ void row(int m, int a, int q, float* out) const {
+        if constexpr (REG) {
+#pragma unroll
+            for (int x = 0; x < ROW; ++x) out[x] = cbr[m][a][ROW * q + x];
+        } else {
+            ld_floats<ROW>(cbs, row_bytes(m, a, q), out);
+        }
+    }
+    // The rows in the order a step visits them, fetched one row ahead when they come from memory: forward order
+    // (m, q, a) and backward order (m, a, q).  Row idx + 1 after the last is the next step's first.
+    static constexpr int NROW = BPT * NI * P;
+    __device__ __forceinline__ void fwd_next(int idx, float* nx) const {
+        if constexpr (!REG) {
+            const int x = (idx + 1) % NROW;
+            row(x / (NI * P), x % P, (x / P) % NI, nx);
+        }
+    }
+    __device__ __forceinline__ void bwd_next(int idx, float* nx) const {
+        if constexpr (!REG) {
+            const int x = (idx + 1) % NROW;
+            row(x / (NI * P), (x / NI) % P, x % NI, nx);
+        }
+    }
+    // this row: from registers, or the prefetched copy (then the next row is fetched into nx)
+    __device__ __forceinline__ void take_fwd(int m, int a, int q, float* c, float* nx) const {
+        if constexpr (REG) {
+            row(m, a, q, c);
+        } else {
+#pragma unroll
+            for (int x = 0; x < ROW; ++x) c[x] = nx[x];
+            fwd_next((m * NI + q) * P + a, nx);
+        }
+    }
+    __device__ __forceinline__ void take_bwd(int m, int a, int q, float* c, float* nx) const {
+        if constexpr (REG) {
+            row(m, a, q, c);
+        } else {
+#pragma unroll
+            for (int x = 0; x < ROW; ++x) c[x] = nx[x];
+            bwd_next((m * P + a) * NI + q, nx);
+        }
+    }
+};
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------------------------
+// soft codeword (and ln Z)
+
+template <int K, int V, int SPT, int LT>
+__global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
+    using Gm = GG<K, V, SPT>;
+    constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TA = Gm::TA, TI = Gm::TI, NA = Gm::NA,
+                  NI = Gm::NI, ROW = Gm::ROW;
+    // codebook in VGPRs only where it leaves room: k = 1 holds 32 inputs per step, k = 4 16 rows of tape loads
+    constexpr bool REG = SPT * V <= 64 && (SPT < 64 || (K == 2 || K == 3));
+    extern __shared__ float lds[];
+    __shared__ float redmax[2][16];
+    __shared__ float redsum[2][16];
+
+    const int L = LT ? LT : args.L, n = args.n, TPS = LT ? (1 << LT) / SPT : (int)blockDim.x, tau = threadIdx.x;
+    const int lane = tau & 63, wv = tau >> 6;
+    const int G = 1 << (L - K), J = 1 << (L - 2 * K);
+    const int WPS = TPS >= 64 ? TPS >> 6 : 1, SEG = TPS >= 64 ? 64 : TPS;
+    const float scale = args.scale, inv_scale = 1.0f / scale;
+    float* msg0 = lds;
+    float* msg1 = args.dbl ? lds + G : lds;
+
+    Owner<K, V, SPT, REG> own;
+    own.init(args.cb, L, TPS);
+
+    // tape of the block's sequence: [n+1][G] R~, [n] normalisers, then the per-wave (S0, S1[V]) of every step
+    const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
+    const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
+    const uint32_t row_bytes = (uint32_t)G * 4u;
+    const uint32_t nrm_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const uint32_t part_base = nrm_base + (uint32_t)align256((size_t)n * 4);
+    const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
+    float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
+    own.fwd_next(-1, cnx);
+
+    for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
+        const float* wb = args.w + b * (int64_t)n * V;
+        const bool has_sigma = args.sigma != nullptr;
+        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+
+        // ------------------------------------------------------------------ forward
+#pragma unroll
+        for (int m = 0; m < BPT; ++m)
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                float r[TI];
+                const int u0 = own.fgroup(m, q);
+#pragma unroll
+                for (int ii = 0; ii < TI; ++ii)
+                    r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
+                st_floats<TI>(r, msg0, u0, tape, 4u * u0, 0u);
+            }
+        lds_barrier();
+
+        float N = 0.f, N_last = 0.f;
+        double A = 0.0;
+        float w_nx[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) w_nx[v] = wb[v];
+        for (int t = 0; t < n; ++t) {
+            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
+            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
+            float wt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) wt[v] = w_nx[v] * scale;
+            if (t + 1 < n) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) w_nx[v] = wb[(t + 1) * V + v];
+            }
+            float rin[BPT][P];
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) rin[m][a] = mc[own.j(m) + J * a];
+            if (!args.dbl) lds_barrier();   // every input read before any output overwrites it
+            float lmax = -3.0e38f;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    float mx[TI], s[TI];
+#pragma unroll
+                    for (int r = 0; r < NA; ++r) {
+                        float x[TA][TI];
+#pragma unroll
+                        for (int aa = 0; aa < TA; ++aa) {
+                            const int a = r * TA + aa;
+                            float c[ROW];
+                            own.take_fwd(m, a, q, c, cnx);
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii) {
+                                float acc = rin[m][a];
+#pragma unroll
+                                for (int v = 0; v < V; ++v) {
+                                    const float d = fmaf(c[ii * V + v], scale, -wt[v]);
+                                    acc = fmaf(-d, d, acc);
+                                }
+                                x[aa][ii] = acc;
+                            }
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            float cm = x[0][ii];
+#pragma unroll
+                            for (int aa = 1; aa < TA; ++aa) cm = fmaxf(cm, x[aa][ii]);
+                            float cs = 0.f;
+#pragma unroll
+                            for (int aa = 0; aa < TA; ++aa) cs += ex2(x[aa][ii] - cm);
+                            if (r == 0) {
+                                mx[ii] = cm;
+                                s[ii] = cs;
+                            } else {
+                                lse_merge(mx[ii], s[ii], cm, cs);
+                            }
+                        }
+                        GEN_SCHED_BARRIER();
+                    }
+                    float o[TI];
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        o[ii] = (mx[ii] - N) + lg2(s[ii]);
+                        lmax = run_max(lmax, o[ii]);
+                    }
+                    const int u0 = own.fgroup(m, q);
+                    st_floats<TI>(o, mn, u0, tape, 4u * u0, (uint32_t)(t + 1) * row_bytes);
+                }
+            if (tau == 0) buf_st(N, tape, 0u, nrm_base + 4u * t);
+            lmax = gseq_max(lmax, SEG);
+            if (WPS > 1 && lane == 0) redmax[t & 1][wv] = lmax;
+            lds_barrier();
+            if (WPS > 1) lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][lane & 15] : -3.0e38f);
+            lmax = uniform_f(lmax);
+            A += (double)N;
+            N_last = N;
+            N = lmax;
+        }
+        // rz = log2 Z - A_n
+        float rz;
+        if (!has_sigma) {
+            const float* mf = args.dbl && (n & 1) ? msg1 : msg0;
+            float part = 0.f;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) part += ex2(mf[own.fgroup(m, q) + ii] - N);
+            part = gseq_sum(part, SEG);
+            if (WPS > 1 && lane == 0) redsum[n & 1][wv] = part;
+            lds_barrier();
+            if (WPS > 1) {
+                part = 0.f;
+                for (int q = 0; q < WPS; ++q) part += redsum[n & 1][q];
+            }
+            rz = N + lg2(part);
+            __syncthreads();
+        } else {
+            __syncthreads();   // the tape rows of the forward pass, written by other threads
+            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
+            float x = r;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float d = fmaf(args.cb[sig * V + v], scale, -(wb[(n - 1) * V + v] * scale));
+                x = fmaf(-d, d, x);
+            }
+            rz = (r < 0.5f * kNeg) ? kNeg : x - N_last;
+        }
+        const bool valid = rz > 0.5f * kNeg;
+        if (tau == 0 && args.log_z)
+            args.log_z[b] = valid ? (float)((A + (double)rz) * 0.6931471805599453) : -__builtin_inff();
+
+        // ------------------------------------------------------------------ backward + posterior
+        float Nb = 0.f, C_ = 0.f, D = 0.f;
+        int t = n - 1;
+        if (!has_sigma) {
+            float* mi = args.dbl && ((n - 1) & 1) ? msg1 : msg0;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) mi[own.fgroup(m, q) + ii] = 0.f;
+        } else {
+            // s_n = sigma: the posterior at n-1 is the indicator of sigma; the one finite message left is
+            // B_{n-2}(sigma >> k) = theta_{n-1}(sigma)
+            float* mi = args.dbl && ((n - 2) & 1) ? msg1 : msg0;
+            float th = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float d = fmaf(args.cb[sig * V + v], scale, -(wb[(n - 1) * V + v] * scale));
+                th = fmaf(-d, d, th);
+            }
+            if (n > 1) {
+#pragma unroll
+                for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                    for (int q = 0; q < NI; ++q)
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
+                            mi[u] = (u == (sig >> K)) ? th : kNeg;
+                        }
+            }
+            if (tau == 0) {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    args.w_soft[(b * n + n - 1) * V + v] = valid ? args.cb[sig * V + v] : __builtin_nanf("");
+            }
+            D = N_last;
+            Nb = th;
+            t = n - 2;
+        }
+        lds_barrier();
+
+        const int t_out = t;
+        float N_nx = 0.f, rq_nx = 0.f;
+        if (t >= 0) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) w_nx[v] = wb[t * V + v];
+            N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
+            rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes);
+        }
+        for (; t >= 0; --t) {
+            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
+            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
+            float wt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) wt[v] = w_nx[v] * scale;
+            const float Nt = uniform_f(N_nx);
+            if (t > 0) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) w_nx[v] = wb[(t - 1) * V + v];
+                N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * (t - 1));
+            }
+            float bin[BPT][I];
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) bin[m][TI * q + ii] = mc[own.fgroup(m, q) + ii];
+            if (!args.dbl) lds_barrier();
+            D += Nt;
+            const float ref = (rz + D) - C_;
+            float lmax = -3.0e38f, S0 = 0.f, S1[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) S1[v] = 0.f;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) {
+                    const int vg = own.j(m) + J * a;   // backward group of row a
+                    // R~_t of this group, and the next group's (or the next step's first) one row ahead
+                    const float rq = rq_nx;
+                    if (m * P + a + 1 < BPT * P) {
+                        const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
+                        rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes +
+                                                          4u * (uint32_t)(own.j(m2) - own.j(0) + J * a2));
+                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
+                        rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes);
+                    }
+                    float mx = 0.f, s = 0.f;
+#pragma unroll
+                    for (int q = 0; q < NI; ++q) {
+                        float c[ROW], y[TI], d[TI][V];
+                        own.take_bwd(m, a, q, c, cnx);
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            float acc = bin[m][TI * q + ii];
+#pragma unroll
+                            for (int v = 0; v < V; ++v) {
+                                d[ii][v] = fmaf(c[ii * V + v], scale, -wt[v]);
+                                acc = fmaf(-d[ii][v], d[ii][v], acc);
+                            }
+                            y[ii] = acc;
+                        }
+                        float cm = y[0];
+#pragma unroll
+                        for (int ii = 1; ii < TI; ++ii) cm = fmaxf(cm, y[ii]);
+                        if constexpr (C > 1) cm = quad_max(cm);
+                        float e[TI], cs = 0.f;
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            e[ii] = ex2(y[ii] - cm);
+                            cs += e[ii];
+                        }
+                        const float f = ex2((cm + rq) - ref);
+                        S0 = fmaf(f, cs, S0);
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            float ed = 0.f;
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii) ed = fmaf(e[ii], d[ii][v], ed);
+                            S1[v] = fmaf(f, ed, S1[v]);
+                        }
+                        if constexpr (C > 1) cs = quad_sum(cs);
+                        if (q == 0) {
+                            mx = cm;
+                            s = cs;
+                        } else {
+                            lse_merge(mx, s, cm, cs);
+                        }
+                    }
+                    const float out = (mx - Nb) + lg2(s);
+                    lmax = run_max(lmax, out);
+                    mn[vg] = out;   // the lanes of a quad store the same value; at t = 0 nobody reads it
+                    pin_order(S0, lmax);
+#pragma unroll
+                    for (int v = 0; v < V; ++v) pin_one(S1[v]);
+                    GEN_SCHED_BARRIER();
+                }
+            lmax = gseq_max(lmax, SEG);
+            S0 = gseq_sum(S0, SEG);
+#pragma unroll
+            for (int v = 0; v < V; ++v) S1[v] = gseq_sum(S1[v], SEG);
+            if (WPS > 1) {
+                if (lane == 0) {
+                    redmax[t & 1][wv] = lmax;
+                    const uint32_t po = part_base + 4u * (uint32_t)((t * WPS + wv) * (1 + V));
+                    buf_st(S0, tape, 0u, po);
+#pragma unroll
+                    for (int v = 0; v < V; ++v) buf_st(S1[v], tape, 0u, po + 4u * (1 + v));
+                }
+            } else if (tau == 0) {
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    args.w_soft[(b * n + t) * V + v] = valid ? wb[t * V + v] + (S1[v] / S0) * inv_scale
+                                                             : __builtin_nanf("");
+            }
+            lds_barrier();
+            if (WPS > 1) lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][lane & 15] : -3.0e38f);
+            lmax = uniform_f(lmax);
+            C_ += Nb;
+            Nb = lmax;
+        }
+        if (WPS > 1) {
+            __syncthreads();   // the per-wave partial sums, written by other waves
+            for (int tt = tau; tt <= t_out; tt += TPS) {
+                float S0 = 0.f, S1[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) S1[v] = 0.f;
+                for (int q = 0; q < WPS; ++q) {
+                    const uint32_t po = part_base + 4u * (uint32_t)((tt * WPS + q) * (1 + V));
+                    S0 += buf_ld(tape, 0u, po);
+#pragma unroll
+                    for (int v = 0; v < V; ++v) S1[v] += buf_ld(tape, 0u, po + 4u * (1 + v));
+                }
+#pragma unroll
+                for (int v = 0; v < V; ++v)
+                    args.w_soft[(b * n + tt) * V + v] = valid ? wb[tt * V + v] + (S1[v] / S0) * inv_scale
+                                                              : __builtin_nanf("");
+            }
+        }
+        __syncthreads();   // the next sequence reuses the tape and LDS
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// Viterbi hard code
+
+template <int K, int V, int SPT, int LT>
+__global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
+    using Gm = GG<K, V, SPT>;
+    constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TI = Gm::TI, NI = Gm::NI, ROW = Gm::ROW;
+    constexpr bool REG = SPT * V <= 64;
+    constexpr float kInf = __builtin_huge_valf();
+    extern __shared__ float lds[];
+    __shared__ float redv[16];
+    __shared__ uint32_t redi[16];
+
+    const int L = LT ? LT : args.L, n = args.n, TPS = LT ? (1 << LT) / SPT : (int)blockDim.x, tau = threadIdx.x;
+    const int lane = tau & 63, wv = tau >> 6;
+    const int G = 1 << (L - K), J = 1 << (L - 2 * K);
+    const int WPS = TPS >= 64 ? TPS >> 6 : 1, SEG = TPS >= 64 ? 64 : TPS;
+    float* msg0 = lds;
+    float* msg1 = args.dbl ? lds + G : lds;
+
+    Owner<K, V, SPT, REG> own;
+    own.init(args.cb, L, TPS);
+
+    // back-pointer tape: 2 buffers (by sequence parity) of [n][TPS] words.  A thread's word of step t holds, for each
+    // of its forward groups g = m I + ii, the k-bit row a of the best predecessor in bits [g k, g k + k).
+    const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
+    const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
+    const uint32_t buf_bytes = (uint32_t)n * TPS * 4u;
+    float cnx[REG ? 1 : ROW];   // the next codebook row (read from memory)
+    own.fwd_next(-1, cnx);
+
+    // the word and bit field of forward group u at any step
+    auto bp_loc = [&](uint32_t u, uint32_t& word_idx, uint32_t& bit) {
+        const uint32_t jj = u >> K, i = u & (uint32_t)(P - 1);
+        if constexpr (C == 1) {
+            word_idx = jj % (uint32_t)TPS;
+            bit = ((jj / (uint32_t)TPS) * I + i) * K;
+        } else {
+            word_idx = jj * C + i / I;
+            bit = (i % I) * K;
+        }
+    };
+
+    // pending traceback (lane tau == 0): the previous sequence's path is traced back one step per forward step
+    int64_t pend_b = -1;
+    int pend_t = 0;
+    uint32_t pend_s = 0, pend_word = 0, pend_par = 0;
+    auto pend_fetch = [&]() {   // the word that decides s_{pend_t - 1}
+        uint32_t wi, bit;
+        bp_loc(pend_s >> K, wi, bit);
+        pend_word = __builtin_bit_cast(uint32_t, buf_ld(tape, 0u, pend_par * buf_bytes + (uint32_t)(pend_t - 1) *
+                                                                          (TPS * 4u) + 4u * wi));
+    };
+    auto pend_step = [&]() {
+        uint32_t wi, bit;
+        const uint32_t u = pend_s >> K;
+        bp_loc(u, wi, bit);
+        const uint32_t a = (pend_word >> bit) & (uint32_t)(P - 1);
+        pend_s = (a << (L - K)) | u;
+        --pend_t;
+        args.states[pend_b * args.n + pend_t] = (int32_t)pend_s;
+        if (pend_t >= 1) pend_fetch();
+    };
+
+    int64_t iter = 0;
+    for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x, ++iter) {
+        const float* wb = args.w + b * (int64_t)n * V;
+        const bool has_sigma = args.sigma != nullptr;
+        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+        const uint32_t par = (uint32_t)(iter & 1);
+
+#pragma unroll
+        for (int m = 0; m < BPT; ++m)
+#pragma unroll
+            for (int q = 0; q < NI; ++q)
+#pragma unroll
+                for (int ii = 0; ii < TI; ++ii) {
+                    const int u = own.fgroup(m, q) + ii;
+                    msg0[u] = (!has_sigma || (uint32_t)u == (sig & (uint32_t)(G - 1))) ? 0.f : kInf;
+                }
+        lds_barrier();
+
+        for (int t = 0; t + 1 < n; ++t) {
+            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
+            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
+            float wt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) wt[v] = wb[t * V + v];
+            float vin[BPT][P];
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) vin[m][a] = mc[own.j(m) + J * a];
+            if (!args.dbl) lds_barrier();
+            uint32_t word = 0;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    float best[TI];
+                    uint32_t arg[TI];
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        best[ii] = kInf;
+                        arg[ii] = 0;
+                    }
+#pragma unroll
+                    for (int a = 0; a < P; ++a) {
+                        float c[ROW];
+                        own.take_fwd(m, a, q, c, cnx);
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            const float M = vmetric<V>(wt, &c[ii * V], vin[m][a]);
+                            const bool take = M < best[ii];   // strict: the smallest a wins ties
+                            best[ii] = take ? M : best[ii];
+                            arg[ii] = take ? (uint32_t)a : arg[ii];
+                        }
+                    }
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        word |= arg[ii] << ((m * I + TI * q + ii) * K);
+                        mn[own.fgroup(m, q) + ii] = best[ii];
+                    }
+                    GEN_SCHED_BARRIER();
+                }
+            buf_st(__builtin_bit_cast(float, word), tape, 4u * tau, par * buf_bytes + (uint32_t)t * (TPS * 4u));
+            if (tau == 0 && pend_b >= 0 && pend_t >= 1) pend_step();
+            lds_barrier();
+        }
+
+        // last step: M_{n-1}(s) of every state and the end state (the smallest s attaining the minimum), or sigma
+        const float* ml = args.dbl && ((n - 1) & 1) ? msg1 : msg0;
+        float wl[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) wl[v] = wb[(n - 1) * V + v];
+        float best = kInf;
+        uint32_t bidx = 0xffffffffu;
+        if (!has_sigma) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) {
+                    const float vin = ml[own.j(m) + J * a];
+#pragma unroll
+                    for (int q = 0; q < NI; ++q) {
+                        float c[ROW];
+                        own.row(m, a, q, c);
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii)
+                            argmin_merge(best, bidx, vmetric<V>(wl, &c[ii * V], vin), own.state(m, a, q, ii));
+                    }
+                }
+            gseq_argmin(best, bidx, SEG);
+            if (WPS > 1 && lane == 0) {
+                redv[wv] = best;
+                redi[wv] = bidx;
+            }
+            __syncthreads();   // also publishes this sequence's back pointers to the traceback lane
+            if (WPS > 1) {
+                for (int q = 0; q < WPS; ++q) argmin_merge(best, bidx, redv[q], redi[q]);
+            }
+        } else {
+            __syncthreads();
+            bidx = sig;
+            best = vmetric<V>(wl, args.cb + (size_t)sig * V, ml[sig >> K]);
+        }
+        if (tau == 0 && args.cost) args.cost[b] = best;
+
+        // finish the previous sequence's traceback and gather its codewords
+        if (tau == 0 && pend_b >= 0) {
+            while (pend_t >= 1) pend_step();
+        }
+        __syncthreads();
+        if (args.w_hard && iter > 0) {
+            const int64_t pb = b - gridDim.x;
+            for (int x = tau; x < n * V; x += TPS) {
+                const int tt = x / V, v = x - tt * V;
+                args.w_hard[pb * n * V + x] = args.cb[(size_t)args.states[pb * n + tt] * V + v];
+            }
+        }
+        if (tau == 0) {
+            pend_b = b;
+            pend_par = par;
+            pend_s = bidx;
+            pend_t = n - 1;
+            args.states[b * n + n - 1] = (int32_t)bidx;
+            if (n > 1) pend_fetch();
+        }
+        __syncthreads();   // LDS and the other back-pointer buffer are reused next
+    }
+
+    if (tau == 0 && pend_b >= 0) {
+        while (pend_t >= 1) pend_step();
+    }
+    __syncthreads();
+    if (args.w_hard && iter > 0) {
+        const int64_t pb = blockIdx.x + (iter - 1) * (int64_t)gridDim.x;
+        for (int x = tau; x < n * V; x += TPS) {
+            const int tt = x / V, v = x - tt * V;
+            args.w_hard[pb * n * V + x] = args.cb[(size_t)args.states[pb * n + tt] * V + v];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// exact gradient with respect to the weights (and the soft codeword)
+//
+// As in the k = 2 gradient kernel: grad_{u,v} = (2/T) Cov_p(c(s_u, v), F) with F = sum_t <g_t, c(s_t) - w_t>, and
+// E[F | s_t] is split into a forward expectation message Q (weighted by the forward softmax over a) and a backward one
+// P (weighted by the backward softmax over i).  Both are re-centred every step by a constant the covariance ignores:
+// Q by its value at the most likely group, P by kappa_{t+1} = <g_{t+1}, w_soft_{t+1} - w_{t+1}>.  The constants are
+// carried as one per-step offset, so E[F | s] - E[F] is formed from small numbers only.
+
+template <int K, int V, int SPT, int LT>
+__global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
+    using Gm = GG<K, V, SPT>;
+    constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TA = Gm::TA, TI = Gm::TI, NA = Gm::NA,
+                  NI = Gm::NI, ROW = Gm::ROW;
+    constexpr bool REG = SPT * V <= 32;
+    constexpr int NS = 2 + 2 * V;   // S0, S1[V], S2, S3[V]
+    extern __shared__ float lds[];
+    __shared__ float redmax[2][16];
+    __shared__ float redq[2][16];
+    __shared__ float reds[2][16][1 + V];
+
+    const int L = LT ? LT : args.L, n = args.n, TPS = LT ? (1 << LT) / SPT : (int)blockDim.x, tau = threadIdx.x;
+    const int lane = tau & 63, wv = tau >> 6;
+    const int G = 1 << (L - K), J = 1 << (L - 2 * K);
+    const int WPS = TPS >= 64 ? TPS >> 6 : 1, SEG = TPS >= 64 ? 64 : TPS;
+    const float scale = args.scale, inv_scale = 1.0f / scale;
+    float* mr = lds;
+    float* mq = lds + G;
+
+    Owner<K, V, SPT, REG> own;
+    own.init(args.cb, L, TPS);
+
+    // tape: [n+1][G] R~, [n+1][G] Q^, [n] normalisers N_t, [n] offsets K_{t-1} (true Q_t = Q^_t + K_{t-1}), then
+    // the per-wave (S0, S1[V], S2, S3[V]) of every step
+    const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
+    const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
+    const uint32_t row_bytes = (uint32_t)G * 4u;
+    const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const uint32_t nrm_base = 2u * q_base;
+    const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
+    const uint32_t part_base = kq_base + (uint32_t)align256((size_t)n * 4);
+    const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
+    float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
+    own.fwd_next(-1, cnx);
+
+    for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
+        const float* wb = args.w + b * (int64_t)n * V;
+        const float* gb = args.g + b * (int64_t)n * V;
+        const bool has_sigma = args.sigma != nullptr;
+        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+
+        // ------------------------------------------------------------------ forward: R~ and Q
+#pragma unroll
+        for (int m = 0; m < BPT; ++m)
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+                float r[TI], z[TI];
+                const int u0 = own.fgroup(m, q);
+#pragma unroll
+                for (int ii = 0; ii < TI; ++ii) {
+                    r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
+                    z[ii] = 0.f;
+                }
+                st_floats<TI>(r, mr, u0, tape, 4u * u0, 0u);
+                st_floats<TI>(z, mq, u0, tape, 4u * u0, q_base);
+            }
+        lds_barrier();
+
+        double A = 0.0;
+        float N = 0.f, kq = 0.f, Kq = 0.f, N_last = 0.f, K_last = 0.f;
+        for (int t = 0; t < n; ++t) {
+            float rin[BPT][P], qin[BPT][P];
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) {
+                    rin[m][a] = mr[own.j(m) + J * a];
+                    qin[m][a] = mq[own.j(m) + J * a] - kq;
+                }
+            lds_barrier();   // every input read before any output overwrites it
+            if (tau == 0) {
+                buf_st(N, tape, 0u, nrm_base + 4u * t);
+                buf_st(Kq, tape, 0u, kq_base + 4u * t);
+            }
+            K_last = Kq;
+            Kq += kq;
+            float wt[V], gt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                wt[v] = wb[t * V + v] * scale;
+                gt[v] = gb[t * V + v] * inv_scale;
+            }
+            float lmax = -3.0e38f, lq = 0.f;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    float mx[TI], s[TI], sz[TI];
+#pragma unroll
+                    for (int r = 0; r < NA; ++r) {
+                        float x[TA][TI], z[TA][TI];
+#pragma unroll
+                        for (int aa = 0; aa < TA; ++aa) {
+                            const int a = r * TA + aa;
+                            float c[ROW];
+                            own.take_fwd(m, a, q, c, cnx);
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii) {
+                                float acc = rin[m][a], zz = qin[m][a];
+#pragma unroll
+                                for (int v = 0; v < V; ++v) {
+                                    const float d = fmaf(c[ii * V + v], scale, -wt[v]);
+                                    acc = fmaf(-d, d, acc);
+                                    zz = fmaf(gt[v], d, zz);
+                                }
+                                x[aa][ii] = acc;
+                                z[aa][ii] = zz;
+                            }
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            float cm = x[0][ii];
+#pragma unroll
+                            for (int aa = 1; aa < TA; ++aa) cm = fmaxf(cm, x[aa][ii]);
+                            float cs = 0.f, cz = 0.f;
+#pragma unroll
+                            for (int aa = 0; aa < TA; ++aa) {
+                                const float e = ex2(x[aa][ii] - cm);
+                                cs += e;
+                                cz = fmaf(e, z[aa][ii], cz);
+                            }
+                            if (r == 0) {
+                                mx[ii] = cm;
+                                s[ii] = cs;
+                                sz[ii] = cz;
+                            } else {
+                                lse_merge(mx[ii], s[ii], sz[ii], cm, cs, cz);
+                            }
+                        }
+                        GEN_SCHED_BARRIER();
+                    }
+                    float ro[TI], qo[TI];
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        ro[ii] = (mx[ii] - N) + lg2(s[ii]);
+                        qo[ii] = sz[ii] * rcp(s[ii]);
+                        const bool up = ro[ii] > lmax;
+                        lmax = up ? ro[ii] : lmax;
+                        lq = up ? qo[ii] : lq;
+                    }
+                    const int u0 = own.fgroup(m, q);
+                    st_floats<TI>(ro, mr, u0, tape, 4u * u0, (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(qo, mq, u0, tape, 4u * u0, q_base + (uint32_t)(t + 1) * row_bytes);
+                }
+            gseq_argmax_payload(lmax, lq, SEG);
+            if (WPS > 1 && lane == 0) {
+                redmax[t & 1][wv] = lmax;
+                redq[t & 1][wv] = lq;
+            }
+            lds_barrier();
+            if (WPS > 1) {
+                const int qs = lane & 15;
+                float bm = qs < WPS ? redmax[t & 1][qs] : -3.0e38f;
+                float bq = qs < WPS ? redq[t & 1][qs] : 0.f;
+                row16_argmax_payload(bm, bq);   // the first wave attaining the maximum
+                lmax = bm;
+                lq = bq;
+            }
+            lmax = uniform_f(lmax);
+            lq = uniform_f(lq);
+            A += (double)N;
+            N_last = N;
+            N = lmax;
+            kq = lq;
+        }
+        // rz = log2 Z - A_n, and E[F], which centres the covariance of the backward pass
+        float rz, EF;
+        if (!has_sigma) {
+            float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        const int u = own.fgroup(m, q) + ii;
+                        const float p = ex2(mr[u] - N);
+                        z0 += p;
+                        z1 = fmaf(p, mq[u], z1);
+                    }
+            z0 = gseq_sum(z0, SEG);
+            z1 = gseq_sum(z1, SEG);
+            if (WPS > 1 && lane == 0) {
+                reds[n & 1][wv][0] = z0;
+                reds[n & 1][wv][1] = z1;
+            }
+            lds_barrier();
+            if (WPS > 1) {
+                z0 = 0.f;
+                z1 = 0.f;
+                for (int q = 0; q < WPS; ++q) {
+                    z0 += reds[n & 1][q][0];
+                    z1 += reds[n & 1][q][1];
+                }
+            }
+            rz = N + lg2(z0);
+            EF = z1 / z0 + Kq;   // the final Q^_n carries the offset K_{n-1}
+            __syncthreads();
+        } else {
+            __syncthreads();   // R~_{n-1} and Q^_{n-1} are on the tape, written by other threads
+            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
+            const float qv = buf_ld_nt(tape, 0u, q_base + (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
+            float x = r;
+            EF = qv + K_last;   // Q^_{n-1} carries the offset K_{n-2}
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float d = fmaf(args.cb[sig * V + v], scale, -(wb[(n - 1) * V + v] * scale));
+                x = fmaf(-d, d, x);
+                EF = fmaf(gb[(n - 1) * V + v] * inv_scale, d, EF);
+            }
+            rz = (r < 0.5f * kNeg) ? kNeg : x - N_last;
+        }
+        const bool valid = rz > 0.5f * kNeg;
+
+        // ------------------------------------------------------------------ backward: B~ and P, covariance
+        float Nb = 0.f, C_ = 0.f, D = 0.f;
+        float kb = 0.f;   // kappa_{t+1}, subtracted from the P inputs
+        float H = 0.f;    // sum of the kappas of the steps after t
+        int t = n - 1;
+        if (!has_sigma) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        const int u = own.fgroup(m, q) + ii;
+                        mr[u] = 0.f;
+                        mq[u] = 0.f;
+                    }
+        } else {
+            // s_n = sigma: the posterior at n-1 is the indicator of sigma (grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
+            // the messages left are B_{n-2}(sigma >> k) = theta_{n-1}(sigma) and P_{n-2}(sigma >> k) = <g, c - w>,
+            // which is kappa_{n-1} as well
+            float th = 0.f, pz = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const float d = fmaf(args.cb[sig * V + v], scale, -(wb[(n - 1) * V + v] * scale));
+                th = fmaf(-d, d, th);
+                pz = fmaf(gb[(n - 1) * V + v] * inv_scale, d, pz);
+            }
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
+                        mr[u] = (u == (sig >> K)) ? th : kNeg;
+                        mq[u] = (u == (sig >> K)) ? pz : 0.f;
+                    }
+            if (tau == 0) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    args.grad[(b * n + n - 1) * V + v] = valid ? 0.f : __builtin_nanf("");
+                    if (args.w_soft)
+                        args.w_soft[(b * n + n - 1) * V + v] = valid ? args.cb[sig * V + v] : __builtin_nanf("");
+                }
+            }
+            D = N_last;
+            Nb = th;
+            kb = pz;
+            H = pz;
+            t = n - 2;
+        }
+        lds_barrier();
+
+        const int t_out = t;
+        float N_nx = 0.f, K_nx = 0.f, rt_nx = 0.f, qt_nx = 0.f;
+        if (t >= 0) {
+            N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
+            K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * t);
+            rt_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes);
+            qt_nx = buf_ld_nt(tape, v_j0, q_base + (uint32_t)t * row_bytes);
+        }
+        for (; t >= 0; --t) {
+            float bin[BPT][I], pin[BPT][I];
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        const int u = own.fgroup(m, q) + ii;
+                        bin[m][TI * q + ii] = mr[u];
+                        pin[m][TI * q + ii] = mq[u] - kb;
+                    }
+            lds_barrier();
+            float wt[V], gt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                wt[v] = wb[t * V + v] * scale;
+                gt[v] = gb[t * V + v] * inv_scale;
+            }
+            const float Nt = uniform_f(N_nx), Kt = uniform_f(K_nx);
+            if (t > 0) {
+                N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * (t - 1));
+                K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * (t - 1));
+            }
+            D += Nt;
+            const float ref = (rz + D) - C_;
+            // E[F | s_t = s] - E[F] = Q^_t(s >> k) + cst + <g_t, c(s) - w_t> + P''_t(s & (G-1)), cst per step
+            const float cst = (Kt - EF) + H;
+            float lmax = -3.0e38f, S0 = 0.f, S2 = 0.f, S1[V], S3[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                S1[v] = 0.f;
+                S3[v] = 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) {
+                    const int vg = own.j(m) + J * a;   // backward group of row a
+                    // R~_t and Q^_t of this group; the next group's (or the next step's first) one row ahead
+                    const float rt = rt_nx;
+                    const float qt = qt_nx + cst;
+                    if (m * P + a + 1 < BPT * P) {
+                        const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
+                        const uint32_t so = (uint32_t)t * row_bytes + 4u * (uint32_t)(own.j(m2) - own.j(0) + J * a2);
+                        rt_nx = buf_ld_nt(tape, v_j0, so);
+                        qt_nx = buf_ld_nt(tape, v_j0, q_base + so);
+                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
+                        const uint32_t so = (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes;
+                        rt_nx = buf_ld_nt(tape, v_j0, so);
+                        qt_nx = buf_ld_nt(tape, v_j0, q_base + so);
+                    }
+                    float mx = 0.f, s = 0.f, sez = 0.f;
+#pragma unroll
+                    for (int q = 0; q < NI; ++q) {
+                        float c[ROW], y[TI], z[TI], d[TI][V];
+                        own.take_bwd(m, a, q, c, cnx);
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            float acc = bin[m][TI * q + ii], zz = pin[m][TI * q + ii];
+#pragma unroll
+                            for (int v = 0; v < V; ++v) {
+                                d[ii][v] = fmaf(c[ii * V + v], scale, -wt[v]);
+                                acc = fmaf(-d[ii][v], d[ii][v], acc);
+                                zz = fmaf(gt[v], d[ii][v], zz);
+                            }
+                            y[ii] = acc;
+                            z[ii] = zz;
+                        }
+                        float cm = y[0];
+#pragma unroll
+                        for (int ii = 1; ii < TI; ++ii) cm = fmaxf(cm, y[ii]);
+                        if constexpr (C > 1) cm = quad_max(cm);
+                        float cs = 0.f, ez = 0.f, er = 0.f, ed[V], edr[V];
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            ed[v] = 0.f;
+                            edr[v] = 0.f;
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            const float e = ex2(y[ii] - cm);
+                            // E[F | s] - E[F], formed before any product: its parts nearly cancel at the likely
+                            // states, and multiplying them separately would keep their rounding
+                            const float r = z[ii] + qt;
+                            cs += e;
+                            ez = fmaf(e, z[ii], ez);
+                            er = fmaf(e, r, er);
+#pragma unroll
+                            for (int v = 0; v < V; ++v) {
+                                const float edv = e * d[ii][v];
+                                ed[v] += edv;
+                                edr[v] = fmaf(edv, r, edr[v]);
+                            }
+                        }
+                        const float f = ex2((cm + rt) - ref);
+                        S0 = fmaf(f, cs, S0);
+                        S2 = fmaf(f, er, S2);
+#pragma unroll
+                        for (int v = 0; v < V; ++v) {
+                            S1[v] = fmaf(f, ed[v], S1[v]);
+                            S3[v] = fmaf(f, edr[v], S3[v]);
+                        }
+                        if constexpr (C > 1) {
+                            cs = quad_sum(cs);
+                            ez = quad_sum(ez);
+                        }
+                        if (q == 0) {
+                            mx = cm;
+                            s = cs;
+                            sez = ez;
+                        } else {
+                            lse_merge(mx, s, sez, cm, cs, ez);
+                        }
+                    }
+                    const float out = (mx - Nb) + lg2(s);
+                    lmax = run_max(lmax, out);
+                    // the lanes of a quad store the same values; at t = 0 nobody reads them
+                    mr[vg] = out;
+                    mq[vg] = sez * rcp(s);
+                    pin_order(S0, S2, lmax);
+#pragma unroll
+                    for (int v = 0; v < V; ++v) pin_order(S1[v], S3[v]);
+                    GEN_SCHED_BARRIER();
+                }
+            lmax = gseq_max(lmax, SEG);
+            float Sv[NS];
+            Sv[0] = gseq_sum(S0, SEG);
+            Sv[1 + V] = gseq_sum(S2, SEG);
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                Sv[1 + v] = gseq_sum(S1[v], SEG);
+                Sv[2 + V + v] = gseq_sum(S3[v], SEG);
+            }
+            if (WPS > 1 && lane == 0) {
+                redmax[t & 1][wv] = lmax;
+#pragma unroll
+                for (int x = 0; x <= V; ++x) reds[t & 1][wv][x] = Sv[x];
+                const uint32_t po = part_base + 4u * (uint32_t)((t * WPS + wv) * NS);
+#pragma unroll
+                for (int x = 0; x < NS; ++x) buf_st(Sv[x], tape, 0u, po + 4u * x);
+            }
+            lds_barrier();
+            float m1[V];   // w_soft_t - w_t per component, in scaled codebook units
+            if (WPS > 1) {
+                const int qs = lane & 15;
+                lmax = row16_max(qs < WPS ? redmax[t & 1][qs] : -3.0e38f);
+                // only the P offset uses m1 here, and any value common to the sequence serves
+                const float s0b = row16_sum(qs < WPS ? reds[t & 1][qs][0] : 0.f);
+#pragma unroll
+                for (int v = 0; v < V; ++v) m1[v] = row16_sum(qs < WPS ? reds[t & 1][qs][1 + v] : 0.f) * rcp(s0b);
+            } else {
+#pragma unroll
+                for (int v = 0; v < V; ++v) m1[v] = Sv[1 + v] * (1.0f / Sv[0]);
+                if (tau == 0) {
+                    const float i0 = 1.0f / Sv[0];
+                    const float m2 = Sv[1 + V] * i0;
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        const float cov = fmaf(-m1[v], m2, Sv[2 + V + v] * i0);
+                        args.grad[(b * n + t) * V + v] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                        if (args.w_soft)
+                            args.w_soft[(b * n + t) * V + v] = valid ? wb[t * V + v] + m1[v] * inv_scale
+                                                                     : __builtin_nanf("");
+                    }
+                }
+            }
+            float kap = 0.f;
+#pragma unroll
+            for (int v = 0; v < V; ++v) kap = fmaf(gt[v], m1[v], kap);
+            kb = uniform_f(kap);
+            lmax = uniform_f(lmax);
+            H += kb;
+            C_ += Nb;
+            Nb = lmax;
+        }
+        if (WPS > 1) {
+            __syncthreads();   // the per-wave partial sums, written by other waves
+            for (int tt = tau; tt <= t_out; tt += TPS) {
+                float Sv[NS];
+#pragma unroll
+                for (int x = 0; x < NS; ++x) Sv[x] = 0.f;
+                for (int q = 0; q < WPS; ++q) {
+                    const uint32_t po = part_base + 4u * (uint32_t)((tt * WPS + q) * NS);
+#pragma unroll
+                    for (int x = 0; x < NS; ++x) Sv[x] += buf_ld(tape, 0u, po + 4u * x);
+                }
+                const float i0 = 1.0f / Sv[0];
+                const float m2 = Sv[1 + V] * i0;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    const float m1 = Sv[1 + v] * i0;
+                    const float cov = fmaf(-m1, m2, Sv[2 + V + v] * i0);
+                    args.grad[(b * n + tt) * V + v] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (args.w_soft)
+                        args.w_soft[(b * n + tt) * V + v] = valid ? wb[tt * V + v] + m1 * inv_scale : __builtin_nanf("");
+                }
+            }
+        }
+        __syncthreads();   // the next sequence reuses the tape and LDS
+    }
+}
+
+// ------------------------------------------------------------------------------------------------------------------
+// host-side launch
+
+namespace {
+
+using GenKernel = void (*)(GenArgs);
+
+template <int K, int V, int SPT, int LT>
+GenKernel pick(int op) {
+    switch (op) {
+        case 0: return gen_soft_kernel<K, V, SPT, LT>;
+        case 1: return gen_grad_kernel<K, V, SPT, LT>;
+        default: return gen_viterbi_kernel<K, V, SPT, LT>;
+    }
+}
+
+// L = 16 (the workloads' trellis) has its own instantiation, whose strides are compile-time; other L read it at run
+// time.
+template <int V, int SPT>
+GenKernel pick_k(int op, int k, int L) {
+    if constexpr (SPT < 64) {
+        switch (k) {
+            case 1: return pick<1, V, SPT, 0>(op);
+            case 2: return pick<2, V, SPT, 0>(op);
+            default: return nullptr;
+        }
+    } else {
+        switch (k) {
+            case 1: return L == 16 ? pick<1, V, SPT, 16>(op) : pick<1, V, SPT, 0>(op);
+            case 2: return L == 16 ? pick<2, V, SPT, 16>(op) : pick<2, V, SPT, 0>(op);
+            case 3: return L == 16 ? pick<3, V, SPT, 16>(op) : pick<3, V, SPT, 0>(op);
+            case 4: return L == 16 ? pick<4, V, SPT, 16>(op) : pick<4, V, SPT, 0>(op);
+            default: return nullptr;
+        }
+    }
+}
+
+template <int V>
+GenKernel pick_spt(int op, int k, int L) {
+    switch (L) {
+        case 4: return pick_k<V, 16>(op, k, L);
+        case 5: return pick_k<V, 32>(op, k, L);
+        default: return pick_k<V, 64>(op, k, L);
+    }
+}
+
+}  // namespace
+
+// op: 0 soft, 1 gradient, 2 Viterbi.  The caller has checked 1 <= k <= 4, 2k <= L <= 16, V in {1, 2}.
+hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
+                          hipStream_t st) {
+    const GenKernel f = V == 1 ? pick_spt<1>(op, k, a.L) : pick_spt<2>(op, k, a.L);
+    if (f == nullptr) return hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(f, dim3(grid), dim3(threads), lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace bcjr

@@ -50,4 +50,26 @@ struct ViterbiArgs {
     int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
 };
 
+// The general trellis (any k with 2k <= L, V weights per step): one argument block for its three kernels.
+struct GenArgs {
+    const float* w;        // [B, n V]
+    const float* cb;       // [2^L, V]
+    const float* g;        // [B, n V] upstream dL/dw_soft (gradient only)
+    int64_t B;
+    int n;                 // trellis steps
+    int L;
+    float scale;           // sqrt(log2(e) / T) (soft and gradient)
+    float two_over_T;
+    const int32_t* sigma;  // [B] or nullptr
+    float* w_soft;         // [B, n V] (soft: required; gradient: optional)
+    float* log_z;          // [B] or nullptr (soft)
+    float* grad;           // [B, n V] (gradient)
+    int32_t* states;       // [B, n] (Viterbi)
+    float* w_hard;         // [B, n V] or nullptr (Viterbi)
+    float* cost;           // [B] or nullptr (Viterbi)
+    unsigned char* ws;
+    size_t slot_bytes;
+    int32_t dbl;           // LDS messages double-buffered (else one buffer, inputs read before outputs are written)
+};
+
 }  // namespace bcjr

@@ -9,10 +9,12 @@
  * in the weight pre-image, and T -> 0 gives back the hard code (same passages).
  *
  * Trellis and energy (readings of the pages, stated once here for every entry point):
- *   - state s_t: an L-bit integer, 0 <= s_t < 2^L; each step shifts in k = 2 new bits at the low end:
- *       s_{t+1} = ((s_t << k) & (2^L - 1)) | b,  b in [0, 2^k).   One weight per step (2 bits per weight).
+ *   - state s_t: an L-bit integer, 0 <= s_t < 2^L; each step shifts in k new bits at the low end:
+ *       s_{t+1} = ((s_t << k) & (2^L - 1)) | b,  b in [0, 2^k).   One weight per step (k bits per weight), or V
+ *     weights per step with the _v entry points (k / V bits per weight).
  *   - a path s_1..s_n emits codebook[s_t] at step t; its energy is E = sum_t (w_t - codebook[s_t])^2 and its
- *     weight exp(-E / T).  Transitions carry no cost.
+ *     weight exp(-E / T).  Transitions carry no cost.  With V weights per step codebook[s] is a V-vector and
+ *     (w_t - codebook[s_t])^2 is the squared Euclidean distance over its components.
  *   - boundary_state == NULL: free start and free end (s_1 and s_n unconstrained).
  *     boundary_state != NULL: sequence b starts from a non-emitting s_0 = sigma_b (so s_1 is a successor of
  *     sigma_b) and ends in s_n = sigma_b (tail-biting with a given state).  sigma_b is masked to its low L bits.
@@ -28,7 +30,10 @@
  *     frees nothing, keeps no state between calls and never synchronizes: the work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
  *     Calls on different streams need different workspaces.
- *   - supported shapes: k == 2, 4 <= L <= 16, 1 <= n <= 4096, 1 <= B <= 2^31 - 1.
+ *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 2k <= L <= 16, and
+ *       soft codeword, gradient, Viterbi: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs kernels tuned for
+ *       it, every other (k, V) one kernel family written for any k; the gradient with k = 1 needs L <= 15);
+ *       codebook gradient and the tail-biting entry points: k == 2 and V = 1.
  *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
  *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
  *     into that sequence's outputs.
@@ -48,8 +53,10 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k != 2; exact tail-biting (choice of sigma, soft
-                                  codeword or gradient under the tail-biting measure) with L > 10; unknown mode */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; k != 2 or V != 1 for the codebook
+                                  gradient and the tail-biting entry points; the gradient with k = 1 and L = 16;
+                                  exact tail-biting (choice of sigma, soft codeword or gradient under the
+                                  tail-biting measure) with L > 10; unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
@@ -164,10 +171,38 @@ int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_
                         size_t workspace_bytes, void* stream);
 
 /*
+ * V weights per trellis step (the pages fix neither k nor V; a state then emits the V-vector codebook[s, 0..V-1]).
+ * The same three operations as bcjr_soft_codeword, bcjr_soft_codeword_grad and viterbi_hard_code, with the same
+ * arguments plus V, and these shapes: codebook float32 [2^L, V] (row-major: state-major, then component); w,
+ * w_soft, grad_w_soft, grad_w and w_hard float32 [B, n V], where step t of row b owns w[b, t V .. t V + V - 1];
+ * states int32 [B, n], one state per step; n counts trellis steps.  The energy of a path is
+ * E = sum_t sum_v (w[b, t V + v] - codebook[s_t, v])^2, so per component
+ *   w_soft[b, t V + v] = sum_s codebook[s, v] p_T(s_t = s | w_b),
+ *   grad_w[b, u V + v] = (2 / T) Cov_p( codebook[s_u, v], sum_t sum_v' grad_w_soft[b, t V + v'] codebook[s_t, v'] ),
+ * and the Viterbi metric adds the components' squares in index order, e = fl(d_0 d_0), e = fl(e + fl(d_v d_v)),
+ * before adding the predecessor's metric, again without fused multiply-add.  V = 1 is the scalar trellis above, and
+ * the entry points without _v are these with V = 1.  V must be 1 or 2 (BCJR_ERR_SHAPE below 1, BCJR_ERR_UNSUPPORTED
+ * above 2).  Workspace: bcjr_workspace_bytes_v with the matching BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI.
+ */
+int bcjr_soft_codeword_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                         int32_t V, float T, const int32_t* boundary_state, float* w_soft, float* log_z,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int bcjr_soft_codeword_grad_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                              int32_t V, float T, const int32_t* boundary_state, const float* grad_w_soft,
+                              float* grad_w, float* w_soft, void* workspace, size_t workspace_bytes, void* stream);
+int viterbi_hard_code_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                        int32_t V, const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace the entry point `op` (one of the BCJR_OP_* values above) needs for
  * these shapes; 0 when the shapes are invalid or unsupported.  Pure host function; no HIP call.
  */
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);
+
+/* The same for V weights per step: bcjr_workspace_bytes(op, ...) when V = 1; for V = 2 only the soft codeword, the
+ * gradient and Viterbi (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_VITERBI) have a size, every other op gives 0. */
+size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 
 /* Static, NUL-terminated description of a status code. */
 const char* bcjr_status_string(int32_t status);

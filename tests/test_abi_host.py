@@ -24,7 +24,8 @@ def test_header_declares_every_op():
     fns = declared_functions()
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
                  "viterbi_hard_code", "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting",
-                 "bcjr_soft_codeword_grad_tail_biting", "bcjr_workspace_bytes", "bcjr_status_string"]:
+                 "bcjr_soft_codeword_grad_tail_biting", "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v",
+                 "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -91,9 +92,60 @@ def test_workspace_bytes_invalid_shapes_are_zero(args):
     assert abi.bcjr_workspace_bytes(99, 1, 4, 8, 2) == 0
 
 
-def test_unsupported_k_has_no_workspace():
-    assert abi.bcjr_workspace_bytes(0, 4, 8, 8, 1) == 0
-    assert abi.bcjr_workspace_bytes(0, 4, 8, 9, 3) == 0
+def _gen_bytes(op, B, n, L, k, V):
+    """The general trellis kernels' workspace: one sequence per workgroup of 2^L / 64 threads (2^L below L = 6), a
+    slot per workgroup of the persistent grid, G = 2^(L-k) message floats per LDS buffer."""
+    S = 1 << L
+    tps = S // min(S, 64)
+    wps = tps // 64 if tps >= 64 else 1
+    G = S >> k
+    lds_cap, lds_static = 160 * 1024, 2048
+    if op == abi.BCJR_OP_GRAD:
+        lds = 2 * G * 4
+    else:
+        lds = 2 * G * 4 if 2 * G * 4 + lds_static <= lds_cap else G * 4
+    if lds + lds_static > lds_cap:
+        return 0
+    bpc = max(1, min(16 // (tps // 64 if tps >= 64 else 1), lds_cap // (lds + lds_static)))
+    grid = min(B, 256 * bpc)
+    tapes, nrm = _a256((n + 1) * G * 4), _a256(n * 4)
+    if op == abi.BCJR_OP_SOFT:
+        slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0)
+    elif op == abi.BCJR_OP_GRAD:
+        slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
+    else:
+        slot = _a256(2 * n * tps * 4)
+    return grid * slot
+
+
+@pytest.mark.parametrize("L,k", [(4, 1), (5, 2), (6, 3), (8, 4), (9, 1), (12, 3), (15, 1), (16, 1), (16, 3), (16, 4)])
+@pytest.mark.parametrize("V", [1, 2])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (4096, 256), (1000, 7)])
+def test_general_trellis_workspace_formula(L, k, V, B, n):
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+        if (k, V) == (2, 1):
+            continue
+        assert abi.bcjr_workspace_bytes_v(op, B, n, L, k, V) == _gen_bytes(op, B, n, L, k, V)
+        if V == 1:
+            assert abi.bcjr_workspace_bytes(op, B, n, L, k) == _gen_bytes(op, B, n, L, k, V)
+
+
+def test_workspace_v_matches_the_scalar_query():
+    for op in range(8):
+        for L in (8, 16):
+            assert abi.bcjr_workspace_bytes_v(op, 64, 32, L, 2, 1) == abi.bcjr_workspace_bytes(op, 64, 32, L, 2)
+
+
+def test_unsupported_trellis_has_no_workspace():
+    assert abi.bcjr_workspace_bytes(0, 4, 8, 10, 5) == 0                 # k > 4
+    assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 3) == 0             # V > 2
+    assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 0) == 0             # V < 1
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 16, 1) == 0  # R and Q exceed LDS at k = 1, L = 16
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 15, 1) > 0
+    for op in (3, 4, 5, 6, 7):                                           # k = 2, V = 1 only
+        assert abi.bcjr_workspace_bytes(op, 4, 8, 8, 1) == 0
+        assert abi.bcjr_workspace_bytes(op, 4, 8, 9, 3) == 0
+        assert abi.bcjr_workspace_bytes_v(op, 4, 8, 8, 2, 2) == 0
 
 
 def _soft(**kw):
@@ -233,11 +285,60 @@ def test_bad_shapes_rejected(kw):
     assert _vit(**kw) == abi.BCJR_ERR_SHAPE
 
 
-def test_unsupported_k_rejected():
-    assert _soft(k=1) == abi.BCJR_ERR_UNSUPPORTED
-    assert _grad(L=9, k=3) == abi.BCJR_ERR_UNSUPPORTED
+def _soft_v(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, V=2, T=0.5, boundary_state=None, w_soft=FAKE, log_z=None,
+             workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_v(*a.values())
+
+
+def _grad_v(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, V=2, T=0.5, boundary_state=None, grad_w_soft=FAKE,
+             grad_w=FAKE, w_soft=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_grad_v(*a.values())
+
+
+def _vit_v(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, V=2, boundary_state=None, states=FAKE, w_hard=None,
+             cost=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.viterbi_hard_code_v(*a.values())
+
+
+def test_unsupported_trellis_rejected():
+    assert _soft(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
+    assert _grad(L=12, k=6) == abi.BCJR_ERR_UNSUPPORTED
+    assert _vit(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
     assert _gc(k=1) == abi.BCJR_ERR_UNSUPPORTED
-    assert _vit(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert _gc(L=9, k=3) == abi.BCJR_ERR_UNSUPPORTED
+    assert _grad(L=16, k=1) == abi.BCJR_ERR_UNSUPPORTED                 # R and Q exceed LDS
+    for fn in (_soft_v, _grad_v, _vit_v):
+        assert fn(V=3) == abi.BCJR_ERR_UNSUPPORTED
+        assert fn(V=0) == abi.BCJR_ERR_SHAPE
+        assert fn(V=-1) == abi.BCJR_ERR_SHAPE
+
+
+def test_general_trellis_reaches_the_workspace_check():
+    # k = 1, 3, 4 and V = 2 have kernels: with no workspace the call stops at the workspace check
+    for L, k in ((8, 1), (9, 3), (8, 4), (16, 4)):
+        assert _soft(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
+        assert _grad(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
+        assert _vit(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
+        for V in (1, 2):
+            assert _soft_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
+            assert _grad_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
+            assert _vit_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
+    need = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT, 4, 8, 9, 3, 2)
+    assert _soft_v(L=9, k=3, workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
+    assert _soft_v(L=9, k=3, workspace=FAKE + 16, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=4097), dict(L=3), dict(L=17), dict(k=0), dict(L=5, k=3)])
+def test_bad_shapes_rejected_v(kw):
+    assert _soft_v(**kw) == abi.BCJR_ERR_SHAPE
+    assert _grad_v(**kw) == abi.BCJR_ERR_SHAPE
+    assert _vit_v(**kw) == abi.BCJR_ERR_SHAPE
 
 
 @pytest.mark.parametrize("T", [0.0, -1.0, float("nan"), float("inf"), 1e-13])
@@ -302,3 +403,10 @@ def test_largest_shape_keeps_workspace_offsets_in_32_bits():
             G, TPS, SPB = _geo(L)
             per_block = abi.bcjr_workspace_bytes(op, SPB, 4096, L, 2)
             assert 0 < per_block < 2 ** 31
+    # the general trellis: one sequence per block
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+        for L, k in ((16, 1), (15, 1), (16, 3), (16, 4), (8, 1)):
+            for V in (1, 2):
+                per_block = abi.bcjr_workspace_bytes_v(op, 1, 4096, L, k, V)
+                assert per_block < 2 ** 31
+                assert per_block > 0 or (op == abi.BCJR_OP_GRAD and (L, k) == (16, 1))

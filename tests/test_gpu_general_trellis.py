@@ -1,0 +1,262 @@
+"""GPU parity of the general trellis kernels against the oracle, through the C-ABI.
+
+The kernels cover k = 1..4 bits shifted in per step and V = 1 or 2 weights per step; k = 2 with V = 1 runs the tuned
+kernels and is covered elsewhere.  Checked:
+
+* the soft codeword and ln Z;
+* the weights' gradient;
+* the Viterbi hard code: states, codewords and float32 costs, bit-exact.
+
+Cases span:
+
+* L = 4..16, which covers both kernel forms: L = 16 (compile-time strides) and the run-time-L form, including
+  sub-wave workgroups;
+* ragged batches, n = 1, free and sigma boundaries;
+* batches larger than the persistent grid, so that a workgroup decodes several sequences in turn.  This exercises the
+  Viterbi traceback pipelined across sequences.
+
+Bars.  They are the k = 2, V = 1 bars multiplied by V max(1, 2/k).  The same float32 recursion runs here, and its
+error comes from the two sources the k = 2 derivation names, both of which grow with the trellis:
+
+* The rounding of a state's log weight theta' = -|c - w|^2 log2(e) / T is proportional to its size.  With V components
+  that log weight is a sum of V squared distances, V times larger on average.
+* The recursion's per-step rounding adds up over the L/k steps of trellis memory, which is twice as long at k = 1 as at
+  k = 2.
+
+At k = 3 and 4 with V = 1 the bars are the k = 2 ones.  Measured maxima over these cases (with other seeds):
+
+* soft codeword at T = 0.05: 1.6e-5 at L = 9, k = 1, V = 2 (free) and 1.5e-5 at L = 5, k = 1, V = 1 (sigma);
+* gradient at T = 0.1: 1.6e-5 elementwise at L = 5, k = 2, V = 2 (free, 2.5e-6 normwise);
+* every k >= 2, V = 1 case at T >= 0.1: within 1e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+import differentiable_bcjr_amd as dba
+import workloads
+from test_gpu_parity import _t, grad_err, grad_tol, norm_err, rel_err, soft_tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    return torch.device("cuda:0")
+
+
+def _vin(L, V, B, n, seed, sigma=False):
+    """Codebook ([2^L] for V = 1, else [2^L, V], unit variance), weights and upstream gradient [B, n V], sigma [B]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = rng.standard_normal((1 << L, V))
+    c = (c / c.std()).astype(np.float32)
+    if V == 1:
+        c = c[:, 0].copy()
+    w = rng.standard_normal((B, n * V)).astype(np.float32)
+    g = rng.standard_normal((B, n * V)).astype(np.float32)
+    s = rng.integers(0, 1 << L, size=B).astype(np.int32) if sigma else None
+    return w, c, g, s
+
+
+# (L, k, V, B, n steps)
+CASES = [(4, 1, 1, 16, 6), (4, 1, 2, 7, 5), (5, 1, 1, 5, 8), (5, 2, 2, 9, 9), (6, 3, 1, 5, 4), (6, 3, 2, 3, 7),
+         (7, 3, 1, 4, 9), (8, 1, 1, 6, 33), (8, 4, 1, 4, 5), (8, 4, 2, 3, 6), (9, 1, 2, 5, 17), (9, 3, 2, 4, 12),
+         (10, 4, 1, 3, 10), (11, 1, 1, 2, 20), (12, 3, 1, 2, 16), (12, 4, 2, 2, 9), (13, 1, 2, 2, 7), (14, 3, 2, 2, 6),
+         (15, 1, 1, 2, 6), (16, 1, 1, 2, 4), (16, 1, 2, 1, 4), (16, 2, 2, 2, 5), (16, 3, 1, 2, 5), (16, 3, 2, 2, 4),
+         (16, 4, 1, 2, 4), (16, 4, 2, 2, 5)]
+IDS = [f"L{L}k{k}V{V}B{B}n{n}" for L, k, V, B, n in CASES]
+
+
+def _scale(k, V):
+    """How much the float32 error grows over the k = 2, V = 1 trellis: a state's log weight is a sum of V squared
+    distances, and the recursion's rounding adds up over L/k steps of trellis memory."""
+    return V * (2 if k == 1 else 1)
+
+
+def vsoft_tol(T, sigma, k, V):
+    return soft_tol(T, sigma) * _scale(k, V)
+
+
+def vgrad_tol(T, sigma, k, V):
+    return grad_tol(T, sigma) * _scale(k, V)
+
+
+def vgrad_norm_ok(x, ref, T, sigma, k, V):
+    return sigma or T >= 0.1 or norm_err(x, ref) <= 1e-5 * _scale(k, V)
+
+
+def _sigma_n(L, k, n):
+    """Enough steps for every sigma to be reachable: the constraint needs at least L/k steps."""
+    return max(n, -(-L // k) + 1)
+
+
+@pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
+@pytest.mark.parametrize("sigma", [False, True])
+def test_soft_codeword_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
+    if sigma:
+        n = _sigma_n(L, k, n)
+    w, c, _, s = _vin(L, V, B, n, 7000 + 31 * L + 7 * k + V + n, sigma)
+    for T in [1.0, 0.1, 0.05]:
+        got, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev), return_log_z=True)
+        ref, rlz = oracle_mod.soft(w, c, L, k, T, sigma=s)
+        e = rel_err(got.cpu().numpy(), ref)
+        el = float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0)))
+        print(f"soft L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {e:.2e}, ln Z {el:.2e}", flush=True)
+        assert e <= vsoft_tol(T, sigma, k, V)
+        assert el <= 1e-5
+
+
+@pytest.mark.parametrize("L,k,V,B,n", [c for c in CASES if c[:2] != (16, 1)],
+                         ids=[i for c, i in zip(CASES, IDS) if c[:2] != (16, 1)])
+@pytest.mark.parametrize("sigma", [False, True])
+def test_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
+    if sigma:
+        n = _sigma_n(L, k, n)
+    w, c, g, s = _vin(L, V, B, n, 7100 + 31 * L + 7 * k + V + n, sigma)
+    for T in [1.0, 0.1, 0.05]:
+        gr, ws = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev), return_w_soft=True)
+        rgr, rws = oracle_mod.grad(w, c, g, L, k, T, sigma=s)
+        e = grad_err(gr.cpu().numpy(), rgr, g, c, T)
+        print(f"grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {e:.2e} "
+              f"(normwise {norm_err(gr.cpu().numpy(), rgr):.2e})", flush=True)
+        assert e <= vgrad_tol(T, sigma, k, V)
+        assert vgrad_norm_ok(gr.cpu().numpy(), rgr, T, sigma, k, V)
+        assert rel_err(ws.cpu().numpy(), rws) <= vsoft_tol(T, sigma, k, V)
+
+
+@pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
+@pytest.mark.parametrize("sigma", [False, True])
+def test_viterbi_matches_oracle_bit_exact(oracle_mod, dev, L, k, V, B, n, sigma):
+    if sigma:
+        n = _sigma_n(L, k, n)
+    w, c, _, s = _vin(L, V, B, n, 7200 + 31 * L + 7 * k + V + n, sigma)
+    st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev)))
+    rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(wh.view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
+
+
+def test_gradient_k1_at_L16_is_unsupported(dev):
+    w, c, g, _ = _vin(16, 1, 1, 4, 1)
+    with pytest.raises(dba.BCJRError) as e:
+        dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), 16, 1, 0.5)
+    assert e.value.status == dba.abi.BCJR_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------------ batches larger than the persistent grid
+
+
+@pytest.mark.parametrize("L,k,V,B,n", [(8, 1, 2, 4600, 5), (9, 3, 1, 4200, 4), (16, 3, 1, 260, 3),
+                                       (16, 4, 2, 258, 3)])
+def test_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n):
+    """More sequences than the grid has workgroups (4096 at L <= 11, 256 at L = 16): every workgroup reuses its slot
+    and LDS, and Viterbi traces one sequence back while it decodes the next."""
+    w, c, g, _ = _vin(L, V, B, n, 7300 + L + k + V)
+    T = 0.1
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T).cpu().numpy()
+    rws, _ = oracle_mod.soft(w, c, L, k, T)
+    assert rel_err(ws, rws) <= vsoft_tol(T, False, k, V)
+    if (L, k) != (16, 1):
+        gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
+        rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
+        assert grad_err(gr, rgr, g, c, T) <= vgrad_tol(T, False, k, V)
+    st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
+    rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(wh.view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------------- edge cases
+
+
+@pytest.mark.parametrize("L,k,V", [(8, 1, 1), (9, 3, 2), (16, 4, 2)])
+def test_one_step(oracle_mod, dev, L, k, V):
+    w, c, g, _ = _vin(L, V, 3, 1, 7400 + L)
+    T = 0.3
+    ws, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, return_log_z=True)
+    rws, rlz = oracle_mod.soft(w, c, L, k, T)
+    assert rel_err(ws.cpu().numpy(), rws) <= 1e-5
+    assert np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0)) <= 1e-5
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
+    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
+    assert grad_err(gr, rgr, g, c, T) <= 1e-5
+    st, _, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
+    rst, _, rcost = oracle_mod.viterbi(w, c, L, k)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
+
+
+@pytest.mark.parametrize("L,k,V", [(8, 1, 2), (12, 3, 1), (16, 4, 2)])
+def test_sigma_without_a_path(oracle_mod, dev, L, k, V):
+    """n < L/k: most sigmas have no admissible path; their outputs are NaN, ln Z = -inf and the Viterbi cost +inf,
+    as in the oracle, while sigmas that do have one match it."""
+    n = max(1, L // k - 2)
+    B = 6
+    w, c, g, s = _vin(L, V, B, n, 7500 + L, sigma=True)
+    T = 0.5
+    ws, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev), return_log_z=True)
+    rws, rlz = oracle_mod.soft(w, c, L, k, T, sigma=s)
+    ws, lz = ws.cpu().numpy(), lz.cpu().numpy()
+    dead = ~np.isfinite(rlz)
+    assert dead.any()
+    assert np.all(np.isnan(ws[dead])) and np.all(lz[dead] == -np.inf)
+    if (~dead).any():
+        assert rel_err(ws[~dead], rws[~dead]) <= 3e-5
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
+    assert np.all(np.isnan(gr[dead]))
+    _, _, cost = dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev))
+    assert np.all(cost.cpu().numpy()[dead] == np.inf)
+
+
+def test_silent_second_component_matches_the_scalar_trellis(dev):
+    """V = 2 with the second codebook column and every second weight at 0 runs the general kernels on the scalar
+    trellis: the first components agree with the k = 2 tuned kernels within the parity bar, the second is 0, and
+    Viterbi is bit-identical (adding 0 * 0 changes no float32 sum)."""
+    L, k, B, n, T = 12, 2, 5, 24, 0.2
+    w1, c1, g1, _ = _vin(L, 1, B, n, 7600)
+    c2 = np.stack([c1, np.zeros_like(c1)], axis=1)
+    w2 = np.stack([w1, np.zeros_like(w1)], axis=2).reshape(B, 2 * n)
+    g2 = np.stack([g1, np.zeros_like(g1)], axis=2).reshape(B, 2 * n)
+    a = dba.soft_codeword(_t(w1, dev), _t(c1, dev), L, k, T).cpu().numpy()
+    b = dba.soft_codeword(_t(w2, dev), _t(c2, dev), L, k, T).cpu().numpy()
+    assert rel_err(b[:, 0::2], a) <= 2e-5 and np.all(b[:, 1::2] == 0.0)
+    ga = dba.soft_codeword_grad(_t(w1, dev), _t(c1, dev), _t(g1, dev), L, k, T).cpu().numpy()
+    gb = dba.soft_codeword_grad(_t(w2, dev), _t(c2, dev), _t(g2, dev), L, k, T).cpu().numpy()
+    assert norm_err(gb[:, 0::2], ga) <= 2e-5
+    assert np.max(np.abs(gb[:, 1::2])) == 0.0
+    sa = [x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w1, dev), _t(c1, dev), L, k)]
+    sb = [x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w2, dev), _t(c2, dev), L, k)]
+    np.testing.assert_array_equal(sa[0], sb[0])
+    np.testing.assert_array_equal(sa[2].view(np.uint32), sb[2].view(np.uint32))
+
+
+# ------------------------------------------------------------------- the 1024x1024 workload at other bit rates
+
+
+@pytest.mark.parametrize("name", ["k3", "k4v2"])
+def test_trellis_variant_workload_rows(oracle_mod, dev, name):
+    """The whole 4096-sequence batch through all three operations; sampled rows against the oracle."""
+    wl = workloads.TRELLIS_VARIANTS[name]
+    c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
+    T = wl.temps[0]
+    ct, wt, gt = _t(c, dev), _t(w, dev), _t(g, dev)
+    ws = dba.soft_codeword(wt, ct, wl.L, wl.k, T).cpu().numpy()
+    gr = dba.soft_codeword_grad(wt, ct, gt, wl.L, wl.k, T).cpu().numpy()
+    st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(wt, ct, wl.L, wl.k))
+    assert np.all(np.isfinite(ws)) and np.all(np.isfinite(gr))
+    rows = wl.sample_rows(3)
+    rws, _ = oracle_mod.soft(w[rows], c, wl.L, wl.k, T)
+    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
+    rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k)
+    e_s, e_g = rel_err(ws[rows], rws), norm_err(gr[rows], rgr)
+    e_ge = grad_err(gr[rows], rgr, g[rows], c, T)
+    print(f"{wl.name}: soft {e_s:.2e}, grad {e_g:.2e} normwise, {e_ge:.2e} elementwise", flush=True)
+    f = _scale(wl.k, wl.V)
+    assert e_s <= 1e-5 * f
+    assert e_g <= 1e-5 * f and e_ge <= 5e-5 * f   # the full-length bars of the k = 2 kernels, scaled as above
+    np.testing.assert_array_equal(st[rows], rst)
+    np.testing.assert_array_equal(wh[rows].view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost[rows].view(np.uint32), rcost.view(np.uint32))

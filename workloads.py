@@ -48,6 +48,13 @@ def codebook(L: int, seed: int, unit_variance: bool = True) -> np.ndarray:
     return z.astype(np.float32)
 
 
+def codebook_v(L: int, V: int, seed: int) -> np.ndarray:
+    """A codebook of V-vectors: [2^L, V] entries ~ N(0,1), scaled by 1/std over all entries (ddof=0, not centred).
+    V = 1 gives codebook(L, seed) as a column."""
+    z = _rng(seed).standard_normal((1 << L, V))
+    return (z / z.std()).astype(np.float32)
+
+
 def weights(B: int, n: int, seed: int) -> np.ndarray:
     """B sequences of n weights ~ N(0,1), float32, row-major [B, n]."""
     return _rng(seed).standard_normal((B, n)).astype(np.float32)
@@ -83,9 +90,17 @@ class Workload:
     n: int
     temps: tuple
     matrix: str
+    V: int = 1   # weights per trellis step; n counts weights, so a sequence has n / V steps
+
+    @property
+    def steps(self) -> int:
+        return self.n // self.V
 
     def codebook(self) -> np.ndarray:
-        return codebook(self.L, 1000 + self.cfg)
+        """[2^L] for V = 1, else [2^L, V]."""
+        if self.V == 1:
+            return codebook(self.L, 1000 + self.cfg)
+        return codebook_v(self.L, self.V, 1000 + self.cfg)
 
     def weights(self, B: int | None = None) -> np.ndarray:
         return weights(self.B if B is None else B, self.n, 2000 + self.cfg)
@@ -110,6 +125,13 @@ WORKLOADS = {
     3: Workload(3, "llama_mlp_8192x2048", 16, 2, 65536, SEQ_LEN, (0.05,), "8192x2048"),
     4: Workload(4, "low_temp_2048x2048", 16, 2, 16384, SEQ_LEN, (1e-1, 1e-2, 1e-3, 1e-4), "2048x2048"),
     5: Workload(5, "llama_layer_all_proj", 16, 2, _layer_sequences(), SEQ_LEN, (0.05,), "q,o,k,v,gate,up,down"),
+}
+
+# Trellis variants of the 1024x1024 workload (the same weights and upstream gradient): 3 bits per weight (k = 3), and
+# 2 bits per weight with two weights per step (k = 4, V = 2).  The pages fix neither k nor V.
+TRELLIS_VARIANTS = {
+    "k3": Workload(2, "qtip_1024x1024_k3", 16, 3, 4096, SEQ_LEN, (0.1,), "1024x1024"),
+    "k4v2": Workload(2, "qtip_1024x1024_k4_v2", 16, 4, 4096, SEQ_LEN, (0.1,), "1024x1024", V=2),
 }
 
 # The brute-force companion of the tiny workload: L=4, k=2, n=6, 16 sequences.
