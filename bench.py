@@ -24,7 +24,10 @@ After the timed steps, and outside them, the codebook gradient (bcjr_soft_codewo
 summed over the batch) is timed on the same inputs and reported under ``next_rows`` with its own roofline.  Its bound
 is HBM: besides the 4 bytes of forward tape per state-step (written once, read once), every state's float32
 accumulator is read and written once per step, 12 bytes per state-step against the 8 TB/s peak.  The tail-biting
-Viterbi with rotate-and-decode start-state choice (viterbi_tail_biting, two decodes) is timed the same way.
+Viterbi with rotate-and-decode start-state choice (viterbi_tail_biting, two decodes) is timed the same way, and so
+are the general-trellis kernels on the same 1024x1024 matrix at 3 bits per weight (k = 3) and at 2 bits per weight with
+two weights per step (k = 4, V = 2): soft codeword, gradient and Viterbi, each against the ALU roofline of its own
+slot count (general_slots).
 
 ``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
 """
@@ -57,6 +60,22 @@ ALU_SLOTS = {
     "viterbi": 3.5 + 2.25 * HALF_SLOTS,
 }
 DIRECTIONS = {"soft": 2, "grad": 2, "viterbi": 1}
+
+
+def general_slots(k: int, V: int) -> dict:
+    """The same counts for P = 2^k predecessors (and successors) per group and V weights per step: one log-sum-exp of
+    P per group, a squared distance of V components per state.  At k = 2, V = 1 they are the counts above.
+      soft     full 5V + 2(2P+1)/P + (3+V)/P, half 2, trans (2P+3)/P
+      grad     full 3V + 1 + (2P+2)/P (forward) + 6V + 5 + (6+2V)/P (backward), half 2, trans (P+2)/P + 1 + 3/P
+      viterbi  full 3V + 0.5, half 2.25"""
+    P = 2 ** k
+    return {
+        "soft": 5 * V + 2 * (2 * P + 1) / P + (3 + V) / P + 2.0 * HALF_SLOTS + (2 * P + 3) / P * TRANS_SLOTS,
+        "grad": (3 * V + 1 + (2 * P + 2) / P + 6 * V + 5 + (6 + 2 * V) / P + 2.0 * HALF_SLOTS
+                 + ((P + 2) / P + 1 + 3 / P) * TRANS_SLOTS),
+        "viterbi": 3 * V + 0.5 + 2.25 * HALF_SLOTS,
+    }
+
 PEAK_SLOTS_PER_S = 256 * 128 * 2.4e9
 KERNEL_SOURCES = {
     "soft": ["soft.hip"],
@@ -64,6 +83,8 @@ KERNEL_SOURCES = {
     "viterbi": ["viterbi.hip"],
     "grad_codebook": ["grad.hip"],
 }
+KERNEL_SOURCES.update({f"gen_{op}_k{k}v{V}": ["general.hip"] for op in ("soft", "grad", "viterbi")
+                       for k, V in ((3, 1), (4, 2))})
 COMMON_SOURCES = ["trellis.hpp", "kernel_args.hpp"]
 KERNEL_NAMES = {"soft": "soft_kernel<16>", "grad": "grad_kernel<16, false>", "viterbi": "viterbi_kernel<16>",
                 "grad_codebook": "grad_kernel<16, true>"}
@@ -86,6 +107,9 @@ def parse_args():
     ap.add_argument("--codebook-grad-steps", type=int, default=3,
                     help="calls of the codebook gradient (and of the tail-biting Viterbi) timed after the step "
                          "(0 skips them)")
+    ap.add_argument("--trellis-variant-steps", type=int, default=2,
+                    help="calls of each op on the 1024x1024 matrix at k = 3 and at k = 4 with V = 2, timed after the "
+                         "step (0 skips them)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (reference dispatch for HBM byte counters)")
     return ap.parse_args()
@@ -146,6 +170,66 @@ def cpu_baseline(wl, T, n_rows_per_thread=4):
             "sample": f"{len(rows)} of the {wl.B} sequences (rows 0 and B-1 included, seed {4000 + wl.cfg}), "
                       f"one full step (soft + grad + viterbi), {dt:.1f} s, weights/s {len(rows) * wl.n / dt:.3g}",
             "weights_per_s": len(rows) * wl.n / dt}
+
+
+def time_variant(vw, T, K, dev, stream, check):
+    """Soft codeword, gradient and Viterbi of one trellis variant of a workload, each timed over K calls with HIP
+    events on the launch stream, with the ALU roofline of each kernel."""
+    import numpy as np
+    import torch
+
+    from differentiable_bcjr_amd import abi
+
+    S, steps, V, k, L, B = 1 << vw.L, vw.steps, vw.V, vw.k, vw.L, vw.B
+    c = torch.from_numpy(vw.codebook()).to(dev)
+    w = torch.from_numpy(vw.weights()).to(dev)
+    g = torch.from_numpy(vw.upstream_grad()).to(dev)
+    out = torch.empty_like(w)
+    grad = torch.empty_like(w)
+    states = torch.empty((B, steps), dtype=torch.int32, device=dev)
+    w_hard = torch.empty_like(w)
+    cost = torch.empty((B,), dtype=torch.float32, device=dev)
+    nbytes = max(abi.bcjr_workspace_bytes_v(op, B, steps, L, k, V)
+                 for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI))
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sp = stream.cuda_stream
+    calls = {
+        "soft": lambda: check(abi.bcjr_soft_codeword_v(w.data_ptr(), c.data_ptr(), B, steps, L, k, V, T, None,
+                                                       out.data_ptr(), None, ws.data_ptr(), nbytes, sp), "soft_v"),
+        "grad": lambda: check(abi.bcjr_soft_codeword_grad_v(w.data_ptr(), c.data_ptr(), B, steps, L, k, V, T, None,
+                                                            g.data_ptr(), grad.data_ptr(), None, ws.data_ptr(), nbytes,
+                                                            sp), "grad_v"),
+        "viterbi": lambda: check(abi.viterbi_hard_code_v(w.data_ptr(), c.data_ptr(), B, steps, L, k, V, None,
+                                                         states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(),
+                                                         ws.data_ptr(), nbytes, sp), "viterbi_v"),
+    }
+    slots = general_slots(k, V)
+    ops = {}
+    for name, fn in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+        ev[0].record(stream)
+        for i in range(K):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
+        units = B * steps * S
+        ops[name] = {"kernel": f"gen_{'grad' if name == 'grad' else name}_kernel<{k}, {V}, 64, 16>",
+                     "ms": round(ms, 4), "state_updates_per_s": DIRECTIONS[name] * units / (ms * 1e-3),
+                     "weights_per_s": B * vw.n / (ms * 1e-3),
+                     "roofline": {"bound": "alu", "achieved": round(slots[name] * units / (ms * 1e-3) / 1e12, 3),
+                                  "peak": round(PEAK_SLOTS_PER_S / 1e12, 3), "unit": "T VALU-slots/s",
+                                  "frac": round(slots[name] * units / (ms * 1e-3) / PEAK_SLOTS_PER_S, 4),
+                                  "traffic": recorded_traffic(f"gen_{name}_k{k}v{V}", "qtip_1024x1024"),
+                                  "per_unit": f"{slots[name]:.4g} fp32 VALU slots per state-step",
+                                  "units_per_launch": units}}
+    step_ms = sum(o["ms"] for o in ops.values())
+    return {"workload": vw.name, "L": L, "k": k, "V": V, "B": B, "steps_per_sequence": steps, "T": T,
+            "entry_points": "bcjr_soft_codeword_v, bcjr_soft_codeword_grad_v, viterbi_hard_code_v",
+            "calls": K, "step_ms": round(step_ms, 4), "weights_per_s": B * vw.n / (step_ms * 1e-3),
+            "state_updates_per_s": 5 * B * steps * S / (step_ms * 1e-3), "ops": ops}
 
 
 def main():
@@ -312,6 +396,10 @@ def main():
                          "frac": round(slots3 / (ms3 * 1e-3) / PEAK_SLOTS_PER_S, 4),
                          "per_unit": f"2 x {ALU_SLOTS['viterbi']} fp32 VALU slots per state-step (two decodes)",
                          "units_per_launch": B * n * S}}
+
+    if args.trellis_variant_steps > 0:
+        for key, vw in workloads.TRELLIS_VARIANTS.items():
+            next_rows[f"trellis_{key}"] = time_variant(vw, T, args.trellis_variant_steps, dev, stream, check)
 
     total_upd = sum(DIRECTIONS[o] for o, _ in ops) * B * n * S
     line = {
