@@ -23,7 +23,7 @@ are exact ("exactly differentiable with respect to the weight pre-image and trel
 Trellis variants: ``k`` (bits shifted in per step) may be 1 to 4 for the soft codeword, its weights' gradient and
 Viterbi.  A codebook of shape [2^L, V] emits V weights per step (V = 1 or 2): the weights are then [B, n V], step t
 of a row owning its weights t V .. t V + V - 1, and Viterbi returns one state per step.  The codebook gradient and
-the tail-biting operations take k = 2 and a codebook [2^L].
+the tail-biting operations take k = 2 and a codebook [2^L]; the codebook gradient takes every (k, V).
 
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
@@ -157,24 +157,28 @@ def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_
                                 k: int = 2, T: float = 1.0, boundary_state: torch.Tensor | None = None, *,
                                 return_grad_w: bool = True, return_w_soft: bool = False,
                                 workspace: torch.Tensor | None = None):
-    """dL/dc [2^L] (summed over the batch) given dL/dw_soft [B, n]; then dL/dw [B, n] if ``return_grad_w`` and the
-    soft codeword if ``return_w_soft``.  Returns a tuple when either is asked for."""
+    """dL/dc with the codebook's shape ([2^L], or [2^L, V] for V weights per step; summed over the batch) given
+    dL/dw_soft with w's shape; then dL/dw if ``return_grad_w`` and the soft codeword if ``return_w_soft``.  Returns a
+    tuple when either is asked for."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     g = _f32(grad_w_soft, "grad_w_soft")
-    if codebook.dim() != 1:
-        raise ValueError("the codebook gradient takes a codebook [2^L] (one weight per step)")
-    if w.dim() != 2 or g.shape != w.shape:
-        raise ValueError("w and grad_w_soft must both be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
+    if g.shape != w.shape:
+        raise ValueError("grad_w_soft must have w's shape")
     sig = _sigma(boundary_state, B, w.device)
-    gc = torch.empty(1 << L, dtype=torch.float32, device=w.device)
+    gc = torch.empty(codebook.shape, dtype=torch.float32, device=w.device)
     grad = torch.empty_like(w) if return_grad_w else None
     ws_out = torch.empty_like(w) if return_w_soft else None
-    ws, need = _workspace(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, k, w.device, workspace)
-    _check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
-                                                g.data_ptr(), gc.data_ptr(), _ptr(grad), _ptr(ws_out), ws.data_ptr(),
-                                                ws.numel(), _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
+                                                    _ptr(sig), g.data_ptr(), gc.data_ptr(), _ptr(grad), _ptr(ws_out),
+                                                    ws.data_ptr(), ws.numel(), _stream(w.device)))
+    else:
+        _check(abi.bcjr_soft_codeword_grad_codebook_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
+                                                      _ptr(sig), g.data_ptr(), gc.data_ptr(), _ptr(grad),
+                                                      _ptr(ws_out), ws.data_ptr(), ws.numel(), _stream(w.device)))
     extra = tuple(x for x in (grad, ws_out) if x is not None)
     return (gc, *extra) if extra else gc
 
@@ -297,6 +301,6 @@ class _SoftQuantize(torch.autograd.Function):
 
 def soft_quantize(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
                   boundary_state: torch.Tensor | None = None) -> torch.Tensor:
-    """The soft codeword of w [B, n] as a differentiable function of w and of the codebook [2^L] (autograd runs the
-    exact gradient kernels)."""
+    """The soft codeword of w as a differentiable function of w and of the codebook ([2^L], or [2^L, V] with w
+    [B, n V]); autograd runs the exact gradient kernels."""
     return _SoftQuantize.apply(w, codebook, L, k, T, boundary_state)

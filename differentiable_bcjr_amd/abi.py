@@ -33,7 +33,8 @@ BCJR_TB_ROTATE = 1
 
 EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
            "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting", "bcjr_soft_codeword_grad_tail_biting",
-           "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v", "viterbi_hard_code_v", "bcjr_workspace_bytes",
+           "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v", "bcjr_soft_codeword_grad_codebook_v",
+           "viterbi_hard_code_v", "bcjr_workspace_bytes",
            "bcjr_workspace_bytes_v", "bcjr_status_string")
 
 _lib = None
@@ -66,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.bcjr_soft_codeword_v.restype = ctypes.c_int
     lib.bcjr_soft_codeword_grad_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     lib.bcjr_soft_codeword_grad_v.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_grad_codebook_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                                                       sz, vp]
+    lib.bcjr_soft_codeword_grad_codebook_v.restype = ctypes.c_int
     lib.viterbi_hard_code_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_hard_code_v.restype = ctypes.c_int
     lib.bcjr_workspace_bytes.argtypes = [i32, i64, i64, i32, i32]
@@ -130,6 +134,12 @@ def bcjr_soft_codeword_grad_v(w, codebook, B, n, L, k, V, T, boundary_state, gra
                               workspace_bytes, stream) -> int:
     return load().bcjr_soft_codeword_grad_v(w, codebook, B, n, L, k, V, T, boundary_state, grad_w_soft, grad_w,
                                             w_soft, workspace, workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_grad_codebook_v(w, codebook, B, n, L, k, V, T, boundary_state, grad_w_soft, grad_codebook,
+                                       grad_w, w_soft, workspace, workspace_bytes, stream) -> int:
+    return load().bcjr_soft_codeword_grad_codebook_v(w, codebook, B, n, L, k, V, T, boundary_state, grad_w_soft,
+                                                     grad_codebook, grad_w, w_soft, workspace, workspace_bytes, stream)
 
 
 def viterbi_hard_code_v(w, codebook, B, n, L, k, V, boundary_state, states, w_hard, cost, workspace, workspace_bytes,

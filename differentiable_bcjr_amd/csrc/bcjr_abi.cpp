@@ -29,6 +29,8 @@ hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n
 struct GenArgs;
 hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
                           hipStream_t st);
+hipError_t launch_codebook_reduce(const unsigned char* ws, size_t stride, uint32_t acc_off, int count, int S,
+                                  float* out, hipStream_t st);
 
 }  // namespace bcjr
 
@@ -117,9 +119,10 @@ struct GenPlan {
     bool ok;          // false: no kernel for these shapes (the gradient's two message arrays exceed LDS)
     int grid, threads, dbl;
     size_t lds, slot_bytes, total;
+    size_t acc_off;   // codebook gradient: offset of the slot's [2^L][V] accumulator
 };
 
-// op: BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI.
+// op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.
 GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
     GenPlan p{};
     const int S = 1 << L;
@@ -128,7 +131,7 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     const int wps = tps >= 64 ? tps / 64 : 1;
     const size_t G = (size_t)S >> k;
     const size_t msg = G * 4;
-    if (op == BCJR_OP_GRAD) {   // R and Q, one buffer each
+    if (op == BCJR_OP_GRAD || op == BCJR_OP_GRAD_CODEBOOK) {   // R and Q, one buffer each
         p.dbl = 0;
         p.lds = 2 * msg;
     } else {
@@ -153,6 +156,10 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
             break;
         case BCJR_OP_GRAD:   // R~ and Q^ tapes, normalisers and Q offsets, per-wave (S0, S1[V], S2, S3[V])
             p.slot_bytes = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
+            break;
+        case BCJR_OP_GRAD_CODEBOOK:   // the gradient's slot + one float accumulator per state and component
+            p.acc_off = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
+            p.slot_bytes = p.acc_off + align256((size_t)S * V * 4);
             break;
         default:   // two back-pointer buffers of [n][threads] words
             p.slot_bytes = align256(2 * (size_t)n * (size_t)tps * 4);
@@ -219,7 +226,7 @@ int check_tb_mode(int32_t mode, int32_t L) {
 extern "C" {
 
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
-    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI) {
+    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI || op == BCJR_OP_GRAD_CODEBOOK) {
         if (check_shape_v(B, n, L, k, V) != BCJR_OK) return 0;
         if (tuned(k, V)) return make_plan(op, B, n, L).total;
         const GenPlan p = make_gen_plan(op, B, n, L, k, V);
@@ -231,7 +238,7 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
 
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
     if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
-    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI)
+    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI || op == BCJR_OP_GRAD_CODEBOOK)
         return bcjr_workspace_bytes_v(op, B, n, L, k, 1);
     if (check_shape(B, n, L, k) != BCJR_OK) return 0;
     if (op == BCJR_OP_SOFT_TAIL_BITING || op == BCJR_OP_GRAD_TAIL_BITING) {
@@ -359,6 +366,56 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     return hip_status(launch_grad(L, a, p.grid, static_cast<hipStream_t>(stream)));
 }
 
+int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
+                       float T, const int32_t* boundary_state, const float* grad_w_soft, float* grad_codebook,
+                       float* grad_w, float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !grad_w_soft || !grad_codebook) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, V);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (!tuned(k, V)) {
+        const GenPlan p = make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V);
+        if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.g = grad_w_soft;
+        a.B = B;
+        a.n = (int)n;
+        a.L = L;
+        a.scale = scale;
+        a.two_over_T = (float)(2.0 / (double)T);
+        a.sigma = boundary_state;
+        a.grad = grad_w;
+        a.w_soft = w_soft;
+        a.ws = static_cast<unsigned char*>(workspace);
+        a.slot_bytes = p.slot_bytes;
+        a.dbl = p.dbl;
+        hipError_t e = launch_general(3, k, V, a, p.grid, p.threads, p.lds, st);
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(launch_codebook_reduce(a.ws, p.slot_bytes, (uint32_t)p.acc_off, p.grid, (1 << L) * V,
+                                                 grad_codebook, st));
+    }
+    const Plan p = make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L);
+    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
+    GradArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.g = grad_w_soft;
+    a.B = B;
+    a.n = (int)n;
+    a.scale = scale;
+    a.two_over_T = (float)(2.0 / (double)T);
+    a.sigma = boundary_state;
+    a.grad = grad_w;
+    a.w_soft = w_soft;
+    a.ws = static_cast<unsigned char*>(workspace);
+    a.slot_bytes = p.slot_bytes;
+    return hip_status(launch_grad_codebook(L, a, p.grid, st, grad_codebook));
+}
+
 int viterbi_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
                  const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost, void* workspace,
                  size_t workspace_bytes, void* stream) {
@@ -435,26 +492,16 @@ int bcjr_soft_codeword_grad_codebook(const float* w, const float* codebook, int6
                                      int32_t k, float T, const int32_t* boundary_state, const float* grad_w_soft,
                                      float* grad_codebook, float* grad_w, float* w_soft, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-    if (!w || !codebook || !grad_w_soft || !grad_codebook) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
-    if (rc) return rc;
-    if ((rc = check_temp(T))) return rc;
-    const Plan p = make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L);
-    if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
-    GradArgs a{};
-    a.w = w;
-    a.cb = codebook;
-    a.g = grad_w_soft;
-    a.B = B;
-    a.n = (int)n;
-    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
-    a.two_over_T = (float)(2.0 / (double)T);
-    a.sigma = boundary_state;
-    a.grad = grad_w;
-    a.w_soft = w_soft;
-    a.ws = static_cast<unsigned char*>(workspace);
-    a.slot_bytes = p.slot_bytes;
-    return hip_status(launch_grad_codebook(L, a, p.grid, static_cast<hipStream_t>(stream), grad_codebook));
+    return grad_codebook_impl(w, codebook, B, n, L, k, 1, T, boundary_state, grad_w_soft, grad_codebook, grad_w,
+                              w_soft, workspace, workspace_bytes, stream);
+}
+
+int bcjr_soft_codeword_grad_codebook_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                       int32_t k, int32_t V, float T, const int32_t* boundary_state,
+                                       const float* grad_w_soft, float* grad_codebook, float* grad_w, float* w_soft,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    return grad_codebook_impl(w, codebook, B, n, L, k, V, T, boundary_state, grad_w_soft, grad_codebook, grad_w,
+                              w_soft, workspace, workspace_bytes, stream);
 }
 
 int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,

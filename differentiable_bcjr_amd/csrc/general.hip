@@ -33,6 +33,8 @@
 // L is a run-time argument: one sequence per workgroup of 2^L / SPT threads, persistent over the batch.  k, V and SPT
 // are compile-time.  The forward tapes, normalisers and per-wave partial sums use the workspace layout of the k = 2
 // kernels.
+#include <type_traits>
+
 #include "kernel_args.hpp"
 #include "trellis.hpp"
 
@@ -82,6 +84,20 @@ __device__ __forceinline__ void ld_floats(rsrc_t r, uint32_t off, float* out) {
     } else {
         static_assert(N == 1, "1, 2 or a multiple of 4 floats");
         out[0] = buf_ld(r, off, 0);
+    }
+}
+
+// N floats to a raw buffer at a byte offset (the whole offset in the VGPR: see buf_st4).
+template <int N>
+__device__ __forceinline__ void st_row(const float* v, rsrc_t r, uint32_t off) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) buf_st4(make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]), r, off + 4u * i, 0u);
+    } else if constexpr (N == 2) {
+        buf_st2(make_float2(v[0], v[1]), r, off, 0u);
+    } else {
+        static_assert(N == 1, "1, 2 or a multiple of 4 floats");
+        buf_st(v[0], r, off, 0u);
     }
 }
 
@@ -828,15 +844,21 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 }
 
 // ------------------------------------------------------------------------------------------------------------------
-// exact gradient with respect to the weights (and the soft codeword)
+// exact gradient with respect to the weights (and the soft codeword; with GC, the codebook values too)
 //
 // As in the k = 2 gradient kernel: grad_{u,v} = (2/T) Cov_p(c(s_u, v), F) with F = sum_t <g_t, c(s_t) - w_t>, and
 // E[F | s_t] is split into a forward expectation message Q (weighted by the forward softmax over a) and a backward one
 // P (weighted by the backward softmax over i).  Both are re-centred every step by a constant the covariance ignores:
 // Q by its value at the most likely group, P by kappa_{t+1} = <g_{t+1}, w_soft_{t+1} - w_{t+1}>.  The constants are
 // carried as one per-step offset, so E[F | s] - E[F] is formed from small numbers only.
+//
+// GC adds the codebook gradient, as in the k = 2 kernel.  For every state s, component v and step t of the backward
+// pass it adds p_t(s) [g_{t,v} + (2/T) (w_{t,v} - c(s, v)) (E[F | s_t = s] - E[F])] to a per-slot float accumulator
+// [2^L][V] at the end of the slot.  Each thread reads and writes only its own states' entries.  Each step's posterior
+// is normalised by the previous step's exact total, with the running normaliser sums in double.  A later reduction
+// sums the slots in a fixed order.
 
-template <int K, int V, int SPT, int LT>
+template <int K, int V, int SPT, int LT, bool GC>
 __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     using Gm = GG<K, V, SPT>;
     constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TA = Gm::TA, TI = Gm::TI, NA = Gm::NA,
@@ -871,6 +893,22 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
     float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
     own.fwd_next(-1, cnx);
+    // the codebook-gradient accumulator of the slot: c(s, v) at acc_base + 4 (s V + v), so a tile row's entries are
+    // contiguous like its codebook values
+    const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * NS * 4) : 0u);
+    using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
+    const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
+    if constexpr (GC) {
+        float z[ROW];
+#pragma unroll
+        for (int x = 0; x < ROW; ++x) z[x] = 0.f;
+#pragma unroll
+        for (int m = 0; m < BPT; ++m)
+#pragma unroll
+            for (int a = 0; a < P; ++a)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) st_row<ROW>(z, tape, acc_base + own.row_bytes(m, a, q));
+    }
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
         const float* wb = args.w + b * (int64_t)n * V;
@@ -1004,6 +1042,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         }
         // rz = log2 Z - A_n, and E[F], which centres the covariance of the backward pass
         float rz, EF;
+        RT rzr;   // rz in the precision of the running sums
         if (!has_sigma) {
             float z0 = 0.f, z1 = 0.f;
 #pragma unroll
@@ -1033,6 +1072,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 }
             }
             rz = N + lg2(z0);
+            rzr = (RT)N + (RT)lg2(z0);
             EF = z1 / z0 + Kq;   // the final Q^_n carries the offset K_{n-1}
             __syncthreads();
         } else {
@@ -1048,11 +1088,14 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 EF = fmaf(gb[(n - 1) * V + v] * inv_scale, d, EF);
             }
             rz = (r < 0.5f * kNeg) ? kNeg : x - N_last;
+            rzr = (r < 0.5f * kNeg) ? (RT)kNeg : (RT)x - (RT)N_last;
         }
         const bool valid = rz > 0.5f * kNeg;
 
         // ------------------------------------------------------------------ backward: B~ and P, covariance
-        float Nb = 0.f, C_ = 0.f, D = 0.f;
+        float Nb = 0.f;
+        RT C_ = 0, D = 0;
+        float lam = 1.f;  // 1 / (posterior total of the previous step), GC only
         float kb = 0.f;   // kappa_{t+1}, subtracted from the P inputs
         float H = 0.f;    // sum of the kappas of the steps after t
         int t = n - 1;
@@ -1091,9 +1134,22 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             if (tau == 0) {
 #pragma unroll
                 for (int v = 0; v < V; ++v) {
-                    args.grad[(b * n + n - 1) * V + v] = valid ? 0.f : __builtin_nanf("");
+                    if (!GC || args.grad) args.grad[(b * n + n - 1) * V + v] = valid ? 0.f : __builtin_nanf("");
                     if (args.w_soft)
                         args.w_soft[(b * n + n - 1) * V + v] = valid ? args.cb[sig * V + v] : __builtin_nanf("");
+                }
+            }
+            if constexpr (GC) {
+                // p_{n-1} is the indicator of sigma and E[F | s_{n-1}] = E[F]: dL/dc(sigma, v) += g_{n-1,v}, added by
+                // the thread that owns sigma (it alone touches that entry)
+                const uint32_t js = (sig >> K) & (uint32_t)(J - 1), is = sig & (uint32_t)(P - 1);
+                const uint32_t owner = C == 1 ? js % (uint32_t)TPS : js * C + is / I;
+                if (valid && (uint32_t)tau == owner) {
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        const uint32_t o = acc_base + 4u * (sig * V + v);
+                        buf_st(buf_ld(tape, 0u, o) + gb[(n - 1) * V + v], tape, 0u, o);
+                    }
                 }
             }
             D = N_last;
@@ -1105,6 +1161,15 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         lds_barrier();
 
         const int t_out = t;
+        // the accumulator row of the next unit (GC), one unit ahead, wrapping to the next step's first
+        float acn[GC ? ROW : 1];
+        auto acc_next = [&](int idx, float* nx) {
+            if constexpr (GC) {
+                const int x = (idx + 1) % (BPT * P * NI);
+                ld_floats<ROW>(tape, acc_base + own.row_bytes(x / (NI * P), (x / NI) % P, x % NI), nx);
+            }
+        };
+        acc_next(-1, acn);
         float N_nx = 0.f, K_nx = 0.f, rt_nx = 0.f, qt_nx = 0.f;
         if (t >= 0) {
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
@@ -1125,19 +1190,20 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         pin[m][TI * q + ii] = mq[u] - kb;
                     }
             lds_barrier();
-            float wt[V], gt[V];
+            float wt[V], gt[V], gnat[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 wt[v] = wb[t * V + v] * scale;
-                gt[v] = gb[t * V + v] * inv_scale;
+                gnat[v] = gb[t * V + v];
+                gt[v] = gnat[v] * inv_scale;
             }
             const float Nt = uniform_f(N_nx), Kt = uniform_f(K_nx);
             if (t > 0) {
                 N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * (t - 1));
                 K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * (t - 1));
             }
-            D += Nt;
-            const float ref = (rz + D) - C_;
+            D += (RT)Nt;
+            const float ref = (float)(((RT)rzr + D) - C_);
             // E[F | s_t = s] - E[F] = Q^_t(s >> k) + cst + <g_t, c(s) - w_t> + P''_t(s & (G-1)), cst per step
             const float cst = (Kt - EF) + H;
             float lmax = -3.0e38f, S0 = 0.f, S2 = 0.f, S1[V], S3[V];
@@ -1185,7 +1251,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                         for (int ii = 1; ii < TI; ++ii) cm = fmaxf(cm, y[ii]);
                         if constexpr (C > 1) cm = quad_max(cm);
-                        float cs = 0.f, ez = 0.f, er = 0.f, ed[V], edr[V];
+                        float cs = 0.f, ez = 0.f, er = 0.f, ed[V], edr[V], e[TI], r[TI];
 #pragma unroll
                         for (int v = 0; v < V; ++v) {
                             ed[v] = 0.f;
@@ -1193,21 +1259,36 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         }
 #pragma unroll
                         for (int ii = 0; ii < TI; ++ii) {
-                            const float e = ex2(y[ii] - cm);
+                            e[ii] = ex2(y[ii] - cm);
                             // E[F | s] - E[F], formed before any product: its parts nearly cancel at the likely
                             // states, and multiplying them separately would keep their rounding
-                            const float r = z[ii] + qt;
-                            cs += e;
-                            ez = fmaf(e, z[ii], ez);
-                            er = fmaf(e, r, er);
+                            r[ii] = z[ii] + qt;
+                            cs += e[ii];
+                            ez = fmaf(e[ii], z[ii], ez);
+                            er = fmaf(e[ii], r[ii], er);
 #pragma unroll
                             for (int v = 0; v < V; ++v) {
-                                const float edv = e * d[ii][v];
+                                const float edv = e[ii] * d[ii][v];
                                 ed[v] += edv;
-                                edr[v] = fmaf(edv, r, edr[v]);
+                                edr[v] = fmaf(edv, r[ii], edr[v]);
                             }
                         }
                         const float f = ex2((cm + rt) - ref);
+                        if constexpr (GC) {
+                            // p_t(s) [g_{t,v} + (2/T)(w_{t,v} - c(s, v)) (E[F | s] - E[F])] with p_t(s) = lam f e
+                            float ac[ROW];
+#pragma unroll
+                            for (int x = 0; x < ROW; ++x) ac[x] = acn[x];
+                            acc_next((m * P + a) * NI + q, acn);
+                            const float fa = lam * f, ka = fa * kap;
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii)
+#pragma unroll
+                                for (int v = 0; v < V; ++v)
+                                    ac[ii * V + v] = fmaf(fa * gnat[v], e[ii],
+                                                          fmaf(-ka, e[ii] * d[ii][v] * r[ii], ac[ii * V + v]));
+                            st_row<ROW>(ac, tape, acc_base + own.row_bytes(m, a, q));
+                        }
                         S0 = fmaf(f, cs, S0);
                         S2 = fmaf(f, er, S2);
 #pragma unroll
@@ -1263,16 +1344,20 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 const float s0b = row16_sum(qs < WPS ? reds[t & 1][qs][0] : 0.f);
 #pragma unroll
                 for (int v = 0; v < V; ++v) m1[v] = row16_sum(qs < WPS ? reds[t & 1][qs][1 + v] : 0.f) * rcp(s0b);
+                if constexpr (GC) lam = uniform_f(rcp(s0b));
             } else {
 #pragma unroll
                 for (int v = 0; v < V; ++v) m1[v] = Sv[1 + v] * (1.0f / Sv[0]);
+                if constexpr (GC) lam = uniform_f(1.0f / Sv[0]);
                 if (tau == 0) {
                     const float i0 = 1.0f / Sv[0];
                     const float m2 = Sv[1 + V] * i0;
 #pragma unroll
                     for (int v = 0; v < V; ++v) {
                         const float cov = fmaf(-m1[v], m2, Sv[2 + V + v] * i0);
-                        args.grad[(b * n + t) * V + v] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                        if (!GC || args.grad)
+                            args.grad[(b * n + t) * V + v] = valid ? args.two_over_T * cov * inv_scale
+                                                                   : __builtin_nanf("");
                         if (args.w_soft)
                             args.w_soft[(b * n + t) * V + v] = valid ? wb[t * V + v] + m1[v] * inv_scale
                                                                      : __builtin_nanf("");
@@ -1285,7 +1370,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             kb = uniform_f(kap);
             lmax = uniform_f(lmax);
             H += kb;
-            C_ += Nb;
+            C_ += (RT)Nb;
             Nb = lmax;
         }
         if (WPS > 1) {
@@ -1305,10 +1390,25 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 for (int v = 0; v < V; ++v) {
                     const float m1 = Sv[1 + v] * i0;
                     const float cov = fmaf(-m1, m2, Sv[2 + V + v] * i0);
-                    args.grad[(b * n + tt) * V + v] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
+                    if (!GC || args.grad)
+                        args.grad[(b * n + tt) * V + v] = valid ? args.two_over_T * cov * inv_scale
+                                                                : __builtin_nanf("");
                     if (args.w_soft)
                         args.w_soft[(b * n + tt) * V + v] = valid ? wb[tt * V + v] + m1 * inv_scale : __builtin_nanf("");
                 }
+            }
+        }
+        if constexpr (GC) {
+            if (!valid) {   // no admissible path: the loss, hence its gradient, is undefined
+                float x[ROW];
+#pragma unroll
+                for (int i = 0; i < ROW; ++i) x[i] = __builtin_nanf("");
+#pragma unroll
+                for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                    for (int a = 0; a < P; ++a)
+#pragma unroll
+                        for (int q = 0; q < NI; ++q) st_row<ROW>(x, tape, acc_base + own.row_bytes(m, a, q));
             }
         }
         __syncthreads();   // the next sequence reuses the tape and LDS
@@ -1326,7 +1426,8 @@ template <int K, int V, int SPT, int LT>
 GenKernel pick(int op) {
     switch (op) {
         case 0: return gen_soft_kernel<K, V, SPT, LT>;
-        case 1: return gen_grad_kernel<K, V, SPT, LT>;
+        case 1: return gen_grad_kernel<K, V, SPT, LT, false>;
+        case 3: return gen_grad_kernel<K, V, SPT, LT, true>;
         default: return gen_viterbi_kernel<K, V, SPT, LT>;
     }
 }
@@ -1363,7 +1464,8 @@ GenKernel pick_spt(int op, int k, int L) {
 
 }  // namespace
 
-// op: 0 soft, 1 gradient, 2 Viterbi.  The caller has checked 1 <= k <= 4, 2k <= L <= 16, V in {1, 2}.
+// op: 0 soft, 1 gradient, 2 Viterbi, 3 gradient with the codebook accumulator (summed afterwards by
+// launch_codebook_reduce).  The caller has checked 1 <= k <= 4, 2k <= L <= 16, V in {1, 2}.
 hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
                           hipStream_t st) {
     const GenKernel f = V == 1 ? pick_spt<1>(op, k, a.L) : pick_spt<2>(op, k, a.L);

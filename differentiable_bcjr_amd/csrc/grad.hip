@@ -628,6 +628,14 @@ hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st) {
     return launch_grad_any<false>(L, a, grid, st);
 }
 
+// dL/dc from `count` per-slot accumulators of S floats each, `stride` bytes apart starting at ws + acc_off.
+hipError_t launch_codebook_reduce(const unsigned char* ws, size_t stride, uint32_t acc_off, int count, int S,
+                                  float* out, hipStream_t st) {
+    const int W = S < 64 ? S : 64;
+    hipLaunchKernelGGL(codebook_reduce_kernel, dim3(S / W), dim3(256), 0, st, ws, stride, acc_off, count, S, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook) {
     const hipError_t e = launch_grad_any<true>(L, a, grid, st);
     if (e != hipSuccess) return e;

@@ -31,9 +31,10 @@
  *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
  *     Calls on different streams need different workspaces.
  *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 2k <= L <= 16, and
- *       soft codeword, gradient, Viterbi: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs kernels tuned for
- *       it, every other (k, V) one kernel family written for any k; the gradient with k = 1 needs L <= 15);
- *       codebook gradient and the tail-biting entry points: k == 2 and V = 1.
+ *       soft codeword, gradient, codebook gradient, Viterbi: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs
+ *       kernels tuned for it, every other (k, V) one kernel family written for any k; both gradients with k = 1
+ *       need L <= 15);
+ *       the tail-biting entry points: k == 2 and V = 1.
  *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
  *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
  *     into that sequence's outputs.
@@ -53,8 +54,8 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; k != 2 or V != 1 for the codebook
-                                  gradient and the tail-biting entry points; the gradient with k = 1 and L = 16;
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; k != 2 or V != 1 for the
+                                  tail-biting entry points; either gradient with k = 1 and L = 16;
                                   exact tail-biting (choice of sigma, soft codeword or gradient under the
                                   tail-biting measure) with L > 10; unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
@@ -182,7 +183,8 @@ int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_
  * and the Viterbi metric adds the components' squares in index order, e = fl(d_0 d_0), e = fl(e + fl(d_v d_v)),
  * before adding the predecessor's metric, again without fused multiply-add.  V = 1 is the scalar trellis above, and
  * the entry points without _v are these with V = 1.  V must be 1 or 2 (BCJR_ERR_SHAPE below 1, BCJR_ERR_UNSUPPORTED
- * above 2).  Workspace: bcjr_workspace_bytes_v with the matching BCJR_OP_SOFT, BCJR_OP_GRAD or BCJR_OP_VITERBI.
+ * above 2).  Workspace: bcjr_workspace_bytes_v with the matching BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK
+ * or BCJR_OP_VITERBI.
  */
 int bcjr_soft_codeword_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
                          int32_t V, float T, const int32_t* boundary_state, float* w_soft, float* log_z,
@@ -193,6 +195,15 @@ int bcjr_soft_codeword_grad_v(const float* w, const float* codebook, int64_t B, 
 int viterbi_hard_code_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
                         int32_t V, const int32_t* boundary_state, int32_t* states, float* w_hard, float* cost,
                         void* workspace, size_t workspace_bytes, void* stream);
+/* The codebook gradient with V weights per step, per component:
+ *   grad_codebook[s, v] = sum_b sum_u p(s_u = s) ( grad_w_soft[b, u V + v]
+ *                                                  + (2 / T) (w[b, u V + v] - codebook[s, v]) (E[F_b | s_u = s] - E[F_b]) ),
+ * F_b = sum_t sum_v grad_w_soft[b, t V + v] codebook[s_t, v]; grad_codebook is float32 [2^L, V].  Otherwise as
+ * bcjr_soft_codeword_grad_codebook.  Workspace: bcjr_workspace_bytes_v with BCJR_OP_GRAD_CODEBOOK. */
+int bcjr_soft_codeword_grad_codebook_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                       int32_t k, int32_t V, float T, const int32_t* boundary_state,
+                                       const float* grad_w_soft, float* grad_codebook, float* grad_w, float* w_soft,
+                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace the entry point `op` (one of the BCJR_OP_* values above) needs for
@@ -201,7 +212,8 @@ int viterbi_hard_code_v(const float* w, const float* codebook, int64_t B, int64_
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);
 
 /* The same for V weights per step: bcjr_workspace_bytes(op, ...) when V = 1; for V = 2 only the soft codeword, the
- * gradient and Viterbi (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_VITERBI) have a size, every other op gives 0. */
+ * two gradients and Viterbi (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK, BCJR_OP_VITERBI) have a size, every
+ * other op gives 0. */
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 
 /* Static, NUL-terminated description of a status code. */

@@ -25,7 +25,7 @@ def test_header_declares_every_op():
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
                  "viterbi_hard_code", "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting",
                  "bcjr_soft_codeword_grad_tail_biting", "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v",
-                 "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
+                 "bcjr_soft_codeword_grad_codebook_v", "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -100,7 +100,7 @@ def _gen_bytes(op, B, n, L, k, V):
     wps = tps // 64 if tps >= 64 else 1
     G = S >> k
     lds_cap, lds_static = 160 * 1024, 2048
-    if op == abi.BCJR_OP_GRAD:
+    if op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
         lds = 2 * G * 4
     else:
         lds = 2 * G * 4 if 2 * G * 4 + lds_static <= lds_cap else G * 4
@@ -113,6 +113,8 @@ def _gen_bytes(op, B, n, L, k, V):
         slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0)
     elif op == abi.BCJR_OP_GRAD:
         slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
+    elif op == abi.BCJR_OP_GRAD_CODEBOOK:   # + one float accumulator per state and component
+        slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0) + _a256(S * V * 4)
     else:
         slot = _a256(2 * n * tps * 4)
     return grid * slot
@@ -122,7 +124,7 @@ def _gen_bytes(op, B, n, L, k, V):
 @pytest.mark.parametrize("V", [1, 2])
 @pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (4096, 256), (1000, 7)])
 def test_general_trellis_workspace_formula(L, k, V, B, n):
-    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK, abi.BCJR_OP_VITERBI):
         if (k, V) == (2, 1):
             continue
         assert abi.bcjr_workspace_bytes_v(op, B, n, L, k, V) == _gen_bytes(op, B, n, L, k, V)
@@ -141,8 +143,9 @@ def test_unsupported_trellis_has_no_workspace():
     assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 3) == 0             # V > 2
     assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 0) == 0             # V < 1
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 16, 1) == 0  # R and Q exceed LDS at k = 1, L = 16
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 16, 1) == 0
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 15, 1) > 0
-    for op in (3, 4, 5, 6, 7):                                           # k = 2, V = 1 only
+    for op in (4, 5, 6, 7):                                              # tail-biting: k = 2, V = 1 only
         assert abi.bcjr_workspace_bytes(op, 4, 8, 8, 1) == 0
         assert abi.bcjr_workspace_bytes(op, 4, 8, 9, 3) == 0
         assert abi.bcjr_workspace_bytes_v(op, 4, 8, 8, 2, 2) == 0
@@ -299,6 +302,13 @@ def _grad_v(**kw):
     return abi.bcjr_soft_codeword_grad_v(*a.values())
 
 
+def _gc_v(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, V=2, T=0.5, boundary_state=None, grad_w_soft=FAKE,
+             grad_codebook=FAKE, grad_w=None, w_soft=None, workspace=FAKE, workspace_bytes=0, stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_grad_codebook_v(*a.values())
+
+
 def _vit_v(**kw):
     a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, V=2, boundary_state=None, states=FAKE, w_hard=None,
              cost=None, workspace=FAKE, workspace_bytes=0, stream=None)
@@ -310,10 +320,10 @@ def test_unsupported_trellis_rejected():
     assert _soft(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
     assert _grad(L=12, k=6) == abi.BCJR_ERR_UNSUPPORTED
     assert _vit(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
-    assert _gc(k=1) == abi.BCJR_ERR_UNSUPPORTED
-    assert _gc(L=9, k=3) == abi.BCJR_ERR_UNSUPPORTED
+    assert _gc(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
     assert _grad(L=16, k=1) == abi.BCJR_ERR_UNSUPPORTED                 # R and Q exceed LDS
-    for fn in (_soft_v, _grad_v, _vit_v):
+    assert _gc(L=16, k=1) == abi.BCJR_ERR_UNSUPPORTED
+    for fn in (_soft_v, _grad_v, _gc_v, _vit_v):
         assert fn(V=3) == abi.BCJR_ERR_UNSUPPORTED
         assert fn(V=0) == abi.BCJR_ERR_SHAPE
         assert fn(V=-1) == abi.BCJR_ERR_SHAPE
@@ -325,7 +335,9 @@ def test_general_trellis_reaches_the_workspace_check():
         assert _soft(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
         assert _grad(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
         assert _vit(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
+        assert _gc(L=L, k=k) == abi.BCJR_ERR_WORKSPACE
         for V in (1, 2):
+            assert _gc_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
             assert _soft_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
             assert _grad_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
             assert _vit_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
@@ -336,6 +348,7 @@ def test_general_trellis_reaches_the_workspace_check():
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=4097), dict(L=3), dict(L=17), dict(k=0), dict(L=5, k=3)])
 def test_bad_shapes_rejected_v(kw):
+    assert _gc_v(**kw) == abi.BCJR_ERR_SHAPE
     assert _soft_v(**kw) == abi.BCJR_ERR_SHAPE
     assert _grad_v(**kw) == abi.BCJR_ERR_SHAPE
     assert _vit_v(**kw) == abi.BCJR_ERR_SHAPE
@@ -404,9 +417,9 @@ def test_largest_shape_keeps_workspace_offsets_in_32_bits():
             per_block = abi.bcjr_workspace_bytes(op, SPB, 4096, L, 2)
             assert 0 < per_block < 2 ** 31
     # the general trellis: one sequence per block
-    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI):
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK, abi.BCJR_OP_VITERBI):
         for L, k in ((16, 1), (15, 1), (16, 3), (16, 4), (8, 1)):
             for V in (1, 2):
                 per_block = abi.bcjr_workspace_bytes_v(op, 1, 4096, L, k, V)
                 assert per_block < 2 ** 31
-                assert per_block > 0 or (op == abi.BCJR_OP_GRAD and (L, k) == (16, 1))
+                assert per_block > 0 or (op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK) and (L, k) == (16, 1))

@@ -260,3 +260,96 @@ def test_trellis_variant_workload_rows(oracle_mod, dev, name):
     np.testing.assert_array_equal(st[rows], rst)
     np.testing.assert_array_equal(wh[rows].view(np.uint32), rwh.view(np.uint32))
     np.testing.assert_array_equal(cost[rows].view(np.uint32), rcost.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------ codebook gradient (row f1)
+# dL/dc [2^L] or [2^L, V], summed over the batch, compared as a vector like the k = 2 codebook gradient: normwise
+# 1e-5 free and 5e-5 sigma, 5e-5 of the largest entry elementwise, scaled as the other bars here.
+
+GC_CASES = [c for c in CASES if c[:2] != (16, 1)]
+GC_IDS = [i for c, i in zip(CASES, IDS) if c[:2] != (16, 1)]
+
+
+def _max_err(x, ref):
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-300))
+
+
+@pytest.mark.parametrize("L,k,V,B,n", GC_CASES, ids=GC_IDS)
+@pytest.mark.parametrize("sigma", [False, True])
+def test_codebook_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
+    if sigma:
+        n = _sigma_n(L, k, n)
+    w, c, g, s = _vin(L, V, B, n, 7700 + 31 * L + 7 * k + V + n, sigma)
+    f = _scale(k, V)
+    for T in [1.0, 0.1, 0.05]:
+        gc, gw, ws = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev),
+                                                     return_w_soft=True)
+        rgc, rgw, rws = oracle_mod.grad_codebook(w, c, g, L, k, T, sigma=s)
+        assert gc.shape == c.shape
+        en, em = norm_err(gc.cpu().numpy(), rgc), _max_err(gc.cpu().numpy(), rgc)
+        eg = grad_err(gw.cpu().numpy(), rgw, g, c, T)
+        print(f"codebook grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {en:.2e} normwise, {em:.2e} of max; "
+              f"weights' grad {eg:.2e}", flush=True)
+        assert en <= (5e-5 if sigma else 1e-5) * f and em <= 5e-5 * f
+        assert eg <= vgrad_tol(T, sigma, k, V) and vgrad_norm_ok(gw.cpu().numpy(), rgw, T, sigma, k, V)
+        assert rel_err(ws.cpu().numpy(), rws) <= vsoft_tol(T, sigma, k, V)
+
+
+@pytest.mark.parametrize("L,k,V", [(9, 3, 2), (12, 1, 1), (16, 4, 2)])
+def test_codebook_grad_translation_identity(dev, L, k, V):
+    """Shifting component v of every codebook entry and of every weight by the same amount leaves every energy
+    unchanged and shifts that component of the soft codeword by it, so per component
+    sum_s dL/dc(s, v) + sum_u dL/dw(u, v) = sum_t g(t, v).  The codebook-only call (no dL/dw requested) agrees with
+    the full one bit for bit."""
+    B, n, T = 40, 24, 0.1
+    w, c, g, _ = _vin(L, V, B, n, 7800 + L)
+    wt, ct, gt = _t(w, dev), _t(c, dev), _t(g, dev)
+    gc, gw = dba.soft_codeword_grad_codebook(wt, ct, gt, L, k, T)
+    only = dba.soft_codeword_grad_codebook(wt, ct, gt, L, k, T, return_grad_w=False)
+    assert torch.equal(only, gc)
+    gc2 = gc.double().cpu().numpy().reshape(1 << L, V)
+    gw2 = gw.double().cpu().numpy().reshape(B, n, V)
+    g2 = g.astype(np.float64).reshape(B, n, V)
+    lhs = gc2.sum(axis=0) + gw2.sum(axis=(0, 1))
+    rhs = g2.sum(axis=(0, 1))
+    scale_ = np.abs(gc2).sum(axis=0) + np.abs(gw2).sum(axis=(0, 1)) + np.abs(g2).sum(axis=(0, 1))
+    assert np.all(np.abs(lhs - rhs) <= 1e-6 * scale_)
+
+
+@pytest.mark.parametrize("L,k,V", [(8, 1, 2), (12, 3, 1)])
+def test_codebook_grad_nan_when_no_path(dev, L, k, V):
+    n = max(1, L // k - 2)
+    w, c, g, s = _vin(L, V, 5, n, 7900 + L, sigma=True)
+    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, 0.5, _t(s, dev),
+                                         return_grad_w=False)
+    assert torch.isnan(gc).all()
+
+
+def test_soft_quantize_trains_the_codebook_at_other_bit_rates(oracle_mod, dev):
+    """Autograd through soft_quantize with a trainable [2^L, 2] codebook at k = 3: both gradients match the oracle."""
+    L, k, V, B, n, T = 9, 3, 2, 6, 14, 0.2
+    w, c, g, _ = _vin(L, V, B, n, 8000)
+    wt = _t(w, dev).requires_grad_(True)
+    ct = _t(c, dev).requires_grad_(True)
+    (dba.soft_quantize(wt, ct, L, k, T) * _t(g, dev)).sum().backward()
+    rgc, rgw, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
+    assert norm_err(ct.grad.cpu().numpy(), rgc) <= 1e-5 * _scale(k, V)
+    assert norm_err(wt.grad.cpu().numpy(), rgw) <= 1e-5 * _scale(k, V)
+
+
+@pytest.mark.parametrize("name", ["k3", "k4v2"])
+def test_codebook_grad_variant_workload_rows(oracle_mod, dev, name):
+    """The codebook gradient of three sampled rows of the 1024x1024 variant workloads, as one batch, against the
+    oracle on the same rows."""
+    wl = workloads.TRELLIS_VARIANTS[name]
+    c = wl.codebook()
+    rows = wl.sample_rows(3)
+    w, g = wl.weights()[rows], wl.upstream_grad()[rows]
+    T = wl.temps[0]
+    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), wl.L, wl.k, T,
+                                         return_grad_w=False).cpu().numpy()
+    rgc, _, _ = oracle_mod.grad_codebook(w, c, g, wl.L, wl.k, T)
+    en = norm_err(gc, rgc)
+    print(f"{wl.name} codebook grad, 3 rows: {en:.2e} normwise, {_max_err(gc, rgc):.2e} of max", flush=True)
+    assert en <= 1e-5 * _scale(wl.k, wl.V)
