@@ -216,7 +216,7 @@ def time_variant(vw, T, K, dev, stream, check):
         torch.cuda.synchronize()
         ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
         units = B * steps * S
-        ops[name] = {"kernel": f"gen_{'grad' if name == 'grad' else name}_kernel<{k}, {V}, 64, 16>",
+        ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{', false' if name == 'grad' else ''}>",
                      "ms": round(ms, 4), "state_updates_per_s": DIRECTIONS[name] * units / (ms * 1e-3),
                      "weights_per_s": B * vw.n / (ms * 1e-3),
                      "roofline": {"bound": "alu", "achieved": round(slots[name] * units / (ms * 1e-3) / 1e12, 3),

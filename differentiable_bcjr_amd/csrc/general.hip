@@ -218,6 +218,17 @@ struct Owner {
     __device__ __forceinline__ uint32_t row_bytes(int m, int a, int q) const {
         return 4u * (uint32_t)V * state(m, a, q, 0);
     }
+    // Position of group u in a tape row (G groups).  It is the identity, except where a thread owns several tiles of
+    // one block's groups (k = 3).  There the row is tile-major, tile 0 of every block first and then tile 1, so each
+    // 16-byte store of a step is contiguous across lanes rather than half of every 32-byte stride.
+    __device__ __forceinline__ uint32_t tpos(uint32_t u, uint32_t G) const {
+        if constexpr (NI > 1) {
+            static_assert(TI == 4 && (P / 4) % NI == 0, "tile index = (u >> 2) mod NI");
+            return ((u >> 2) & (uint32_t)(NI - 1)) * (G / NI) + (u >> K) * TI + (u & (uint32_t)(TI - 1));
+        } else {
+            return u;
+        }
+    }
 
     __device__ __forceinline__ void init(const float* cb, int L_, int TPS_) {
         L = L_;
@@ -314,6 +325,16 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
     const uint32_t nrm_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
     const uint32_t part_base = nrm_base + (uint32_t)align256((size_t)n * 4);
     const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
+    // tape offset of backward group j(m) + J a: a lane part (VGPR) and a uniform part, or all of it in the VGPR when
+    // the row is tile-major
+    auto grp_voff = [&](int m, int a) -> uint32_t {
+        if constexpr (NI > 1) return 4u * own.tpos((uint32_t)(own.j(m) + J * a), (uint32_t)G);
+        else return v_j0;
+    };
+    auto grp_soff = [&](int m, int a) -> uint32_t {
+        if constexpr (NI > 1) return 0u;
+        else return 4u * (uint32_t)(own.j(m) - own.j(0) + J * a);
+    };
     float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
     own.fwd_next(-1, cnx);
 
@@ -332,7 +353,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                 for (int ii = 0; ii < TI; ++ii)
                     r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
-                st_floats<TI>(r, msg0, u0, tape, 4u * u0, 0u);
+                st_floats<TI>(r, msg0, u0, tape, 4u * own.tpos(u0, G), 0u);
             }
         lds_barrier();
 
@@ -406,7 +427,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                         lmax = run_max(lmax, o[ii]);
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(o, mn, u0, tape, 4u * u0, (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(o, mn, u0, tape, 4u * own.tpos(u0, G), (uint32_t)(t + 1) * row_bytes);
                 }
             if (tau == 0) buf_st(N, tape, 0u, nrm_base + 4u * t);
             lmax = gseq_max(lmax, SEG);
@@ -440,7 +461,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             __syncthreads();
         } else {
             __syncthreads();   // the tape rows of the forward pass, written by other threads
-            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
+            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
             float x = r;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -502,7 +523,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
             for (int v = 0; v < V; ++v) w_nx[v] = wb[t * V + v];
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
-            rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes);
+            rq_nx = buf_ld_nt(tape, grp_voff(0, 0), (uint32_t)t * row_bytes + grp_soff(0, 0));
         }
         for (; t >= 0; --t) {
             const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
@@ -538,10 +559,10 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     const float rq = rq_nx;
                     if (m * P + a + 1 < BPT * P) {
                         const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
-                        rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes +
-                                                          4u * (uint32_t)(own.j(m2) - own.j(0) + J * a2));
+                        rq_nx = buf_ld_nt(tape, grp_voff(m2, a2), (uint32_t)t * row_bytes + grp_soff(m2, a2));
                     } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
-                        rq_nx = buf_ld_nt(tape, v_j0, (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes);
+                        rq_nx = buf_ld_nt(tape, grp_voff(0, 0),
+                                          (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes + grp_soff(0, 0));
                     }
                     float mx = 0.f, s = 0.f;
 #pragma unroll
@@ -891,6 +912,16 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
     const uint32_t part_base = kq_base + (uint32_t)align256((size_t)n * 4);
     const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
+    // tape offset of backward group j(m) + J a: a lane part (VGPR) and a uniform part, or all of it in the VGPR when
+    // the row is tile-major
+    auto grp_voff = [&](int m, int a) -> uint32_t {
+        if constexpr (NI > 1) return 4u * own.tpos((uint32_t)(own.j(m) + J * a), (uint32_t)G);
+        else return v_j0;
+    };
+    auto grp_soff = [&](int m, int a) -> uint32_t {
+        if constexpr (NI > 1) return 0u;
+        else return 4u * (uint32_t)(own.j(m) - own.j(0) + J * a);
+    };
     float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
     own.fwd_next(-1, cnx);
     // the codebook-gradient accumulator of the slot: c(s, v) at acc_base + 4 (s V + v), so a tile row's entries are
@@ -928,8 +959,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
                     z[ii] = 0.f;
                 }
-                st_floats<TI>(r, mr, u0, tape, 4u * u0, 0u);
-                st_floats<TI>(z, mq, u0, tape, 4u * u0, q_base);
+                st_floats<TI>(r, mr, u0, tape, 4u * own.tpos(u0, G), 0u);
+                st_floats<TI>(z, mq, u0, tape, 4u * own.tpos(u0, G), q_base);
             }
         lds_barrier();
 
@@ -1016,8 +1047,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         lq = up ? qo[ii] : lq;
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(ro, mr, u0, tape, 4u * u0, (uint32_t)(t + 1) * row_bytes);
-                    st_floats<TI>(qo, mq, u0, tape, 4u * u0, q_base + (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(ro, mr, u0, tape, 4u * own.tpos(u0, G), (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(qo, mq, u0, tape, 4u * own.tpos(u0, G), q_base + (uint32_t)(t + 1) * row_bytes);
                 }
             gseq_argmax_payload(lmax, lq, SEG);
             if (WPS > 1 && lane == 0) {
@@ -1077,8 +1108,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             __syncthreads();
         } else {
             __syncthreads();   // R~_{n-1} and Q^_{n-1} are on the tape, written by other threads
-            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
-            const float qv = buf_ld_nt(tape, 0u, q_base + (uint32_t)(n - 1) * row_bytes + 4u * (sig >> K));
+            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
+            const float qv = buf_ld_nt(tape, 0u, q_base + (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
             float x = r;
             EF = qv + K_last;   // Q^_{n-1} carries the offset K_{n-2}
 #pragma unroll
@@ -1174,8 +1205,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         if (t >= 0) {
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
             K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * t);
-            rt_nx = buf_ld_nt(tape, v_j0, (uint32_t)t * row_bytes);
-            qt_nx = buf_ld_nt(tape, v_j0, q_base + (uint32_t)t * row_bytes);
+            rt_nx = buf_ld_nt(tape, grp_voff(0, 0), (uint32_t)t * row_bytes + grp_soff(0, 0));
+            qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + (uint32_t)t * row_bytes + grp_soff(0, 0));
         }
         for (; t >= 0; --t) {
             float bin[BPT][I], pin[BPT][I];
@@ -1222,13 +1253,13 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     const float qt = qt_nx + cst;
                     if (m * P + a + 1 < BPT * P) {
                         const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
-                        const uint32_t so = (uint32_t)t * row_bytes + 4u * (uint32_t)(own.j(m2) - own.j(0) + J * a2);
-                        rt_nx = buf_ld_nt(tape, v_j0, so);
-                        qt_nx = buf_ld_nt(tape, v_j0, q_base + so);
+                        const uint32_t so = (uint32_t)t * row_bytes + grp_soff(m2, a2);
+                        rt_nx = buf_ld_nt(tape, grp_voff(m2, a2), so);
+                        qt_nx = buf_ld_nt(tape, grp_voff(m2, a2), q_base + so);
                     } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
-                        const uint32_t so = (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes;
-                        rt_nx = buf_ld_nt(tape, v_j0, so);
-                        qt_nx = buf_ld_nt(tape, v_j0, q_base + so);
+                        const uint32_t so = (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes + grp_soff(0, 0);
+                        rt_nx = buf_ld_nt(tape, grp_voff(0, 0), so);
+                        qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + so);
                     }
                     float mx = 0.f, s = 0.f, sez = 0.f;
 #pragma unroll
