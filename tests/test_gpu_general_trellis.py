@@ -353,3 +353,66 @@ def test_codebook_grad_variant_workload_rows(oracle_mod, dev, name):
     en = norm_err(gc, rgc)
     print(f"{wl.name} codebook grad, 3 rows: {en:.2e} normwise, {_max_err(gc, rgc):.2e} of max", flush=True)
     assert en <= 1e-5 * _scale(wl.k, wl.V)
+
+
+# ------------------------------------------------------------------------------------ seeded random configurations
+
+
+def _random_cases(count=30, seed=4242):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    for i in range(count):
+        k = int(rng.integers(1, 5))
+        V = int(rng.integers(1, 3))
+        if (k, V) == (2, 1):
+            V = 2
+        L = int(rng.integers(max(4, 2 * k), 17))
+        sigma = bool(rng.integers(0, 2))
+        n = int(rng.integers(1, 40)) if L <= 12 else int(rng.integers(1, 8))
+        if sigma:
+            n = _sigma_n(L, k, n)
+        B = int(rng.integers(1, 30)) if L <= 12 else int(rng.integers(1, 4))
+        T = float(rng.choice([1.0, 0.3, 0.1]))
+        cases.append((i, L, k, V, B, n, sigma, T))
+    return cases
+
+
+def _ulp(a, rng):
+    """a moved by one float32 ulp, up or down at random, element by element."""
+    d = np.where(rng.integers(0, 2, a.shape) == 1, np.float32(np.inf), np.float32(-np.inf)).astype(np.float32)
+    return np.nextafter(a, d)
+
+
+def grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s, trials=4, seed=0):
+    """The exact gradient, and how far it moves (grad_err) when w and c move by one float32 ulp: the conditioning of
+    the problem at float32 resolution.  Rounding the inputs alone moves the answer that far, so no float32 evaluation
+    can be held closer.  Computed by the oracle alone."""
+    ref, _ = oracle_mod.grad(w, c, g, L, k, T, sigma=s)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    worst = 0.0
+    for _ in range(trials):
+        moved, _ = oracle_mod.grad(_ulp(w, rng), _ulp(c, rng), g, L, k, T, sigma=s)
+        worst = max(worst, grad_err(moved, ref, g, c, T))
+    return ref, worst
+
+
+@pytest.mark.parametrize("i,L,k,V,B,n,sigma,T", _random_cases())
+def test_general_trellis_random_configuration(oracle_mod, dev, i, L, k, V, B, n, sigma, T):
+    """Random shapes: the gradient bar is the larger of the derived one and the one-ulp sensitivity above, since some
+    draws are ill-conditioned at float32 resolution (e.g. L = 6, k = 2, V = 2, T = 0.1: one-ulp input moves shift the
+    exact gradient by 4.7e-5)."""
+    w, c, g, s = _vin(L, V, B, n, 9900 + i, sigma)
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev)).cpu().numpy()
+    rws, _ = oracle_mod.soft(w, c, L, k, T, sigma=s)
+    assert rel_err(ws, rws) <= vsoft_tol(T, sigma, k, V)
+    if (L, k) != (16, 1):
+        gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
+        rgr, sens = grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s)
+        e = grad_err(gr, rgr, g, c, T)
+        print(f"random {i}: L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: grad {e:.2e} "
+              f"(one-ulp sensitivity {sens:.2e})", flush=True)
+        assert e <= max(vgrad_tol(T, sigma, k, V), sens)
+    st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev)))
+    rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
