@@ -416,3 +416,31 @@ def test_general_trellis_random_configuration(oracle_mod, dev, i, L, k, V, B, n,
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
     np.testing.assert_array_equal(st, rst)
     np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
+
+
+@pytest.mark.parametrize("L,k,V,B,n", [(9, 3, 2, 4200, 3), (8, 1, 1, 4400, 4), (16, 4, 2, 300, 2)])
+def test_codebook_grad_several_sequences_per_slot(oracle_mod, dev, L, k, V, B, n):
+    """More sequences than the grid has workgroups: each slot's accumulator sums several sequences before the
+    reduction over slots."""
+    w, c, g, _ = _vin(L, V, B, n, 8100 + L + k)
+    T = 0.2
+    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, return_grad_w=False)
+    rgc, _, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
+    assert norm_err(gc.cpu().numpy(), rgc) <= 1e-5 * _scale(k, V)
+
+
+@pytest.mark.parametrize("L,k,V", [(10, 3, 2), (8, 1, 1), (12, 4, 1)])
+def test_longest_sequences(oracle_mod, dev, L, k, V):
+    """n = 4096 steps, the largest the boundary accepts (the workspace offsets of the longest tapes)."""
+    n, B, T = 4096, 2, 0.3
+    w, c, g, _ = _vin(L, V, B, n, 8200 + L)
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T).cpu().numpy()
+    rws, _ = oracle_mod.soft(w, c, L, k, T)
+    assert rel_err(ws, rws) <= 1e-5 * _scale(k, V)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
+    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
+    assert norm_err(gr, rgr) <= 1e-5 * _scale(k, V)
+    st, _, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
+    rst, _, rcost = oracle_mod.viterbi(w, c, L, k)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
