@@ -397,6 +397,40 @@ def main():
                          "per_unit": f"2 x {ALU_SLOTS['viterbi']} fp32 VALU slots per state-step (two decodes)",
                          "units_per_launch": B * n * S}}
 
+    if args.codebook_grad_steps > 0:
+        # the soft codeword in its checkpoint-and-recompute memory mode (the smallest workspace)
+        ck_bytes = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, 1)
+        ws_ck = torch.empty(ck_bytes, dtype=torch.uint8, device=dev)
+        out_ck = torch.empty_like(w)
+
+        def soft_ck():
+            check(abi.bcjr_soft_codeword(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, out_ck.data_ptr(), None,
+                                         ws_ck.data_ptr(), ck_bytes, sp), "soft checkpoint")
+
+        soft_ck()
+        torch.cuda.synchronize()
+        K4 = args.codebook_grad_steps
+        ev4 = [torch.cuda.Event(enable_timing=True) for _ in range(K4 + 1)]
+        ev4[0].record(stream)
+        for i in range(K4):
+            soft_ck()
+            ev4[i + 1].record(stream)
+        torch.cuda.synchronize()
+        ms4 = float(np.mean([ev4[i].elapsed_time(ev4[i + 1]) for i in range(K4)]))
+        slots4 = ALU_SLOTS["soft"] * B * n * S
+        next_rows["soft_checkpoint"] = {
+            "entry_point": "bcjr_soft_codeword with bcjr_workspace_bytes_min", "kernel": f"gen_soft_kernel<{k}, 1, 64, 16>",
+            "checkpoint_interval": int(np.ceil(np.sqrt(n))), "workspace_bytes": ck_bytes,
+            "full_tape_workspace_bytes": abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, k),
+            "calls": K4, "ms": round(ms4, 4), "state_updates_per_s": 2 * B * n * S / (ms4 * 1e-3),
+            "weights_per_s": B * n / (ms4 * 1e-3),
+            "roofline": {"bound": "alu", "achieved": round(slots4 / (ms4 * 1e-3) / 1e12, 3),
+                         "peak": round(PEAK_SLOTS_PER_S / 1e12, 3), "unit": "T VALU-slots/s",
+                         "frac": round(slots4 / (ms4 * 1e-3) / PEAK_SLOTS_PER_S, 4),
+                         "per_unit": f"{ALU_SLOTS['soft']} fp32 VALU slots per state-step (the method's work; the "
+                                     "recompute's extra forward pass is overhead)",
+                         "units_per_launch": B * n * S}}
+
     if args.trellis_variant_steps > 0:
         for key, vw in workloads.TRELLIS_VARIANTS.items():
             next_rows[f"trellis_{key}"] = time_variant(vw, T, args.trellis_variant_steps, dev, stream, check)

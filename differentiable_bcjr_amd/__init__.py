@@ -109,15 +109,19 @@ def _steps(w: torch.Tensor, codebook: torch.Tensor, L: int):
 
 def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
                   boundary_state: torch.Tensor | None = None, *, return_log_z: bool = False,
-                  workspace: torch.Tensor | None = None):
+                  workspace: torch.Tensor | None = None, checkpoint: bool = False):
     """Soft codeword with w's shape (and ln Z [B] if ``return_log_z``) for weights w [B, n] and codebook [2^L], or
-    w [B, n V] and codebook [2^L, V]."""
+    w [B, n V] and codebook [2^L, V].  ``checkpoint`` allocates the smallest workspace, which runs the checkpoint-and-
+    recompute memory mode (about 2 sqrt(n) message rows per in-flight sequence instead of n + 1)."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     B, n, V = _steps(w, codebook, L)
     sig = _sigma(boundary_state, B, w.device)
     out = torch.empty_like(w)
     lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
+    if checkpoint and workspace is None:
+        workspace = torch.empty(max(abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V), 1),
+                                dtype=torch.uint8, device=w.device)
     ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace, V)
     if V == 1:
         _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),

@@ -34,7 +34,7 @@ BCJR_TB_ROTATE = 1
 EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
            "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting", "bcjr_soft_codeword_grad_tail_biting",
            "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v", "bcjr_soft_codeword_grad_codebook_v",
-           "viterbi_hard_code_v", "bcjr_workspace_bytes",
+           "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_min",
            "bcjr_workspace_bytes_v", "bcjr_status_string")
 
 _lib = None
@@ -76,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.bcjr_workspace_bytes.restype = sz
     lib.bcjr_workspace_bytes_v.argtypes = [i32, i64, i64, i32, i32, i32]
     lib.bcjr_workspace_bytes_v.restype = sz
+    lib.bcjr_workspace_bytes_min.argtypes = [i32, i64, i64, i32, i32, i32]
+    lib.bcjr_workspace_bytes_min.restype = sz
     lib.bcjr_status_string.argtypes = [i32]
     lib.bcjr_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -154,6 +156,10 @@ def bcjr_workspace_bytes(op, B, n, L, k) -> int:
 
 def bcjr_workspace_bytes_v(op, B, n, L, k, V) -> int:
     return int(load().bcjr_workspace_bytes_v(op, B, n, L, k, V))
+
+
+def bcjr_workspace_bytes_min(op, B, n, L, k, V) -> int:
+    return int(load().bcjr_workspace_bytes_min(op, B, n, L, k, V))
 
 
 def bcjr_status_string(status) -> str:

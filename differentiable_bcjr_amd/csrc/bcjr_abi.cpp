@@ -117,14 +117,27 @@ constexpr size_t kLdsStatic = 2048;   // the kernels' own reduction slots
 
 struct GenPlan {
     bool ok;          // false: no kernel for these shapes (the gradient's two message arrays exceed LDS)
-    int grid, threads, dbl;
+    int grid, threads, dbl, ckpt;
     size_t lds, slot_bytes, total;
     size_t acc_off;   // codebook gradient: offset of the slot's [2^L][V] accumulator
 };
 
-// op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.
-GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+// The checkpoint interval of the recompute mode: about sqrt(n) rows stored and about sqrt(n) rebuilt per segment.
+int checkpoint_interval(int64_t n) {
+    int c = 1;
+    while ((int64_t)c * c < n) ++c;
+    return c;
+}
+
+// Rows of forward messages a slot holds: every step (n + 1), or with checkpoint interval c the n / c + 1 checkpoints
+// and the c - 1 rows of one segment.
+size_t tape_rows(int ckpt, int64_t n) { return ckpt == 0 ? (size_t)n + 1 : (size_t)(n / ckpt + ckpt); }
+
+// op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.  ckpt > 0 (soft codeword only):
+// the checkpoint-and-recompute mode with that interval.
+GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V, int ckpt = 0) {
     GenPlan p{};
+    p.ckpt = ckpt;
     const int S = 1 << L;
     const int spt = S < 64 ? S : 64;
     const int tps = S / spt;
@@ -135,7 +148,7 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
         p.dbl = 0;
         p.lds = 2 * msg;
     } else {
-        p.dbl = 2 * msg + kLdsStatic <= kLdsBytes;
+        p.dbl = ckpt == 0 && 2 * msg + kLdsStatic <= kLdsBytes;   // the recompute mode uses one buffer
         p.lds = p.dbl ? 2 * msg : msg;
     }
     p.ok = p.lds + kLdsStatic <= kLdsBytes;
@@ -148,11 +161,12 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     if (bpc < 1) bpc = 1;
     const int64_t cap = (int64_t)kNumCU * bpc;
     p.grid = (int)(B < cap ? B : cap);
-    const size_t tapes = align256((size_t)(n + 1) * G * 4);
+    const size_t tapes = align256(tape_rows(ckpt, n) * G * 4);
     const size_t nrm = align256((size_t)n * 4);
     switch (op) {
-        case BCJR_OP_SOFT:   // R~ tape, normalisers, per-wave (S0, S1[V]) of every step
-            p.slot_bytes = tapes + nrm + (wps > 1 ? align256((size_t)n * wps * (1 + V) * 4) : 0);
+        case BCJR_OP_SOFT:   // R~ rows, normalisers, per-wave (S0, S1[V]) of every step (+ the saved message)
+            p.slot_bytes = tapes + nrm + (wps > 1 ? align256((size_t)n * wps * (1 + V) * 4) : 0) +
+                           (ckpt ? align256(G * 4) : 0);
             break;
         case BCJR_OP_GRAD:   // R~ and Q^ tapes, normalisers and Q offsets, per-wave (S0, S1[V], S2, S3[V])
             p.slot_bytes = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
@@ -236,6 +250,13 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
     return bcjr_workspace_bytes(op, B, n, L, k);
 }
 
+size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    const size_t full = bcjr_workspace_bytes_v(op, B, n, L, k, V);
+    if (full == 0 || op != BCJR_OP_SOFT) return full;
+    const GenPlan p = make_gen_plan(op, B, n, L, k, V, checkpoint_interval(n));
+    return p.ok && p.total < full ? p.total : full;
+}
+
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
     if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
     if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI || op == BCJR_OP_GRAD_CODEBOOK)
@@ -286,8 +307,11 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     if (rc) return rc;
     if ((rc = check_temp(T))) return rc;
     const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
-    if (!tuned(k, V)) {
-        const GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V);
+    // memory: the full tape when the workspace holds it, else checkpoints with per-segment recompute
+    const size_t full = tuned(k, V) ? make_plan(BCJR_OP_SOFT, B, n, L).total : make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V).total;
+    const bool recompute = workspace != nullptr && workspace_bytes < full;
+    if (!tuned(k, V) || recompute) {
+        const GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
         a.w = w;
@@ -302,6 +326,7 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
         a.ws = static_cast<unsigned char*>(workspace);
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
+        a.ckpt = p.ckpt;
         return hip_status(launch_general(0, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
     const Plan p = make_plan(BCJR_OP_SOFT, B, n, L);

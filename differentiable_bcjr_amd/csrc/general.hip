@@ -101,23 +101,48 @@ __device__ __forceinline__ void st_row(const float* v, rsrc_t r, uint32_t off) {
     }
 }
 
-// N floats to LDS and to the tape at one element offset (N = 1, 2 or 4, aligned to N floats).
+// N floats to LDS and (when `store`) to the tape at one element offset (N = 1, 2 or 4, aligned to N floats).
 template <int N>
 __device__ __forceinline__ void st_floats(const float* v, float* lds, int idx, rsrc_t tape, uint32_t voff,
-                                          uint32_t soff) {
+                                          uint32_t soff, bool store = true) {
     if constexpr (N == 4) {
         const float4 x = make_float4(v[0], v[1], v[2], v[3]);
         *reinterpret_cast<float4*>(lds + idx) = x;
-        buf_st4_nt(x, tape, voff, soff);
+        if (store) buf_st4_nt(x, tape, voff, soff);
     } else if constexpr (N == 2) {
         const float2 x = make_float2(v[0], v[1]);
         *reinterpret_cast<float2*>(lds + idx) = x;
-        buf_st2(x, tape, voff, soff);
+        if (store) buf_st2(x, tape, voff, soff);
     } else {
         lds[idx] = v[0];
-        buf_st(v[0], tape, voff, soff);
+        if (store) buf_st(v[0], tape, voff, soff);
     }
 }
+
+// N floats from the tape at one element offset into LDS (restoring a checkpoint row).
+template <int N>
+__device__ __forceinline__ void ld_to_lds(float* lds, int idx, rsrc_t tape, uint32_t voff, uint32_t soff) {
+    float v[N];
+    ld_floats<N>(tape, voff + soff, v);
+#pragma unroll
+    for (int i = 0; i < N; ++i) lds[idx + i] = v[i];
+}
+
+// Tape rows of the forward messages.  Without checkpoints row t sits at t * row_bytes.  With checkpoint interval c,
+// rows t = 0, c, 2c, .. (n / c + 1 of them) come first, then c - 1 rows for the steps inside one segment: row t at
+// segment position t mod c - 1.  The forward pass stores the checkpoints and row n - 1 (which the sigma end reads);
+// the backward pass recomputes each segment's other rows from its checkpoint.
+struct TapeRows {
+    int c, n;
+    uint32_t row_bytes, seg_base;
+    __device__ __forceinline__ uint32_t off(int t) const {
+        if (c == 0) return (uint32_t)t * row_bytes;
+        const int r = t % c;
+        return r == 0 ? (uint32_t)(t / c) * row_bytes : seg_base + (uint32_t)(r - 1) * row_bytes;
+    }
+    __device__ __forceinline__ bool stored(int t) const { return c == 0 || t % c == 0 || t == n - 1; }
+    __host__ __device__ static constexpr size_t rows(int c, int n) { return c == 0 ? (size_t)n + 1 : (size_t)(n / c + c); }
+};
 
 // Maximum and sum over the SEG lanes of one sequence (SEG = 64, or the whole sub-wave block).
 __device__ __forceinline__ float gseq_max(float x, int seg) {
@@ -318,12 +343,16 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
     Owner<K, V, SPT, REG> own;
     own.init(args.cb, L, TPS);
 
-    // tape of the block's sequence: [n+1][G] R~, [n] normalisers, then the per-wave (S0, S1[V]) of every step
+    // tape of the block's sequence: the R~ rows (TapeRows), [n] normalisers, the per-wave (S0, S1[V]) of every step,
+    // then (checkpoint mode) each thread's share of the backward message while a segment is recomputed
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
     const uint32_t row_bytes = (uint32_t)G * 4u;
-    const uint32_t nrm_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const int ck = args.ckpt;
+    const TapeRows rows{ck, n, row_bytes, ck ? (uint32_t)(n / ck + 1) * row_bytes : 0u};
+    const uint32_t nrm_base = (uint32_t)align256(TapeRows::rows(ck, n) * G * 4);
     const uint32_t part_base = nrm_base + (uint32_t)align256((size_t)n * 4);
+    const uint32_t save_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * (1 + V) * 4) : 0u);
     const uint32_t v_j0 = 4u * (uint32_t)own.j(0);   // lane part of a backward group's tape offset
     // tape offset of backward group j(m) + J a: a lane part (VGPR) and a uniform part, or all of it in the VGPR when
     // the row is tile-major
@@ -357,21 +386,11 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             }
         lds_barrier();
 
-        float N = 0.f, N_last = 0.f;
-        double A = 0.0;
-        float w_nx[V];
-#pragma unroll
-        for (int v = 0; v < V; ++v) w_nx[v] = wb[v];
-        for (int t = 0; t < n; ++t) {
-            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
-            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
-            float wt[V];
-#pragma unroll
-            for (int v = 0; v < V; ++v) wt[v] = w_nx[v] * scale;
-            if (t + 1 < n) {
-#pragma unroll
-                for (int v = 0; v < V; ++v) w_nx[v] = wb[(t + 1) * V + v];
-            }
+        // One forward step: R~_{t+1} = logsumexp over the predecessors minus Nt, from mc into mn (the same buffer when
+        // single-buffered: every input is read before a barrier), and into the tape at row_soff when `store`.  Returns
+        // this thread's maximum of the outputs.  The checkpoint recompute runs it again with the stored normalisers,
+        // so the recomputed rows are bit-identical to the first pass's.
+        auto fwd_step = [&](const float* wt, float Nt, const float* mc, float* mn, uint32_t row_soff, bool store) {
             float rin[BPT][P];
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
@@ -423,12 +442,32 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     float o[TI];
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
-                        o[ii] = (mx[ii] - N) + lg2(s[ii]);
+                        o[ii] = (mx[ii] - Nt) + lg2(s[ii]);
                         lmax = run_max(lmax, o[ii]);
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(o, mn, u0, tape, 4u * own.tpos(u0, G), (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(o, mn, u0, tape, 4u * own.tpos(u0, G), row_soff, store);
                 }
+            return lmax;
+        };
+
+        float N = 0.f, N_last = 0.f;
+        double A = 0.0;
+        float w_nx[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) w_nx[v] = wb[v];
+        for (int t = 0; t < n; ++t) {
+            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
+            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
+            float wt[V];
+#pragma unroll
+            for (int v = 0; v < V; ++v) wt[v] = w_nx[v] * scale;
+            if (t + 1 < n) {
+#pragma unroll
+                for (int v = 0; v < V; ++v) w_nx[v] = wb[(t + 1) * V + v];
+            }
+            const float lmax_t = fwd_step(wt, N, mc, mn, rows.off(t + 1), rows.stored(t + 1));
+            float lmax = lmax_t;
             if (tau == 0) buf_st(N, tape, 0u, nrm_base + 4u * t);
             lmax = gseq_max(lmax, SEG);
             if (WPS > 1 && lane == 0) redmax[t & 1][wv] = lmax;
@@ -461,7 +500,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             __syncthreads();
         } else {
             __syncthreads();   // the tape rows of the forward pass, written by other threads
-            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
+            const float r = buf_ld_nt(tape, 0u, rows.off(n - 1) + 4u * own.tpos(sig >> K, G));
             float x = r;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -523,9 +562,42 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
             for (int v = 0; v < V; ++v) w_nx[v] = wb[t * V + v];
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
-            rq_nx = buf_ld_nt(tape, grp_voff(0, 0), (uint32_t)t * row_bytes + grp_soff(0, 0));
+            rq_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
         }
-        for (; t >= 0; --t) {
+        while (t >= 0) {
+        const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
+        if (ck) {
+            // checkpoint mode: keep this thread's share of the backward message in the workspace, rebuild
+            // R~_{t0+1..t} from checkpoint t0 with the stored normalisers, then restore the message
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) st_row<TI>(msg0 + own.fgroup(m, q), tape, save_base + 4u * own.fgroup(m, q));
+            lds_barrier();   // every share read before the recompute overwrites the buffer
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+                    ld_to_lds<TI>(msg0, own.fgroup(m, q), tape, 4u * own.tpos(own.fgroup(m, q), G), rows.off(t0));
+            lds_barrier();
+            for (int tt = t0; tt < t; ++tt) {
+                float wr[V];
+#pragma unroll
+                for (int v = 0; v < V; ++v) wr[v] = wb[tt * V + v] * scale;
+                const float Nr = uniform_f(buf_ld(tape, 0u, nrm_base + 4u * tt));
+                fwd_step(wr, Nr, msg0, msg0, rows.off(tt + 1), true);
+                lds_barrier();
+            }
+            __syncthreads();   // the recomputed rows, written by other threads, before the backward reads them
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+                    ld_to_lds<TI>(msg0, own.fgroup(m, q), tape, save_base + 4u * own.fgroup(m, q), 0u);
+            lds_barrier();
+            rq_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
+        }
+        for (; t >= t0; --t) {
             const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
             float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
             float wt[V];
@@ -559,10 +631,10 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     const float rq = rq_nx;
                     if (m * P + a + 1 < BPT * P) {
                         const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
-                        rq_nx = buf_ld_nt(tape, grp_voff(m2, a2), (uint32_t)t * row_bytes + grp_soff(m2, a2));
-                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
-                        rq_nx = buf_ld_nt(tape, grp_voff(0, 0),
-                                          (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes + grp_soff(0, 0));
+                        rq_nx = buf_ld_nt(tape, grp_voff(m2, a2), rows.off(t) + grp_soff(m2, a2));
+                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0; in checkpoint mode
+                               // re-read after the next segment is rebuilt)
+                        rq_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t > 0 ? t - 1 : 0) + grp_soff(0, 0));
                     }
                     float mx = 0.f, s = 0.f;
 #pragma unroll
@@ -638,6 +710,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             C_ += Nb;
             Nb = lmax;
         }
+        }   // segments
         if (WPS > 1) {
             __syncthreads();   // the per-wave partial sums, written by other waves
             for (int tt = tau; tt <= t_out; tt += TPS) {

@@ -70,6 +70,8 @@ struct GenArgs {
     unsigned char* ws;
     size_t slot_bytes;
     int32_t dbl;           // LDS messages double-buffered (else one buffer, inputs read before outputs are written)
+    int32_t ckpt;          // 0: every forward message row on the tape; c > 0: every c-th row, the backward pass
+                           // recomputes each c-step segment from its checkpoint (soft codeword and gradient)
 };
 
 }  // namespace bcjr

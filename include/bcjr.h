@@ -216,6 +216,19 @@ size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t
  * other op gives 0. */
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 
+/*
+ * The smallest workspace `op` runs with.  The soft codeword (BCJR_OP_SOFT) has two memory modes, and the entry point
+ * picks one by the workspace_bytes it is given:
+ *   - the full tape: every forward message row kept for the backward pass (bcjr_workspace_bytes[_v], the fastest);
+ *   - checkpoints: every c-th row kept, c = ceil(sqrt(n)), and the backward pass recomputes the rows of each c-step
+ *     segment from its checkpoint before it consumes them.  That costs one more forward pass of compute; the
+ *     workspace per in-flight sequence drops from (n + 1) rows to about 2 sqrt(n), e.g. 4097 -> 128 rows at n = 4096.
+ * A workspace at least bcjr_workspace_bytes_min but smaller than the full tape selects the second; the results are
+ * the same up to rounding (the recomputed rows are bit-identical; the two modes may run different kernels).  For the
+ * other ops this is bcjr_workspace_bytes_v.  Pure host function; 0 when the shapes are invalid or unsupported.
+ */
+size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
+
 /* Static, NUL-terminated description of a status code. */
 const char* bcjr_status_string(int32_t status);
 

@@ -25,7 +25,7 @@ def test_header_declares_every_op():
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
                  "viterbi_hard_code", "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting",
                  "bcjr_soft_codeword_grad_tail_biting", "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v",
-                 "bcjr_soft_codeword_grad_codebook_v", "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
+                 "bcjr_soft_codeword_grad_codebook_v", "viterbi_hard_code_v", "bcjr_workspace_bytes_min", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -92,9 +92,10 @@ def test_workspace_bytes_invalid_shapes_are_zero(args):
     assert abi.bcjr_workspace_bytes(99, 1, 4, 8, 2) == 0
 
 
-def _gen_bytes(op, B, n, L, k, V):
+def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     """The general trellis kernels' workspace: one sequence per workgroup of 2^L / 64 threads (2^L below L = 6), a
-    slot per workgroup of the persistent grid, G = 2^(L-k) message floats per LDS buffer."""
+    slot per workgroup of the persistent grid, G = 2^(L-k) message floats per LDS buffer.  ckpt > 0: the soft
+    codeword's checkpoint mode (n / c + 1 checkpoint rows, c - 1 segment rows, one saved message; one LDS buffer)."""
     S = 1 << L
     tps = S // min(S, 64)
     wps = tps // 64 if tps >= 64 else 1
@@ -103,14 +104,14 @@ def _gen_bytes(op, B, n, L, k, V):
     if op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
         lds = 2 * G * 4
     else:
-        lds = 2 * G * 4 if 2 * G * 4 + lds_static <= lds_cap else G * 4
+        lds = 2 * G * 4 if (ckpt == 0 and 2 * G * 4 + lds_static <= lds_cap) else G * 4
     if lds + lds_static > lds_cap:
         return 0
     bpc = max(1, min(16 // (tps // 64 if tps >= 64 else 1), lds_cap // (lds + lds_static)))
     grid = min(B, 256 * bpc)
-    tapes, nrm = _a256((n + 1) * G * 4), _a256(n * 4)
+    tapes, nrm = _a256(((n + 1) if ckpt == 0 else (n // ckpt + ckpt)) * G * 4), _a256(n * 4)
     if op == abi.BCJR_OP_SOFT:
-        slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0)
+        slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0) + (_a256(G * 4) if ckpt else 0)
     elif op == abi.BCJR_OP_GRAD:
         slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
     elif op == abi.BCJR_OP_GRAD_CODEBOOK:   # + one float accumulator per state and component
@@ -130,6 +131,23 @@ def test_general_trellis_workspace_formula(L, k, V, B, n):
         assert abi.bcjr_workspace_bytes_v(op, B, n, L, k, V) == _gen_bytes(op, B, n, L, k, V)
         if V == 1:
             assert abi.bcjr_workspace_bytes(op, B, n, L, k) == _gen_bytes(op, B, n, L, k, V)
+
+
+@pytest.mark.parametrize("L,k,V", [(16, 2, 1), (16, 3, 1), (16, 4, 2), (12, 1, 2), (8, 2, 1), (4, 1, 1)])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 2), (4096, 256), (100, 4096), (3, 17)])
+def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
+    """The soft codeword's smallest workspace: checkpoints every c = ceil(sqrt(n)) rows, when that is smaller than the
+    full tape; the other ops have one memory mode."""
+    c = 1
+    while c * c < n:
+        c += 1
+    full = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT, B, n, L, k, V)
+    want = min(full, _gen_bytes(abi.BCJR_OP_SOFT, B, n, L, k, V, ckpt=c))
+    assert abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V) == want
+    for op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI, abi.BCJR_OP_GRAD_CODEBOOK):
+        assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
+    if n >= 256 and L == 16:
+        assert abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V) * 6 < full
 
 
 def test_workspace_v_matches_the_scalar_query():
@@ -341,7 +359,7 @@ def test_general_trellis_reaches_the_workspace_check():
             assert _soft_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
             assert _grad_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
             assert _vit_v(L=L, k=k, V=V) == abi.BCJR_ERR_WORKSPACE
-    need = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT, 4, 8, 9, 3, 2)
+    need = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, 4, 8, 9, 3, 2)   # below it no memory mode fits
     assert _soft_v(L=9, k=3, workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
     assert _soft_v(L=9, k=3, workspace=FAKE + 16, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
 
@@ -369,7 +387,8 @@ def test_viterbi_ignores_temperature_and_checks_workspace():
 
 
 def test_workspace_too_small_or_misaligned_rejected():
-    need = abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4, 8, 8, 2)
+    need = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, 4, 8, 8, 2, 1)   # the checkpoint mode's size
+    assert need < abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, 4, 8, 8, 2)
     assert _soft(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
     assert _soft(workspace=None, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
     assert _soft(workspace=FAKE + 64, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
