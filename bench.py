@@ -27,7 +27,9 @@ accumulator is read and written once per step, 12 bytes per state-step against t
 Viterbi with rotate-and-decode start-state choice (viterbi_tail_biting, two decodes) is timed the same way, and so
 are the general-trellis kernels on the same 1024x1024 matrix at 3 bits per weight (k = 3) and at 2 bits per weight with
 two weights per step (k = 4, V = 2): soft codeword, gradient and Viterbi, each against the ALU roofline of its own
-slot count (general_slots).
+slot count (general_slots).  The soft codeword and the gradient are also timed in their checkpoint-and-recompute
+memory mode (given bcjr_workspace_bytes_min: every ceil(sqrt(n))-th message row kept, the rest rebuilt per segment),
+with the workspace that mode needs beside the full tape's.
 
 ``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
 """
@@ -216,7 +218,7 @@ def time_variant(vw, T, K, dev, stream, check):
         torch.cuda.synchronize()
         ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
         units = B * steps * S
-        ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{', false' if name == 'grad' else ''}>",
+        ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{', false, false' if name == 'grad' else ''}>",
                      "ms": round(ms, 4), "state_updates_per_s": DIRECTIONS[name] * units / (ms * 1e-3),
                      "weights_per_s": B * vw.n / (ms * 1e-3),
                      "roofline": {"bound": "alu", "achieved": round(slots[name] * units / (ms * 1e-3) / 1e12, 3),
@@ -398,38 +400,49 @@ def main():
                          "units_per_launch": B * n * S}}
 
     if args.codebook_grad_steps > 0:
-        # the soft codeword in its checkpoint-and-recompute memory mode (the smallest workspace)
-        ck_bytes = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, 1)
-        ws_ck = torch.empty(ck_bytes, dtype=torch.uint8, device=dev)
-        out_ck = torch.empty_like(w)
+        # the soft codeword and the gradient in their checkpoint-and-recompute memory mode (the smallest workspace)
+        g_ck = torch.empty_like(w)
+        for name, op_id in (("soft", abi.BCJR_OP_SOFT), ("grad", abi.BCJR_OP_GRAD)):
+            ck_bytes = abi.bcjr_workspace_bytes_min(op_id, B, n, L, k, 1)
+            ws_ck = torch.empty(ck_bytes, dtype=torch.uint8, device=dev)
+            out_ck = torch.empty_like(w)
 
-        def soft_ck():
-            check(abi.bcjr_soft_codeword(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, out_ck.data_ptr(), None,
-                                         ws_ck.data_ptr(), ck_bytes, sp), "soft checkpoint")
+            def run_ck(name=name, ws_ck=ws_ck, out_ck=out_ck, ck_bytes=ck_bytes):
+                if name == "soft":
+                    check(abi.bcjr_soft_codeword(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, out_ck.data_ptr(),
+                                                 None, ws_ck.data_ptr(), ck_bytes, sp), "soft checkpoint")
+                else:
+                    check(abi.bcjr_soft_codeword_grad(w.data_ptr(), c.data_ptr(), B, n, L, k, T, None, g.data_ptr(),
+                                                      out_ck.data_ptr(), g_ck.data_ptr(), ws_ck.data_ptr(), ck_bytes,
+                                                      sp), "grad checkpoint")
 
-        soft_ck()
-        torch.cuda.synchronize()
-        K4 = args.codebook_grad_steps
-        ev4 = [torch.cuda.Event(enable_timing=True) for _ in range(K4 + 1)]
-        ev4[0].record(stream)
-        for i in range(K4):
-            soft_ck()
-            ev4[i + 1].record(stream)
-        torch.cuda.synchronize()
-        ms4 = float(np.mean([ev4[i].elapsed_time(ev4[i + 1]) for i in range(K4)]))
-        slots4 = ALU_SLOTS["soft"] * B * n * S
-        next_rows["soft_checkpoint"] = {
-            "entry_point": "bcjr_soft_codeword with bcjr_workspace_bytes_min", "kernel": f"gen_soft_kernel<{k}, 1, 64, 16>",
-            "checkpoint_interval": int(np.ceil(np.sqrt(n))), "workspace_bytes": ck_bytes,
-            "full_tape_workspace_bytes": abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, k),
-            "calls": K4, "ms": round(ms4, 4), "state_updates_per_s": 2 * B * n * S / (ms4 * 1e-3),
-            "weights_per_s": B * n / (ms4 * 1e-3),
-            "roofline": {"bound": "alu", "achieved": round(slots4 / (ms4 * 1e-3) / 1e12, 3),
-                         "peak": round(PEAK_SLOTS_PER_S / 1e12, 3), "unit": "T VALU-slots/s",
-                         "frac": round(slots4 / (ms4 * 1e-3) / PEAK_SLOTS_PER_S, 4),
-                         "per_unit": f"{ALU_SLOTS['soft']} fp32 VALU slots per state-step (the method's work; the "
-                                     "recompute's extra forward pass is overhead)",
-                         "units_per_launch": B * n * S}}
+            run_ck()
+            torch.cuda.synchronize()
+            K4 = args.codebook_grad_steps
+            ev4 = [torch.cuda.Event(enable_timing=True) for _ in range(K4 + 1)]
+            ev4[0].record(stream)
+            for i in range(K4):
+                run_ck()
+                ev4[i + 1].record(stream)
+            torch.cuda.synchronize()
+            ms4 = float(np.mean([ev4[i].elapsed_time(ev4[i + 1]) for i in range(K4)]))
+            slots4 = ALU_SLOTS[name] * B * n * S
+            entry = "bcjr_soft_codeword" if name == "soft" else "bcjr_soft_codeword_grad"
+            next_rows[f"{name}_checkpoint"] = {
+                "entry_point": f"{entry} with bcjr_workspace_bytes_min",
+                "kernel": f"gen_soft_kernel<{k}, 1, 64, 16>" if name == "soft"
+                else f"gen_grad_kernel<{k}, 1, 64, 16, false, true>",
+                "checkpoint_interval": int(np.ceil(np.sqrt(n))), "workspace_bytes": ck_bytes,
+                "full_tape_workspace_bytes": abi.bcjr_workspace_bytes(op_id, B, n, L, k),
+                "calls": K4, "ms": round(ms4, 4), "state_updates_per_s": 2 * B * n * S / (ms4 * 1e-3),
+                "weights_per_s": B * n / (ms4 * 1e-3),
+                "roofline": {"bound": "alu", "achieved": round(slots4 / (ms4 * 1e-3) / 1e12, 3),
+                             "peak": round(PEAK_SLOTS_PER_S / 1e12, 3), "unit": "T VALU-slots/s",
+                             "frac": round(slots4 / (ms4 * 1e-3) / PEAK_SLOTS_PER_S, 4),
+                             "per_unit": f"{ALU_SLOTS[name]} fp32 VALU slots per state-step (the method's work; the "
+                                         "recompute's extra forward pass is overhead)",
+                             "units_per_launch": B * n * S}}
+            del ws_ck
 
     if args.trellis_variant_steps > 0:
         for key, vw in workloads.TRELLIS_VARIANTS.items():

@@ -84,8 +84,13 @@ def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2, V: int = 1) -> 
     return abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
 
 
-def _workspace(op, B, n, L, k, device, workspace, V=1):
+def _workspace(op, B, n, L, k, device, workspace, V=1, checkpoint=False):
+    """The caller's workspace, or a new one: the full tape, or with ``checkpoint`` the smallest the op accepts (the
+    checkpoint-and-recompute memory mode)."""
     need = workspace_bytes(op, B, n, L, k, V)
+    if checkpoint and workspace is None:
+        workspace = torch.empty(max(abi.bcjr_workspace_bytes_min(op, B, n, L, k, V), 1), dtype=torch.uint8,
+                                device=device)
     if workspace is None:
         # torch's allocator hands out 512-byte aligned blocks; the library checks 256-byte alignment itself
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
@@ -119,10 +124,7 @@ def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T
     sig = _sigma(boundary_state, B, w.device)
     out = torch.empty_like(w)
     lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
-    if checkpoint and workspace is None:
-        workspace = torch.empty(max(abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V), 1),
-                                dtype=torch.uint8, device=w.device)
-    ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace, V)
+    ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace, V, checkpoint)
     if V == 1:
         _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
                                       out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
@@ -134,8 +136,9 @@ def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T
 
 def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int, k: int = 2,
                        T: float = 1.0, boundary_state: torch.Tensor | None = None, *, return_w_soft: bool = False,
-                       workspace: torch.Tensor | None = None):
-    """dL/dw given dL/dw_soft, both with w's shape (and the soft codeword if ``return_w_soft``)."""
+                       workspace: torch.Tensor | None = None, checkpoint: bool = False):
+    """dL/dw given dL/dw_soft, both with w's shape (and the soft codeword if ``return_w_soft``).  ``checkpoint``
+    allocates the smallest workspace, which runs the checkpoint-and-recompute memory mode."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     g = _f32(grad_w_soft, "grad_w_soft")
@@ -145,7 +148,7 @@ def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: tor
     sig = _sigma(boundary_state, B, w.device)
     grad = torch.empty_like(w)
     ws_out = torch.empty_like(w) if return_w_soft else None
-    ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace, V)
+    ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace, V, checkpoint)
     if V == 1:
         _check(abi.bcjr_soft_codeword_grad(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
                                            g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
@@ -160,10 +163,10 @@ def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: tor
 def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int,
                                 k: int = 2, T: float = 1.0, boundary_state: torch.Tensor | None = None, *,
                                 return_grad_w: bool = True, return_w_soft: bool = False,
-                                workspace: torch.Tensor | None = None):
+                                workspace: torch.Tensor | None = None, checkpoint: bool = False):
     """dL/dc with the codebook's shape ([2^L], or [2^L, V] for V weights per step; summed over the batch) given
     dL/dw_soft with w's shape; then dL/dw if ``return_grad_w`` and the soft codeword if ``return_w_soft``.  Returns a
-    tuple when either is asked for."""
+    tuple when either is asked for.  ``checkpoint`` allocates the smallest workspace (checkpoint-and-recompute)."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
     g = _f32(grad_w_soft, "grad_w_soft")
@@ -174,7 +177,7 @@ def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_
     gc = torch.empty(codebook.shape, dtype=torch.float32, device=w.device)
     grad = torch.empty_like(w) if return_grad_w else None
     ws_out = torch.empty_like(w) if return_w_soft else None
-    ws, need = _workspace(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, k, w.device, workspace, V)
+    ws, need = _workspace(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, k, w.device, workspace, V, checkpoint)
     if V == 1:
         _check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
                                                     _ptr(sig), g.data_ptr(), gc.data_ptr(), _ptr(grad), _ptr(ws_out),

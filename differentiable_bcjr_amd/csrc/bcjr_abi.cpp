@@ -133,8 +133,8 @@ int checkpoint_interval(int64_t n) {
 // and the c - 1 rows of one segment.
 size_t tape_rows(int ckpt, int64_t n) { return ckpt == 0 ? (size_t)n + 1 : (size_t)(n / ckpt + ckpt); }
 
-// op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.  ckpt > 0 (soft codeword only):
-// the checkpoint-and-recompute mode with that interval.
+// op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.  ckpt > 0 (not Viterbi): the
+// checkpoint-and-recompute mode with that interval.
 GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V, int ckpt = 0) {
     GenPlan p{};
     p.ckpt = ckpt;
@@ -169,11 +169,10 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
                            (ckpt ? align256(G * 4) : 0);
             break;
         case BCJR_OP_GRAD:   // R~ and Q^ tapes, normalisers and Q offsets, per-wave (S0, S1[V], S2, S3[V])
-            p.slot_bytes = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
-            break;
-        case BCJR_OP_GRAD_CODEBOOK:   // the gradient's slot + one float accumulator per state and component
+        case BCJR_OP_GRAD_CODEBOOK:   // + one float accumulator per state and component
             p.acc_off = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
-            p.slot_bytes = p.acc_off + align256((size_t)S * V * 4);
+            p.slot_bytes = p.acc_off + (op == BCJR_OP_GRAD_CODEBOOK ? align256((size_t)S * V * 4) : 0) +
+                           (ckpt ? nrm + align256(2 * G * 4) : 0);   // + the Q input offsets, the saved messages
             break;
         default:   // two back-pointer buffers of [n][threads] words
             p.slot_bytes = align256(2 * (size_t)n * (size_t)tps * 4);
@@ -252,7 +251,7 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
 
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
     const size_t full = bcjr_workspace_bytes_v(op, B, n, L, k, V);
-    if (full == 0 || op != BCJR_OP_SOFT) return full;
+    if (full == 0 || op == BCJR_OP_VITERBI) return full;
     const GenPlan p = make_gen_plan(op, B, n, L, k, V, checkpoint_interval(n));
     return p.ok && p.total < full ? p.total : full;
 }
@@ -353,8 +352,10 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     if (rc) return rc;
     if ((rc = check_temp(T))) return rc;
     const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
-    if (!tuned(k, V)) {
-        const GenPlan p = make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V);
+    const size_t full = tuned(k, V) ? make_plan(BCJR_OP_GRAD, B, n, L).total : make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V).total;
+    const bool recompute = workspace != nullptr && workspace_bytes < full;
+    if (!tuned(k, V) || recompute) {
+        const GenPlan p = make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
         a.w = w;
@@ -371,6 +372,7 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
         a.ws = static_cast<unsigned char*>(workspace);
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
+        a.ckpt = p.ckpt;
         return hip_status(launch_general(1, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
     const Plan p = make_plan(BCJR_OP_GRAD, B, n, L);
@@ -400,8 +402,11 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
     if ((rc = check_temp(T))) return rc;
     const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    if (!tuned(k, V)) {
-        const GenPlan p = make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V);
+    const size_t full = tuned(k, V) ? make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L).total
+                                    : make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V).total;
+    const bool recompute = workspace != nullptr && workspace_bytes < full;
+    if (!tuned(k, V) || recompute) {
+        const GenPlan p = make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
         a.w = w;
@@ -418,6 +423,7 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
         a.ws = static_cast<unsigned char*>(workspace);
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
+        a.ckpt = p.ckpt;
         hipError_t e = launch_general(3, k, V, a, p.grid, p.threads, p.lds, st);
         if (e != hipSuccess) return hip_status(e);
         return hip_status(launch_codebook_reduce(a.ws, p.slot_bytes, (uint32_t)p.acc_off, p.grid, (1 << L) * V,

@@ -952,7 +952,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 // is normalised by the previous step's exact total, with the running normaliser sums in double.  A later reduction
 // sums the slots in a fixed order.
 
-template <int K, int V, int SPT, int LT, bool GC>
+template <int K, int V, int SPT, int LT, bool GC, bool CK>
 __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     using Gm = GG<K, V, SPT>;
     constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TA = Gm::TA, TI = Gm::TI, NA = Gm::NA,
@@ -975,12 +975,16 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     Owner<K, V, SPT, REG> own;
     own.init(args.cb, L, TPS);
 
-    // tape: [n+1][G] R~, [n+1][G] Q^, [n] normalisers N_t, [n] offsets K_{t-1} (true Q_t = Q^_t + K_{t-1}), then
-    // the per-wave (S0, S1[V], S2, S3[V]) of every step
+    // tape: the R~ rows and the Q^ rows (TapeRows each), [n] normalisers N_t, [n] offsets K_{t-1} (true
+    // Q_t = Q^_t + K_{t-1}), the per-wave (S0, S1[V], S2, S3[V]) of every step, the codebook accumulator (GC), then
+    // (checkpoint mode) the [n] per-step Q input offsets and each thread's share of the two backward messages while a
+    // segment is recomputed
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
     const uint32_t row_bytes = (uint32_t)G * 4u;
-    const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const int ck = CK ? args.ckpt : 0;   // a compile-time 0 keeps the full-tape kernels free of the recompute
+    const TapeRows rows{ck, n, row_bytes, ck ? (uint32_t)(n / ck + 1) * row_bytes : 0u};
+    const uint32_t q_base = (uint32_t)align256(TapeRows::rows(ck, n) * G * 4);
     const uint32_t nrm_base = 2u * q_base;
     const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
     const uint32_t part_base = kq_base + (uint32_t)align256((size_t)n * 4);
@@ -1000,6 +1004,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     // the codebook-gradient accumulator of the slot: c(s, v) at acc_base + 4 (s V + v), so a tile row's entries are
     // contiguous like its codebook values
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * NS * 4) : 0u);
+    const uint32_t kin_base = acc_base + (GC ? (uint32_t)align256(((size_t)V * 4) << L) : 0u);
+    const uint32_t save_base = kin_base + (uint32_t)align256((size_t)n * 4);
     using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
     const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
     if constexpr (GC) {
@@ -1037,31 +1043,28 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             }
         lds_barrier();
 
-        double A = 0.0;
-        float N = 0.f, kq = 0.f, Kq = 0.f, N_last = 0.f, K_last = 0.f;
-        for (int t = 0; t < n; ++t) {
+        // One forward step t: R~_{t+1} and Q^_{t+1} from R~_t and Q^_t - kqt, normalised by Nt, into LDS (inputs read
+        // before a barrier, outputs written in place) and into the tape at row_soff when `store`.  Returns this
+        // thread's maximum of R~_{t+1} and the Q^ of the group attaining it.  The checkpoint recompute runs it again
+        // with the stored Nt and kqt, so the recomputed rows are bit-identical to the first pass's.
+        auto fwd_step = [&](int tt, float Nt, float kqt, uint32_t row_soff, bool store, float& lmax, float& lq) {
             float rin[BPT][P], qin[BPT][P];
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
                 for (int a = 0; a < P; ++a) {
                     rin[m][a] = mr[own.j(m) + J * a];
-                    qin[m][a] = mq[own.j(m) + J * a] - kq;
+                    qin[m][a] = mq[own.j(m) + J * a] - kqt;
                 }
             lds_barrier();   // every input read before any output overwrites it
-            if (tau == 0) {
-                buf_st(N, tape, 0u, nrm_base + 4u * t);
-                buf_st(Kq, tape, 0u, kq_base + 4u * t);
-            }
-            K_last = Kq;
-            Kq += kq;
             float wt[V], gt[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                wt[v] = wb[t * V + v] * scale;
-                gt[v] = gb[t * V + v] * inv_scale;
+                wt[v] = wb[tt * V + v] * scale;
+                gt[v] = gb[tt * V + v] * inv_scale;
             }
-            float lmax = -3.0e38f, lq = 0.f;
+            lmax = -3.0e38f;
+            lq = 0.f;
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
@@ -1113,16 +1116,30 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     float ro[TI], qo[TI];
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
-                        ro[ii] = (mx[ii] - N) + lg2(s[ii]);
+                        ro[ii] = (mx[ii] - Nt) + lg2(s[ii]);
                         qo[ii] = sz[ii] * rcp(s[ii]);
                         const bool up = ro[ii] > lmax;
                         lmax = up ? ro[ii] : lmax;
                         lq = up ? qo[ii] : lq;
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(ro, mr, u0, tape, 4u * own.tpos(u0, G), (uint32_t)(t + 1) * row_bytes);
-                    st_floats<TI>(qo, mq, u0, tape, 4u * own.tpos(u0, G), q_base + (uint32_t)(t + 1) * row_bytes);
+                    st_floats<TI>(ro, mr, u0, tape, 4u * own.tpos(u0, G), row_soff, store);
+                    st_floats<TI>(qo, mq, u0, tape, 4u * own.tpos(u0, G), q_base + row_soff, store);
                 }
+        };
+
+        double A = 0.0;
+        float N = 0.f, kq = 0.f, Kq = 0.f, N_last = 0.f, K_last = 0.f;
+        for (int t = 0; t < n; ++t) {
+            if (tau == 0) {
+                buf_st(N, tape, 0u, nrm_base + 4u * t);
+                buf_st(Kq, tape, 0u, kq_base + 4u * t);
+                if (ck) buf_st(kq, tape, 0u, kin_base + 4u * t);
+            }
+            K_last = Kq;
+            Kq += kq;
+            float lmax, lq;
+            fwd_step(t, N, kq, rows.off(t + 1), rows.stored(t + 1), lmax, lq);
             gseq_argmax_payload(lmax, lq, SEG);
             if (WPS > 1 && lane == 0) {
                 redmax[t & 1][wv] = lmax;
@@ -1181,8 +1198,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             __syncthreads();
         } else {
             __syncthreads();   // R~_{n-1} and Q^_{n-1} are on the tape, written by other threads
-            const float r = buf_ld_nt(tape, 0u, (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
-            const float qv = buf_ld_nt(tape, 0u, q_base + (uint32_t)(n - 1) * row_bytes + 4u * own.tpos(sig >> K, G));
+            const float r = buf_ld_nt(tape, 0u, rows.off(n - 1) + 4u * own.tpos(sig >> K, G));
+            const float qv = buf_ld_nt(tape, 0u, q_base + rows.off(n - 1) + 4u * own.tpos(sig >> K, G));
             float x = r;
             EF = qv + K_last;   // Q^_{n-1} carries the offset K_{n-2}
 #pragma unroll
@@ -1278,10 +1295,53 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         if (t >= 0) {
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
             K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * t);
-            rt_nx = buf_ld_nt(tape, grp_voff(0, 0), (uint32_t)t * row_bytes + grp_soff(0, 0));
-            qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + (uint32_t)t * row_bytes + grp_soff(0, 0));
+            rt_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
+            qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + rows.off(t) + grp_soff(0, 0));
         }
-        for (; t >= 0; --t) {
+        while (t >= 0) {
+        const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
+        if (ck) {
+            // checkpoint mode: keep this thread's share of both backward messages in the workspace, rebuild R~ and
+            // Q^ of steps t0+1..t from checkpoint t0 with the stored normalisers and offsets, then restore them
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    const int u0 = own.fgroup(m, q);
+                    st_row<TI>(mr + u0, tape, save_base + 4u * u0);
+                    st_row<TI>(mq + u0, tape, save_base + row_bytes + 4u * u0);
+                }
+            lds_barrier();   // every share read before the recompute overwrites the buffers
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    const int u0 = own.fgroup(m, q);
+                    ld_to_lds<TI>(mr, u0, tape, 4u * own.tpos(u0, G), rows.off(t0));
+                    ld_to_lds<TI>(mq, u0, tape, 4u * own.tpos(u0, G), q_base + rows.off(t0));
+                }
+            lds_barrier();
+            for (int tt = t0; tt < t; ++tt) {
+                const float Nr = uniform_f(buf_ld(tape, 0u, nrm_base + 4u * tt));
+                const float kr = uniform_f(buf_ld(tape, 0u, kin_base + 4u * tt));
+                float lm, lqr;
+                fwd_step(tt, Nr, kr, rows.off(tt + 1), true, lm, lqr);
+                lds_barrier();
+            }
+            __syncthreads();   // the recomputed rows, written by other threads, before the backward reads them
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    const int u0 = own.fgroup(m, q);
+                    ld_to_lds<TI>(mr, u0, tape, save_base + 4u * u0, 0u);
+                    ld_to_lds<TI>(mq, u0, tape, save_base + row_bytes + 4u * u0, 0u);
+                }
+            lds_barrier();
+            rt_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
+            qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + rows.off(t) + grp_soff(0, 0));
+        }
+        for (; t >= t0; --t) {
             float bin[BPT][I], pin[BPT][I];
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
@@ -1306,6 +1366,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * (t - 1));
                 K_nx = buf_ld_nt(tape, 0u, kq_base + 4u * (t - 1));
             }
+            const uint32_t row_t = rows.off(t), row_prev = rows.off(t > 0 ? t - 1 : 0);
             D += (RT)Nt;
             const float ref = (float)(((RT)rzr + D) - C_);
             // E[F | s_t = s] - E[F] = Q^_t(s >> k) + cst + <g_t, c(s) - w_t> + P''_t(s & (G-1)), cst per step
@@ -1326,11 +1387,12 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     const float qt = qt_nx + cst;
                     if (m * P + a + 1 < BPT * P) {
                         const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
-                        const uint32_t so = (uint32_t)t * row_bytes + grp_soff(m2, a2);
+                        const uint32_t so = row_t + grp_soff(m2, a2);
                         rt_nx = buf_ld_nt(tape, grp_voff(m2, a2), so);
                         qt_nx = buf_ld_nt(tape, grp_voff(m2, a2), q_base + so);
-                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0)
-                        const uint32_t so = (uint32_t)(t > 0 ? t - 1 : 0) * row_bytes + grp_soff(0, 0);
+                    } else {   // the next step's first (a harmless re-read of row 0 at t = 0; in checkpoint mode
+                               // re-read after the next segment is rebuilt)
+                        const uint32_t so = row_prev + grp_soff(0, 0);
                         rt_nx = buf_ld_nt(tape, grp_voff(0, 0), so);
                         qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + so);
                     }
@@ -1477,6 +1539,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             C_ += (RT)Nb;
             Nb = lmax;
         }
+        }   // segments
         if (WPS > 1) {
             __syncthreads();   // the per-wave partial sums, written by other waves
             for (int tt = tau; tt <= t_out; tt += TPS) {
@@ -1527,11 +1590,11 @@ namespace {
 using GenKernel = void (*)(GenArgs);
 
 template <int K, int V, int SPT, int LT>
-GenKernel pick(int op) {
+GenKernel pick(int op, bool ck) {
     switch (op) {
         case 0: return gen_soft_kernel<K, V, SPT, LT>;
-        case 1: return gen_grad_kernel<K, V, SPT, LT, false>;
-        case 3: return gen_grad_kernel<K, V, SPT, LT, true>;
+        case 1: return ck ? gen_grad_kernel<K, V, SPT, LT, false, true> : gen_grad_kernel<K, V, SPT, LT, false, false>;
+        case 3: return ck ? gen_grad_kernel<K, V, SPT, LT, true, true> : gen_grad_kernel<K, V, SPT, LT, true, false>;
         default: return gen_viterbi_kernel<K, V, SPT, LT>;
     }
 }
@@ -1539,30 +1602,30 @@ GenKernel pick(int op) {
 // L = 16 (the workloads' trellis) has its own instantiation, whose strides are compile-time; other L read it at run
 // time.
 template <int V, int SPT>
-GenKernel pick_k(int op, int k, int L) {
+GenKernel pick_k(int op, bool ck, int k, int L) {
     if constexpr (SPT < 64) {
         switch (k) {
-            case 1: return pick<1, V, SPT, 0>(op);
-            case 2: return pick<2, V, SPT, 0>(op);
+            case 1: return pick<1, V, SPT, 0>(op, ck);
+            case 2: return pick<2, V, SPT, 0>(op, ck);
             default: return nullptr;
         }
     } else {
         switch (k) {
-            case 1: return L == 16 ? pick<1, V, SPT, 16>(op) : pick<1, V, SPT, 0>(op);
-            case 2: return L == 16 ? pick<2, V, SPT, 16>(op) : pick<2, V, SPT, 0>(op);
-            case 3: return L == 16 ? pick<3, V, SPT, 16>(op) : pick<3, V, SPT, 0>(op);
-            case 4: return L == 16 ? pick<4, V, SPT, 16>(op) : pick<4, V, SPT, 0>(op);
+            case 1: return L == 16 ? pick<1, V, SPT, 16>(op, ck) : pick<1, V, SPT, 0>(op, ck);
+            case 2: return L == 16 ? pick<2, V, SPT, 16>(op, ck) : pick<2, V, SPT, 0>(op, ck);
+            case 3: return L == 16 ? pick<3, V, SPT, 16>(op, ck) : pick<3, V, SPT, 0>(op, ck);
+            case 4: return L == 16 ? pick<4, V, SPT, 16>(op, ck) : pick<4, V, SPT, 0>(op, ck);
             default: return nullptr;
         }
     }
 }
 
 template <int V>
-GenKernel pick_spt(int op, int k, int L) {
+GenKernel pick_spt(int op, bool ck, int k, int L) {
     switch (L) {
-        case 4: return pick_k<V, 16>(op, k, L);
-        case 5: return pick_k<V, 32>(op, k, L);
-        default: return pick_k<V, 64>(op, k, L);
+        case 4: return pick_k<V, 16>(op, ck, k, L);
+        case 5: return pick_k<V, 32>(op, ck, k, L);
+        default: return pick_k<V, 64>(op, ck, k, L);
     }
 }
 
@@ -1572,7 +1635,8 @@ GenKernel pick_spt(int op, int k, int L) {
 // launch_codebook_reduce).  The caller has checked 1 <= k <= 4, 2k <= L <= 16, V in {1, 2}.
 hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
                           hipStream_t st) {
-    const GenKernel f = V == 1 ? pick_spt<1>(op, k, a.L) : pick_spt<2>(op, k, a.L);
+    const bool ck = a.ckpt != 0;
+    const GenKernel f = V == 1 ? pick_spt<1>(op, ck, k, a.L) : pick_spt<2>(op, ck, k, a.L);
     if (f == nullptr) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes);

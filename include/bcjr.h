@@ -217,15 +217,17 @@ size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 
 /*
- * The smallest workspace `op` runs with.  The soft codeword (BCJR_OP_SOFT) has two memory modes, and the entry point
- * picks one by the workspace_bytes it is given:
+ * The smallest workspace `op` runs with.  The soft codeword and the two gradients (BCJR_OP_SOFT, BCJR_OP_GRAD,
+ * BCJR_OP_GRAD_CODEBOOK) have two memory modes, and the entry point picks one by the workspace_bytes it is given:
  *   - the full tape: every forward message row kept for the backward pass (bcjr_workspace_bytes[_v], the fastest);
  *   - checkpoints: every c-th row kept, c = ceil(sqrt(n)), and the backward pass recomputes the rows of each c-step
  *     segment from its checkpoint before it consumes them.  That costs one more forward pass of compute; the
- *     workspace per in-flight sequence drops from (n + 1) rows to about 2 sqrt(n), e.g. 4097 -> 128 rows at n = 4096.
+ *     message rows per in-flight sequence drop from (n + 1) to about 2 sqrt(n), e.g. 4097 -> 128 rows at n = 4096
+ *     (the gradients keep two such tapes; the codebook gradient's [2^L][V] accumulator per slot is not reduced).
  * A workspace at least bcjr_workspace_bytes_min but smaller than the full tape selects the second; the results are
- * the same up to rounding (the recomputed rows are bit-identical; the two modes may run different kernels).  For the
- * other ops this is bcjr_workspace_bytes_v.  Pure host function; 0 when the shapes are invalid or unsupported.
+ * the same up to rounding (the recomputed rows are bit-identical; the two modes may run different kernels).  Where
+ * the rounding to 256-byte areas leaves checkpoints no smaller (n <= 3, or tiny rows), this equals the full tape.
+ * For Viterbi this is bcjr_workspace_bytes_v.  Pure host function; 0 when the shapes are invalid or unsupported.
  */
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 

@@ -94,8 +94,9 @@ def test_workspace_bytes_invalid_shapes_are_zero(args):
 
 def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     """The general trellis kernels' workspace: one sequence per workgroup of 2^L / 64 threads (2^L below L = 6), a
-    slot per workgroup of the persistent grid, G = 2^(L-k) message floats per LDS buffer.  ckpt > 0: the soft
-    codeword's checkpoint mode (n / c + 1 checkpoint rows, c - 1 segment rows, one saved message; one LDS buffer)."""
+    slot per workgroup of the persistent grid, G = 2^(L-k) message floats per LDS buffer.  ckpt > 0: the checkpoint
+    mode (n / c + 1 checkpoint rows and c - 1 segment rows per message tape; the soft codeword saves one message and
+    uses one LDS buffer, the gradients save two messages and keep the [n] per-step Q input offsets)."""
     S = 1 << L
     tps = S // min(S, 64)
     wps = tps // 64 if tps >= 64 else 1
@@ -112,10 +113,10 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     tapes, nrm = _a256(((n + 1) if ckpt == 0 else (n // ckpt + ckpt)) * G * 4), _a256(n * 4)
     if op == abi.BCJR_OP_SOFT:
         slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0) + (_a256(G * 4) if ckpt else 0)
-    elif op == abi.BCJR_OP_GRAD:
+    elif op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):   # GC: + one float accumulator per state, component
         slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
-    elif op == abi.BCJR_OP_GRAD_CODEBOOK:   # + one float accumulator per state and component
-        slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0) + _a256(S * V * 4)
+        slot += _a256(S * V * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
+        slot += nrm + _a256(2 * G * 4) if ckpt else 0
     else:
         slot = _a256(2 * n * tps * 4)
     return grid * slot
@@ -136,18 +137,20 @@ def test_general_trellis_workspace_formula(L, k, V, B, n):
 @pytest.mark.parametrize("L,k,V", [(16, 2, 1), (16, 3, 1), (16, 4, 2), (12, 1, 2), (8, 2, 1), (4, 1, 1)])
 @pytest.mark.parametrize("B,n", [(1, 1), (16, 2), (4096, 256), (100, 4096), (3, 17)])
 def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
-    """The soft codeword's smallest workspace: checkpoints every c = ceil(sqrt(n)) rows, when that is smaller than the
-    full tape; the other ops have one memory mode."""
+    """The smallest workspace of the soft codeword and the two gradients: checkpoints every c = ceil(sqrt(n)) rows,
+    when that is smaller than the full tape; Viterbi has one memory mode."""
     c = 1
     while c * c < n:
         c += 1
-    full = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT, B, n, L, k, V)
-    want = min(full, _gen_bytes(abi.BCJR_OP_SOFT, B, n, L, k, V, ckpt=c))
-    assert abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V) == want
-    for op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_VITERBI, abi.BCJR_OP_GRAD_CODEBOOK):
-        assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
-    if n >= 256 and L == 16:
-        assert abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, B, n, L, k, V) * 6 < full
+    for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
+        full = abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
+        want = min(full, _gen_bytes(op, B, n, L, k, V, ckpt=c)) if full else 0
+        assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == want
+        if n >= 256 and L == 16 and full:   # the codebook gradient's [2^L][V] accumulator is not reduced
+            factor = 6 if op != abi.BCJR_OP_GRAD_CODEBOOK else 4
+            assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) * factor < full
+    op = abi.BCJR_OP_VITERBI
+    assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
 
 
 def test_workspace_v_matches_the_scalar_query():
@@ -392,9 +395,10 @@ def test_workspace_too_small_or_misaligned_rejected():
     assert _soft(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
     assert _soft(workspace=None, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
     assert _soft(workspace=FAKE + 64, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
-    needg = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 8, 2)
+    needg = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_GRAD, 4, 8, 8, 2, 1)   # the checkpoint mode's sizes
+    assert needg < abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 8, 2)
     assert _grad(workspace_bytes=needg - 1) == abi.BCJR_ERR_WORKSPACE
-    needc = abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 8, 2)
+    needc = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 8, 2, 1)
     assert needc > needg
     assert _gc(workspace_bytes=needg) == abi.BCJR_ERR_WORKSPACE   # the gradient's workspace is not enough
     assert _gc(workspace_bytes=needc - 1) == abi.BCJR_ERR_WORKSPACE
