@@ -193,16 +193,14 @@ def viterbi_tail_biting(w, c, L: int, k: int, mode: int = TB_EXACT):
     A tail-biting path has s_0 = s_n (the non-emitting start equals the last emitting state).  Both modes end with a
     sigma-mode decode, so the result is a tail-biting path and its cost follows the fixed float32 order.
       TB_EXACT:  sigma = the smallest state whose sigma-mode cost is the minimum over all 2^L states.
-      TB_ROTATE: decode the sequence rotated left by n // 2 with a free boundary; sigma = the state of that path at
-                 the original last weight (rotated position n - 1 - n // 2), where the cycle closes.
-    Composed from this module's Viterbi (its own pins cover it); the selection is a plain argmin.
+      TB_ROTATE: decode the sequence rotated left by n // 2 trellis steps with a free boundary; sigma = the state of
+                 that path at the original last step (rotated position n - 1 - n // 2), where the cycle closes.
+    w is [B, n V] for a codebook [2^L, V] (n steps of V weights).  Composed from this module's Viterbi (its own pins
+    cover it); the selection is a plain argmin.
     """
     w = _f32(w)
     c = _f32(c)
-    if c.ndim != 1:
-        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
-    _check_shapes(w, c, L)
-    B, n = w.shape
+    B, n, V = _check_shapes(w, c, L)
     S = 1 << L
     if mode == TB_EXACT:
         reps = np.repeat(w, S, axis=0)
@@ -212,7 +210,7 @@ def viterbi_tail_biting(w, c, L: int, k: int, mode: int = TB_EXACT):
         sigma = np.argmin(costs, axis=1).astype(np.int32)   # first index attaining the minimum
     elif mode == TB_ROTATE:
         r = n // 2
-        st, _, _ = viterbi(np.roll(w, -r, axis=1), c, L, k)
+        st, _, _ = viterbi(np.roll(w, -r * V, axis=1), c, L, k)
         sigma = st[:, n - 1 - r].astype(np.int32)
     else:
         raise ValueError("mode must be TB_EXACT or TB_ROTATE")
@@ -225,12 +223,11 @@ def soft_tail_biting(w, c, L: int, k: int, T: float):
 
     The measure is the mixture over sigma of the sigma-constrained measures with weights Z_sigma / sum Z, so
     w_soft = sum_sigma pi_sigma w_soft_sigma and ln Z = logsumexp_sigma ln Z_sigma (a sigma with no admissible path
-    has Z_sigma = 0).  Composed from this module's sigma-mode soft codeword.
+    has Z_sigma = 0).  w is [B, n V] for a codebook [2^L, V].  Composed from this module's sigma-mode soft codeword.
     """
     w = _f32(w)
-    if np.ndim(c) != 1:
-        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
-    B, n = w.shape
+    _check_shapes(w, _f32(c), L)
+    B, n = w.shape   # n: weights per row (steps times V)
     S = 1 << L
     ws_all, lz_all = soft(np.repeat(w, S, axis=0), c, L, k, T, sigma=np.tile(np.arange(S, dtype=np.int32), B))
     lz_all = lz_all.reshape(B, S)
@@ -249,13 +246,13 @@ def grad_tail_biting(w, c, g, L: int, k: int, T: float):
     With pi_sigma = Z_sigma / sum Z and d ln Z_sigma / d w_u = (2/T) (w_soft_sigma,u - w_u):
       grad_u = sum_sigma pi_sigma grad_sigma,u
              + (2/T) sum_sigma pi_sigma (w_soft_sigma,u - w_soft_u) (F_sigma - sum_sigma' pi_sigma' F_sigma'),
-    F_sigma = sum_t g_t w_soft_sigma,t.  Composed from this module's sigma-mode soft codeword and gradient.
+    F_sigma = sum_t g_t w_soft_sigma,t.  With V weights per step the same holds for every weight component (u, v), the
+    energy being a sum over components.  Composed from this module's sigma-mode soft codeword and gradient.
     """
     w = _f32(w)
     g = _f32(g)
-    if np.ndim(c) != 1:
-        raise ValueError("the tail-biting helpers take a scalar codebook [2^L]")
-    B, n = w.shape
+    _check_shapes(w, _f32(c), L)
+    B, n = w.shape   # n: weights per row (steps times V)
     S = 1 << L
     sig = np.tile(np.arange(S, dtype=np.int32), B)
     W = np.repeat(w, S, axis=0)

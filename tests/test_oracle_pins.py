@@ -669,3 +669,53 @@ def test_vector_trellis_with_a_silent_component_is_the_scalar_trellis(oracle_mod
     sb, _, cb = oracle_mod.viterbi(w2, c2, L, k)
     np.testing.assert_array_equal(sa, sb)
     np.testing.assert_array_equal(ca, cb)
+
+
+# ------------------------------------------- P13 tail-biting on the general trellis (k = 1, 3, 4; V weights per step)
+# The P10 and P11 pins again, on trellises other than k = 2, V = 1: every quantity by enumerating the paths with
+# s_0 = s_n.
+
+TB_TRELLISES = [(4, 1, 6, 1), (6, 3, 4, 1), (8, 4, 3, 1), (4, 2, 5, 2), (4, 1, 5, 2), (6, 3, 3, 2), (8, 4, 2, 2),
+                (4, 2, 4, 3)]
+TB_IDS = [f"L{L}k{k}n{n}V{V}" for L, k, n, V in TB_TRELLISES]
+
+
+@pytest.mark.parametrize("L,k,n,V", TB_TRELLISES, ids=TB_IDS)
+def test_vector_tail_biting_exact_matches_brute_force(oracle_mod, L, k, n, V):
+    w, c, _ = _vec_inputs(L, n, V, 1300 + 31 * L + 7 * k + V)
+    st, wh, cost, sig = oracle_mod.viterbi_tail_biting(w, c, L, k, oracle_mod.TB_EXACT)
+    for b in range(w.shape[0]):
+        best, arg, sets = _brute_tail_biting(L, k, n, w[b], c)
+        assert cost[b] == best and sig[b] == arg
+        assert any(np.array_equal(st[b], p) for p in sets[arg])
+        np.testing.assert_array_equal(wh[b], c[st[b]].reshape(-1))
+
+
+@pytest.mark.parametrize("L,k,n,V", [(4, 1, 7, 2), (6, 3, 4, 1), (8, 4, 3, 2)], ids=["L4k1V2", "L6k3V1", "L8k4V2"])
+def test_vector_tail_biting_rotate_matches_brute_force_composition(oracle_mod, L, k, n, V):
+    """Rotation by n // 2 trellis steps (n // 2 * V weights), then the sigma-constrained minimum, by brute force."""
+    w, c, _ = _vec_inputs(L, n, V, 1400 + L + k, B=4)
+    st, _, cost, sig = oracle_mod.viterbi_tail_biting(w, c, L, k, oracle_mod.TB_ROTATE)
+    free = pins.free_paths(L, k, n)
+    r = n // 2
+    for b in range(w.shape[0]):
+        acc, idx = pins.brute_viterbi_fp32(free, np.roll(w[b], -r * V), c)
+        assert sig[b] in {int(free[i][n - 1 - r]) for i in idx}
+        acc2, _ = pins.brute_viterbi_fp32(pins.sigma_paths(L, k, n, int(sig[b])), w[b], c)
+        assert cost[b] == acc2.min()
+
+
+@pytest.mark.parametrize("L,k,n,V", TB_TRELLISES, ids=TB_IDS)
+@pytest.mark.parametrize("T", [1.0, 0.3])
+def test_vector_soft_tail_biting_matches_brute_force(oracle_mod, L, k, n, V, T):
+    w, c, g = _vec_inputs(L, n, V, 1500 + 31 * L + 7 * k + V)
+    paths = _tail_biting_paths(L, k, n)
+    ws, lz = oracle_mod.soft_tail_biting(w, c, L, k, T)
+    gr, ws2 = oracle_mod.grad_tail_biting(w, c, g, L, k, T)
+    for b in range(w.shape[0]):
+        ref, lnz, _ = pins.brute_soft(paths, w[b], c, T)
+        np.testing.assert_allclose(ws[b], ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ws2[b], ref, rtol=0, atol=1e-12)
+        assert abs(lz[b] - lnz) <= 1e-12 * max(1.0, abs(lnz))
+        gref = pins.brute_jacobian(paths, w[b], c, T) @ g[b].astype(np.float64)
+        np.testing.assert_allclose(gr[b], gref, rtol=0, atol=1e-11 * max(1.0, np.abs(gref).max()))
