@@ -214,40 +214,47 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
 
 def soft_codeword_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0, *,
                               return_log_z: bool = False, workspace: torch.Tensor | None = None):
-    """Soft codeword [B, n] (and ln Z [B]) under the tail-biting measure: every path with s_0 = s_n (L <= 10)."""
+    """Soft codeword with w's shape (and ln Z [B]) under the tail-biting measure: every path with s_0 = s_n
+    (L <= 10).  w [B, n] with codebook [2^L], or w [B, n V] with codebook [2^L, V]."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
-    if codebook.dim() != 1:
-        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
-    if w.dim() != 2:
-        raise ValueError("w must be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
     out = torch.empty_like(w)
     lz = torch.empty(B, dtype=torch.float32, device=w.device) if return_log_z else None
-    ws, need = _workspace(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, w.device, workspace)
-    _check(abi.bcjr_soft_codeword_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
-                                              out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.bcjr_soft_codeword_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
+                                                  out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(),
+                                                  _stream(w.device)))
+    else:
+        _check(abi.bcjr_soft_codeword_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
+                                                    out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(),
+                                                    _stream(w.device)))
     return (out, lz) if return_log_z else out
 
 
 def soft_codeword_grad_tail_biting(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int,
                                    k: int = 2, T: float = 1.0, *, return_w_soft: bool = False,
                                    workspace: torch.Tensor | None = None):
-    """dL/dw [B, n] under the tail-biting measure given dL/dw_soft [B, n] (and that measure's soft codeword)."""
+    """dL/dw under the tail-biting measure given dL/dw_soft, both with w's shape (and that measure's soft
+    codeword).  w [B, n] with codebook [2^L], or w [B, n V] with codebook [2^L, V]."""
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
-    if codebook.dim() != 1:
-        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
     g = _f32(grad_w_soft, "grad_w_soft")
-    if w.dim() != 2 or g.shape != w.shape:
-        raise ValueError("w and grad_w_soft must both be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
+    if g.shape != w.shape:
+        raise ValueError("grad_w_soft must have w's shape")
     grad = torch.empty_like(w)
     ws_out = torch.empty_like(w) if return_w_soft else None
-    ws, need = _workspace(abi.BCJR_OP_GRAD_TAIL_BITING, B, n, L, k, w.device, workspace)
-    _check(abi.bcjr_soft_codeword_grad_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
-                                                   g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
-                                                   ws.numel(), _stream(w.device)))
+    ws, need = _workspace(abi.BCJR_OP_GRAD_TAIL_BITING, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.bcjr_soft_codeword_grad_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
+                                                       g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
+                                                       ws.numel(), _stream(w.device)))
+    else:
+        _check(abi.bcjr_soft_codeword_grad_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
+                                                         g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
+                                                         ws.numel(), _stream(w.device)))
     return (grad, ws_out) if return_w_soft else grad
 
 
@@ -257,26 +264,28 @@ _TB_MODES = {"exact": (abi.BCJR_TB_EXACT, abi.BCJR_OP_VITERBI_TB_EXACT),
 
 def viterbi_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, mode: str = "exact", *,
                         workspace: torch.Tensor | None = None):
-    """(states [B, n] int32, w_hard [B, n], cost [B], sigma [B] int32) of the minimum-energy tail-biting paths
-    (s_0 = s_n), the start state chosen ``"exact"``ly (L <= 10) or by ``"rotate"``-and-decode."""
+    """(states [B, n] int32, w_hard with w's shape, cost [B], sigma [B] int32) of the minimum-energy tail-biting
+    paths (s_0 = s_n), the start state chosen ``"exact"``ly (L <= 10) or by ``"rotate"``-and-decode.  w [B, n] with
+    codebook [2^L], or w [B, n V] with codebook [2^L, V] (n trellis steps)."""
     if mode not in _TB_MODES:
         raise ValueError(f"mode must be one of {sorted(_TB_MODES)}")
     tb_mode, op = _TB_MODES[mode]
     w = _f32(w, "w")
     codebook = _f32(codebook, "codebook")
-    if codebook.dim() != 1:
-        raise ValueError("the tail-biting operations take a codebook [2^L] (one weight per step)")
-    if w.dim() != 2:
-        raise ValueError("w must be [B, n]")
-    B, n = w.shape
+    B, n, V = _steps(w, codebook, L)
     states = torch.empty((B, n), dtype=torch.int32, device=w.device)
     w_hard = torch.empty_like(w)
     cost = torch.empty(B, dtype=torch.float32, device=w.device)
     sigma = torch.empty(B, dtype=torch.int32, device=w.device)
-    ws, need = _workspace(op, B, n, L, k, w.device, workspace)
-    _check(abi.viterbi_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, tb_mode, states.data_ptr(),
-                                   w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(), ws.data_ptr(), ws.numel(),
-                                   _stream(w.device)))
+    ws, need = _workspace(op, B, n, L, k, w.device, workspace, V)
+    if V == 1:
+        _check(abi.viterbi_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, tb_mode, states.data_ptr(),
+                                       w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(), ws.data_ptr(),
+                                       ws.numel(), _stream(w.device)))
+    else:
+        _check(abi.viterbi_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, tb_mode,
+                                         states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(),
+                                         ws.data_ptr(), ws.numel(), _stream(w.device)))
     return states, w_hard, cost, sigma
 
 

@@ -34,7 +34,8 @@ BCJR_TB_ROTATE = 1
 EXPORTS = ("bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook", "viterbi_hard_code",
            "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting", "bcjr_soft_codeword_grad_tail_biting",
            "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v", "bcjr_soft_codeword_grad_codebook_v",
-           "viterbi_hard_code_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_min",
+           "viterbi_hard_code_v", "bcjr_soft_codeword_tail_biting_v", "bcjr_soft_codeword_grad_tail_biting_v",
+           "viterbi_tail_biting_v", "bcjr_workspace_bytes", "bcjr_workspace_bytes_min",
            "bcjr_workspace_bytes_v", "bcjr_status_string")
 
 _lib = None
@@ -72,6 +73,13 @@ def load() -> ctypes.CDLL:
     lib.bcjr_soft_codeword_grad_codebook_v.restype = ctypes.c_int
     lib.viterbi_hard_code_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.viterbi_hard_code_v.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_tail_biting_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, vp, vp, vp, sz, vp]
+    lib.bcjr_soft_codeword_tail_biting_v.restype = ctypes.c_int
+    lib.bcjr_soft_codeword_grad_tail_biting_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, vp, vp, vp, vp, sz,
+                                                          vp]
+    lib.bcjr_soft_codeword_grad_tail_biting_v.restype = ctypes.c_int
+    lib.viterbi_tail_biting_v.argtypes = [vp, vp, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    lib.viterbi_tail_biting_v.restype = ctypes.c_int
     lib.bcjr_workspace_bytes.argtypes = [i32, i64, i64, i32, i32]
     lib.bcjr_workspace_bytes.restype = sz
     lib.bcjr_workspace_bytes_v.argtypes = [i32, i64, i64, i32, i32, i32]
@@ -148,6 +156,24 @@ def viterbi_hard_code_v(w, codebook, B, n, L, k, V, boundary_state, states, w_ha
                         stream) -> int:
     return load().viterbi_hard_code_v(w, codebook, B, n, L, k, V, boundary_state, states, w_hard, cost, workspace,
                                       workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_tail_biting_v(w, codebook, B, n, L, k, V, T, w_soft, log_z, workspace, workspace_bytes,
+                                     stream) -> int:
+    return load().bcjr_soft_codeword_tail_biting_v(w, codebook, B, n, L, k, V, T, w_soft, log_z, workspace,
+                                                   workspace_bytes, stream)
+
+
+def bcjr_soft_codeword_grad_tail_biting_v(w, codebook, B, n, L, k, V, T, grad_w_soft, grad_w, w_soft, workspace,
+                                          workspace_bytes, stream) -> int:
+    return load().bcjr_soft_codeword_grad_tail_biting_v(w, codebook, B, n, L, k, V, T, grad_w_soft, grad_w, w_soft,
+                                                        workspace, workspace_bytes, stream)
+
+
+def viterbi_tail_biting_v(w, codebook, B, n, L, k, V, mode, states, w_hard, cost, sigma, workspace, workspace_bytes,
+                          stream) -> int:
+    return load().viterbi_tail_biting_v(w, codebook, B, n, L, k, V, mode, states, w_hard, cost, sigma, workspace,
+                                        workspace_bytes, stream)
 
 
 def bcjr_workspace_bytes(op, B, n, L, k) -> int:

@@ -60,14 +60,6 @@ int check_dims(int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
     return BCJR_OK;
 }
 
-// The entry points that exist for k = 2, V = 1 only (codebook gradient, tail-biting).
-int check_shape(int64_t B, int64_t n, int32_t L, int32_t k) {
-    const int rc = check_dims(B, n, L, k, 1);
-    if (rc) return rc;
-    if (k != 2) return BCJR_ERR_UNSUPPORTED;
-    return BCJR_OK;
-}
-
 // Soft codeword, gradient and Viterbi: the k = 2, V = 1 kernels, or the general ones.
 int check_shape_v(int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
     const int rc = check_dims(B, n, L, k, V);
@@ -228,6 +220,45 @@ MixturePlan make_mixture_plan(bool with_grad, int64_t B, int64_t n, int32_t L) {
     return m;
 }
 
+// The same two plans for the general trellis kernels (one sequence per workgroup; slots as in make_gen_plan).
+struct GenTailBitingPlan {
+    bool ok;
+    GenPlan rows, first;
+    size_t slots_bytes, aux_off, sigma_off, total;
+};
+
+GenTailBitingPlan make_gen_tb_plan(int32_t mode, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    GenTailBitingPlan t{};
+    t.rows = make_gen_plan(BCJR_OP_VITERBI, B, n, L, k, V);
+    t.first = mode == BCJR_TB_EXACT ? make_gen_plan(BCJR_OP_VITERBI, B << L, n, L, k, V) : t.rows;
+    t.ok = t.rows.ok && t.first.ok;
+    t.slots_bytes = align256(t.first.total > t.rows.total ? t.first.total : t.rows.total);
+    t.aux_off = t.slots_bytes;
+    const size_t aux = mode == BCJR_TB_EXACT ? (size_t)(B << L) * 4 : (size_t)B * (size_t)n * 4;
+    t.sigma_off = t.aux_off + align256(aux);
+    t.total = t.sigma_off + align256((size_t)B * 4);
+    return t;
+}
+
+struct GenMixturePlan {
+    bool ok;
+    GenPlan soft, grad;
+    size_t ws_off, lz_off, gr_off, total;
+};
+
+GenMixturePlan make_gen_mixture_plan(bool with_grad, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    GenMixturePlan m{};
+    const int64_t S = B << L;   // one virtual sequence per (row, sigma)
+    m.soft = make_gen_plan(BCJR_OP_SOFT, S, n, L, k, V);
+    m.grad = with_grad ? make_gen_plan(BCJR_OP_GRAD, S, n, L, k, V) : m.soft;
+    m.ok = m.soft.ok && m.grad.ok;
+    m.ws_off = align256(m.grad.total > m.soft.total ? m.grad.total : m.soft.total);
+    m.lz_off = m.ws_off + align256((size_t)S * (size_t)n * V * 4);
+    m.gr_off = m.lz_off + align256((size_t)S * 4);
+    m.total = m.gr_off + (with_grad ? align256((size_t)S * (size_t)n * V * 4) : 0);
+    return m;
+}
+
 int check_tb_mode(int32_t mode, int32_t L) {
     if (mode == BCJR_TB_ROTATE) return BCJR_OK;
     if (mode == BCJR_TB_EXACT && L <= kMaxTailBitingExactL) return BCJR_OK;
@@ -239,14 +270,25 @@ int check_tb_mode(int32_t mode, int32_t L) {
 extern "C" {
 
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
+    if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
+    if (check_shape_v(B, n, L, k, V) != BCJR_OK) return 0;
     if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI || op == BCJR_OP_GRAD_CODEBOOK) {
-        if (check_shape_v(B, n, L, k, V) != BCJR_OK) return 0;
         if (tuned(k, V)) return make_plan(op, B, n, L).total;
         const GenPlan p = make_gen_plan(op, B, n, L, k, V);
         return p.ok ? p.total : 0;
     }
-    if (V != 1) return 0;
-    return bcjr_workspace_bytes(op, B, n, L, k);
+    if (op == BCJR_OP_SOFT_TAIL_BITING || op == BCJR_OP_GRAD_TAIL_BITING) {
+        if (L > kMaxTailBitingExactL) return 0;
+        const bool with_grad = op == BCJR_OP_GRAD_TAIL_BITING;
+        if (tuned(k, V)) return make_mixture_plan(with_grad, B, n, L).total;
+        const GenMixturePlan m = make_gen_mixture_plan(with_grad, B, n, L, k, V);
+        return m.ok ? m.total : 0;
+    }
+    const int32_t mode = op == BCJR_OP_VITERBI_TB_EXACT ? BCJR_TB_EXACT : BCJR_TB_ROTATE;
+    if (check_tb_mode(mode, L) != BCJR_OK) return 0;
+    if (tuned(k, V)) return make_tb_plan(mode, B, n, L).total;
+    const GenTailBitingPlan t = make_gen_tb_plan(mode, B, n, L, k, V);
+    return t.ok ? t.total : 0;
 }
 
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
@@ -257,20 +299,7 @@ size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int
 }
 
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k) {
-    if (op < BCJR_OP_SOFT || op > BCJR_OP_GRAD_TAIL_BITING) return 0;
-    if (op == BCJR_OP_SOFT || op == BCJR_OP_GRAD || op == BCJR_OP_VITERBI || op == BCJR_OP_GRAD_CODEBOOK)
-        return bcjr_workspace_bytes_v(op, B, n, L, k, 1);
-    if (check_shape(B, n, L, k) != BCJR_OK) return 0;
-    if (op == BCJR_OP_SOFT_TAIL_BITING || op == BCJR_OP_GRAD_TAIL_BITING) {
-        if (L > kMaxTailBitingExactL) return 0;
-        return make_mixture_plan(op == BCJR_OP_GRAD_TAIL_BITING, B, n, L).total;
-    }
-    if (op == BCJR_OP_VITERBI_TB_EXACT || op == BCJR_OP_VITERBI_TB_ROTATE) {
-        const int32_t mode = op == BCJR_OP_VITERBI_TB_EXACT ? BCJR_TB_EXACT : BCJR_TB_ROTATE;
-        if (check_tb_mode(mode, L) != BCJR_OK) return 0;
-        return make_tb_plan(mode, B, n, L).total;
-    }
-    return make_plan(op, B, n, L).total;
+    return bcjr_workspace_bytes_v(op, B, n, L, k, 1);
 }
 
 const char* bcjr_status_string(int32_t status) {
@@ -280,8 +309,8 @@ const char* bcjr_status_string(int32_t status) {
         case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16, V >= 1";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
         case BCJR_ERR_UNSUPPORTED:
-            return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2 (k = 2, V = 1 only for the codebook "
-                   "gradient and tail-biting; the gradient at k = 1 needs L <= 15); exact tail-biting needs L <= 10";
+            return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2 (the gradient at k = 1 needs "
+                   "L <= 15); exact tail-biting and the tail-biting soft codeword and gradient need L <= 10";
         case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
@@ -487,6 +516,255 @@ int viterbi_impl(const float* w, const float* codebook, int64_t B, int64_t n, in
     return hip_status(launch_viterbi(L, a, p.grid, static_cast<hipStream_t>(stream)));
 }
 
+// Tail-biting: the per-(row, sigma) or rotated passes of the k = 2, V = 1 kernels, or of the general ones, then the
+// selection / combine kernels (which see a row as n V floats).
+int soft_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
+                 float T, float* w_soft, float* log_z, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, V);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    hipError_t e;
+    if (!tuned(k, V)) {
+        const GenMixturePlan mp = make_gen_mixture_plan(false, B, n, L, k, V);
+        if (!mp.ok) return BCJR_ERR_UNSUPPORTED;
+        if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+            return BCJR_ERR_WORKSPACE;
+        float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+        float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.B = B << L;
+        a.n = (int)n;
+        a.L = L;
+        a.scale = scale;
+        a.w_soft = ws_all;
+        a.log_z = lz_all;
+        a.ws = ws;
+        a.slot_bytes = mp.soft.slot_bytes;
+        a.dbl = mp.soft.dbl;
+        a.sigma_enum = 1;
+        if ((e = launch_general(0, k, V, a, mp.soft.grid, mp.soft.threads, mp.soft.lds, st)) != hipSuccess)
+            return hip_status(e);
+        return hip_status(launch_tb_soft_combine(ws_all, lz_all, B, (int)(n * V), 1 << L, w_soft, log_z, st));
+    }
+    const MixturePlan mp = make_mixture_plan(false, B, n, L);
+    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+    SoftArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B << L;
+    a.n = (int)n;
+    a.scale = scale;
+    a.w_soft = ws_all;
+    a.log_z = lz_all;
+    a.ws = ws;
+    a.slot_bytes = mp.soft.slot_bytes;
+    a.sigma_enum = 1;
+    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
+    return hip_status(launch_tb_soft_combine(ws_all, lz_all, B, (int)n, 1 << L, w_soft, log_z, st));
+}
+
+int grad_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
+                 float T, const float* grad_w_soft, float* grad_w, float* w_soft, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !grad_w_soft || !grad_w) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, V);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
+    const float two_over_T = (float)(2.0 / (double)T);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    hipError_t e;
+    if (!tuned(k, V)) {
+        const GenMixturePlan mp = make_gen_mixture_plan(true, B, n, L, k, V);
+        if (!mp.ok) return BCJR_ERR_UNSUPPORTED;
+        if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+            return BCJR_ERR_WORKSPACE;
+        float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+        float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+        float* gr_all = reinterpret_cast<float*>(ws + mp.gr_off);
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.B = B << L;
+        a.n = (int)n;
+        a.L = L;
+        a.scale = scale;
+        a.w_soft = ws_all;
+        a.log_z = lz_all;
+        a.ws = ws;
+        a.slot_bytes = mp.soft.slot_bytes;
+        a.dbl = mp.soft.dbl;
+        a.sigma_enum = 1;
+        if ((e = launch_general(0, k, V, a, mp.soft.grid, mp.soft.threads, mp.soft.lds, st)) != hipSuccess)
+            return hip_status(e);
+        GenArgs ga{};
+        ga.w = w;
+        ga.cb = codebook;
+        ga.g = grad_w_soft;
+        ga.B = B << L;
+        ga.n = (int)n;
+        ga.L = L;
+        ga.scale = scale;
+        ga.two_over_T = two_over_T;
+        ga.grad = gr_all;
+        ga.ws = ws;
+        ga.slot_bytes = mp.grad.slot_bytes;
+        ga.dbl = mp.grad.dbl;
+        ga.sigma_enum = 1;
+        if ((e = launch_general(1, k, V, ga, mp.grad.grid, mp.grad.threads, mp.grad.lds, st)) != hipSuccess)
+            return hip_status(e);
+        return hip_status(launch_tb_grad_combine(ws_all, lz_all, gr_all, grad_w_soft, B, (int)(n * V), 1 << L,
+                                                 two_over_T, grad_w, w_soft, st));
+    }
+    const MixturePlan mp = make_mixture_plan(true, B, n, L);
+    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
+    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
+    float* gr_all = reinterpret_cast<float*>(ws + mp.gr_off);
+    SoftArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B << L;
+    a.n = (int)n;
+    a.scale = scale;
+    a.w_soft = ws_all;
+    a.log_z = lz_all;
+    a.ws = ws;
+    a.slot_bytes = mp.soft.slot_bytes;
+    a.sigma_enum = 1;
+    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
+    GradArgs ga{};
+    ga.w = w;
+    ga.cb = codebook;
+    ga.g = grad_w_soft;
+    ga.B = B << L;
+    ga.n = (int)n;
+    ga.scale = scale;
+    ga.two_over_T = two_over_T;
+    ga.grad = gr_all;
+    ga.ws = ws;
+    ga.slot_bytes = mp.grad.slot_bytes;
+    ga.sigma_enum = 1;
+    if ((e = launch_grad(L, ga, mp.grad.grid, st)) != hipSuccess) return hip_status(e);
+    return hip_status(launch_tb_grad_combine(ws_all, lz_all, gr_all, grad_w_soft, B, (int)n, 1 << L, two_over_T,
+                                             grad_w, w_soft, st));
+}
+
+int viterbi_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V,
+                    int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (!w || !codebook || !states) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, V);
+    if (rc) return rc;
+    if ((rc = check_tb_mode(mode, L))) return rc;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int r = (int)(n / 2);   // rotate: the rows rotated left by n / 2 trellis steps
+    hipError_t e;
+    if (!tuned(k, V)) {
+        const GenTailBitingPlan tp = make_gen_tb_plan(mode, B, n, L, k, V);
+        if (!tp.ok) return BCJR_ERR_UNSUPPORTED;
+        if (workspace == nullptr || workspace_bytes < tp.total || ((uintptr_t)workspace & 255u) != 0)
+            return BCJR_ERR_WORKSPACE;
+        int32_t* sig_ws = reinterpret_cast<int32_t*>(ws + tp.sigma_off);
+        GenArgs f{};
+        f.w = w;
+        f.cb = codebook;
+        f.n = (int)n;
+        f.L = L;
+        f.ws = ws;
+        f.slot_bytes = tp.first.slot_bytes;
+        f.dbl = tp.first.dbl;
+        if (mode == BCJR_TB_EXACT) {   // the cost of every (row, sigma), no traceback
+            float* costs = reinterpret_cast<float*>(ws + tp.aux_off);
+            f.B = B << L;
+            f.sigma_enum = 1;
+            f.cost = costs;
+            if ((e = launch_general(2, k, V, f, tp.first.grid, tp.first.threads, tp.first.lds, st)) != hipSuccess)
+                return hip_status(e);
+            if ((e = launch_tb_select(costs, B, 1 << L, sig_ws, sigma, st)) != hipSuccess) return hip_status(e);
+        } else {
+            int32_t* rot_states = reinterpret_cast<int32_t*>(ws + tp.aux_off);
+            f.B = B;
+            f.rot = r;
+            f.states = rot_states;
+            if ((e = launch_general(2, k, V, f, tp.first.grid, tp.first.threads, tp.first.lds, st)) != hipSuccess)
+                return hip_status(e);
+            if ((e = launch_tb_rotate_sigma(rot_states, B, (int)n, (int)(n - 1 - r), sig_ws, sigma, st)) !=
+                hipSuccess)
+                return hip_status(e);
+        }
+        GenArgs a{};
+        a.w = w;
+        a.cb = codebook;
+        a.B = B;
+        a.n = (int)n;
+        a.L = L;
+        a.sigma = sig_ws;
+        a.states = states;
+        a.w_hard = w_hard;
+        a.cost = cost;
+        a.ws = ws;
+        a.slot_bytes = tp.rows.slot_bytes;
+        a.dbl = tp.rows.dbl;
+        return hip_status(launch_general(2, k, V, a, tp.rows.grid, tp.rows.threads, tp.rows.lds, st));
+    }
+    const TailBitingPlan tp = make_tb_plan(mode, B, n, L);
+    if (workspace == nullptr || workspace_bytes < tp.total || ((uintptr_t)workspace & 255u) != 0)
+        return BCJR_ERR_WORKSPACE;
+    int32_t* sig_ws = reinterpret_cast<int32_t*>(ws + tp.sigma_off);
+
+    // first pass: the cost of every (row, sigma), or the free decode of the rows rotated left by n / 2
+    ViterbiArgs f{};
+    f.w = w;
+    f.cb = codebook;
+    f.n = (int)n;
+    f.ws = ws;
+    f.slot_bytes = tp.first.slot_bytes;
+    if (mode == BCJR_TB_EXACT) {
+        float* costs = reinterpret_cast<float*>(ws + tp.aux_off);
+        f.B = B << L;
+        f.sigma_enum = 1;
+        f.cost = costs;
+        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
+        if ((e = launch_tb_select(costs, B, 1 << L, sig_ws, sigma, st)) != hipSuccess) return hip_status(e);
+    } else {
+        int32_t* rot_states = reinterpret_cast<int32_t*>(ws + tp.aux_off);
+        f.B = B;
+        f.rot = r;
+        f.states = rot_states;
+        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
+        if ((e = launch_tb_rotate_sigma(rot_states, B, (int)n, (int)(n - 1 - r), sig_ws, sigma, st)) != hipSuccess)
+            return hip_status(e);
+    }
+    // second pass: the sigma-constrained decode of the rows with the chosen start state
+    ViterbiArgs a{};
+    a.w = w;
+    a.cb = codebook;
+    a.B = B;
+    a.n = (int)n;
+    a.sigma = sig_ws;
+    a.states = states;
+    a.w_hard = w_hard;
+    a.cost = cost;
+    a.ws = ws;
+    a.slot_bytes = tp.rows.slot_bytes;
+    return hip_status(launch_viterbi(L, a, tp.rows.grid, st));
+}
+
 }  // namespace
 
 extern "C" {
@@ -552,133 +830,41 @@ int viterbi_hard_code_v(const float* w, const float* codebook, int64_t B, int64_
 int bcjr_soft_codeword_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
                                    int32_t k, float T, float* w_soft, float* log_z, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
-    if (rc) return rc;
-    if ((rc = check_temp(T))) return rc;
-    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
-    const MixturePlan mp = make_mixture_plan(false, B, n, L);
-    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
-        return BCJR_ERR_WORKSPACE;
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
-    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    SoftArgs a{};
-    a.w = w;
-    a.cb = codebook;
-    a.B = B << L;
-    a.n = (int)n;
-    a.scale = (float)std::sqrt(1.4426950408889634 / (double)T);
-    a.w_soft = ws_all;
-    a.log_z = lz_all;
-    a.ws = ws;
-    a.slot_bytes = mp.soft.slot_bytes;
-    a.sigma_enum = 1;
-    hipError_t e;
-    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
-    return hip_status(launch_tb_soft_combine(ws_all, lz_all, B, (int)n, 1 << L, w_soft, log_z, st));
+    return soft_tb_impl(w, codebook, B, n, L, k, 1, T, w_soft, log_z, workspace, workspace_bytes, stream);
+}
+
+int bcjr_soft_codeword_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                     int32_t k, int32_t V, float T, float* w_soft, float* log_z, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    return soft_tb_impl(w, codebook, B, n, L, k, V, T, w_soft, log_z, workspace, workspace_bytes, stream);
 }
 
 int bcjr_soft_codeword_grad_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
                                         int32_t k, float T, const float* grad_w_soft, float* grad_w, float* w_soft,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-    if (!w || !codebook || !grad_w_soft || !grad_w) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
-    if (rc) return rc;
-    if ((rc = check_temp(T))) return rc;
-    if (L > kMaxTailBitingExactL) return BCJR_ERR_UNSUPPORTED;
-    const MixturePlan mp = make_mixture_plan(true, B, n, L);
-    if (workspace == nullptr || workspace_bytes < mp.total || ((uintptr_t)workspace & 255u) != 0)
-        return BCJR_ERR_WORKSPACE;
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    float* ws_all = reinterpret_cast<float*>(ws + mp.ws_off);
-    float* lz_all = reinterpret_cast<float*>(ws + mp.lz_off);
-    float* gr_all = reinterpret_cast<float*>(ws + mp.gr_off);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
-    SoftArgs a{};
-    a.w = w;
-    a.cb = codebook;
-    a.B = B << L;
-    a.n = (int)n;
-    a.scale = scale;
-    a.w_soft = ws_all;
-    a.log_z = lz_all;
-    a.ws = ws;
-    a.slot_bytes = mp.soft.slot_bytes;
-    a.sigma_enum = 1;
-    hipError_t e;
-    if ((e = launch_soft(L, a, mp.soft.grid, st)) != hipSuccess) return hip_status(e);
-    GradArgs ga{};
-    ga.w = w;
-    ga.cb = codebook;
-    ga.g = grad_w_soft;
-    ga.B = B << L;
-    ga.n = (int)n;
-    ga.scale = scale;
-    ga.two_over_T = (float)(2.0 / (double)T);
-    ga.grad = gr_all;
-    ga.ws = ws;
-    ga.slot_bytes = mp.grad.slot_bytes;
-    ga.sigma_enum = 1;
-    if ((e = launch_grad(L, ga, mp.grad.grid, st)) != hipSuccess) return hip_status(e);
-    return hip_status(launch_tb_grad_combine(ws_all, lz_all, gr_all, grad_w_soft, B, (int)n, 1 << L,
-                                             (float)(2.0 / (double)T), grad_w, w_soft, st));
+    return grad_tb_impl(w, codebook, B, n, L, k, 1, T, grad_w_soft, grad_w, w_soft, workspace, workspace_bytes,
+                        stream);
+}
+
+int bcjr_soft_codeword_grad_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                          int32_t k, int32_t V, float T, const float* grad_w_soft, float* grad_w,
+                                          float* w_soft, void* workspace, size_t workspace_bytes, void* stream) {
+    return grad_tb_impl(w, codebook, B, n, L, k, V, T, grad_w_soft, grad_w, w_soft, workspace, workspace_bytes,
+                        stream);
 }
 
 int viterbi_tail_biting(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
                         int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma, void* workspace,
                         size_t workspace_bytes, void* stream) {
-    if (!w || !codebook || !states) return BCJR_ERR_NULL;
-    int rc = check_shape(B, n, L, k);
-    if (rc) return rc;
-    if ((rc = check_tb_mode(mode, L))) return rc;
-    const TailBitingPlan tp = make_tb_plan(mode, B, n, L);
-    if (workspace == nullptr || workspace_bytes < tp.total || ((uintptr_t)workspace & 255u) != 0)
-        return BCJR_ERR_WORKSPACE;
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    int32_t* sig_ws = reinterpret_cast<int32_t*>(ws + tp.sigma_off);
-    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return viterbi_tb_impl(w, codebook, B, n, L, k, 1, mode, states, w_hard, cost, sigma, workspace,
+                           workspace_bytes, stream);
+}
 
-    // first pass: the cost of every (row, sigma), or the free decode of the rows rotated left by n / 2
-    ViterbiArgs f{};
-    f.w = w;
-    f.cb = codebook;
-    f.n = (int)n;
-    f.ws = ws;
-    f.slot_bytes = tp.first.slot_bytes;
-    hipError_t e;
-    if (mode == BCJR_TB_EXACT) {
-        float* costs = reinterpret_cast<float*>(ws + tp.aux_off);
-        f.B = B << L;
-        f.sigma_enum = 1;
-        f.cost = costs;
-        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
-        if ((e = launch_tb_select(costs, B, 1 << L, sig_ws, sigma, st)) != hipSuccess) return hip_status(e);
-    } else {
-        int32_t* rot_states = reinterpret_cast<int32_t*>(ws + tp.aux_off);
-        const int r = (int)(n / 2);
-        f.B = B;
-        f.rot = r;
-        f.states = rot_states;
-        if ((e = launch_viterbi(L, f, tp.first.grid, st)) != hipSuccess) return hip_status(e);
-        if ((e = launch_tb_rotate_sigma(rot_states, B, (int)n, (int)(n - 1 - r), sig_ws, sigma, st)) != hipSuccess)
-            return hip_status(e);
-    }
-    // second pass: the sigma-constrained decode of the rows with the chosen start state
-    ViterbiArgs a{};
-    a.w = w;
-    a.cb = codebook;
-    a.B = B;
-    a.n = (int)n;
-    a.sigma = sig_ws;
-    a.states = states;
-    a.w_hard = w_hard;
-    a.cost = cost;
-    a.ws = ws;
-    a.slot_bytes = tp.rows.slot_bytes;
-    return hip_status(launch_viterbi(L, a, tp.rows.grid, st));
+int viterbi_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                          int32_t V, int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return viterbi_tb_impl(w, codebook, B, n, L, k, V, mode, states, w_hard, cost, sigma, workspace,
+                           workspace_bytes, stream);
 }
 
 }  // extern "C"

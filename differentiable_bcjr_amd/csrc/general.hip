@@ -368,9 +368,11 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
     own.fwd_next(-1, cnx);
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
-        const float* wb = args.w + b * (int64_t)n * V;
-        const bool has_sigma = args.sigma != nullptr;
-        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+        const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
+        const float* wb = args.w + row * (int64_t)n * V;
+        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+        const uint32_t sig = args.sigma_enum ? (uint32_t)(b & ((1 << L) - 1))
+                                             : has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
 
         // ------------------------------------------------------------------ forward
 #pragma unroll
@@ -776,6 +778,8 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
         }
     };
 
+    const int rot = args.rot;
+    const bool trace = args.states != nullptr;   // else costs only: no back pointers, no traceback
     // pending traceback (lane tau == 0): the previous sequence's path is traced back one step per forward step
     int64_t pend_b = -1;
     int pend_t = 0;
@@ -799,9 +803,11 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 
     int64_t iter = 0;
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x, ++iter) {
-        const float* wb = args.w + b * (int64_t)n * V;
-        const bool has_sigma = args.sigma != nullptr;
-        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+        const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
+        const float* wb = args.w + row * (int64_t)n * V;
+        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+        const uint32_t sig = args.sigma_enum ? (uint32_t)(b & ((1 << L) - 1))
+                                             : has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
         const uint32_t par = (uint32_t)(iter & 1);
 
 #pragma unroll
@@ -819,8 +825,9 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
             const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
             float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
             float wt[V];
+            const int tw = t + rot < n ? t + rot : t + rot - n;   // the row's step emitted at step t
 #pragma unroll
-            for (int v = 0; v < V; ++v) wt[v] = wb[t * V + v];
+            for (int v = 0; v < V; ++v) wt[v] = wb[tw * V + v];
             float vin[BPT][P];
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
@@ -858,7 +865,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
                     }
                     GEN_SCHED_BARRIER();
                 }
-            buf_st(__builtin_bit_cast(float, word), tape, 4u * tau, par * buf_bytes + (uint32_t)t * (TPS * 4u));
+            if (trace) buf_st(__builtin_bit_cast(float, word), tape, 4u * tau, par * buf_bytes + (uint32_t)t * (TPS * 4u));
             if (tau == 0 && pend_b >= 0 && pend_t >= 1) pend_step();
             lds_barrier();
         }
@@ -866,8 +873,9 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
         // last step: M_{n-1}(s) of every state and the end state (the smallest s attaining the minimum), or sigma
         const float* ml = args.dbl && ((n - 1) & 1) ? msg1 : msg0;
         float wl[V];
+        const int tl = rot ? rot - 1 : n - 1;   // (n - 1 + rot) mod n
 #pragma unroll
-        for (int v = 0; v < V; ++v) wl[v] = wb[(n - 1) * V + v];
+        for (int v = 0; v < V; ++v) wl[v] = wb[tl * V + v];
         float best = kInf;
         uint32_t bidx = 0xffffffffu;
         if (!has_sigma) {
@@ -913,7 +921,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
                 args.w_hard[pb * n * V + x] = args.cb[(size_t)args.states[pb * n + tt] * V + v];
             }
         }
-        if (tau == 0) {
+        if (tau == 0 && trace) {
             pend_b = b;
             pend_par = par;
             pend_s = bidx;
@@ -1021,10 +1029,12 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     }
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
-        const float* wb = args.w + b * (int64_t)n * V;
-        const float* gb = args.g + b * (int64_t)n * V;
-        const bool has_sigma = args.sigma != nullptr;
-        const uint32_t sig = has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
+        const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
+        const float* wb = args.w + row * (int64_t)n * V;
+        const float* gb = args.g + row * (int64_t)n * V;
+        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+        const uint32_t sig = args.sigma_enum ? (uint32_t)(b & ((1 << L) - 1))
+                                             : has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
 
         // ------------------------------------------------------------------ forward: R~ and Q
 #pragma unroll

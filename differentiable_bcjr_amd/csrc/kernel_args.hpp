@@ -64,7 +64,7 @@ struct GenArgs {
     float* w_soft;         // [B, n V] (soft: required; gradient: optional)
     float* log_z;          // [B] or nullptr (soft)
     float* grad;           // [B, n V] (gradient)
-    int32_t* states;       // [B, n] (Viterbi)
+    int32_t* states;       // [B, n] (Viterbi), or nullptr for costs only (no traceback; w_hard must be nullptr)
     float* w_hard;         // [B, n V] or nullptr (Viterbi)
     float* cost;           // [B] or nullptr (Viterbi)
     unsigned char* ws;
@@ -72,6 +72,8 @@ struct GenArgs {
     int32_t dbl;           // LDS messages double-buffered (else one buffer, inputs read before outputs are written)
     int32_t ckpt;          // 0: every forward message row on the tape; c > 0: every c-th row, the backward pass
                            // recomputes each c-step segment from its checkpoint (soft codeword and gradient)
+    int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
+    int32_t rot;           // Viterbi: sequence b emits step (t + rot) mod n of its row at step t (0 <= rot < n)
 };
 
 }  // namespace bcjr

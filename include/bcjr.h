@@ -31,10 +31,10 @@
  *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
  *     Calls on different streams need different workspaces.
  *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 2k <= L <= 16, and
- *       soft codeword, gradient, codebook gradient, Viterbi: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs
- *       kernels tuned for it, every other (k, V) one kernel family written for any k; both gradients with k = 1
- *       need L <= 15);
- *       the tail-biting entry points: k == 2 and V = 1.
+ *       every entry point: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs kernels tuned for it, every other
+ *       (k, V) one kernel family written for any k; both gradients with k = 1 need L <= 15);
+ *       exact tail-biting (the exact start-state choice, and the soft codeword and gradient under the
+ *       tail-biting measure) needs L <= 10.
  *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
  *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
  *     into that sequence's outputs.
@@ -54,10 +54,9 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; k != 2 or V != 1 for the
-                                  tail-biting entry points; either gradient with k = 1 and L = 16;
-                                  exact tail-biting (choice of sigma, soft codeword or gradient under the
-                                  tail-biting measure) with L > 10; unknown mode */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; either gradient with k = 1
+                                  and L = 16; exact tail-biting (choice of sigma, soft codeword or gradient
+                                  under the tail-biting measure) with L > 10; unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
@@ -204,6 +203,19 @@ int bcjr_soft_codeword_grad_codebook_v(const float* w, const float* codebook, in
                                        int32_t k, int32_t V, float T, const int32_t* boundary_state,
                                        const float* grad_w_soft, float* grad_codebook, float* grad_w, float* w_soft,
                                        void* workspace, size_t workspace_bytes, void* stream);
+/* The three tail-biting entry points with V weights per step (shapes as above: w, w_soft, grad_w_soft, grad_w and
+ * w_hard [B, n V], codebook [2^L, V], states [B, n]).  The mixture formulas hold per weight component, the sums over
+ * t running over all n V weights of the row; BCJR_TB_ROTATE rotates by n/2 trellis steps (n/2 V weights).
+ * Workspace: bcjr_workspace_bytes_v with the matching BCJR_OP_*_TAIL_BITING or BCJR_OP_VITERBI_TB_* value. */
+int bcjr_soft_codeword_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                     int32_t k, int32_t V, float T, float* w_soft, float* log_z, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int bcjr_soft_codeword_grad_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L,
+                                          int32_t k, int32_t V, float T, const float* grad_w_soft, float* grad_w,
+                                          float* w_soft, void* workspace, size_t workspace_bytes, void* stream);
+int viterbi_tail_biting_v(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                          int32_t V, int32_t mode, int32_t* states, float* w_hard, float* cost, int32_t* sigma,
+                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace the entry point `op` (one of the BCJR_OP_* values above) needs for
@@ -211,9 +223,7 @@ int bcjr_soft_codeword_grad_codebook_v(const float* w, const float* codebook, in
  */
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);
 
-/* The same for V weights per step: bcjr_workspace_bytes(op, ...) when V = 1; for V = 2 only the soft codeword, the
- * two gradients and Viterbi (BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK, BCJR_OP_VITERBI) have a size, every
- * other op gives 0. */
+/* The same for V weights per step, every op: bcjr_workspace_bytes(op, ...) is this with V = 1. */
 size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 
 /*

@@ -25,7 +25,9 @@ def test_header_declares_every_op():
     for name in ["bcjr_soft_codeword", "bcjr_soft_codeword_grad", "bcjr_soft_codeword_grad_codebook",
                  "viterbi_hard_code", "viterbi_tail_biting", "bcjr_soft_codeword_tail_biting",
                  "bcjr_soft_codeword_grad_tail_biting", "bcjr_soft_codeword_v", "bcjr_soft_codeword_grad_v",
-                 "bcjr_soft_codeword_grad_codebook_v", "viterbi_hard_code_v", "bcjr_workspace_bytes_min", "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
+                 "bcjr_soft_codeword_grad_codebook_v", "viterbi_hard_code_v", "bcjr_soft_codeword_tail_biting_v",
+                 "bcjr_soft_codeword_grad_tail_biting_v", "viterbi_tail_biting_v", "bcjr_workspace_bytes_min",
+                 "bcjr_workspace_bytes", "bcjr_workspace_bytes_v", "bcjr_status_string"]:
         assert name in fns
 
 
@@ -166,10 +168,11 @@ def test_unsupported_trellis_has_no_workspace():
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 16, 1) == 0  # R and Q exceed LDS at k = 1, L = 16
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 16, 1) == 0
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 15, 1) > 0
-    for op in (4, 5, 6, 7):                                              # tail-biting: k = 2, V = 1 only
-        assert abi.bcjr_workspace_bytes(op, 4, 8, 8, 1) == 0
-        assert abi.bcjr_workspace_bytes(op, 4, 8, 9, 3) == 0
-        assert abi.bcjr_workspace_bytes_v(op, 4, 8, 8, 2, 2) == 0
+    for op in (4, 6, 7):                                                 # exact tail-biting: L <= 10, any (k, V)
+        assert abi.bcjr_workspace_bytes_v(op, 4, 8, 12, 3, 2) == 0
+        assert abi.bcjr_workspace_bytes_v(op, 4, 8, 10, 3, 2) > 0
+        assert abi.bcjr_workspace_bytes_v(op, 4, 8, 10, 5, 1) == 0       # k > 4
+    assert abi.bcjr_workspace_bytes_v(5, 4, 8, 16, 4, 2) > 0             # rotate: any L
 
 
 def _soft(**kw):
@@ -239,6 +242,30 @@ def test_tail_biting_measure_workspace_formula(L, B, n):
     assert grad == _a256(slots * grad_slot) + _a256(V * n * 4) + _a256(V * 4) + _a256(V * n * 4)
 
 
+@pytest.mark.parametrize("L,k,V", [(4, 1, 1), (6, 3, 2), (8, 4, 1), (10, 1, 2), (8, 2, 2), (12, 3, 1), (16, 4, 2)])
+@pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (33, 7)])
+def test_general_tail_biting_workspace_formula(L, k, V, B, n):
+    """The general kernels' plans: the Viterbi slots of the larger pass, then the per-(row, sigma) costs (exact) or
+    the rotated pass's states, then sigma; the mixture: the soft (and gradient) slots of the B 2^L virtual
+    sequences, then their soft codewords, ln Z (and gradients)."""
+    vit_rows = _gen_bytes(abi.BCJR_OP_VITERBI, B, n, L, k, V)
+    rot = _a256(vit_rows) + _a256(B * n * 4) + _a256(B * 4)
+    assert abi.bcjr_workspace_bytes_v(abi.BCJR_OP_VITERBI_TB_ROTATE, B, n, L, k, V) == rot
+    exact = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_VITERBI_TB_EXACT, B, n, L, k, V)
+    soft = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, V)
+    grad = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_GRAD_TAIL_BITING, B, n, L, k, V)
+    if L > 10:
+        assert exact == 0 and soft == 0 and grad == 0
+        return
+    S = B << L
+    first = max(_gen_bytes(abi.BCJR_OP_VITERBI, S, n, L, k, V), vit_rows)
+    assert exact == _a256(first) + _a256(S * 4) + _a256(B * 4)
+    s_slots = _gen_bytes(abi.BCJR_OP_SOFT, S, n, L, k, V)
+    g_slots = max(s_slots, _gen_bytes(abi.BCJR_OP_GRAD, S, n, L, k, V))
+    assert soft == _a256(s_slots) + _a256(S * n * V * 4) + _a256(S * 4)
+    assert grad == _a256(g_slots) + _a256(S * n * V * 4) + _a256(S * 4) + _a256(S * n * V * 4)
+
+
 def test_tail_biting_measure_checks():
     def soft(**kw):
         a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, w_soft=FAKE, log_z=None, workspace=FAKE,
@@ -257,7 +284,8 @@ def test_tail_biting_measure_checks():
     assert soft(n=0) == abi.BCJR_ERR_SHAPE and grad(B=0) == abi.BCJR_ERR_SHAPE
     assert soft(T=0.0) == abi.BCJR_ERR_TEMP and grad(T=float("nan")) == abi.BCJR_ERR_TEMP
     assert soft(L=12) == abi.BCJR_ERR_UNSUPPORTED and grad(L=11) == abi.BCJR_ERR_UNSUPPORTED
-    assert soft(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert soft(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED and grad(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
+    assert soft(k=1) == abi.BCJR_ERR_WORKSPACE and grad(k=3) == abi.BCJR_ERR_WORKSPACE   # the general kernels
     need = abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT_TAIL_BITING, 4, 8, 8, 2)
     assert soft(workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
     assert soft(workspace=FAKE + 8, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
@@ -269,7 +297,8 @@ def test_tail_biting_checks():
     assert _tb(states=None) == abi.BCJR_ERR_NULL
     assert _tb(w=None) == abi.BCJR_ERR_NULL
     assert _tb(n=0) == abi.BCJR_ERR_SHAPE
-    assert _tb(k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert _tb(k=1) == abi.BCJR_ERR_WORKSPACE and _tb(k=4) == abi.BCJR_ERR_WORKSPACE   # the general kernels
+    assert _tb(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
     assert _tb(mode=7) == abi.BCJR_ERR_UNSUPPORTED
     assert _tb(L=12) == abi.BCJR_ERR_UNSUPPORTED                       # exact above L = 10
     assert _tb(L=12, mode=abi.BCJR_TB_ROTATE) == abi.BCJR_ERR_WORKSPACE   # rotate has no L limit
