@@ -117,6 +117,12 @@ def parse_args():
     return ap.parse_args()
 
 
+def viterbi_pairs(L: int, k: int, V: int) -> int:
+    """Sequences per workgroup of the general Viterbi kernel: 2 where the codebook is read from memory (V = 2,
+    L >= 12) and two message arrays fit in LDS, as the library's plan chooses."""
+    return 2 if V == 2 and L >= 12 and 2 * (4 << (L - k)) + 2048 <= 160 * 1024 else 1
+
+
 def source_digest(op: str) -> str:
     """Digest of a kernel's sources with comments and whitespace removed (comment edits keep counters valid)."""
     h = hashlib.sha256()
@@ -218,7 +224,8 @@ def time_variant(vw, T, K, dev, stream, check):
         torch.cuda.synchronize()
         ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
         units = B * steps * S
-        ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{', false, false' if name == 'grad' else ''}>",
+        tail = {"grad": ", false, false", "viterbi": f", {viterbi_pairs(L, k, V)}"}.get(name, "")
+        ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{tail}>",
                      "ms": round(ms, 4), "state_updates_per_s": DIRECTIONS[name] * units / (ms * 1e-3),
                      "weights_per_s": B * vw.n / (ms * 1e-3),
                      "roofline": {"bound": "alu", "achieved": round(slots[name] * units / (ms * 1e-3) / 1e12, 3),

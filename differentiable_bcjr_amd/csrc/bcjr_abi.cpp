@@ -26,6 +26,7 @@ hipError_t launch_tb_select(const float* costs, int64_t rows, int S, int32_t* si
                             hipStream_t st);
 hipError_t launch_tb_rotate_sigma(const int32_t* states_rot, int64_t rows, int n, int pos, int32_t* sigma,
                                   int32_t* sigma_out, hipStream_t st);
+hipError_t launch_tb_rotate_rows(const float* w, int64_t rows, int nv, int shift, float* out, hipStream_t st);
 struct GenArgs;
 hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
                           hipStream_t st);
@@ -110,6 +111,7 @@ constexpr size_t kLdsStatic = 2048;   // the kernels' own reduction slots
 struct GenPlan {
     bool ok;          // false: no kernel for these shapes (the gradient's two message arrays exceed LDS)
     int grid, threads, dbl, ckpt;
+    int nsq;          // Viterbi: sequences per workgroup (2 where the codebook streams and two fit in LDS)
     size_t lds, slot_bytes, total;
     size_t acc_off;   // codebook gradient: offset of the slot's [2^L][V] accumulator
 };
@@ -140,9 +142,13 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
         p.dbl = 0;
         p.lds = 2 * msg;
     } else {
-        p.dbl = ckpt == 0 && 2 * msg + kLdsStatic <= kLdsBytes;   // the recompute mode uses one buffer
-        p.lds = p.dbl ? 2 * msg : msg;
+        // Viterbi with V = 2 at L >= 12 reads its codebook through L1 every step: pair the sequences so each row
+        // read serves two (their message buffers side by side)
+        p.nsq = op == BCJR_OP_VITERBI && V == 2 && L >= 12 && 2 * msg + kLdsStatic <= kLdsBytes ? 2 : 1;
+        p.dbl = ckpt == 0 && p.nsq * 2 * msg + kLdsStatic <= kLdsBytes;   // the recompute mode uses one buffer
+        p.lds = p.nsq * (p.dbl ? 2 * msg : msg);
     }
+    if (p.nsq < 1) p.nsq = 1;
     p.ok = p.lds + kLdsStatic <= kLdsBytes;
     p.threads = tps;
     // blocks per CU: 16 waves of at most 128 VGPRs, and the LDS
@@ -152,7 +158,8 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     if (bpc_lds < bpc) bpc = bpc_lds;
     if (bpc < 1) bpc = 1;
     const int64_t cap = (int64_t)kNumCU * bpc;
-    p.grid = (int)(B < cap ? B : cap);
+    const int64_t rounds = (B + p.nsq - 1) / p.nsq;
+    p.grid = (int)(rounds < cap ? rounds : cap);
     const size_t tapes = align256(tape_rows(ckpt, n) * G * 4);
     const size_t nrm = align256((size_t)n * 4);
     switch (op) {
@@ -166,8 +173,8 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
             p.slot_bytes = p.acc_off + (op == BCJR_OP_GRAD_CODEBOOK ? align256((size_t)S * V * 4) : 0) +
                            (ckpt ? nrm + align256(2 * G * 4) : 0);   // + the Q input offsets, the saved messages
             break;
-        default:   // two back-pointer buffers of [n][threads] words
-            p.slot_bytes = align256(2 * (size_t)n * (size_t)tps * 4);
+        default:   // two back-pointer buffers (by round parity) of [n][threads] words per sequence of a round
+            p.slot_bytes = align256(2 * (size_t)p.nsq * (size_t)n * (size_t)tps * 4);
             break;
     }
     p.total = (size_t)p.grid * p.slot_bytes;
@@ -224,7 +231,7 @@ MixturePlan make_mixture_plan(bool with_grad, int64_t B, int64_t n, int32_t L) {
 struct GenTailBitingPlan {
     bool ok;
     GenPlan rows, first;
-    size_t slots_bytes, aux_off, sigma_off, total;
+    size_t slots_bytes, aux_off, sigma_off, rotw_off, total;   // rotw: the rotated rows (rotate mode)
 };
 
 GenTailBitingPlan make_gen_tb_plan(int32_t mode, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
@@ -236,7 +243,8 @@ GenTailBitingPlan make_gen_tb_plan(int32_t mode, int64_t B, int64_t n, int32_t L
     t.aux_off = t.slots_bytes;
     const size_t aux = mode == BCJR_TB_EXACT ? (size_t)(B << L) * 4 : (size_t)B * (size_t)n * 4;
     t.sigma_off = t.aux_off + align256(aux);
-    t.total = t.sigma_off + align256((size_t)B * 4);
+    t.rotw_off = t.sigma_off + align256((size_t)B * 4);
+    t.total = t.rotw_off + (mode == BCJR_TB_ROTATE ? align256((size_t)B * (size_t)n * V * 4) : 0);
     return t;
 }
 
@@ -498,6 +506,7 @@ int viterbi_impl(const float* w, const float* codebook, int64_t B, int64_t n, in
         a.ws = static_cast<unsigned char*>(workspace);
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
+        a.nsq = p.nsq;
         return hip_status(launch_general(2, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
     const Plan p = make_plan(BCJR_OP_VITERBI, B, n, L);
@@ -688,6 +697,7 @@ int viterbi_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n,
         f.ws = ws;
         f.slot_bytes = tp.first.slot_bytes;
         f.dbl = tp.first.dbl;
+        f.nsq = tp.first.nsq;
         if (mode == BCJR_TB_EXACT) {   // the cost of every (row, sigma), no traceback
             float* costs = reinterpret_cast<float*>(ws + tp.aux_off);
             f.B = B << L;
@@ -696,10 +706,12 @@ int viterbi_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n,
             if ((e = launch_general(2, k, V, f, tp.first.grid, tp.first.threads, tp.first.lds, st)) != hipSuccess)
                 return hip_status(e);
             if ((e = launch_tb_select(costs, B, 1 << L, sig_ws, sigma, st)) != hipSuccess) return hip_status(e);
-        } else {
+        } else {   // the free decode of a rotated copy of the rows
             int32_t* rot_states = reinterpret_cast<int32_t*>(ws + tp.aux_off);
+            float* rot_w = reinterpret_cast<float*>(ws + tp.rotw_off);
+            if ((e = launch_tb_rotate_rows(w, B, (int)(n * V), r * V, rot_w, st)) != hipSuccess) return hip_status(e);
+            f.w = rot_w;
             f.B = B;
-            f.rot = r;
             f.states = rot_states;
             if ((e = launch_general(2, k, V, f, tp.first.grid, tp.first.threads, tp.first.lds, st)) != hipSuccess)
                 return hip_status(e);
@@ -720,6 +732,7 @@ int viterbi_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n,
         a.ws = ws;
         a.slot_bytes = tp.rows.slot_bytes;
         a.dbl = tp.rows.dbl;
+        a.nsq = tp.rows.nsq;
         return hip_status(launch_general(2, k, V, a, tp.rows.grid, tp.rows.threads, tp.rows.lds, st));
     }
     const TailBitingPlan tp = make_tb_plan(mode, B, n, L);

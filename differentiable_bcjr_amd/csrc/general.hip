@@ -738,28 +738,30 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 // ------------------------------------------------------------------------------------------------------------------
 // Viterbi hard code
 
-template <int K, int V, int SPT, int LT>
+// NSQ = 2: the workgroup decodes two sequences in lockstep, so every codebook row it reads from memory serves both
+// (where the codebook does not fit in registers, its stream through L1 otherwise takes most of a step).  Lanes 0..NSQ-1
+// trace the sequences back, so a workgroup needs at least NSQ threads (the host pairs sequences only at L >= 12).
+template <int K, int V, int SPT, int LT, int NSQ>
 __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
     using Gm = GG<K, V, SPT>;
     constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TI = Gm::TI, NI = Gm::NI, ROW = Gm::ROW;
     constexpr bool REG = SPT * V <= 64;
     constexpr float kInf = __builtin_huge_valf();
     extern __shared__ float lds[];
-    __shared__ float redv[16];
-    __shared__ uint32_t redi[16];
+    __shared__ float redv[NSQ][16];
+    __shared__ uint32_t redi[NSQ][16];
 
     const int L = LT ? LT : args.L, n = args.n, TPS = LT ? (1 << LT) / SPT : (int)blockDim.x, tau = threadIdx.x;
     const int lane = tau & 63, wv = tau >> 6;
     const int G = 1 << (L - K), J = 1 << (L - 2 * K);
     const int WPS = TPS >= 64 ? TPS >> 6 : 1, SEG = TPS >= 64 ? 64 : TPS;
-    float* msg0 = lds;
-    float* msg1 = args.dbl ? lds + G : lds;
+    const int MB = args.dbl ? 2 * G : G;   // floats of one sequence's message buffers (sequence z at lds + z MB)
 
     Owner<K, V, SPT, REG> own;
     own.init(args.cb, L, TPS);
 
-    // back-pointer tape: 2 buffers (by sequence parity) of [n][TPS] words.  A thread's word of step t holds, for each
-    // of its forward groups g = m I + ii, the k-bit row a of the best predecessor in bits [g k, g k + k).
+    // back-pointer tape: 2 parities (by round) x NSQ sequences of [n][TPS] words.  A thread's word of step t holds,
+    // for each of its forward groups g = m I + ii, the k-bit row a of the best predecessor in bits [g k, g k + k).
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
     const uint32_t buf_bytes = (uint32_t)n * TPS * 4u;
@@ -778,17 +780,16 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
         }
     };
 
-    const int rot = args.rot;
-    const bool trace = args.states != nullptr;   // else costs only: no back pointers, no traceback
-    // pending traceback (lane tau == 0): the previous sequence's path is traced back one step per forward step
+    const bool trace = args.states != nullptr;   // else costs only: no traceback (the back pointers are still kept)
+    // pending traceback: lane z (tau == z) traces back the previous round's sequence z, one step per forward step
     int64_t pend_b = -1;
     int pend_t = 0;
-    uint32_t pend_s = 0, pend_word = 0, pend_par = 0;
+    uint32_t pend_s = 0, pend_word = 0, pend_buf = 0;
     auto pend_fetch = [&]() {   // the word that decides s_{pend_t - 1}
         uint32_t wi, bit;
         bp_loc(pend_s >> K, wi, bit);
-        pend_word = __builtin_bit_cast(uint32_t, buf_ld(tape, 0u, pend_par * buf_bytes + (uint32_t)(pend_t - 1) *
-                                                                          (TPS * 4u) + 4u * wi));
+        pend_word = __builtin_bit_cast(uint32_t, buf_ld(tape, 0u, pend_buf + (uint32_t)(pend_t - 1) * (TPS * 4u) +
+                                                                          4u * wi));
     };
     auto pend_step = [&]() {
         uint32_t wi, bit;
@@ -800,149 +801,203 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
         args.states[pend_b * args.n + pend_t] = (int32_t)pend_s;
         if (pend_t >= 1) pend_fetch();
     };
-
-    int64_t iter = 0;
-    for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x, ++iter) {
-        const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
-        const float* wb = args.w + row * (int64_t)n * V;
-        const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
-        const uint32_t sig = args.sigma_enum ? (uint32_t)(b & ((1 << L) - 1))
-                                             : has_sigma ? ((uint32_t)args.sigma[b] & ((1u << L) - 1u)) : 0u;
-        const uint32_t par = (uint32_t)(iter & 1);
-
+    // codewords of a finished round's sequences (their states are complete)
+    auto gather = [&](int64_t rr) {
 #pragma unroll
-        for (int m = 0; m < BPT; ++m)
-#pragma unroll
-            for (int q = 0; q < NI; ++q)
-#pragma unroll
-                for (int ii = 0; ii < TI; ++ii) {
-                    const int u = own.fgroup(m, q) + ii;
-                    msg0[u] = (!has_sigma || (uint32_t)u == (sig & (uint32_t)(G - 1))) ? 0.f : kInf;
-                }
-        lds_barrier();
-
-        for (int t = 0; t + 1 < n; ++t) {
-            const float* mc = args.dbl && (t & 1) ? msg1 : msg0;
-            float* mn = args.dbl ? ((t & 1) ? msg0 : msg1) : msg0;
-            float wt[V];
-            const int tw = t + rot < n ? t + rot : t + rot - n;   // the row's step emitted at step t
-#pragma unroll
-            for (int v = 0; v < V; ++v) wt[v] = wb[tw * V + v];
-            float vin[BPT][P];
-#pragma unroll
-            for (int m = 0; m < BPT; ++m)
-#pragma unroll
-                for (int a = 0; a < P; ++a) vin[m][a] = mc[own.j(m) + J * a];
-            if (!args.dbl) lds_barrier();
-            uint32_t word = 0;
-#pragma unroll
-            for (int m = 0; m < BPT; ++m)
-#pragma unroll
-                for (int q = 0; q < NI; ++q) {
-                    float best[TI];
-                    uint32_t arg[TI];
-#pragma unroll
-                    for (int ii = 0; ii < TI; ++ii) {
-                        best[ii] = kInf;
-                        arg[ii] = 0;
-                    }
-#pragma unroll
-                    for (int a = 0; a < P; ++a) {
-                        float c[ROW];
-                        own.take_fwd(m, a, q, c, cnx);
-#pragma unroll
-                        for (int ii = 0; ii < TI; ++ii) {
-                            const float M = vmetric<V>(wt, &c[ii * V], vin[m][a]);
-                            const bool take = M < best[ii];   // strict: the smallest a wins ties
-                            best[ii] = take ? M : best[ii];
-                            arg[ii] = take ? (uint32_t)a : arg[ii];
-                        }
-                    }
-#pragma unroll
-                    for (int ii = 0; ii < TI; ++ii) {
-                        word |= arg[ii] << ((m * I + TI * q + ii) * K);
-                        mn[own.fgroup(m, q) + ii] = best[ii];
-                    }
-                    GEN_SCHED_BARRIER();
-                }
-            if (trace) buf_st(__builtin_bit_cast(float, word), tape, 4u * tau, par * buf_bytes + (uint32_t)t * (TPS * 4u));
-            if (tau == 0 && pend_b >= 0 && pend_t >= 1) pend_step();
-            lds_barrier();
-        }
-
-        // last step: M_{n-1}(s) of every state and the end state (the smallest s attaining the minimum), or sigma
-        const float* ml = args.dbl && ((n - 1) & 1) ? msg1 : msg0;
-        float wl[V];
-        const int tl = rot ? rot - 1 : n - 1;   // (n - 1 + rot) mod n
-#pragma unroll
-        for (int v = 0; v < V; ++v) wl[v] = wb[tl * V + v];
-        float best = kInf;
-        uint32_t bidx = 0xffffffffu;
-        if (!has_sigma) {
-#pragma unroll
-            for (int m = 0; m < BPT; ++m)
-#pragma unroll
-                for (int a = 0; a < P; ++a) {
-                    const float vin = ml[own.j(m) + J * a];
-#pragma unroll
-                    for (int q = 0; q < NI; ++q) {
-                        float c[ROW];
-                        own.row(m, a, q, c);
-#pragma unroll
-                        for (int ii = 0; ii < TI; ++ii)
-                            argmin_merge(best, bidx, vmetric<V>(wl, &c[ii * V], vin), own.state(m, a, q, ii));
-                    }
-                }
-            gseq_argmin(best, bidx, SEG);
-            if (WPS > 1 && lane == 0) {
-                redv[wv] = best;
-                redi[wv] = bidx;
-            }
-            __syncthreads();   // also publishes this sequence's back pointers to the traceback lane
-            if (WPS > 1) {
-                for (int q = 0; q < WPS; ++q) argmin_merge(best, bidx, redv[q], redi[q]);
-            }
-        } else {
-            __syncthreads();
-            bidx = sig;
-            best = vmetric<V>(wl, args.cb + (size_t)sig * V, ml[sig >> K]);
-        }
-        if (tau == 0 && args.cost) args.cost[b] = best;
-
-        // finish the previous sequence's traceback and gather its codewords
-        if (tau == 0 && pend_b >= 0) {
-            while (pend_t >= 1) pend_step();
-        }
-        __syncthreads();
-        if (args.w_hard && iter > 0) {
-            const int64_t pb = b - gridDim.x;
+        for (int z = 0; z < NSQ; ++z) {
+            const int64_t pb = rr * NSQ + z;
+            if (pb >= args.B) continue;
             for (int x = tau; x < n * V; x += TPS) {
                 const int tt = x / V, v = x - tt * V;
                 args.w_hard[pb * n * V + x] = args.cb[(size_t)args.states[pb * n + tt] * V + v];
             }
         }
-        if (tau == 0 && trace) {
-            pend_b = b;
-            pend_par = par;
-            pend_s = bidx;
-            pend_t = n - 1;
-            args.states[b * n + n - 1] = (int32_t)bidx;
-            if (n > 1) pend_fetch();
+    };
+
+    const int64_t rounds = (args.B + NSQ - 1) / NSQ;
+    const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
+    int64_t iter = 0;
+    for (int64_t r = blockIdx.x; r < rounds; r += gridDim.x, ++iter) {
+        const uint32_t par = (uint32_t)(iter & 1);
+        int64_t bz[NSQ];
+        const float* wb[NSQ];
+        uint32_t sig[NSQ];
+#pragma unroll
+        for (int z = 0; z < NSQ; ++z) {
+            bz[z] = r * NSQ + z;
+            const int64_t bb = bz[z] < args.B ? bz[z] : args.B - 1;   // a missing second sequence repeats the last
+            const int64_t row = args.sigma_enum ? (bb >> L) : bb;      // the weights' row (sigma enumeration: v >> L)
+            wb[z] = args.w + row * (int64_t)n * V;
+            sig[z] = args.sigma_enum ? (uint32_t)(bb & ((1 << L) - 1))
+                                     : has_sigma ? ((uint32_t)args.sigma[bb] & ((1u << L) - 1u)) : 0u;
         }
-        __syncthreads();   // LDS and the other back-pointer buffer are reused next
+
+#pragma unroll
+        for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q)
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+                        const int u = own.fgroup(m, q) + ii;
+                        lds[z * MB + u] = (!has_sigma || (uint32_t)u == (sig[z] & (uint32_t)(G - 1))) ? 0.f : kInf;
+                    }
+        lds_barrier();
+
+        for (int t = 0; t + 1 < n; ++t) {
+            const int oc = args.dbl && (t & 1) ? G : 0, on = args.dbl ? ((t & 1) ? 0 : G) : 0;
+            float wt[NSQ][V];
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                for (int v = 0; v < V; ++v) wt[z][v] = wb[z][t * V + v];
+            float vin[NSQ][BPT][P];
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                    for (int a = 0; a < P; ++a) vin[z][m][a] = lds[z * MB + oc + own.j(m) + J * a];
+            if (!args.dbl) lds_barrier();
+            uint32_t word[NSQ];
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z) word[z] = 0;
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int q = 0; q < NI; ++q) {
+                    float best[NSQ][TI];
+                    uint32_t arg[NSQ][TI];
+#pragma unroll
+                    for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            best[z][ii] = kInf;
+                            arg[z][ii] = 0;
+                        }
+#pragma unroll
+                    for (int a = 0; a < P; ++a) {
+                        float c[ROW];
+                        own.take_fwd(m, a, q, c, cnx);
+#pragma unroll
+                        for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii) {
+                                const float M = vmetric<V>(wt[z], &c[ii * V], vin[z][m][a]);
+                                const bool take = M < best[z][ii];   // strict: the smallest a wins ties
+                                best[z][ii] = take ? M : best[z][ii];
+                                arg[z][ii] = take ? (uint32_t)a : arg[z][ii];
+                            }
+                        if constexpr (NSQ > 1) GEN_SCHED_BARRIER();   // one row at a time: bounds the live values
+                    }
+#pragma unroll
+                    for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                        for (int ii = 0; ii < TI; ++ii) {
+                            word[z] |= arg[z][ii] << ((m * I + TI * q + ii) * K);
+                            lds[z * MB + on + own.fgroup(m, q) + ii] = best[z][ii];
+                        }
+                    GEN_SCHED_BARRIER();
+                }
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z)
+                buf_st(__builtin_bit_cast(float, word[z]), tape, 4u * tau,
+                       (par * NSQ + z) * buf_bytes + (uint32_t)t * (TPS * 4u));
+            if (tau < NSQ && pend_b >= 0 && pend_t >= 1) pend_step();
+            lds_barrier();
+        }
+
+        // last step: M_{n-1}(s) of every state and the end state (the smallest s attaining the minimum), or sigma
+        const int ol = args.dbl && ((n - 1) & 1) ? G : 0;
+        float wl[NSQ][V];
+#pragma unroll
+        for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+            for (int v = 0; v < V; ++v) wl[z][v] = wb[z][(n - 1) * V + v];
+        float best[NSQ];
+        uint32_t bidx[NSQ];
+#pragma unroll
+        for (int z = 0; z < NSQ; ++z) {
+            best[z] = kInf;
+            bidx[z] = 0xffffffffu;
+        }
+        if (!has_sigma) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                for (int a = 0; a < P; ++a) {
+                    float vl[NSQ];
+#pragma unroll
+                    for (int z = 0; z < NSQ; ++z) vl[z] = lds[z * MB + ol + own.j(m) + J * a];
+#pragma unroll
+                    for (int q = 0; q < NI; ++q) {
+                        float c[ROW];
+                        own.row(m, a, q, c);
+#pragma unroll
+                        for (int z = 0; z < NSQ; ++z)
+#pragma unroll
+                            for (int ii = 0; ii < TI; ++ii)
+                                argmin_merge(best[z], bidx[z], vmetric<V>(wl[z], &c[ii * V], vl[z]),
+                                             own.state(m, a, q, ii));
+                    }
+                }
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z) {
+                gseq_argmin(best[z], bidx[z], SEG);
+                if (WPS > 1 && lane == 0) {
+                    redv[z][wv] = best[z];
+                    redi[z][wv] = bidx[z];
+                }
+            }
+            __syncthreads();   // also publishes this round's back pointers to the traceback lanes
+            if (WPS > 1) {
+#pragma unroll
+                for (int z = 0; z < NSQ; ++z)
+                    for (int q = 0; q < WPS; ++q) argmin_merge(best[z], bidx[z], redv[z][q], redi[z][q]);
+            }
+        } else {
+            __syncthreads();
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z) {
+                bidx[z] = sig[z];
+                best[z] = vmetric<V>(wl[z], args.cb + (size_t)sig[z] * V, lds[z * MB + ol + (sig[z] >> K)]);
+            }
+        }
+        if (tau == 0 && args.cost) {
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z)
+                if (bz[z] < args.B) args.cost[bz[z]] = best[z];
+        }
+
+        // finish the previous round's tracebacks and gather its codewords
+        if (tau < NSQ && pend_b >= 0) {
+            while (pend_t >= 1) pend_step();
+        }
+        __syncthreads();
+        if (args.w_hard && iter > 0) gather(r - gridDim.x);
+        if (tau < NSQ && trace) {
+            pend_b = -1;
+#pragma unroll
+            for (int z = 0; z < NSQ; ++z) {
+                if (z == tau && bz[z] < args.B) {   // lane z takes this round's sequence z
+                    pend_b = bz[z];
+                    pend_buf = (par * NSQ + z) * buf_bytes;
+                    pend_s = bidx[z];
+                    pend_t = n - 1;
+                    args.states[bz[z] * n + n - 1] = (int32_t)bidx[z];
+                    if (n > 1) pend_fetch();
+                }
+            }
+        }
+        __syncthreads();   // LDS and the other parity's back-pointer buffers are reused next
     }
 
-    if (tau == 0 && pend_b >= 0) {
+    if (tau < NSQ && pend_b >= 0) {
         while (pend_t >= 1) pend_step();
     }
     __syncthreads();
-    if (args.w_hard && iter > 0) {
-        const int64_t pb = blockIdx.x + (iter - 1) * (int64_t)gridDim.x;
-        for (int x = tau; x < n * V; x += TPS) {
-            const int tt = x / V, v = x - tt * V;
-            args.w_hard[pb * n * V + x] = args.cb[(size_t)args.states[pb * n + tt] * V + v];
-        }
-    }
+    if (args.w_hard && iter > 0) gather(blockIdx.x + (iter - 1) * (int64_t)gridDim.x);
 }
 
 // ------------------------------------------------------------------------------------------------------------------
@@ -1600,42 +1655,46 @@ namespace {
 using GenKernel = void (*)(GenArgs);
 
 template <int K, int V, int SPT, int LT>
-GenKernel pick(int op, bool ck) {
+GenKernel pick(int op, bool ck, int nsq) {
     switch (op) {
         case 0: return gen_soft_kernel<K, V, SPT, LT>;
         case 1: return ck ? gen_grad_kernel<K, V, SPT, LT, false, true> : gen_grad_kernel<K, V, SPT, LT, false, false>;
         case 3: return ck ? gen_grad_kernel<K, V, SPT, LT, true, true> : gen_grad_kernel<K, V, SPT, LT, true, false>;
-        default: return gen_viterbi_kernel<K, V, SPT, LT>;
+        default:
+            if constexpr (V == 2 && SPT == 64) {   // the codebook streams: two sequences per workgroup share it
+                if (nsq == 2) return gen_viterbi_kernel<K, V, SPT, LT, 2>;
+            }
+            return nsq == 1 ? gen_viterbi_kernel<K, V, SPT, LT, 1> : nullptr;
     }
 }
 
 // L = 16 (the workloads' trellis) has its own instantiation, whose strides are compile-time; other L read it at run
 // time.
 template <int V, int SPT>
-GenKernel pick_k(int op, bool ck, int k, int L) {
+GenKernel pick_k(int op, bool ck, int nsq, int k, int L) {
     if constexpr (SPT < 64) {
         switch (k) {
-            case 1: return pick<1, V, SPT, 0>(op, ck);
-            case 2: return pick<2, V, SPT, 0>(op, ck);
+            case 1: return pick<1, V, SPT, 0>(op, ck, nsq);
+            case 2: return pick<2, V, SPT, 0>(op, ck, nsq);
             default: return nullptr;
         }
     } else {
         switch (k) {
-            case 1: return L == 16 ? pick<1, V, SPT, 16>(op, ck) : pick<1, V, SPT, 0>(op, ck);
-            case 2: return L == 16 ? pick<2, V, SPT, 16>(op, ck) : pick<2, V, SPT, 0>(op, ck);
-            case 3: return L == 16 ? pick<3, V, SPT, 16>(op, ck) : pick<3, V, SPT, 0>(op, ck);
-            case 4: return L == 16 ? pick<4, V, SPT, 16>(op, ck) : pick<4, V, SPT, 0>(op, ck);
+            case 1: return L == 16 ? pick<1, V, SPT, 16>(op, ck, nsq) : pick<1, V, SPT, 0>(op, ck, nsq);
+            case 2: return L == 16 ? pick<2, V, SPT, 16>(op, ck, nsq) : pick<2, V, SPT, 0>(op, ck, nsq);
+            case 3: return L == 16 ? pick<3, V, SPT, 16>(op, ck, nsq) : pick<3, V, SPT, 0>(op, ck, nsq);
+            case 4: return L == 16 ? pick<4, V, SPT, 16>(op, ck, nsq) : pick<4, V, SPT, 0>(op, ck, nsq);
             default: return nullptr;
         }
     }
 }
 
 template <int V>
-GenKernel pick_spt(int op, bool ck, int k, int L) {
+GenKernel pick_spt(int op, bool ck, int nsq, int k, int L) {
     switch (L) {
-        case 4: return pick_k<V, 16>(op, ck, k, L);
-        case 5: return pick_k<V, 32>(op, ck, k, L);
-        default: return pick_k<V, 64>(op, ck, k, L);
+        case 4: return pick_k<V, 16>(op, ck, nsq, k, L);
+        case 5: return pick_k<V, 32>(op, ck, nsq, k, L);
+        default: return pick_k<V, 64>(op, ck, nsq, k, L);
     }
 }
 
@@ -1646,7 +1705,8 @@ GenKernel pick_spt(int op, bool ck, int k, int L) {
 hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int threads, size_t lds_bytes,
                           hipStream_t st) {
     const bool ck = a.ckpt != 0;
-    const GenKernel f = V == 1 ? pick_spt<1>(op, ck, k, a.L) : pick_spt<2>(op, ck, k, a.L);
+    const int nsq = a.nsq > 1 ? a.nsq : 1;
+    const GenKernel f = V == 1 ? pick_spt<1>(op, ck, nsq, k, a.L) : pick_spt<2>(op, ck, nsq, k, a.L);
     if (f == nullptr) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes);

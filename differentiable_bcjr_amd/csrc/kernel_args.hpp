@@ -73,7 +73,7 @@ struct GenArgs {
     int32_t ckpt;          // 0: every forward message row on the tape; c > 0: every c-th row, the backward pass
                            // recomputes each c-step segment from its checkpoint (soft codeword and gradient)
     int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
-    int32_t rot;           // Viterbi: sequence b emits step (t + rot) mod n of its row at step t (0 <= rot < n)
+    int32_t nsq;           // Viterbi: sequences decoded together by one workgroup (1, or 2 where the plan pairs them)
 };
 
 }  // namespace bcjr

@@ -107,6 +107,26 @@ __global__ void __launch_bounds__(kThreads) tb_grad_combine_kernel(const float* 
     }
 }
 
+// Rows rotated left by `shift` floats: out[row, x] = w[row, (x + shift) mod nv].  The rotate-and-decode start-state
+// choice on the general trellis decodes these copies (shift = n/2 trellis steps of V weights).
+__global__ void __launch_bounds__(kThreads) tb_rotate_rows_kernel(const float* w, int64_t rows, int nv, int shift,
+                                                                 float* out) {
+    const int64_t total = rows * nv;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+        const int64_t row = i / nv;
+        const int x = (int)(i - row * nv);
+        const int src = x + shift < nv ? x + shift : x + shift - nv;
+        out[i] = w[row * nv + src];
+    }
+}
+
+hipError_t launch_tb_rotate_rows(const float* w, int64_t rows, int nv, int shift, float* out, hipStream_t st) {
+    const int64_t blocks = (rows * nv + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(tb_rotate_rows_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(kThreads), 0, st,
+                       w, rows, nv, shift, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_tb_soft_combine(const float* ws_all, const float* lz_all, int64_t rows, int n, int S,
                                   float* w_soft, float* log_z, hipStream_t st) {
     hipLaunchKernelGGL(tb_soft_combine_kernel, dim3((unsigned)rows), dim3(kThreads), 0, st, ws_all, lz_all, n, S,

@@ -104,14 +104,18 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     wps = tps // 64 if tps >= 64 else 1
     G = S >> k
     lds_cap, lds_static = 160 * 1024, 2048
+    nsq = 1
     if op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
         lds = 2 * G * 4
     else:
-        lds = 2 * G * 4 if (ckpt == 0 and 2 * G * 4 + lds_static <= lds_cap) else G * 4
+        # Viterbi with V = 2 at L >= 12 decodes two sequences per workgroup (they share the codebook reads)
+        if op == abi.BCJR_OP_VITERBI and V == 2 and L >= 12 and 2 * G * 4 + lds_static <= lds_cap:
+            nsq = 2
+        lds = nsq * (2 * G * 4 if (ckpt == 0 and nsq * 2 * G * 4 + lds_static <= lds_cap) else G * 4)
     if lds + lds_static > lds_cap:
         return 0
     bpc = max(1, min(16 // (tps // 64 if tps >= 64 else 1), lds_cap // (lds + lds_static)))
-    grid = min(B, 256 * bpc)
+    grid = min(-(-B // nsq), 256 * bpc)
     tapes, nrm = _a256(((n + 1) if ckpt == 0 else (n // ckpt + ckpt)) * G * 4), _a256(n * 4)
     if op == abi.BCJR_OP_SOFT:
         slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0) + (_a256(G * 4) if ckpt else 0)
@@ -120,7 +124,7 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
         slot += _a256(S * V * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
         slot += nrm + _a256(2 * G * 4) if ckpt else 0
     else:
-        slot = _a256(2 * n * tps * 4)
+        slot = _a256(2 * nsq * n * tps * 4)
     return grid * slot
 
 
@@ -246,10 +250,10 @@ def test_tail_biting_measure_workspace_formula(L, B, n):
 @pytest.mark.parametrize("B,n", [(1, 1), (16, 64), (33, 7)])
 def test_general_tail_biting_workspace_formula(L, k, V, B, n):
     """The general kernels' plans: the Viterbi slots of the larger pass, then the per-(row, sigma) costs (exact) or
-    the rotated pass's states, then sigma; the mixture: the soft (and gradient) slots of the B 2^L virtual
+    the rotated pass's states, then sigma (and the rotated rows, rotate); the mixture: the soft (and gradient) slots of the B 2^L virtual
     sequences, then their soft codewords, ln Z (and gradients)."""
     vit_rows = _gen_bytes(abi.BCJR_OP_VITERBI, B, n, L, k, V)
-    rot = _a256(vit_rows) + _a256(B * n * 4) + _a256(B * 4)
+    rot = _a256(vit_rows) + _a256(B * n * 4) + _a256(B * 4) + _a256(B * n * V * 4)   # + the rotated rows
     assert abi.bcjr_workspace_bytes_v(abi.BCJR_OP_VITERBI_TB_ROTATE, B, n, L, k, V) == rot
     exact = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_VITERBI_TB_EXACT, B, n, L, k, V)
     soft = abi.bcjr_workspace_bytes_v(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, V)
