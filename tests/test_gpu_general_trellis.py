@@ -444,3 +444,19 @@ def test_longest_sequences(oracle_mod, dev, L, k, V):
     rst, _, rcost = oracle_mod.viterbi(w, c, L, k)
     np.testing.assert_array_equal(st, rst)
     np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
+
+
+@pytest.mark.parametrize("L,k,V,B,n,sigma", [(12, 3, 2, 8301, 3, False), (12, 4, 2, 8195, 2, True),
+                                             (13, 2, 2, 1027, 5, False), (12, 1, 2, 9, 1, False)])
+def test_viterbi_paired_sequences(oracle_mod, dev, L, k, V, B, n, sigma):
+    """V = 2 at L >= 12 decodes two sequences per workgroup (they share each codebook row read): odd batches (a
+    missing second sequence), more pairs than the grid holds (several rounds per workgroup and both back-pointer
+    parities), sigma mode, n = 1.  Bit-exact against the oracle."""
+    if sigma:
+        n = _sigma_n(L, k, n)
+    w, c, _, s = _vin(L, V, B, n, 8400 + L + k + n, sigma)
+    st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev)))
+    rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
+    np.testing.assert_array_equal(st, rst)
+    np.testing.assert_array_equal(wh.view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
