@@ -293,30 +293,32 @@ class _SoftQuantize(torch.autograd.Function):
     """w_soft = soft_codeword(w, c); dL/dw and dL/dc from the exact gradient kernels."""
 
     @staticmethod
-    def forward(ctx, w, codebook, L, k, T, boundary_state):
+    def forward(ctx, w, codebook, L, k, T, boundary_state, checkpoint):
         ctx.save_for_backward(w, codebook, boundary_state)
-        ctx.params = (L, k, T)
-        return soft_codeword(w, codebook, L, k, T, boundary_state)
+        ctx.params = (L, k, T, checkpoint)
+        return soft_codeword(w, codebook, L, k, T, boundary_state, checkpoint=checkpoint)
 
     @staticmethod
     def backward(ctx, grad_w_soft):
         w, codebook, boundary_state = ctx.saved_tensors
-        L, k, T = ctx.params
+        L, k, T, ck = ctx.params
         g = grad_w_soft.contiguous()
         grad_w = grad_c = None
         if ctx.needs_input_grad[1]:
             if ctx.needs_input_grad[0]:
-                grad_c, grad_w = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state)
+                grad_c, grad_w = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state, checkpoint=ck)
             else:
-                grad_c = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state, return_grad_w=False)
+                grad_c = soft_codeword_grad_codebook(w, codebook, g, L, k, T, boundary_state, return_grad_w=False,
+                                                     checkpoint=ck)
             grad_c = grad_c.to(codebook.dtype)
         elif ctx.needs_input_grad[0]:
-            grad_w = soft_codeword_grad(w, codebook, g, L, k, T, boundary_state)
-        return grad_w, grad_c, None, None, None, None
+            grad_w = soft_codeword_grad(w, codebook, g, L, k, T, boundary_state, checkpoint=ck)
+        return grad_w, grad_c, None, None, None, None, None
 
 
 def soft_quantize(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
-                  boundary_state: torch.Tensor | None = None) -> torch.Tensor:
+                  boundary_state: torch.Tensor | None = None, *, checkpoint: bool = False) -> torch.Tensor:
     """The soft codeword of w as a differentiable function of w and of the codebook ([2^L], or [2^L, V] with w
-    [B, n V]); autograd runs the exact gradient kernels."""
-    return _SoftQuantize.apply(w, codebook, L, k, T, boundary_state)
+    [B, n V]); autograd runs the exact gradient kernels.  ``checkpoint`` runs the forward and backward calls with
+    the smallest workspaces (checkpoint-and-recompute: about 2 sqrt(n) message rows per in-flight sequence)."""
+    return _SoftQuantize.apply(w, codebook, L, k, T, boundary_state, checkpoint)

@@ -198,3 +198,27 @@ def test_grad_checkpoint_mode_headline_workload_rows(oracle_mod, dev):
     e_n, e_e = norm_err(gr[rows], rgr), grad_err(gr[rows], rgr, g[rows], c, T)
     print(f"grad checkpoint mode, {wl.name}: {e_n:.2e} normwise, {e_e:.2e} elementwise", flush=True)
     assert e_n <= TOL and e_e <= GRAD_ELEM_TOL_LONG
+
+
+@pytest.mark.parametrize("L,k,V", [(9, 3, 2), (10, 2, 1)])
+def test_soft_quantize_checkpoint_mode(oracle_mod, dev, L, k, V):
+    """Autograd through soft_quantize with checkpoint=True: the forward, dL/dw and dL/dc with the smallest
+    workspaces.  Off the tuned trellis they are bit-identical to the full-tape mode; at k = 2, V = 1 they match the
+    oracle (the two modes run different kernels there)."""
+    B, n, T = 5, 40, 0.2
+    w, c, g, _ = _vin(L, V, B, n, 6800 + L)
+    outs = {}
+    for ck in (False, True):
+        wt = _t(w, dev).requires_grad_(True)
+        ct = _t(c, dev).requires_grad_(True)
+        out = dba.soft_quantize(wt, ct, L, k, T, checkpoint=ck)
+        (out * _t(g, dev)).sum().backward()
+        outs[ck] = (out.detach(), wt.grad, ct.grad)
+    if (k, V) != (2, 1):
+        for a, b in zip(outs[False], outs[True]):
+            assert torch.equal(a, b)
+    rgc, rgw, rws = oracle_mod.grad_codebook(w, c, g, L, k, T)
+    ws, gw, gc = (x.cpu().numpy() for x in outs[True])
+    assert rel_err(ws, rws) <= 1e-5 * _scale(k, V)
+    assert norm_err(gw, rgw) <= 1e-5 * _scale(k, V)
+    assert norm_err(gc, rgc) <= 1e-5 * _scale(k, V)
