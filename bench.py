@@ -18,7 +18,9 @@ Counting.  A state-update is one trellis state at one step in one direction: the
 The roofline object covers the step's longest kernel.  Its bound is VALU issue: the work per state-step is counted in
 full-rate fp32 VALU lane slots (a half-rate max/compare/select costs 2, a quarter-rate exp2/log2/rcp 4), and the peak is
 256 CUs x 128 fp32 lanes x 2.4 GHz = 78.6e12 slots/s (the published 157.3 TFLOP/s fp32 vector rate with an FMA as
-two flops).  Kernel times come from HIP events recorded on the stream the kernels run on.
+two flops).  Kernel times come from HIP events recorded on the stream the kernels run on.  Its ``hbm_view`` puts the
+same kernel's counter-measured HBM bytes (the message tape) over its time against a plain 1 GiB device copy timed in
+the same run: the gradient kernel's forward pass writes its tape near that rate.
 
 After the timed steps, and outside them, the codebook gradient (bcjr_soft_codeword_grad_codebook, the exact dL/dc
 summed over the batch) is timed on the same inputs and reported under ``next_rows`` with its own roofline.  Its bound
@@ -121,6 +123,25 @@ def viterbi_pairs(L: int, k: int, V: int) -> int:
     """Sequences per workgroup of the general Viterbi kernel: 2 where the codebook is read from memory (V = 2,
     L >= 12) and two message arrays fit in LDS, as the library's plan chooses."""
     return 2 if V == 2 and L >= 12 and 2 * (4 << (L - k)) + 2048 <= 160 * 1024 else 1
+
+
+def device_copy_rate(dev, stream, reps: int = 5) -> float:
+    """GB/s of read plus write traffic of a plain 1 GiB device-to-device copy, timed with events on `stream`."""
+    import torch
+
+    src = torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * (1 << 30) / (ms * 1e-3) / 1e9
 
 
 def source_digest(op: str) -> str:
@@ -346,6 +367,15 @@ def main():
                 "traffic": recorded_traffic(dom, wl.name),
                 "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (half-rate op = 2, transcendental = 4)",
                 "units_per_launch": B * n * S}
+    # The same kernel seen from HBM: its counter-measured bytes (the message tape) over its time, against a plain
+    # 1 GiB device copy (2^30 bytes read and 2^30 written) timed here, after the step, on the same stream.
+    copy_rate = device_copy_rate(dev, stream)
+    if roofline["traffic"]:
+        rate = roofline["traffic"] / (d["ms"] * 1e-3) / 1e9
+        roofline["hbm_view"] = {"traffic_GBps": round(rate, 1), "device_copy_GBps": round(copy_rate, 1),
+                                "frac_of_copy": round(rate / copy_rate, 4),
+                                "note": "tape bytes per launch from the committed counters over the launch time, "
+                                        "against a plain device copy measured in this run"}
 
     next_rows = {}
     if args.codebook_grad_steps > 0:
