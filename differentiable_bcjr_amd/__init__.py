@@ -15,15 +15,14 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 
 ``soft_quantize`` ties them together for autograd: its forward is ``soft_codeword``; its backward is
 ``soft_codeword_grad``, or ``soft_codeword_grad_codebook`` when the codebook needs a gradient too.  Both gradients
-are exact ("exactly differentiable with respect to the weight pre-image and trellis parameters", Technical Summary,
-"Core Mechanism").
+are exact: the pages state that the soft codeword is differentiable without approximation in the weights and in the
+trellis parameters (Technical Summary, "Core Mechanism").
 
 ``temperature_schedule`` gives the annealing sequence T0 -> T_end for a QAT run (host-side, see ``anneal``).
 
-Trellis variants: ``k`` (bits shifted in per step) may be 1 to 4 for the soft codeword, its weights' gradient and
-Viterbi.  A codebook of shape [2^L, V] emits V weights per step (V = 1 or 2): the weights are then [B, n V], step t
-of a row owning its weights t V .. t V + V - 1, and Viterbi returns one state per step.  The codebook gradient and
-the tail-biting operations take k = 2 and a codebook [2^L]; the codebook gradient takes every (k, V).
+Trellis variants: ``k`` (bits shifted in per step) may be 1 to 4 for every operation.  A codebook of shape [2^L, V]
+emits V weights per step (V = 1 or 2): the weights are then [B, n V], step t of a row owning its weights
+t V .. t V + V - 1, and Viterbi returns one state per step.
 
 These wrappers only marshal arguments: they check tensor dtypes/devices, allocate outputs and the workspace with
 torch, and pass raw device pointers and the current HIP stream to the library.  Every step of the computation runs
