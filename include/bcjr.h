@@ -86,8 +86,8 @@ int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t
                        size_t workspace_bytes, void* stream);
 
 /*
- * Gradient of the soft codeword with respect to the weight pre-image w ("exactly differentiable with respect to
- * the weight pre-image", gist.science Technical Summary, "Core Mechanism"):
+ * Gradient of the soft codeword with respect to the weight pre-image w (the soft codeword is differentiable in w
+ * without approximation, gist.science Technical Summary, "Core Mechanism"):
  *   grad_w[b, u] = sum_t grad_w_soft[b, t] * d w_soft[b, t] / d w[b, u]
  *               = (2 / T) * Cov_p( codebook[s_u], sum_t grad_w_soft[b, t] * codebook[s_t] ),
  * the covariance taken under the same Boltzmann path measure.  grad_w_soft is the upstream dL/dw_soft (required).
@@ -130,7 +130,8 @@ int viterbi_hard_code(const float* w, const float* codebook, int64_t B, int64_t 
 
 /*
  * Soft codeword under the tail-biting measure: every path with s_0 = s_n weighs exp(-E / T), whatever that state
- * (the "start state = end state" variant of the soft codeword, with the state summed over rather than given).
+ * (the variant of the soft codeword whose start state equals its end state, that state summed over rather than
+ * given).
  * It is the mixture over sigma of the sigma-mode measures with weights Z_sigma / sum Z, so
  *   w_soft[b, t] = sum_sigma pi_sigma w_soft_sigma[b, t],   log_z[b] = ln sum_sigma Z_sigma (optional output),
  * computed exactly from one sigma-mode pass per (row, sigma): L <= 10, else BCJR_ERR_UNSUPPORTED.  Workspace:
@@ -154,8 +155,8 @@ int bcjr_soft_codeword_grad_tail_biting(const float* w, const float* codebook, i
 
 /*
  * Tail-biting Viterbi hard code with the start state chosen by the decoder: the minimum-energy path under the
- * constraint s_0 = s_n (the non-emitting start state equals the last emitting state), the "start state = end state"
- * variant of the hard code.  The pages fix no rule for choosing the state; two are offered:
+ * constraint s_0 = s_n (the non-emitting start state equals the last emitting state), the hard code's variant whose
+ * start state equals its end state.  The pages fix no rule for choosing the state; two are offered:
  *   BCJR_TB_EXACT   every sigma in [0, 2^L) is decoded as in viterbi_hard_code's sigma mode, and sigma is the
  *                   smallest state whose path cost is the minimum (L <= 10, else BCJR_ERR_UNSUPPORTED);
  *   BCJR_TB_ROTATE  rotate-and-decode: the sequence rotated left by n/2 (weight (t + n/2) mod n at step t) is
