@@ -280,8 +280,8 @@ struct Owner {
             ld_floats<ROW>(cbs, row_bytes(m, a, q), out);
         }
     }
-    // The rows in the order a step visits them, fetched one row ahead when they come from memory: forward order
-    // (m, q, a) and backward order (m, a, q).  Row idx + 1 after the last is the next step's first.
+    // The rows in the order a step visits them, fetched ahead when they come from memory: forward order (m, q, a)
+    // and backward order (m, a, q).  Row idx + 1 after the last is the next step's first.
     static constexpr int NROW = BPT * NI * P;
     __device__ __forceinline__ void fwd_next(int idx, float* nx) const {
         if constexpr (!REG) {
@@ -295,23 +295,48 @@ struct Owner {
             row(x / (NI * P), (x / NI) % P, x % NI, nx);
         }
     }
-    // this row: from registers, or the prefetched copy (then the next row is fetched into nx)
-    __device__ __forceinline__ void take_fwd(int m, int a, int q, float* c, float* nx) const {
-        if constexpr (REG) {
-            row(m, a, q, c);
-        } else {
+    // Rows in flight from memory: two cover the L2 latency for the gradient (k = 3: 82.9 -> 78.6 ms); three cost it
+    // registers.  The forward and backward orders differ from the second row on, so a change of direction primes the
+    // ring again.
+    static constexpr int PFD = 2;
+    using Ring = float[REG ? 1 : PFD][REG ? 1 : ROW];
+    __device__ __forceinline__ void fwd_prime(Ring& nx) const {
+        if constexpr (!REG) {
 #pragma unroll
-            for (int x = 0; x < ROW; ++x) c[x] = nx[x];
-            fwd_next((m * NI + q) * P + a, nx);
+            for (int d = 0; d < PFD; ++d) fwd_next(d - 1, nx[d]);
         }
     }
-    __device__ __forceinline__ void take_bwd(int m, int a, int q, float* c, float* nx) const {
+    __device__ __forceinline__ void bwd_prime(Ring& nx) const {
+        if constexpr (!REG) {
+#pragma unroll
+            for (int d = 0; d < PFD; ++d) bwd_next(d - 1, nx[d]);
+        }
+    }
+    // this row: from registers, or the oldest prefetched copy (then the row PFD ahead is fetched into the ring)
+    __device__ __forceinline__ void take_fwd(int m, int a, int q, float* c, Ring& nx) const {
         if constexpr (REG) {
             row(m, a, q, c);
         } else {
 #pragma unroll
-            for (int x = 0; x < ROW; ++x) c[x] = nx[x];
-            bwd_next((m * P + a) * NI + q, nx);
+            for (int x = 0; x < ROW; ++x) c[x] = nx[0][x];
+#pragma unroll
+            for (int d = 0; d + 1 < PFD; ++d)
+#pragma unroll
+                for (int x = 0; x < ROW; ++x) nx[d][x] = nx[d + 1][x];
+            fwd_next((m * NI + q) * P + a + PFD - 1, nx[PFD - 1]);
+        }
+    }
+    __device__ __forceinline__ void take_bwd(int m, int a, int q, float* c, Ring& nx) const {
+        if constexpr (REG) {
+            row(m, a, q, c);
+        } else {
+#pragma unroll
+            for (int x = 0; x < ROW; ++x) c[x] = nx[0][x];
+#pragma unroll
+            for (int d = 0; d + 1 < PFD; ++d)
+#pragma unroll
+                for (int x = 0; x < ROW; ++x) nx[d][x] = nx[d + 1][x];
+            bwd_next((m * P + a) * NI + q + PFD - 1, nx[PFD - 1]);
         }
     }
 };
@@ -364,10 +389,11 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
         if constexpr (NI > 1) return 0u;
         else return 4u * (uint32_t)(own.j(m) - own.j(0) + J * a);
     };
-    float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
-    own.fwd_next(-1, cnx);
+    typename Owner<K, V, SPT, REG>::Ring cnx;          // the next codebook rows (read from memory)
+    own.fwd_prime(cnx);
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
+        if (b != blockIdx.x) own.fwd_prime(cnx);   // the backward pass left the ring in its own order
         const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
         const float* wb = args.w + row * (int64_t)n * V;
         const bool has_sigma = args.sigma_enum || args.sigma != nullptr;
@@ -566,6 +592,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
             rq_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
         }
+        own.bwd_prime(cnx);
         while (t >= 0) {
         const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
         if (ck) {
@@ -582,6 +609,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                 for (int q = 0; q < NI; ++q)
                     ld_to_lds<TI>(msg0, own.fgroup(m, q), tape, 4u * own.tpos(own.fgroup(m, q), G), rows.off(t0));
             lds_barrier();
+            own.fwd_prime(cnx);
             for (int tt = t0; tt < t; ++tt) {
                 float wr[V];
 #pragma unroll
@@ -590,6 +618,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                 fwd_step(wr, Nr, msg0, msg0, rows.off(tt + 1), true);
                 lds_barrier();
             }
+            own.bwd_prime(cnx);
             __syncthreads();   // the recomputed rows, written by other threads, before the backward reads them
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
@@ -765,8 +794,8 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
     const uint32_t buf_bytes = (uint32_t)n * TPS * 4u;
-    float cnx[REG ? 1 : ROW];   // the next codebook row (read from memory)
-    own.fwd_next(-1, cnx);
+    typename Owner<K, V, SPT, REG>::Ring cnx;   // the next codebook rows (read from memory)
+    own.fwd_prime(cnx);
 
     // the word and bit field of forward group u at any step
     auto bp_loc = [&](uint32_t u, uint32_t& word_idx, uint32_t& bit) {
@@ -1062,8 +1091,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         if constexpr (NI > 1) return 0u;
         else return 4u * (uint32_t)(own.j(m) - own.j(0) + J * a);
     };
-    float cnx[REG ? 1 : ROW];                        // the next codebook row (read from memory)
-    own.fwd_next(-1, cnx);
+    typename Owner<K, V, SPT, REG>::Ring cnx;          // the next codebook rows (read from memory)
+    own.fwd_prime(cnx);
     // the codebook-gradient accumulator of the slot: c(s, v) at acc_base + 4 (s V + v), so a tile row's entries are
     // contiguous like its codebook values
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * NS * 4) : 0u);
@@ -1084,6 +1113,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     }
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
+        if (b != blockIdx.x) own.fwd_prime(cnx);   // the backward pass left the ring in its own order
         const int64_t row = args.sigma_enum ? (b >> L) : b;   // the weights' row (sigma enumeration: v >> L)
         const float* wb = args.w + row * (int64_t)n * V;
         const float* gb = args.g + row * (int64_t)n * V;
@@ -1363,6 +1393,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             rt_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
             qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + rows.off(t) + grp_soff(0, 0));
         }
+        own.bwd_prime(cnx);
         while (t >= 0) {
         const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
         if (ck) {
@@ -1386,6 +1417,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     ld_to_lds<TI>(mq, u0, tape, 4u * own.tpos(u0, G), q_base + rows.off(t0));
                 }
             lds_barrier();
+            own.fwd_prime(cnx);
             for (int tt = t0; tt < t; ++tt) {
                 const float Nr = uniform_f(buf_ld(tape, 0u, nrm_base + 4u * tt));
                 const float kr = uniform_f(buf_ld(tape, 0u, kin_base + 4u * tt));
@@ -1393,6 +1425,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 fwd_step(tt, Nr, kr, rows.off(tt + 1), true, lm, lqr);
                 lds_barrier();
             }
+            own.bwd_prime(cnx);
             __syncthreads();   // the recomputed rows, written by other threads, before the backward reads them
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
