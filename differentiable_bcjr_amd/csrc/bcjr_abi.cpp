@@ -109,9 +109,10 @@ constexpr size_t kLdsBytes = 160 * 1024;
 constexpr size_t kLdsStatic = 2048;   // the kernels' own reduction slots
 
 struct GenPlan {
-    bool ok;          // false: no kernel for these shapes (the gradient's two message arrays exceed LDS)
+    bool ok;          // false: no kernel for these shapes (the messages exceed LDS)
     int grid, threads, dbl, ckpt;
     int nsq;          // Viterbi: sequences per workgroup (2 where the codebook streams and two fit in LDS)
+    int qg;           // gradients: the Q^ message in the workspace (its two messages exceed LDS: k = 1, L = 16)
     size_t lds, slot_bytes, total;
     size_t acc_off;   // codebook gradient: offset of the slot's [2^L][V] accumulator
 };
@@ -140,7 +141,9 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     const size_t msg = G * 4;
     if (op == BCJR_OP_GRAD || op == BCJR_OP_GRAD_CODEBOOK) {   // R and Q, one buffer each
         p.dbl = 0;
-        p.lds = 2 * msg;
+        // R~ in LDS, and Q^ too unless both exceed it: then Q^ goes to a buffer in the slot
+        p.qg = 2 * msg + kLdsStatic > kLdsBytes && msg + kLdsStatic <= kLdsBytes ? 1 : 0;
+        p.lds = p.qg ? msg : 2 * msg;
     } else {
         // Viterbi with V = 2 at L >= 12 reads its codebook through L1 every step: pair the sequences so each row
         // read serves two (their message buffers side by side)
@@ -171,7 +174,8 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
         case BCJR_OP_GRAD_CODEBOOK:   // + one float accumulator per state and component
             p.acc_off = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
             p.slot_bytes = p.acc_off + (op == BCJR_OP_GRAD_CODEBOOK ? align256((size_t)S * V * 4) : 0) +
-                           (ckpt ? nrm + align256(2 * G * 4) : 0);   // + the Q input offsets, the saved messages
+                           (ckpt ? nrm + align256(2 * G * 4) : 0) +   // + the Q input offsets, the saved messages
+                           (p.qg ? align256(G * 4) : 0);              // + the Q^ message
             break;
         default:   // two back-pointer buffers (by round parity) of [n][threads] words per sequence of a round
             p.slot_bytes = align256(2 * (size_t)p.nsq * (size_t)n * (size_t)tps * 4);
@@ -317,8 +321,8 @@ const char* bcjr_status_string(int32_t status) {
         case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16, V >= 1";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
         case BCJR_ERR_UNSUPPORTED:
-            return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2 (the gradient at k = 1 needs "
-                   "L <= 15); exact tail-biting and the tail-biting soft codeword and gradient need L <= 10";
+            return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2; exact tail-biting and the "
+                   "tail-biting soft codeword and gradient need L <= 10";
         case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
@@ -410,6 +414,7 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
         a.ckpt = p.ckpt;
+        a.qg = p.qg;
         return hip_status(launch_general(1, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
     const Plan p = make_plan(BCJR_OP_GRAD, B, n, L);
@@ -461,6 +466,7 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
         a.slot_bytes = p.slot_bytes;
         a.dbl = p.dbl;
         a.ckpt = p.ckpt;
+        a.qg = p.qg;
         hipError_t e = launch_general(3, k, V, a, p.grid, p.threads, p.lds, st);
         if (e != hipSuccess) return hip_status(e);
         return hip_status(launch_codebook_reduce(a.ws, p.slot_bytes, (uint32_t)p.acc_off, p.grid, (1 << L) * V,
@@ -631,6 +637,7 @@ int grad_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n, in
         ga.ws = ws;
         ga.slot_bytes = mp.grad.slot_bytes;
         ga.dbl = mp.grad.dbl;
+        ga.qg = mp.grad.qg;
         ga.sigma_enum = 1;
         if ((e = launch_general(1, k, V, ga, mp.grad.grid, mp.grad.threads, mp.grad.lds, st)) != hipSuccess)
             return hip_status(e);

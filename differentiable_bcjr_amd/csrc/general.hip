@@ -1044,7 +1044,9 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 // is normalised by the previous step's exact total, with the running normaliser sums in double.  A later reduction
 // sums the slots in a fixed order.
 
-template <int K, int V, int SPT, int LT, bool GC, bool CK>
+// QG: the expectation message Q^ lives in the workspace (served from L2) instead of LDS, for trellises whose two
+// message arrays exceed LDS (k = 1 at L = 16: 2 x 128 KiB); the step barriers then fence global memory as well.
+template <int K, int V, int SPT, int LT, bool GC, bool CK, bool QG>
 __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     using Gm = GG<K, V, SPT>;
     constexpr int P = Gm::P, I = Gm::I, BPT = Gm::BPT, C = Gm::C, TA = Gm::TA, TI = Gm::TI, NA = Gm::NA,
@@ -1062,7 +1064,6 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     const int WPS = TPS >= 64 ? TPS >> 6 : 1, SEG = TPS >= 64 ? 64 : TPS;
     const float scale = args.scale, inv_scale = 1.0f / scale;
     float* mr = lds;
-    float* mq = lds + G;
 
     Owner<K, V, SPT, REG> own;
     own.init(args.cb, L, TPS);
@@ -1070,7 +1071,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     // tape: the R~ rows and the Q^ rows (TapeRows each), [n] normalisers N_t, [n] offsets K_{t-1} (true
     // Q_t = Q^_t + K_{t-1}), the per-wave (S0, S1[V], S2, S3[V]) of every step, the codebook accumulator (GC), then
     // (checkpoint mode) the [n] per-step Q input offsets and each thread's share of the two backward messages while a
-    // segment is recomputed
+    // segment is recomputed, then (QG) the Q^ message buffer
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * args.slot_bytes, slot_bytes);
     const uint32_t row_bytes = (uint32_t)G * 4u;
@@ -1098,6 +1099,17 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * NS * 4) : 0u);
     const uint32_t kin_base = acc_base + (GC ? (uint32_t)align256(((size_t)V * 4) << L) : 0u);
     const uint32_t save_base = kin_base + (uint32_t)align256((size_t)n * 4);
+    float* mq;
+    if constexpr (QG) {
+        const uint32_t qmsg_base = ck ? save_base + (uint32_t)align256((size_t)2 * G * 4) : kin_base;
+        mq = reinterpret_cast<float*>(args.ws + (size_t)blockIdx.x * args.slot_bytes + qmsg_base);
+    } else {
+        mq = lds + G;
+    }
+    auto bar = [&]() {   // a step barrier: LDS only, or global memory too when Q^ is in the workspace
+        if constexpr (QG) __syncthreads();
+        else lds_barrier();
+    };
     using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
     const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
     if constexpr (GC) {
@@ -1136,7 +1148,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 st_floats<TI>(r, mr, u0, tape, 4u * own.tpos(u0, G), 0u);
                 st_floats<TI>(z, mq, u0, tape, 4u * own.tpos(u0, G), q_base);
             }
-        lds_barrier();
+        bar();
 
         // One forward step t: R~_{t+1} and Q^_{t+1} from R~_t and Q^_t - kqt, normalised by Nt, into LDS (inputs read
         // before a barrier, outputs written in place) and into the tape at row_soff when `store`.  Returns this
@@ -1151,7 +1163,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     rin[m][a] = mr[own.j(m) + J * a];
                     qin[m][a] = mq[own.j(m) + J * a] - kqt;
                 }
-            lds_barrier();   // every input read before any output overwrites it
+            bar();   // every input read before any output overwrites it
             float wt[V], gt[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -1240,7 +1252,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 redmax[t & 1][wv] = lmax;
                 redq[t & 1][wv] = lq;
             }
-            lds_barrier();
+            bar();
             if (WPS > 1) {
                 const int qs = lane & 15;
                 float bm = qs < WPS ? redmax[t & 1][qs] : -3.0e38f;
@@ -1278,7 +1290,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 reds[n & 1][wv][0] = z0;
                 reds[n & 1][wv][1] = z1;
             }
-            lds_barrier();
+            bar();
             if (WPS > 1) {
                 z0 = 0.f;
                 z1 = 0.f;
@@ -1374,7 +1386,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             H = pz;
             t = n - 2;
         }
-        lds_barrier();
+        bar();
 
         const int t_out = t;
         // the accumulator row of the next unit (GC), one unit ahead, wrapping to the next step's first
@@ -1407,7 +1419,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     st_row<TI>(mr + u0, tape, save_base + 4u * u0);
                     st_row<TI>(mq + u0, tape, save_base + row_bytes + 4u * u0);
                 }
-            lds_barrier();   // every share read before the recompute overwrites the buffers
+            bar();   // every share read before the recompute overwrites the buffers
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
@@ -1416,14 +1428,14 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     ld_to_lds<TI>(mr, u0, tape, 4u * own.tpos(u0, G), rows.off(t0));
                     ld_to_lds<TI>(mq, u0, tape, 4u * own.tpos(u0, G), q_base + rows.off(t0));
                 }
-            lds_barrier();
+            bar();
             own.fwd_prime(cnx);
             for (int tt = t0; tt < t; ++tt) {
                 const float Nr = uniform_f(buf_ld(tape, 0u, nrm_base + 4u * tt));
                 const float kr = uniform_f(buf_ld(tape, 0u, kin_base + 4u * tt));
                 float lm, lqr;
                 fwd_step(tt, Nr, kr, rows.off(tt + 1), true, lm, lqr);
-                lds_barrier();
+                bar();
             }
             own.bwd_prime(cnx);
             __syncthreads();   // the recomputed rows, written by other threads, before the backward reads them
@@ -1435,7 +1447,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     ld_to_lds<TI>(mr, u0, tape, save_base + 4u * u0, 0u);
                     ld_to_lds<TI>(mq, u0, tape, save_base + row_bytes + 4u * u0, 0u);
                 }
-            lds_barrier();
+            bar();
             rt_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
             qt_nx = buf_ld_nt(tape, grp_voff(0, 0), q_base + rows.off(t) + grp_soff(0, 0));
         }
@@ -1451,7 +1463,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         bin[m][TI * q + ii] = mr[u];
                         pin[m][TI * q + ii] = mq[u] - kb;
                     }
-            lds_barrier();
+            bar();
             float wt[V], gt[V], gnat[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -1599,7 +1611,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                 for (int x = 0; x < NS; ++x) buf_st(Sv[x], tape, 0u, po + 4u * x);
             }
-            lds_barrier();
+            bar();
             float m1[V];   // w_soft_t - w_t per component, in scaled codebook units
             if (WPS > 1) {
                 const int qs = lane & 15;
@@ -1688,11 +1700,24 @@ namespace {
 using GenKernel = void (*)(GenArgs);
 
 template <int K, int V, int SPT, int LT>
-GenKernel pick(int op, bool ck, int nsq) {
+GenKernel pick(int op, bool ck, int nsq, bool qg) {
     switch (op) {
         case 0: return gen_soft_kernel<K, V, SPT, LT>;
-        case 1: return ck ? gen_grad_kernel<K, V, SPT, LT, false, true> : gen_grad_kernel<K, V, SPT, LT, false, false>;
-        case 3: return ck ? gen_grad_kernel<K, V, SPT, LT, true, true> : gen_grad_kernel<K, V, SPT, LT, true, false>;
+        case 1:
+        case 3:
+            if (qg) {   // Q^ in the workspace: instantiated where it is needed, k = 1 at L = 16
+                if constexpr (K == 1 && LT == 16) {
+                    if (op == 1) return ck ? gen_grad_kernel<K, V, SPT, LT, false, true, true>
+                                           : gen_grad_kernel<K, V, SPT, LT, false, false, true>;
+                    return ck ? gen_grad_kernel<K, V, SPT, LT, true, true, true>
+                              : gen_grad_kernel<K, V, SPT, LT, true, false, true>;
+                }
+                return nullptr;
+            }
+            if (op == 1) return ck ? gen_grad_kernel<K, V, SPT, LT, false, true, false>
+                                   : gen_grad_kernel<K, V, SPT, LT, false, false, false>;
+            return ck ? gen_grad_kernel<K, V, SPT, LT, true, true, false>
+                      : gen_grad_kernel<K, V, SPT, LT, true, false, false>;
         default:
             if constexpr (V == 2 && SPT == 64) {   // the codebook streams: two sequences per workgroup share it
                 if (nsq == 2) return gen_viterbi_kernel<K, V, SPT, LT, 2>;
@@ -1704,30 +1729,30 @@ GenKernel pick(int op, bool ck, int nsq) {
 // L = 16 (the workloads' trellis) has its own instantiation, whose strides are compile-time; other L read it at run
 // time.
 template <int V, int SPT>
-GenKernel pick_k(int op, bool ck, int nsq, int k, int L) {
+GenKernel pick_k(int op, bool ck, int nsq, bool qg, int k, int L) {
     if constexpr (SPT < 64) {
         switch (k) {
-            case 1: return pick<1, V, SPT, 0>(op, ck, nsq);
-            case 2: return pick<2, V, SPT, 0>(op, ck, nsq);
+            case 1: return pick<1, V, SPT, 0>(op, ck, nsq, qg);
+            case 2: return pick<2, V, SPT, 0>(op, ck, nsq, qg);
             default: return nullptr;
         }
     } else {
         switch (k) {
-            case 1: return L == 16 ? pick<1, V, SPT, 16>(op, ck, nsq) : pick<1, V, SPT, 0>(op, ck, nsq);
-            case 2: return L == 16 ? pick<2, V, SPT, 16>(op, ck, nsq) : pick<2, V, SPT, 0>(op, ck, nsq);
-            case 3: return L == 16 ? pick<3, V, SPT, 16>(op, ck, nsq) : pick<3, V, SPT, 0>(op, ck, nsq);
-            case 4: return L == 16 ? pick<4, V, SPT, 16>(op, ck, nsq) : pick<4, V, SPT, 0>(op, ck, nsq);
+            case 1: return L == 16 ? pick<1, V, SPT, 16>(op, ck, nsq, qg) : pick<1, V, SPT, 0>(op, ck, nsq, qg);
+            case 2: return L == 16 ? pick<2, V, SPT, 16>(op, ck, nsq, qg) : pick<2, V, SPT, 0>(op, ck, nsq, qg);
+            case 3: return L == 16 ? pick<3, V, SPT, 16>(op, ck, nsq, qg) : pick<3, V, SPT, 0>(op, ck, nsq, qg);
+            case 4: return L == 16 ? pick<4, V, SPT, 16>(op, ck, nsq, qg) : pick<4, V, SPT, 0>(op, ck, nsq, qg);
             default: return nullptr;
         }
     }
 }
 
 template <int V>
-GenKernel pick_spt(int op, bool ck, int nsq, int k, int L) {
+GenKernel pick_spt(int op, bool ck, int nsq, bool qg, int k, int L) {
     switch (L) {
-        case 4: return pick_k<V, 16>(op, ck, nsq, k, L);
-        case 5: return pick_k<V, 32>(op, ck, nsq, k, L);
-        default: return pick_k<V, 64>(op, ck, nsq, k, L);
+        case 4: return pick_k<V, 16>(op, ck, nsq, qg, k, L);
+        case 5: return pick_k<V, 32>(op, ck, nsq, qg, k, L);
+        default: return pick_k<V, 64>(op, ck, nsq, qg, k, L);
     }
 }
 
@@ -1739,7 +1764,8 @@ hipError_t launch_general(int op, int k, int V, const GenArgs& a, int grid, int 
                           hipStream_t st) {
     const bool ck = a.ckpt != 0;
     const int nsq = a.nsq > 1 ? a.nsq : 1;
-    const GenKernel f = V == 1 ? pick_spt<1>(op, ck, nsq, k, a.L) : pick_spt<2>(op, ck, nsq, k, a.L);
+    const bool qg = a.qg != 0;
+    const GenKernel f = V == 1 ? pick_spt<1>(op, ck, nsq, qg, k, a.L) : pick_spt<2>(op, ck, nsq, qg, k, a.L);
     if (f == nullptr) return hipErrorInvalidValue;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(f), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)lds_bytes);

@@ -74,6 +74,7 @@ struct GenArgs {
                            // recomputes each c-step segment from its checkpoint (soft codeword and gradient)
     int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
     int32_t nsq;           // Viterbi: sequences decoded together by one workgroup (1, or 2 where the plan pairs them)
+    int32_t qg;            // gradients: nonzero puts the Q^ message in the workspace (its two messages exceed LDS)
 };
 
 }  // namespace bcjr

@@ -32,7 +32,7 @@
  *     Calls on different streams need different workspaces.
  *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 2k <= L <= 16, and
  *       every entry point: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs kernels tuned for it, every other
- *       (k, V) one kernel family written for any k; both gradients with k = 1 need L <= 15);
+ *       (k, V) one kernel family written for any k);
  *       exact tail-biting (the exact start-state choice, and the soft codeword and gradient under the
  *       tail-biting measure) needs L <= 10.
  *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
@@ -54,9 +54,9 @@ enum {
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
     BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
-    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; either gradient with k = 1
-                                  and L = 16; exact tail-biting (choice of sigma, soft codeword or gradient
-                                  under the tail-biting measure) with L > 10; unknown mode */
+    BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; exact tail-biting (choice of
+                                  sigma, soft codeword or gradient under the tail-biting measure) with L > 10;
+                                  unknown mode */
     BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };

@@ -105,8 +105,11 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     G = S >> k
     lds_cap, lds_static = 160 * 1024, 2048
     nsq = 1
+    qg = 0
     if op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
-        lds = 2 * G * 4
+        # R~ and Q^ in LDS, or Q^ in a buffer of the slot when the two exceed it (k = 1 at L = 16)
+        qg = 1 if 2 * G * 4 + lds_static > lds_cap and G * 4 + lds_static <= lds_cap else 0
+        lds = G * 4 if qg else 2 * G * 4
     else:
         # Viterbi with V = 2 at L >= 12 decodes two sequences per workgroup (they share the codebook reads)
         if op == abi.BCJR_OP_VITERBI and V == 2 and L >= 12 and 2 * G * 4 + lds_static <= lds_cap:
@@ -123,6 +126,7 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
         slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
         slot += _a256(S * V * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
         slot += nrm + _a256(2 * G * 4) if ckpt else 0
+        slot += _a256(G * 4) if qg else 0
     else:
         slot = _a256(2 * nsq * n * tps * 4)
     return grid * slot
@@ -169,8 +173,8 @@ def test_unsupported_trellis_has_no_workspace():
     assert abi.bcjr_workspace_bytes(0, 4, 8, 10, 5) == 0                 # k > 4
     assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 3) == 0             # V > 2
     assert abi.bcjr_workspace_bytes_v(0, 4, 8, 8, 2, 0) == 0             # V < 1
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 16, 1) == 0  # R and Q exceed LDS at k = 1, L = 16
-    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 16, 1) == 0
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 16, 1) > 0   # k = 1, L = 16: Q^ in the workspace
+    assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, 4, 8, 16, 1) > 0
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, 4, 8, 15, 1) > 0
     for op in (4, 6, 7):                                                 # exact tail-biting: L <= 10, any (k, V)
         assert abi.bcjr_workspace_bytes_v(op, 4, 8, 12, 3, 2) == 0
@@ -375,8 +379,8 @@ def test_unsupported_trellis_rejected():
     assert _grad(L=12, k=6) == abi.BCJR_ERR_UNSUPPORTED
     assert _vit(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
     assert _gc(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
-    assert _grad(L=16, k=1) == abi.BCJR_ERR_UNSUPPORTED                 # R and Q exceed LDS
-    assert _gc(L=16, k=1) == abi.BCJR_ERR_UNSUPPORTED
+    assert _grad(L=16, k=1) == abi.BCJR_ERR_WORKSPACE                   # Q^ in the workspace at k = 1, L = 16
+    assert _gc(L=16, k=1) == abi.BCJR_ERR_WORKSPACE
     for fn in (_soft_v, _grad_v, _gc_v, _vit_v):
         assert fn(V=3) == abi.BCJR_ERR_UNSUPPORTED
         assert fn(V=0) == abi.BCJR_ERR_SHAPE
@@ -478,4 +482,4 @@ def test_largest_shape_keeps_workspace_offsets_in_32_bits():
             for V in (1, 2):
                 per_block = abi.bcjr_workspace_bytes_v(op, 1, 4096, L, k, V)
                 assert per_block < 2 ** 31
-                assert per_block > 0 or (op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK) and (L, k) == (16, 1))
+                assert per_block > 0

@@ -99,7 +99,7 @@ def test_checkpoint_mode_headline_workload_rows(oracle_mod, dev):
 
 # ------------------------------------------------------------------------------- the gradients' checkpoint mode
 
-GRAD_CASES = [c for c in CASES if c[:2] != (16, 1)]   # no gradient kernel at k = 1, L = 16 (LDS)
+GRAD_CASES = CASES
 GRAD_IDS = [f"L{c[0]}k{c[1]}V{c[2]}B{c[3]}n{c[4]}" for c in GRAD_CASES]
 
 

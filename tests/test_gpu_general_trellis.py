@@ -107,8 +107,7 @@ def test_soft_codeword_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
         assert el <= 1e-5
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [c for c in CASES if c[:2] != (16, 1)],
-                         ids=[i for c, i in zip(CASES, IDS) if c[:2] != (16, 1)])
+@pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
 @pytest.mark.parametrize("sigma", [False, True])
 def test_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     if sigma:
@@ -138,11 +137,19 @@ def test_viterbi_matches_oracle_bit_exact(oracle_mod, dev, L, k, V, B, n, sigma)
     np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
 
 
-def test_gradient_k1_at_L16_is_unsupported(dev):
-    w, c, g, _ = _vin(16, 1, 1, 4, 1)
-    with pytest.raises(dba.BCJRError) as e:
-        dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), 16, 1, 0.5)
-    assert e.value.status == dba.abi.BCJR_ERR_UNSUPPORTED
+def test_gradient_k1_at_L16_keeps_q_in_the_workspace(oracle_mod, dev):
+    """k = 1 at L = 16: the two 128 KiB messages exceed LDS, so the gradients keep Q^ in a workspace buffer.  Both
+    gradients, with and without checkpoints, against the oracle."""
+    L, k, B, n, T = 16, 1, 2, 7, 0.3
+    for V in (1, 2):
+        w, c, g, _ = _vin(L, V, B, n, 7090 + V)
+        rgc, rgw, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
+        for ck in (False, True):
+            gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, checkpoint=ck).cpu().numpy()
+            assert grad_err(gr, rgw, g, c, T) <= vgrad_tol(T, False, k, V)
+            gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, return_grad_w=False,
+                                                 checkpoint=ck).cpu().numpy()
+            assert norm_err(gc, rgc) <= 1e-5 * _scale(k, V)
 
 
 # ------------------------------------------------------------------------ batches larger than the persistent grid
@@ -158,10 +165,9 @@ def test_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n):
     ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T).cpu().numpy()
     rws, _ = oracle_mod.soft(w, c, L, k, T)
     assert rel_err(ws, rws) <= vsoft_tol(T, False, k, V)
-    if (L, k) != (16, 1):
-        gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
-        rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
-        assert grad_err(gr, rgr, g, c, T) <= vgrad_tol(T, False, k, V)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
+    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
+    assert grad_err(gr, rgr, g, c, T) <= vgrad_tol(T, False, k, V)
     st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k)
     np.testing.assert_array_equal(st, rst)
@@ -266,8 +272,8 @@ def test_trellis_variant_workload_rows(oracle_mod, dev, name):
 # dL/dc [2^L] or [2^L, V], summed over the batch, compared as a vector like the k = 2 codebook gradient: normwise
 # 1e-5 free and 5e-5 sigma, 5e-5 of the largest entry elementwise, scaled as the other bars here.
 
-GC_CASES = [c for c in CASES if c[:2] != (16, 1)]
-GC_IDS = [i for c, i in zip(CASES, IDS) if c[:2] != (16, 1)]
+GC_CASES = CASES
+GC_IDS = IDS
 
 
 def _max_err(x, ref):
@@ -405,13 +411,12 @@ def test_general_trellis_random_configuration(oracle_mod, dev, i, L, k, V, B, n,
     ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev)).cpu().numpy()
     rws, _ = oracle_mod.soft(w, c, L, k, T, sigma=s)
     assert rel_err(ws, rws) <= vsoft_tol(T, sigma, k, V)
-    if (L, k) != (16, 1):
-        gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
-        rgr, sens = grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s)
-        e = grad_err(gr, rgr, g, c, T)
-        print(f"random {i}: L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: grad {e:.2e} "
-              f"(one-ulp sensitivity {sens:.2e})", flush=True)
-        assert e <= max(vgrad_tol(T, sigma, k, V), sens)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
+    rgr, sens = grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s)
+    e = grad_err(gr, rgr, g, c, T)
+    print(f"random {i}: L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: grad {e:.2e} "
+          f"(one-ulp sensitivity {sens:.2e})", flush=True)
+    assert e <= max(vgrad_tol(T, sigma, k, V), sens)
     st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev)))
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
     np.testing.assert_array_equal(st, rst)
