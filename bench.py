@@ -245,7 +245,7 @@ def time_variant(vw, T, K, dev, stream, check):
         torch.cuda.synchronize()
         ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(K)]))
         units = B * steps * S
-        tail = {"grad": ", false, false", "viterbi": f", {viterbi_pairs(L, k, V)}"}.get(name, "")
+        tail = {"grad": ", false, false, false", "viterbi": f", {viterbi_pairs(L, k, V)}"}.get(name, "")
         ops[name] = {"kernel": f"gen_{name}_kernel<{k}, {V}, 64, 16{tail}>",
                      "ms": round(ms, 4), "state_updates_per_s": DIRECTIONS[name] * units / (ms * 1e-3),
                      "weights_per_s": B * vw.n / (ms * 1e-3),
@@ -468,7 +468,7 @@ def main():
             next_rows[f"{name}_checkpoint"] = {
                 "entry_point": f"{entry} with bcjr_workspace_bytes_min",
                 "kernel": f"gen_soft_kernel<{k}, 1, 64, 16>" if name == "soft"
-                else f"gen_grad_kernel<{k}, 1, 64, 16, false, true>",
+                else f"gen_grad_kernel<{k}, 1, 64, 16, false, true, false>",
                 "checkpoint_interval": int(np.ceil(np.sqrt(n))), "workspace_bytes": ck_bytes,
                 "full_tape_workspace_bytes": abi.bcjr_workspace_bytes(op_id, B, n, L, k),
                 "calls": K4, "ms": round(ms4, 4), "state_updates_per_s": 2 * B * n * S / (ms4 * 1e-3),
