@@ -144,7 +144,8 @@ def test_general_trellis_workspace_formula(L, k, V, B, n):
             assert abi.bcjr_workspace_bytes(op, B, n, L, k) == _gen_bytes(op, B, n, L, k, V)
 
 
-@pytest.mark.parametrize("L,k,V", [(16, 2, 1), (16, 3, 1), (16, 4, 2), (12, 1, 2), (8, 2, 1), (4, 1, 1)])
+@pytest.mark.parametrize("L,k,V", [(16, 2, 1), (16, 3, 1), (16, 4, 2), (16, 1, 1), (16, 1, 2), (12, 1, 2), (8, 2, 1),
+                                   (4, 1, 1)])
 @pytest.mark.parametrize("B,n", [(1, 1), (16, 2), (4096, 256), (100, 4096), (3, 17)])
 def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
     """The smallest workspace of the soft codeword and the two gradients: checkpoints every c = ceil(sqrt(n)) rows,
