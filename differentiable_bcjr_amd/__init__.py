@@ -85,8 +85,14 @@ def workspace_bytes(op: int, B: int, n: int, L: int, k: int = 2, V: int = 1) -> 
 
 def _workspace(op, B, n, L, k, device, workspace, V=1, checkpoint=False):
     """The caller's workspace, or a new one: the full tape, or with ``checkpoint`` the smallest the op accepts (the
-    checkpoint-and-recompute memory mode)."""
+    checkpoint-and-recompute memory mode).  A caller's workspace must be a contiguous device tensor on the weights'
+    device; its size in bytes is what the library is told."""
     need = workspace_bytes(op, B, n, L, k, V)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.device != device:
+            raise TypeError("workspace must be a CUDA (HIP) tensor on the weights' device")
+        if not workspace.is_contiguous():
+            raise TypeError("workspace must be contiguous")
     if checkpoint and workspace is None:
         workspace = torch.empty(max(abi.bcjr_workspace_bytes_min(op, B, n, L, k, V), 1), dtype=torch.uint8,
                                 device=device)
@@ -94,6 +100,10 @@ def _workspace(op, B, n, L, k, device, workspace, V=1, checkpoint=False):
         # torch's allocator hands out 512-byte aligned blocks; the library checks 256-byte alignment itself
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, need
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def _steps(w: torch.Tensor, codebook: torch.Tensor, L: int):
@@ -126,10 +136,10 @@ def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T
     ws, need = _workspace(abi.BCJR_OP_SOFT, B, n, L, k, w.device, workspace, V, checkpoint)
     if V == 1:
         _check(abi.bcjr_soft_codeword(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
-                                      out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+                                      out.data_ptr(), _ptr(lz), ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     else:
         _check(abi.bcjr_soft_codeword_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T), _ptr(sig),
-                                        out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(), _stream(w.device)))
+                                        out.data_ptr(), _ptr(lz), ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     return (out, lz) if return_log_z else out
 
 
@@ -150,11 +160,11 @@ def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: tor
     ws, need = _workspace(abi.BCJR_OP_GRAD, B, n, L, k, w.device, workspace, V, checkpoint)
     if V == 1:
         _check(abi.bcjr_soft_codeword_grad(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
-                                           g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
+                                           g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), _nbytes(ws),
                                            _stream(w.device)))
     else:
         _check(abi.bcjr_soft_codeword_grad_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T), _ptr(sig),
-                                             g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), ws.numel(),
+                                             g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(), _nbytes(ws),
                                              _stream(w.device)))
     return (grad, ws_out) if return_w_soft else grad
 
@@ -180,11 +190,11 @@ def soft_codeword_grad_codebook(w: torch.Tensor, codebook: torch.Tensor, grad_w_
     if V == 1:
         _check(abi.bcjr_soft_codeword_grad_codebook(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
                                                     _ptr(sig), g.data_ptr(), gc.data_ptr(), _ptr(grad), _ptr(ws_out),
-                                                    ws.data_ptr(), ws.numel(), _stream(w.device)))
+                                                    ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     else:
         _check(abi.bcjr_soft_codeword_grad_codebook_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
                                                       _ptr(sig), g.data_ptr(), gc.data_ptr(), _ptr(grad),
-                                                      _ptr(ws_out), ws.data_ptr(), ws.numel(), _stream(w.device)))
+                                                      _ptr(ws_out), ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     extra = tuple(x for x in (grad, ws_out) if x is not None)
     return (gc, *extra) if extra else gc
 
@@ -202,12 +212,12 @@ def viterbi_hard_code(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 
     ws, need = _workspace(abi.BCJR_OP_VITERBI, B, n, L, k, w.device, workspace, V)
     if V == 1:
         _check(abi.viterbi_hard_code(w.data_ptr(), codebook.data_ptr(), B, n, L, k, _ptr(sig), states.data_ptr(),
-                                     w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(), _nbytes(ws),
                                      _stream(w.device)))
     else:
         _check(abi.viterbi_hard_code_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, _ptr(sig),
                                        states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(), ws.data_ptr(),
-                                       ws.numel(), _stream(w.device)))
+                                       _nbytes(ws), _stream(w.device)))
     return states, w_hard, cost
 
 
@@ -223,11 +233,11 @@ def soft_codeword_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k
     ws, need = _workspace(abi.BCJR_OP_SOFT_TAIL_BITING, B, n, L, k, w.device, workspace, V)
     if V == 1:
         _check(abi.bcjr_soft_codeword_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
-                                                  out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(),
+                                                  out.data_ptr(), _ptr(lz), ws.data_ptr(), _nbytes(ws),
                                                   _stream(w.device)))
     else:
         _check(abi.bcjr_soft_codeword_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
-                                                    out.data_ptr(), _ptr(lz), ws.data_ptr(), ws.numel(),
+                                                    out.data_ptr(), _ptr(lz), ws.data_ptr(), _nbytes(ws),
                                                     _stream(w.device)))
     return (out, lz) if return_log_z else out
 
@@ -249,11 +259,11 @@ def soft_codeword_grad_tail_biting(w: torch.Tensor, codebook: torch.Tensor, grad
     if V == 1:
         _check(abi.bcjr_soft_codeword_grad_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T),
                                                        g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
-                                                       ws.numel(), _stream(w.device)))
+                                                       _nbytes(ws), _stream(w.device)))
     else:
         _check(abi.bcjr_soft_codeword_grad_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T),
                                                          g.data_ptr(), grad.data_ptr(), _ptr(ws_out), ws.data_ptr(),
-                                                         ws.numel(), _stream(w.device)))
+                                                         _nbytes(ws), _stream(w.device)))
     return (grad, ws_out) if return_w_soft else grad
 
 
@@ -280,11 +290,11 @@ def viterbi_tail_biting(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int 
     if V == 1:
         _check(abi.viterbi_tail_biting(w.data_ptr(), codebook.data_ptr(), B, n, L, k, tb_mode, states.data_ptr(),
                                        w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(), ws.data_ptr(),
-                                       ws.numel(), _stream(w.device)))
+                                       _nbytes(ws), _stream(w.device)))
     else:
         _check(abi.viterbi_tail_biting_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, tb_mode,
                                          states.data_ptr(), w_hard.data_ptr(), cost.data_ptr(), sigma.data_ptr(),
-                                         ws.data_ptr(), ws.numel(), _stream(w.device)))
+                                         ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     return states, w_hard, cost, sigma
 
 

@@ -1,6 +1,6 @@
 """Build libbcjr.so (HIP kernels + C-ABI) for gfx950, in-tree.
 
-Usage: ``python -m differentiable_bcjr_amd.build`` or ``build()`` from Python.  Every translation unit is compiled
+Usage: ``python -m differentiable_bcjr_amd.build [--incremental]`` or ``build()`` from Python.  Every translation unit is compiled
 with hipcc for gfx950 only, then linked into ``differentiable_bcjr_amd/libbcjr.so``.
 """
 from __future__ import annotations
@@ -46,12 +46,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libbcjr.so; returns its path."""
+def _stale(src: str) -> bool:
+    """The object of src is missing or older than src or any header it may include."""
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    deps = [os.path.join(CSRC, src)] + [os.path.join(d, f) for d in (CSRC, INCLUDE) for f in os.listdir(d)
+                                        if f.endswith((".hpp", ".h"))]
+    return os.path.getmtime(obj) < max(os.path.getmtime(d) for d in deps)
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every HIP source for gfx950 (with ``incremental``, only those whose object is out of date) and link
+    libbcjr.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
+    todo = [s for s in SOURCES if not incremental or _stale(s)]
+    jobs = min(max(len(todo), 1), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,5 +77,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

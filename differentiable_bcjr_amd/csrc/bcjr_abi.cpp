@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 
 #include "trellis.hpp"
@@ -56,9 +57,32 @@ struct Plan {
 constexpr int32_t kMaxGenK = 4;   // the general trellis kernels: 1 <= k <= 4
 constexpr int32_t kMaxGenV = 2;   // and V = 1 or 2 weights per step
 
+// L >= 4 for every k: the k = 2 kernels hand out quads of 16 states, and the general kernels give a thread at least
+// 16 states (a 64-lane wave covers the 2^L states of the smallest trellis several times over).
+constexpr int32_t kMinL = 4;
+
 int check_dims(int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
-    if (B < 1 || B > kMaxB || n < 1 || n > kMaxN || k < 1 || L < 2 * k || L > 16 || V < 1) return BCJR_ERR_SHAPE;
+    if (B < 1 || B > kMaxB || n < 1 || n > kMaxN || k < 1 || L < 2 * k || L < kMinL || L > 16 || V < 1)
+        return BCJR_ERR_SHAPE;
     return BCJR_OK;
+}
+
+// Compute units of the current device, asked of the runtime once per device.  The persistent grids are sized from
+// it (one or more workgroups per CU), and so are the workspaces.  With no device visible (a host that only plans
+// workspaces) it is 256, an MI355X's count.
+constexpr int kMaxDevices = 64;
+constexpr int kDefaultCUs = 256;
+
+int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];   // 0 until asked
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return kDefaultCUs;
+    int cus = cache[dev].load(std::memory_order_relaxed);
+    if (cus > 0) return cus;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = kDefaultCUs;
+    cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 // Soft codeword, gradient and Viterbi: the k = 2, V = 1 kernels, or the general ones.
@@ -80,7 +104,7 @@ int check_temp(float T) {
 Plan make_plan(int op, int64_t B, int64_t n, int L) {
     const GeoRT g = geo_rt(L);
     const int64_t groups = (B + g.SPB - 1) / g.SPB;
-    const int64_t cap = (int64_t)kNumCU * blocks_per_cu(L);
+    const int64_t cap = (int64_t)device_cus() * blocks_per_cu(L);
     Plan p{};
     p.grid = (int)(groups < cap ? groups : cap);
     p.slots = p.grid * g.SPB;
@@ -160,7 +184,7 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     const int bpc_lds = (int)(kLdsBytes / (p.lds + kLdsStatic));
     if (bpc_lds < bpc) bpc = bpc_lds;
     if (bpc < 1) bpc = 1;
-    const int64_t cap = (int64_t)kNumCU * bpc;
+    const int64_t cap = (int64_t)device_cus() * bpc;
     const int64_t rounds = (B + p.nsq - 1) / p.nsq;
     p.grid = (int)(rounds < cap ? rounds : cap);
     const size_t tapes = align256(tape_rows(ckpt, n) * G * 4);
@@ -305,7 +329,8 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
 
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V) {
     const size_t full = bcjr_workspace_bytes_v(op, B, n, L, k, V);
-    if (full == 0 || op == BCJR_OP_VITERBI) return full;
+    // only the soft codeword and the two gradients have a checkpoint mode
+    if (full == 0 || (op != BCJR_OP_SOFT && op != BCJR_OP_GRAD && op != BCJR_OP_GRAD_CODEBOOK)) return full;
     const GenPlan p = make_gen_plan(op, B, n, L, k, V, checkpoint_interval(n));
     return p.ok && p.total < full ? p.total : full;
 }
@@ -318,12 +343,14 @@ const char* bcjr_status_string(int32_t status) {
     switch (status) {
         case BCJR_OK: return "BCJR_OK: success";
         case BCJR_ERR_NULL: return "BCJR_ERR_NULL: a required pointer is NULL";
-        case BCJR_ERR_SHAPE: return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 2k <= L <= 16, V >= 1";
+        case BCJR_ERR_SHAPE:
+            return "BCJR_ERR_SHAPE: need 1 <= B < 2^31, 1 <= n <= 4096, k >= 1, 4 <= L <= 16 with L >= 2k, V >= 1";
         case BCJR_ERR_TEMP: return "BCJR_ERR_TEMP: temperature must be finite and >= 1e-12";
         case BCJR_ERR_UNSUPPORTED:
             return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2; exact tail-biting and the "
                    "tail-biting soft codeword and gradient need L <= 10";
-        case BCJR_ERR_WORKSPACE: return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
+        case BCJR_ERR_WORKSPACE:
+            return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
     }

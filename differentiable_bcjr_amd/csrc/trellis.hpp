@@ -49,9 +49,9 @@ __host__ __device__ constexpr GeoRT geo_rt(int L) {
     return GeoRT{G, Q, QPT, TPS, NT, NT / TPS, TPS >= 64 ? TPS / 64 : 1};
 }
 
-// Blocks per CU the launch plans for (bounds the grid, hence the workspace): one block fills a CU at L >= 15.
+// Blocks per CU the launch plans for (bounds the grid, hence the workspace): one block fills a CU at L >= 15.  The
+// host multiplies this by the device's CU count.
 __host__ __device__ constexpr int blocks_per_cu(int L) { return L >= 15 ? 1 : (L == 14 ? 2 : 8); }
-constexpr int kNumCU = 256;   // MI355X
 
 // ---------------------------------------------------------------------------------------------------------------
 // fast math (hardware transcendental units; inputs here are always in range)

@@ -30,12 +30,15 @@
  *     frees nothing, keeps no state between calls and never synchronizes: the work is enqueued on `stream`
  *     (a hipStream_t; NULL = the default stream) and outputs are valid once the caller synchronizes with it.
  *     Calls on different streams need different workspaces.
- *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 2k <= L <= 16, and
+ *   - supported shapes: 1 <= n <= 4096, 1 <= B <= 2^31 - 1, 4 <= L <= 16 with L >= 2k, and
  *       every entry point: 1 <= k <= 4 and V = 1 or 2 (k = 2 with V = 1 runs kernels tuned for it, every other
  *       (k, V) one kernel family written for any k);
  *       exact tail-biting (the exact start-state choice, and the soft codeword and gradient under the
  *       tail-biting measure) needs L <= 10.
- *   - every check except BCJR_ERR_HIP runs on the host before any HIP call; on error nothing is enqueued and
+ *   - the kernels run persistent grids of one or more workgroups per compute unit of the current device, so the
+ *     workspace sizes scale with its CU count (asked of the runtime once per device; 256, an MI355X's count, when
+ *     no device is visible).  Query the workspace with the device current that will run the call.
+ *   - every check except BCJR_ERR_HIP runs on the host before any kernel launch; on error nothing is enqueued and
  *     the outputs are untouched.  NaN/Inf inside w, codebook or grad_w_soft are not checked: they propagate
  *     into that sequence's outputs.
  */
@@ -52,7 +55,7 @@ extern "C" {
 enum {
     BCJR_OK = 0,
     BCJR_ERR_NULL = -1,        /* a required pointer is NULL */
-    BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 2k or L > 16 */
+    BCJR_ERR_SHAPE = -2,       /* B < 1 or B >= 2^31, n < 1 or n > 4096, k < 1, L < 4, L < 2k or L > 16 */
     BCJR_ERR_TEMP = -3,        /* T not finite, or T < 1e-12 (soft and gradient only) */
     BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; exact tail-biting (choice of
                                   sigma, soft codeword or gradient under the tail-biting measure) with L > 10;
@@ -220,7 +223,8 @@ int viterbi_tail_biting_v(const float* w, const float* codebook, int64_t B, int6
 
 /*
  * Bytes of device workspace the entry point `op` (one of the BCJR_OP_* values above) needs for
- * these shapes; 0 when the shapes are invalid or unsupported.  Pure host function; no HIP call.
+ * these shapes on the current device; 0 when the shapes are invalid or unsupported.  Enqueues nothing; the only
+ * HIP call is the one-time query of the device's CU count.
  */
 size_t bcjr_workspace_bytes(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k);
 
@@ -238,7 +242,7 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
  * A workspace at least bcjr_workspace_bytes_min but smaller than the full tape selects the second; the results are
  * the same up to rounding (the recomputed rows are bit-identical; the two modes may run different kernels).  Where
  * the rounding to 256-byte areas leaves checkpoints no smaller (n <= 3, or tiny rows), this equals the full tape.
- * For Viterbi this is bcjr_workspace_bytes_v.  Pure host function; 0 when the shapes are invalid or unsupported.
+ * For Viterbi and the tail-biting ops this is bcjr_workspace_bytes_v.  0 when the shapes are invalid or unsupported.
  */
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
 

@@ -160,8 +160,21 @@ def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
         if n >= 256 and L == 16 and full:   # the codebook gradient's [2^L][V] accumulator is not reduced
             factor = 6 if op != abi.BCJR_OP_GRAD_CODEBOOK else 4
             assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) * factor < full
-    op = abi.BCJR_OP_VITERBI
-    assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
+    # Viterbi and the tail-biting ops have one memory mode: their smallest workspace is the full one
+    for op in (abi.BCJR_OP_VITERBI, abi.BCJR_OP_VITERBI_TB_EXACT, abi.BCJR_OP_VITERBI_TB_ROTATE,
+               abi.BCJR_OP_SOFT_TAIL_BITING, abi.BCJR_OP_GRAD_TAIL_BITING):
+        assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
+
+
+@pytest.mark.parametrize("L,k,V", [(8, 2, 1), (8, 1, 2), (10, 3, 1)])
+def test_workspace_min_of_the_tail_biting_ops_runs_them(L, k, V):
+    """The size bcjr_workspace_bytes_min gives a tail-biting op is one that op accepts (at B = 4, n = 64, L = 8 it
+    was once a plain Viterbi slot, far smaller than the op needs)."""
+    B, n = 4, 64
+    for op in (abi.BCJR_OP_VITERBI_TB_EXACT, abi.BCJR_OP_VITERBI_TB_ROTATE, abi.BCJR_OP_SOFT_TAIL_BITING,
+               abi.BCJR_OP_GRAD_TAIL_BITING):
+        full = abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
+        assert full > 0 and abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == full
 
 
 def test_workspace_v_matches_the_scalar_query():
@@ -403,6 +416,38 @@ def test_general_trellis_reaches_the_workspace_check():
     need = abi.bcjr_workspace_bytes_min(abi.BCJR_OP_SOFT, 4, 8, 9, 3, 2)   # below it no memory mode fits
     assert _soft_v(L=9, k=3, workspace_bytes=need - 1) == abi.BCJR_ERR_WORKSPACE
     assert _soft_v(L=9, k=3, workspace=FAKE + 16, workspace_bytes=need) == abi.BCJR_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("L,k", [(2, 1), (3, 1)])
+def test_trellis_below_four_state_bits_rejected(L, k):
+    """L < 4 is refused for every k (the kernels give every thread at least 16 states): each entry point returns
+    BCJR_ERR_SHAPE before anything else, and every workspace query returns 0."""
+    for fn in (_soft, _grad, _gc, _vit):
+        assert fn(L=L, k=k) == abi.BCJR_ERR_SHAPE
+    for fn in (_soft_v, _grad_v, _gc_v, _vit_v):
+        for V in (1, 2):
+            assert fn(L=L, k=k, V=V) == abi.BCJR_ERR_SHAPE
+    assert _tb(L=L, k=k) == abi.BCJR_ERR_SHAPE and _tb(L=L, k=k, mode=abi.BCJR_TB_ROTATE) == abi.BCJR_ERR_SHAPE
+    a = [FAKE, FAKE, 4, 8, L, k, 0.5]
+    assert abi.bcjr_soft_codeword_tail_biting(*a, FAKE, None, FAKE, 1 << 30, None) == abi.BCJR_ERR_SHAPE
+    assert abi.bcjr_soft_codeword_grad_tail_biting(*a, FAKE, FAKE, None, FAKE, 1 << 30, None) == abi.BCJR_ERR_SHAPE
+    for op in range(8):
+        for V in (1, 2):
+            assert abi.bcjr_workspace_bytes_v(op, 4, 8, L, k, V) == 0
+            assert abi.bcjr_workspace_bytes_min(op, 4, 8, L, k, V) == 0
+        assert abi.bcjr_workspace_bytes(op, 4, 8, L, k) == 0
+
+
+def test_python_wrapper_checks_a_callers_workspace():
+    """A caller's workspace must be a contiguous device tensor on the weights' device; a host tensor would hand the
+    kernels a host pointer."""
+    import torch
+
+    import differentiable_bcjr_amd as dba
+
+    for ws in (torch.empty(1 << 12, dtype=torch.uint8), object()):
+        with pytest.raises(TypeError):
+            dba._workspace(abi.BCJR_OP_SOFT, 2, 8, 8, 2, torch.device("cuda:0"), ws)
 
 
 @pytest.mark.parametrize("kw", [dict(B=0), dict(n=0), dict(n=4097), dict(L=3), dict(L=17), dict(k=0), dict(L=5, k=3)])
