@@ -15,27 +15,21 @@ Cases span:
 * batches larger than the persistent grid, so that a workgroup decodes several sequences in turn.  This exercises the
   Viterbi traceback pipelined across sequences.
 
-Bars.  They are the k = 2, V = 1 bars multiplied by V max(1, 2/k).  The same float32 recursion runs here, and its
-error comes from the two sources the k = 2 derivation names, both of which grow with the trellis:
-
-* The rounding of a state's log weight theta' = -|c - w|^2 log2(e) / T is proportional to its size.  With V components
-  that log weight is a sum of V squared distances, V times larger on average.
-* The recursion's per-step rounding adds up over the L/k steps of trellis memory, which is twice as long at k = 1 as at
-  k = 2.
-
-At k = 3 and 4 with V = 1 the bars are the k = 2 ones.  Measured maxima over these cases (with other seeds):
-
-* soft codeword at T = 0.05: 1.6e-5 at L = 9, k = 1, V = 2 (free) and 1.5e-5 at L = 5, k = 1, V = 1 (sigma);
-* gradient at T = 0.1: 1.6e-5 elementwise at L = 5, k = 2, V = 2 (free, 2.5e-6 normwise);
-* every k >= 2, V = 1 case at T >= 0.1: within 1e-5.
+Bars: max(1e-5, kappa) for every quantity, kappa being the case's one-ulp conditioning computed by the oracle alone
+(tests/parity.py); Viterbi bit-exact.  The same float32 recursion runs here as at k = 2, with its error growing with
+the trellis (a state's log weight sums V squared distances, and the recursion's rounding adds up over L/k steps of
+trellis memory), and the conditioning of the exact answer grows the same way: one-ulp moves of V inputs per step
+reach the log weights, over the same L/k steps.
 """
 import numpy as np
 import pytest
 import torch
 
 import differentiable_bcjr_amd as dba
+import parity
 import workloads
-from test_gpu_parity import _t, grad_err, grad_tol, norm_err, rel_err, soft_tol
+from parity import norm_err
+from test_gpu_parity import _t
 
 pytestmark = pytest.mark.gpu
 
@@ -68,24 +62,6 @@ CASES = [(4, 1, 1, 16, 6), (4, 1, 2, 7, 5), (5, 1, 1, 5, 8), (5, 2, 2, 9, 9), (6
 IDS = [f"L{L}k{k}V{V}B{B}n{n}" for L, k, V, B, n in CASES]
 
 
-def _scale(k, V):
-    """How much the float32 error grows over the k = 2, V = 1 trellis: a state's log weight is a sum of V squared
-    distances, and the recursion's rounding adds up over L/k steps of trellis memory."""
-    return V * (2 if k == 1 else 1)
-
-
-def vsoft_tol(T, sigma, k, V):
-    return soft_tol(T, sigma) * _scale(k, V)
-
-
-def vgrad_tol(T, sigma, k, V):
-    return grad_tol(T, sigma) * _scale(k, V)
-
-
-def vgrad_norm_ok(x, ref, T, sigma, k, V):
-    return sigma or T >= 0.1 or norm_err(x, ref) <= 1e-5 * _scale(k, V)
-
-
 def _sigma_n(L, k, n):
     """Enough steps for every sigma to be reachable: the constraint needs at least L/k steps."""
     return max(n, -(-L // k) + 1)
@@ -97,14 +73,12 @@ def test_soft_codeword_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     if sigma:
         n = _sigma_n(L, k, n)
     w, c, _, s = _vin(L, V, B, n, 7000 + 31 * L + 7 * k + V + n, sigma)
+    ok = True
     for T in [1.0, 0.1, 0.05]:
         got, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev), return_log_z=True)
-        ref, rlz = oracle_mod.soft(w, c, L, k, T, sigma=s)
-        e = rel_err(got.cpu().numpy(), ref)
-        el = float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0)))
-        print(f"soft L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {e:.2e}, ln Z {el:.2e}", flush=True)
-        assert e <= vsoft_tol(T, sigma, k, V)
-        assert el <= 1e-5
+        print(f"soft L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}:", flush=True)
+        ok &= parity.soft_ok(oracle_mod, got, lz, w, c, L, k, T, s)
+    assert ok
 
 
 @pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
@@ -113,15 +87,12 @@ def test_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     if sigma:
         n = _sigma_n(L, k, n)
     w, c, g, s = _vin(L, V, B, n, 7100 + 31 * L + 7 * k + V + n, sigma)
+    ok = True
     for T in [1.0, 0.1, 0.05]:
         gr, ws = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev), return_w_soft=True)
-        rgr, rws = oracle_mod.grad(w, c, g, L, k, T, sigma=s)
-        e = grad_err(gr.cpu().numpy(), rgr, g, c, T)
-        print(f"grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {e:.2e} "
-              f"(normwise {norm_err(gr.cpu().numpy(), rgr):.2e})", flush=True)
-        assert e <= vgrad_tol(T, sigma, k, V)
-        assert vgrad_norm_ok(gr.cpu().numpy(), rgr, T, sigma, k, V)
-        assert rel_err(ws.cpu().numpy(), rws) <= vsoft_tol(T, sigma, k, V)
+        print(f"grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}:", flush=True)
+        ok &= parity.grad_ok(oracle_mod, gr, ws, w, c, g, L, k, T, s)
+    assert ok
 
 
 @pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
@@ -141,33 +112,37 @@ def test_gradient_k1_at_L16_keeps_q_in_the_workspace(oracle_mod, dev):
     """k = 1 at L = 16: the two 128 KiB messages exceed LDS, so the gradients keep Q^ in a workspace buffer.  Both
     gradients, with and without checkpoints, against the oracle."""
     L, k, B, n, T = 16, 1, 2, 7, 0.3
+    ok = True
     for V in (1, 2):
         w, c, g, _ = _vin(L, V, B, n, 7090 + V)
-        rgc, rgw, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
         for ck in (False, True):
-            gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, checkpoint=ck).cpu().numpy()
-            assert grad_err(gr, rgw, g, c, T) <= vgrad_tol(T, False, k, V)
+            print(f"k = 1, L = 16, V = {V}, checkpoint={ck}:", flush=True)
+            gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, checkpoint=ck)
+            ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, k, T)
             gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, return_grad_w=False,
-                                                 checkpoint=ck).cpu().numpy()
-            assert norm_err(gc, rgc) <= 1e-5 * _scale(k, V)
+                                                 checkpoint=ck)
+            ok &= parity.codebook_grad_ok(oracle_mod, gc, None, None, w, c, g, L, k, T)
+    assert ok
 
 
 # ------------------------------------------------------------------------ batches larger than the persistent grid
 
 
 @pytest.mark.parametrize("L,k,V,B,n", [(8, 1, 2, 4600, 5), (9, 3, 1, 4200, 4), (16, 3, 1, 260, 3),
-                                       (16, 4, 2, 258, 3)])
-def test_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n):
+                                       (16, 4, 2, 258, 3), (16, 1, 1, 260, 3), (16, 1, 2, 258, 3)])
+@pytest.mark.parametrize("ck", [False, True], ids=["full-tape", "checkpoint"])
+def test_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n, ck):
     """More sequences than the grid has workgroups (4096 at L <= 11, 256 at L = 16): every workgroup reuses its slot
-    and LDS, and Viterbi traces one sequence back while it decodes the next."""
+    and LDS (at k = 1, L = 16 the gradient's Q^ message buffer in the slot too), and Viterbi traces one sequence back
+    while it decodes the next; in both memory modes."""
     w, c, g, _ = _vin(L, V, B, n, 7300 + L + k + V)
     T = 0.1
-    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T).cpu().numpy()
-    rws, _ = oracle_mod.soft(w, c, L, k, T)
-    assert rel_err(ws, rws) <= vsoft_tol(T, False, k, V)
-    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
-    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
-    assert grad_err(gr, rgr, g, c, T) <= vgrad_tol(T, False, k, V)
+    print(f"L{L} k{k} V{V} B{B} n{n} checkpoint={ck}:", flush=True)
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, checkpoint=ck)
+    ok = parity.soft_ok(oracle_mod, ws, None, w, c, L, k, T)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, checkpoint=ck)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, k, T)
+    assert ok
     st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k)
     np.testing.assert_array_equal(st, rst)
@@ -183,12 +158,10 @@ def test_one_step(oracle_mod, dev, L, k, V):
     w, c, g, _ = _vin(L, V, 3, 1, 7400 + L)
     T = 0.3
     ws, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, return_log_z=True)
-    rws, rlz = oracle_mod.soft(w, c, L, k, T)
-    assert rel_err(ws.cpu().numpy(), rws) <= 1e-5
-    assert np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0)) <= 1e-5
-    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
-    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
-    assert grad_err(gr, rgr, g, c, T) <= 1e-5
+    ok = parity.soft_ok(oracle_mod, ws, lz, w, c, L, k, T)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, k, T)
+    assert ok
     st, _, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
     rst, _, rcost = oracle_mod.viterbi(w, c, L, k)
     np.testing.assert_array_equal(st, rst)
@@ -210,7 +183,8 @@ def test_sigma_without_a_path(oracle_mod, dev, L, k, V):
     assert dead.any()
     assert np.all(np.isnan(ws[dead])) and np.all(lz[dead] == -np.inf)
     if (~dead).any():
-        assert rel_err(ws[~dead], rws[~dead]) <= 3e-5
+        live = np.flatnonzero(~dead)
+        assert parity.soft_ok(oracle_mod, ws, None, w, c, L, k, T, s, rows=live)
     gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
     assert np.all(np.isnan(gr[dead]))
     _, _, cost = dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev))
@@ -228,10 +202,11 @@ def test_silent_second_component_matches_the_scalar_trellis(dev):
     g2 = np.stack([g1, np.zeros_like(g1)], axis=2).reshape(B, 2 * n)
     a = dba.soft_codeword(_t(w1, dev), _t(c1, dev), L, k, T).cpu().numpy()
     b = dba.soft_codeword(_t(w2, dev), _t(c2, dev), L, k, T).cpu().numpy()
-    assert rel_err(b[:, 0::2], a) <= 2e-5 and np.all(b[:, 1::2] == 0.0)
+    # two float32 evaluations of one quantity, each within the 1e-5 bar of the scalar trellis's exact answer
+    assert parity.rel_err(b[:, 0::2], a) <= 2 * parity.TOL and np.all(b[:, 1::2] == 0.0)
     ga = dba.soft_codeword_grad(_t(w1, dev), _t(c1, dev), _t(g1, dev), L, k, T).cpu().numpy()
     gb = dba.soft_codeword_grad(_t(w2, dev), _t(c2, dev), _t(g2, dev), L, k, T).cpu().numpy()
-    assert norm_err(gb[:, 0::2], ga) <= 2e-5
+    assert norm_err(gb[:, 0::2], ga) <= 2 * parity.TOL
     assert np.max(np.abs(gb[:, 1::2])) == 0.0
     sa = [x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w1, dev), _t(c1, dev), L, k)]
     sb = [x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w2, dev), _t(c2, dev), L, k)]
@@ -254,31 +229,22 @@ def test_trellis_variant_workload_rows(oracle_mod, dev, name):
     st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(wt, ct, wl.L, wl.k))
     assert np.all(np.isfinite(ws)) and np.all(np.isfinite(gr))
     rows = wl.sample_rows(3)
-    rws, _ = oracle_mod.soft(w[rows], c, wl.L, wl.k, T)
-    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
+    print(f"{wl.name}, rows {rows.tolist()}:", flush=True)
+    ok = parity.soft_ok(oracle_mod, ws, None, w, c, wl.L, wl.k, T, rows=rows)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, wl.L, wl.k, T, rows=rows)
+    assert ok
     rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k)
-    e_s, e_g = rel_err(ws[rows], rws), norm_err(gr[rows], rgr)
-    e_ge = grad_err(gr[rows], rgr, g[rows], c, T)
-    print(f"{wl.name}: soft {e_s:.2e}, grad {e_g:.2e} normwise, {e_ge:.2e} elementwise", flush=True)
-    f = _scale(wl.k, wl.V)
-    assert e_s <= 1e-5 * f
-    assert e_g <= 1e-5 * f and e_ge <= 5e-5 * f   # the full-length bars of the k = 2 kernels, scaled as above
     np.testing.assert_array_equal(st[rows], rst)
     np.testing.assert_array_equal(wh[rows].view(np.uint32), rwh.view(np.uint32))
     np.testing.assert_array_equal(cost[rows].view(np.uint32), rcost.view(np.uint32))
 
 
 # ------------------------------------------------------------------------------------ codebook gradient (row f1)
-# dL/dc [2^L] or [2^L, V], summed over the batch, compared as a vector like the k = 2 codebook gradient: normwise
-# 1e-5 free and 5e-5 sigma, 5e-5 of the largest entry elementwise, scaled as the other bars here.
+# dL/dc [2^L] or [2^L, V], summed over the batch, compared as a vector (normwise and against its largest entry) like
+# the k = 2 codebook gradient, within the conditioning bars.
 
 GC_CASES = CASES
 GC_IDS = IDS
-
-
-def _max_err(x, ref):
-    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
-    return float(np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-300))
 
 
 @pytest.mark.parametrize("L,k,V,B,n", GC_CASES, ids=GC_IDS)
@@ -287,19 +253,13 @@ def test_codebook_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     if sigma:
         n = _sigma_n(L, k, n)
     w, c, g, s = _vin(L, V, B, n, 7700 + 31 * L + 7 * k + V + n, sigma)
-    f = _scale(k, V)
+    ok = True
     for T in [1.0, 0.1, 0.05]:
         gc, gw, ws = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev),
                                                      return_w_soft=True)
-        rgc, rgw, rws = oracle_mod.grad_codebook(w, c, g, L, k, T, sigma=s)
-        assert gc.shape == c.shape
-        en, em = norm_err(gc.cpu().numpy(), rgc), _max_err(gc.cpu().numpy(), rgc)
-        eg = grad_err(gw.cpu().numpy(), rgw, g, c, T)
-        print(f"codebook grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: {en:.2e} normwise, {em:.2e} of max; "
-              f"weights' grad {eg:.2e}", flush=True)
-        assert en <= (5e-5 if sigma else 1e-5) * f and em <= 5e-5 * f
-        assert eg <= vgrad_tol(T, sigma, k, V) and vgrad_norm_ok(gw.cpu().numpy(), rgw, T, sigma, k, V)
-        assert rel_err(ws.cpu().numpy(), rws) <= vsoft_tol(T, sigma, k, V)
+        print(f"codebook grad L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}:", flush=True)
+        ok &= parity.codebook_grad_ok(oracle_mod, gc, gw, ws, w, c, g, L, k, T, s)
+    assert ok
 
 
 @pytest.mark.parametrize("L,k,V", [(9, 3, 2), (12, 1, 1), (16, 4, 2)])
@@ -339,9 +299,7 @@ def test_soft_quantize_trains_the_codebook_at_other_bit_rates(oracle_mod, dev):
     wt = _t(w, dev).requires_grad_(True)
     ct = _t(c, dev).requires_grad_(True)
     (dba.soft_quantize(wt, ct, L, k, T) * _t(g, dev)).sum().backward()
-    rgc, rgw, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
-    assert norm_err(ct.grad.cpu().numpy(), rgc) <= 1e-5 * _scale(k, V)
-    assert norm_err(wt.grad.cpu().numpy(), rgw) <= 1e-5 * _scale(k, V)
+    assert parity.codebook_grad_ok(oracle_mod, ct.grad, wt.grad, None, w, c, g, L, k, T)
 
 
 @pytest.mark.parametrize("name", ["k3", "k4v2"])
@@ -353,12 +311,9 @@ def test_codebook_grad_variant_workload_rows(oracle_mod, dev, name):
     rows = wl.sample_rows(3)
     w, g = wl.weights()[rows], wl.upstream_grad()[rows]
     T = wl.temps[0]
-    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), wl.L, wl.k, T,
-                                         return_grad_w=False).cpu().numpy()
-    rgc, _, _ = oracle_mod.grad_codebook(w, c, g, wl.L, wl.k, T)
-    en = norm_err(gc, rgc)
-    print(f"{wl.name} codebook grad, 3 rows: {en:.2e} normwise, {_max_err(gc, rgc):.2e} of max", flush=True)
-    assert en <= 1e-5 * _scale(wl.k, wl.V)
+    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), wl.L, wl.k, T, return_grad_w=False)
+    print(f"{wl.name} codebook grad, rows {rows.tolist()}:", flush=True)
+    assert parity.codebook_grad_ok(oracle_mod, gc, None, None, w, c, g, wl.L, wl.k, T)
 
 
 # ------------------------------------------------------------------------------------ seeded random configurations
@@ -383,55 +338,36 @@ def _random_cases(count=30, seed=4242):
     return cases
 
 
-def _ulp(a, rng):
-    """a moved by one float32 ulp, up or down at random, element by element."""
-    d = np.where(rng.integers(0, 2, a.shape) == 1, np.float32(np.inf), np.float32(-np.inf)).astype(np.float32)
-    return np.nextafter(a, d)
-
-
-def grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s, trials=4, seed=0):
-    """The exact gradient, and how far it moves (grad_err) when w and c move by one float32 ulp: the conditioning of
-    the problem at float32 resolution.  Rounding the inputs alone moves the answer that far, so no float32 evaluation
-    can be held closer.  Computed by the oracle alone."""
-    ref, _ = oracle_mod.grad(w, c, g, L, k, T, sigma=s)
-    rng = np.random.Generator(np.random.PCG64(seed))
-    worst = 0.0
-    for _ in range(trials):
-        moved, _ = oracle_mod.grad(_ulp(w, rng), _ulp(c, rng), g, L, k, T, sigma=s)
-        worst = max(worst, grad_err(moved, ref, g, c, T))
-    return ref, worst
-
-
 @pytest.mark.parametrize("i,L,k,V,B,n,sigma,T", _random_cases())
 def test_general_trellis_random_configuration(oracle_mod, dev, i, L, k, V, B, n, sigma, T):
-    """Random shapes: the gradient bar is the larger of the derived one and the one-ulp sensitivity above, since some
-    draws are ill-conditioned at float32 resolution (e.g. L = 6, k = 2, V = 2, T = 0.1: one-ulp input moves shift the
-    exact gradient by 4.7e-5)."""
+    """Random shapes, some of them ill-conditioned at float32 resolution (e.g. L = 6, k = 2, V = 2, T = 0.1: one-ulp
+    input moves shift the exact gradient by 4.7e-5), which the conditioning bars follow."""
     w, c, g, s = _vin(L, V, B, n, 9900 + i, sigma)
-    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev)).cpu().numpy()
-    rws, _ = oracle_mod.soft(w, c, L, k, T, sigma=s)
-    assert rel_err(ws, rws) <= vsoft_tol(T, sigma, k, V)
-    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev)).cpu().numpy()
-    rgr, sens = grad_ulp_sensitivity(oracle_mod, w, c, g, L, k, T, s)
-    e = grad_err(gr, rgr, g, c, T)
-    print(f"random {i}: L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}: grad {e:.2e} "
-          f"(one-ulp sensitivity {sens:.2e})", flush=True)
-    assert e <= max(vgrad_tol(T, sigma, k, V), sens)
+    print(f"random {i}: L{L} k{k} V{V} B{B} n{n} sigma={sigma} T={T}:", flush=True)
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T, _t(s, dev))
+    ok = parity.soft_ok(oracle_mod, ws, None, w, c, L, k, T, s)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, _t(s, dev))
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, k, T, s)
+    assert ok
     st, wh, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k, _t(s, dev)))
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, k, sigma=s)
     np.testing.assert_array_equal(st, rst)
     np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [(9, 3, 2, 4200, 3), (8, 1, 1, 4400, 4), (16, 4, 2, 300, 2)])
-def test_codebook_grad_several_sequences_per_slot(oracle_mod, dev, L, k, V, B, n):
+@pytest.mark.parametrize("L,k,V,B,n", [(9, 3, 2, 4200, 3), (8, 1, 1, 4400, 4), (16, 4, 2, 300, 2),
+                                       (16, 1, 1, 260, 3), (16, 1, 2, 258, 3)])
+@pytest.mark.parametrize("ck", [False, True], ids=["full-tape", "checkpoint"])
+def test_codebook_grad_several_sequences_per_slot(oracle_mod, dev, L, k, V, B, n, ck):
     """More sequences than the grid has workgroups: each slot's accumulator sums several sequences before the
-    reduction over slots."""
+    reduction over slots (at k = 1, L = 16 each slot's Q^ message buffer serves them in turn), in both memory
+    modes."""
     w, c, g, _ = _vin(L, V, B, n, 8100 + L + k)
     T = 0.2
-    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, return_grad_w=False)
-    rgc, _, _ = oracle_mod.grad_codebook(w, c, g, L, k, T)
-    assert norm_err(gc.cpu().numpy(), rgc) <= 1e-5 * _scale(k, V)
+    print(f"L{L} k{k} V{V} B{B} n{n} checkpoint={ck}:", flush=True)
+    gc = dba.soft_codeword_grad_codebook(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T, return_grad_w=False,
+                                         checkpoint=ck)
+    assert parity.codebook_grad_ok(oracle_mod, gc, None, None, w, c, g, L, k, T)
 
 
 @pytest.mark.parametrize("L,k,V", [(10, 3, 2), (8, 1, 1), (12, 4, 1)])
@@ -439,12 +375,11 @@ def test_longest_sequences(oracle_mod, dev, L, k, V):
     """n = 4096 steps, the largest the boundary accepts (the workspace offsets of the longest tapes)."""
     n, B, T = 4096, 2, 0.3
     w, c, g, _ = _vin(L, V, B, n, 8200 + L)
-    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T).cpu().numpy()
-    rws, _ = oracle_mod.soft(w, c, L, k, T)
-    assert rel_err(ws, rws) <= 1e-5 * _scale(k, V)
-    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T).cpu().numpy()
-    rgr, _ = oracle_mod.grad(w, c, g, L, k, T)
-    assert norm_err(gr, rgr) <= 1e-5 * _scale(k, V)
+    ws = dba.soft_codeword(_t(w, dev), _t(c, dev), L, k, T)
+    ok = parity.soft_ok(oracle_mod, ws, None, w, c, L, k, T)
+    gr = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, k, T)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, k, T)
+    assert ok
     st, _, cost = (x.cpu().numpy() for x in dba.viterbi_hard_code(_t(w, dev), _t(c, dev), L, k))
     rst, _, rcost = oracle_mod.viterbi(w, c, L, k)
     np.testing.assert_array_equal(st, rst)

@@ -1,64 +1,33 @@
 """GPU parity: the HIP path, called through the C-ABI, against the CPU oracle on the same seeded inputs.
 
-Bars:
-* Viterbi states and float32 path costs: bit-exact.
-* Soft codeword and ln Z: 1e-5 under err_t = |x_t - ref_t| / max(|ref_t|, rms over the sequence), free and sigma
-  mode, T >= 0.01 (sigma mode at T = 0.01: 3e-5, see below).
-* Gradient, short sequences (n <= 64): 1e-5 under the same form with the floor taken as the rms over the batch, free
-  mode, T >= 0.1.  Looser where float32 itself cannot do better (derivation): a posterior weight is 2^x with x a float32
-  sum of log-weights theta' = -(c - w)^2 log2(e) / T, each rounded at 2^-24 |theta'|, so the weights' relative error
-  grows as 1/T, and a covariance amplifies it by E|dc dR| / |Cov| (2..5 here).  Free-mode paths fit w closely
-  ((c - w)^2 ~ 0.1): at T = 0.05 that gives up to ~1e-5 elementwise (a random configuration measured 1.26e-5), so the
-  bar there is 2e-5 elementwise with the vector held to 1e-5 normwise; at T = 0.01, 3e-5 elementwise and 1e-5
-  normwise.  When sigma forces the last L/k states ((c - w)^2 up to ~8, |theta'| ~ 10/T) the weights carry
-  ~1e-6..1e-5 relative error at any of these T: 5e-5.
-* Gradient, full-length sequences (n = 256, the matrix workloads): 1e-5 as the relative error of the gradient
-  vector, ||x - ref||_2 / ||ref||_2, and 5e-5 elementwise.  A float32 log-domain recursion cannot hold every element to
-  1e-5 there: rounding the messages to float32 inside the recursion (every other operation exact) already moves
-  individual gradient elements by 1-3e-5 of the rms at T = 0.05, because the recursion errors of the ~L/k steps of
-  trellis memory add up in the posterior and the covariance amplifies posterior errors as above; the vector as a
-  whole stays at ~4e-6.
-* Below T = 0.01 the soft codeword is checked for convergence to the Viterbi code and against a stated bound.
+Bars (tests/parity.py):
+* Viterbi states, codewords and float32 path costs: bit-exact.
+* Soft codeword, ln Z, gradient (elementwise and as a vector): max(1e-5, kappa), kappa being the case's one-ulp
+  conditioning, which the oracle alone computes by moving every float32 weight and codebook value by one ulp.  A
+  well-conditioned case is held to the benchmark spec's 1e-5; one whose exact answer itself moves by more than that when
+  its inputs move by one float32 ulp is held to that movement, the resolution float32 inputs carry.
+* Full-size workloads: the whole batch runs on the GPU in the launch configuration the benchmark times, and 64 sampled
+  rows (rows 0 and B - 1 among them) are compared with stored oracle answers and kappas
+  (tests/golden/make_full_size.py).
+* Below T = 0.01 the soft codeword is also checked for convergence to the Viterbi code.
 """
 import numpy as np
 import pytest
 import torch
 
 import differentiable_bcjr_amd as dba
+import parity
 import workloads
 from differentiable_bcjr_amd import abi
+from parity import check, grad_norm_rows, grad_rows, lz_rows, rel_rows
 
 pytestmark = pytest.mark.gpu
-
-TOL = 1e-5
 
 
 @pytest.fixture(scope="module")
 def dev():
     assert torch.cuda.is_available(), "GPU tests need an MI355X"
     return torch.device("cuda:0")
-
-
-def rel_err(x, ref):
-    """max over t of |x_t - ref_t| / max(|ref_t|, rms(ref)) per sequence, then the max over sequences."""
-    x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
-    rms = np.sqrt(np.mean(ref * ref, axis=-1, keepdims=True))
-    den = np.maximum(np.abs(ref), np.maximum(rms, 1e-30))
-    return float(np.max(np.abs(x - ref) / den))
-
-
-def grad_err(x, ref, g, c, T):
-    """Like rel_err, but the floor is the larger of the rms of the reference gradient over the whole batch and 1e-3
-    of the gradient's natural unit (2/T) rms(g) Var(c) (each dw_soft_t / dw_u is (2/T) Cov(c_t, c_u)).  A sequence
-    whose posterior is frozen has a true gradient of ~1e-13 that no float32 evaluation resolves, and a batch made
-    only of such sequences has no rms to measure against."""
-    x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
-    rms = np.sqrt(np.mean(ref * ref))
-    unit = (2.0 / T) * np.sqrt(np.mean(np.asarray(g, np.float64) ** 2)) * np.var(np.asarray(c, np.float64))
-    den = np.maximum(np.abs(ref), max(rms, 1e-3 * unit, 1e-30))
-    return float(np.max(np.abs(x - ref) / den))
 
 
 def _inputs(L, B, n, seed, sigma=False):
@@ -81,49 +50,20 @@ TEMPS = [1.0, 0.1, 0.01]
 GRAD_TEMPS = [1.0, 0.1, 0.05, 0.01]
 
 
-def norm_err(x, ref):
-    """||x - ref||_2 / ||ref||_2 over every element given."""
-    x = np.asarray(x, np.float64)
-    ref = np.asarray(ref, np.float64)
-    return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-300))
-
-
-GRAD_ELEM_TOL_LONG = 5e-5
-
-
-def grad_tol(T, sigma):
-    """Elementwise gradient bar: the benchmark spec's 1e-5 in free mode at T >= 0.1; float32-limited cases per the module doc
-    (below T = 0.1 the vector is also held to 1e-5 normwise, see grad_norm_ok)."""
-    if sigma:
-        return 5e-5
-    if T >= 0.1:
-        return 1e-5
-    return 2e-5 if T >= 0.05 else 3e-5
-
-
-def grad_norm_ok(x, ref, T, sigma):
-    """Free mode below T = 0.1: the gradient vector within 1e-5 normwise (the spec bar read for a vector)."""
-    return sigma or T >= 0.1 or norm_err(x, ref) <= 1e-5
-
-
-def soft_tol(T, sigma):
-    return 3e-5 if (sigma and T < 0.05) else TOL
-
-
 @pytest.mark.parametrize("L,B,n", SMALL)
 @pytest.mark.parametrize("sigma", [False, True])
 def test_soft_codeword_matches_oracle(oracle_mod, dev, L, B, n, sigma):
     if sigma and n < (L + 1) // 2:
         n = (L + 1) // 2 + 1   # the sigma constraint needs at least L/k steps to be satisfiable for every sigma
     w, c, _, s = _inputs(L, B, n, 100 + 7 * L + n, sigma)
+    ok = True
     for T in TEMPS:
         got, lz = dba.soft_codeword(_t(w, dev), _t(c, dev), L, 2, T, _t(s, dev), return_log_z=True)
-        ref, rlz = oracle_mod.soft(w, c, L, 2, T, sigma=s)
-        e = rel_err(got.cpu().numpy(), ref)
-        elz = float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0)))
-        print(f"soft L={L} B={B} n={n} T={T} sigma={sigma}: err {e:.2e}, log_z err {elz:.2e}", flush=True)
-        assert e <= soft_tol(T, sigma)
-        assert elz <= TOL
+        ref, rlz, k_ws, k_lz = parity.soft_reference(oracle_mod, w, c, L, 2, T, sigma=s)
+        print(f"soft L={L} B={B} n={n} T={T} sigma={sigma}:", flush=True)
+        ok &= check("w_soft", rel_rows(got.cpu().numpy(), ref), k_ws)
+        ok &= check("ln Z", lz_rows(lz.cpu().numpy(), rlz), k_lz)
+    assert ok
 
 
 @pytest.mark.parametrize("L,B,n", SMALL)
@@ -133,17 +73,13 @@ def test_gradient_matches_oracle(oracle_mod, dev, L, B, n, sigma):
         n = (L + 1) // 2 + 2   # a unique path (n = L/k) has an exactly zero gradient, checked separately
     B = max(B, 4)             # the error floor is the batch rms: keep some sequences whose posterior is not frozen
     w, c, g, s = _inputs(L, B, n, 200 + 5 * L + n, sigma)
+    ok = True
     for T in GRAD_TEMPS:
         got, ws = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), L, 2, T, _t(s, dev),
                                          return_w_soft=True)
-        ref, rws = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
-        e = grad_err(got.cpu().numpy(), ref, g, c, T)
-        ew = rel_err(ws.cpu().numpy(), rws)
-        ea = float(np.max(np.abs(got.cpu().numpy() - ref)))
-        print(f"grad L={L} B={B} n={n} T={T} sigma={sigma}: err {e:.2e} (abs {ea:.1e}, rms {np.sqrt(np.mean(ref**2)):.1e}),"
-              f" w_soft err {ew:.2e}", flush=True)
-        assert e <= grad_tol(T, sigma) and grad_norm_ok(got.cpu().numpy(), ref, T, sigma)
-        assert ew <= soft_tol(T, sigma)
+        print(f"grad L={L} B={B} n={n} T={T} sigma={sigma}:", flush=True)
+        ok &= parity.grad_ok(oracle_mod, got, ws, w, c, g, L, 2, T, s)
+    assert ok
 
 
 @pytest.mark.parametrize("L,B,n", SMALL)
@@ -219,53 +155,72 @@ def test_raw_abi_call_on_a_stream(oracle_mod, dev):
                                     ws.data_ptr(), need, st.cuda_stream)
     assert rc == abi.BCJR_OK
     st.synchronize()
-    ref, _ = oracle_mod.soft(w, c, L, 2, T)
-    assert rel_err(out.cpu().numpy(), ref) <= TOL
+    ref, _, k_ws, _ = parity.soft_reference(oracle_mod, w, c, L, 2, T)
+    assert check("w_soft", rel_rows(out.cpu().numpy(), ref), k_ws)
 
 
 # ------------------------------------------------------------------------------------------------------------------
 # full-size workloads, in the launch configuration the benchmark times; sampled rows against the oracle
 
 
-def _sampled(oracle_mod, fn, rows):
-    return fn(rows)
+def _golden_soft(G, got, lz, T, sigma=False):
+    """A stored soft-codeword entry against the GPU's answers on its rows, each row within its own bar."""
+    key = parity.golden_key("soft", T, sigma)
+    rows = G["rows"]
+    ok = check(f"{key} w_soft", rel_rows(got.cpu().numpy()[rows], G[key + "/w_soft"]), G[key + "/kappa_w_soft"])
+    if lz is not None:
+        ok &= check(f"{key} ln Z", lz_rows(lz.cpu().numpy()[rows], G[key + "/log_z"]), G[key + "/kappa_log_z"])
+    return ok
 
 
-def test_headline_workload_sampled(oracle_mod, dev):
+def _golden_grad(G, gr, ws, g, c, T, sigma=False):
+    """A stored gradient entry (gradient elementwise and as a vector, and the pass's soft codeword) against the
+    GPU's answers on its rows, each row within its own bar."""
+    key = parity.golden_key("grad", T, sigma)
+    rows = G["rows"]
+    floor = float(G[key + "/grad_floor"])
+    got, ref = gr.cpu().numpy()[rows], G[key + "/grad"]
+    ok = check(f"{key} grad", grad_rows(got, ref, g[rows], c, T, floor), G[key + "/kappa_grad"])
+    ok &= check(f"{key} grad normwise", grad_norm_rows(got, ref, g[rows], c, T, floor), G[key + "/kappa_grad_norm"])
+    if ws is not None:
+        ok &= check(f"{key} w_soft", rel_rows(ws.cpu().numpy()[rows], G[key + "/w_soft"]), G[key + "/kappa_w_soft"])
+    return ok
+
+
+def _viterbi_rows(oracle_mod, st, wh, cost, w, c, wl, rows, sig=None):
+    rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k, sigma=None if sig is None else sig[rows])
+    np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
+    if wh is not None:
+        np.testing.assert_array_equal(wh.cpu().numpy()[rows].view(np.uint32), rwh.view(np.uint32))
+    np.testing.assert_array_equal(cost.cpu().numpy()[rows].view(np.uint32), rcost.view(np.uint32))
+    return rst
+
+
+def test_headline_workload_sampled(dev):
     """4096 sequences x 256 weights, 2^16-state trellis (a 1024x1024 matrix): the benchmark's workload."""
     wl = workloads.WORKLOADS[2]
-    c = wl.codebook()
-    w = wl.weights()
-    rows = wl.sample_rows(4)
-    wt, ct = _t(w, dev), _t(c, dev)
+    G = parity.load_golden(2)
+    wt, ct = _t(wl.weights(), dev), _t(wl.codebook(), dev)
+    ok = True
     for T in wl.temps:
         got, lz = dba.soft_codeword(wt, ct, wl.L, wl.k, T, return_log_z=True)
-        got = got.cpu().numpy()[rows]
-        ref, rlz = oracle_mod.soft(w[rows], c, wl.L, wl.k, T)
-        e = rel_err(got, ref)
-        elz = float(np.max(np.abs(lz.cpu().numpy()[rows] - rlz) / np.abs(rlz)))
-        print(f"headline T={T} rows={rows.tolist()}: err {e:.2e} log_z err {elz:.2e}", flush=True)
-        assert e <= TOL and elz <= TOL
+        print(f"headline T={T}, {len(G['rows'])} rows:", flush=True)
+        ok &= _golden_soft(G, got, lz, T)
+    assert ok
 
 
 def test_headline_workload_gradient_and_viterbi_sampled(oracle_mod, dev):
     """The benchmark's step on the same workload: gradient at T = 0.1 and the Viterbi code."""
     wl = workloads.WORKLOADS[2]
+    G = parity.load_golden(2)
     c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
-    rows = wl.sample_rows(4)
     T = 0.1
     wt, ct = _t(w, dev), _t(c, dev)
     gr, ws = dba.soft_codeword_grad(wt, ct, _t(g, dev), wl.L, wl.k, T, return_w_soft=True)
-    ref, rws = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
-    got = gr.cpu().numpy()[rows]
-    e, en, ew = grad_err(got, ref, g[rows], c, T), norm_err(got, ref), rel_err(ws.cpu().numpy()[rows], rws)
-    print(f"headline grad rows={rows.tolist()}: {en:.2e} normwise, {e:.2e} elementwise; w_soft {ew:.2e}", flush=True)
-    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG and ew <= TOL
+    print(f"headline grad, {len(G['rows'])} rows:", flush=True)
+    assert _golden_grad(G, gr, ws, g, c, T)
     st, wh, cost = dba.viterbi_hard_code(wt, ct, wl.L, wl.k)
-    rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k)
-    np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
-    np.testing.assert_array_equal(wh.cpu().numpy()[rows].view(np.uint32), rwh.view(np.uint32))
-    np.testing.assert_array_equal(cost.cpu().numpy()[rows].view(np.uint32), rcost.view(np.uint32))
+    _viterbi_rows(oracle_mod, st, wh, cost, w, c, wl, G["rows"])
 
 
 # ------------------------------------------------------------------------------------------------------------------
@@ -279,14 +234,13 @@ def test_longest_sequences(oracle_mod, dev, sigma):
     w, c, g, s = _inputs(L, B, n, 77, sigma)
     wt, ct, st_ = _t(w, dev), _t(c, dev), _t(s, dev)
     got, lz = dba.soft_codeword(wt, ct, L, 2, T, st_, return_log_z=True)
-    ref, rlz = oracle_mod.soft(w, c, L, 2, T, sigma=s)
-    assert rel_err(got.cpu().numpy(), ref) <= TOL
-    assert float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.abs(rlz))) <= TOL
-    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T, st_).cpu().numpy()
-    rgr, _ = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
-    en, e = norm_err(gr, rgr), grad_err(gr, rgr, g, c, T)
-    print(f"n=4096 sigma={sigma}: grad {en:.2e} normwise, {e:.2e} elementwise", flush=True)
-    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG
+    ref, rlz, k_ws, k_lz = parity.soft_reference(oracle_mod, w, c, L, 2, T, sigma=s)
+    print(f"n=4096 sigma={sigma}:", flush=True)
+    ok = check("w_soft", rel_rows(got.cpu().numpy(), ref), k_ws)
+    ok &= check("ln Z", lz_rows(lz.cpu().numpy(), rlz), k_lz)
+    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T, st_)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, 2, T, s)
+    assert ok
     stt, _, cost = dba.viterbi_hard_code(wt, ct, L, 2, st_)
     rst, _, rcost = oracle_mod.viterbi(w, c, L, 2, sigma=s)
     np.testing.assert_array_equal(stt.cpu().numpy(), rst)
@@ -305,11 +259,11 @@ def test_batch_edges(oracle_mod, dev, L, B, n, rows):
     rows = np.asarray(rows)
     wt, ct = _t(w, dev), _t(c, dev)
     got = dba.soft_codeword(wt, ct, L, 2, T).cpu().numpy()[rows]
-    ref, _ = oracle_mod.soft(w[rows], c, L, 2, T)
-    assert rel_err(got, ref) <= TOL
-    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T).cpu().numpy()[rows]
-    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], L, 2, T)
-    assert grad_err(gr, rgr, g[rows], c, T) <= grad_tol(T, False)
+    ref, _, k_ws, _ = parity.soft_reference(oracle_mod, w[rows], c, L, 2, T)
+    ok = check("w_soft", rel_rows(got, ref), k_ws)
+    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T)
+    ok &= parity.grad_ok(oracle_mod, gr, None, w, c, g, L, 2, T, None, rows=rows)
+    assert ok
     st, _, cost = dba.viterbi_hard_code(wt, ct, L, 2)
     rst, _, rcost = oracle_mod.viterbi(w[rows], c, L, 2)
     np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
@@ -319,88 +273,70 @@ def test_batch_edges(oracle_mod, dev, L, B, n, rows):
 def test_mlp_layer_gradient_sampled(oracle_mod, dev):
     """65536 sequences (an 8192x2048 matrix), T = 0.05: soft codeword and gradient."""
     wl = workloads.WORKLOADS[3]
+    G = parity.load_golden(3)
     c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
-    rows = wl.sample_rows(4)
     T = wl.temps[0]
     gr, ws = dba.soft_codeword_grad(_t(w, dev), _t(c, dev), _t(g, dev), wl.L, wl.k, T, return_w_soft=True)
-    ref, rws = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
-    got = gr.cpu().numpy()[rows]
-    e, en = grad_err(got, ref, g[rows], c, T), norm_err(got, ref)
-    ew = rel_err(ws.cpu().numpy()[rows], rws)
-    print(f"mlp grad rows={rows.tolist()}: grad err {en:.2e} normwise, {e:.2e} elementwise; w_soft err {ew:.2e}",
-          flush=True)
-    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG and ew <= TOL
+    print(f"mlp layer, {len(G['rows'])} rows:", flush=True)
+    assert _golden_grad(G, gr, ws, g, c, T)
 
 
 def test_low_temperature_sweep_and_viterbi_sampled(oracle_mod, dev):
     """16384 sequences (2048x2048): Viterbi bit-exact (free and sigma), soft codeword down to T = 1e-4."""
     wl = workloads.WORKLOADS[4]
+    G = parity.load_golden(4)
+    rows = G["rows"]
     c, w = wl.codebook(), wl.weights()
     sig = wl.boundary_states()
-    rows = wl.sample_rows(4)
     wt, ct = _t(w, dev), _t(c, dev)
     st, wh, cost = dba.viterbi_hard_code(wt, ct, wl.L, wl.k)
-    rst, rwh, rcost = oracle_mod.viterbi(w[rows], c, wl.L, wl.k)
-    np.testing.assert_array_equal(st.cpu().numpy()[rows], rst)
-    np.testing.assert_array_equal(cost.cpu().numpy()[rows].view(np.uint32), rcost.view(np.uint32))
-    sts, _, costs = dba.viterbi_hard_code(wt, ct, wl.L, wl.k, _t(sig, dev))
-    rsts, _, rcosts = oracle_mod.viterbi(w[rows], c, wl.L, wl.k, sigma=sig[rows])
-    np.testing.assert_array_equal(sts.cpu().numpy()[rows], rsts)
-    np.testing.assert_array_equal(costs.cpu().numpy()[rows].view(np.uint32), rcosts.view(np.uint32))
+    rst = _viterbi_rows(oracle_mod, st, wh, cost, w, c, wl, rows)
+    sts, whs, costs = dba.viterbi_hard_code(wt, ct, wl.L, wl.k, _t(sig, dev))
+    _viterbi_rows(oracle_mod, sts, whs, costs, w, c, wl, rows, sig)
     hard = c[rst]
+    ok = True
     for T in wl.temps:
-        got = dba.soft_codeword(wt, ct, wl.L, wl.k, T).cpu().numpy()[rows]
-        ref, _ = oracle_mod.soft(w[rows], c, wl.L, wl.k, T)
-        e = rel_err(got, ref)
-        to_hard = float(np.median(np.abs(got - hard)))
-        print(f"low-T T={T}: err vs oracle {e:.2e}, median |w_soft - c(s*)| {to_hard:.2e}", flush=True)
-        if T >= 0.01:
-            assert e <= TOL
-        else:
-            # float32 log-weights of size ~|theta| carry ~|theta| * 2^-24 error: bound stated in the design notes
-            assert e <= 2e-3
+        got = dba.soft_codeword(wt, ct, wl.L, wl.k, T)
+        print(f"low-T T={T}, {len(rows)} rows: median |w_soft - c(s*)| "
+              f"{float(np.median(np.abs(got.cpu().numpy()[rows] - hard))):.2e}", flush=True)
+        ok &= _golden_soft(G, got, None, T)
+    assert ok
     # convergence to the hard code as T -> 0
     got = dba.soft_codeword(wt, ct, wl.L, wl.k, 1e-4).cpu().numpy()[rows]
     assert np.mean(np.abs(got - hard) < 1e-3) > 0.9
 
 
-def test_low_temperature_workload_sigma_sampled(oracle_mod, dev):
+def test_low_temperature_workload_sigma_sampled(dev):
     """The same 16384 sequences with s_0 = s_n = sigma: soft codeword at T = 0.1 and 0.01, gradient at T = 0.1."""
     wl = workloads.WORKLOADS[4]
+    G = parity.load_golden(4)
     c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
     sig = wl.boundary_states()
-    rows = wl.sample_rows(4)
     wt, ct, st_ = _t(w, dev), _t(c, dev), _t(sig, dev)
+    ok = True
     for T in (0.1, 0.01):
         got, lz = dba.soft_codeword(wt, ct, wl.L, wl.k, T, st_, return_log_z=True)
-        ref, rlz = oracle_mod.soft(w[rows], c, wl.L, wl.k, T, sigma=sig[rows])
-        e = rel_err(got.cpu().numpy()[rows], ref)
-        elz = float(np.max(np.abs(lz.cpu().numpy()[rows] - rlz) / np.abs(rlz)))
-        print(f"low-T sigma T={T}: soft err {e:.2e}, log_z err {elz:.2e}", flush=True)
-        assert e <= soft_tol(T, True) and elz <= TOL
+        print(f"low-T sigma T={T}, {len(G['rows'])} rows:", flush=True)
+        ok &= _golden_soft(G, got, lz, T, sigma=True)
     T = 0.1
-    gr = dba.soft_codeword_grad(wt, ct, _t(g, dev), wl.L, wl.k, T, st_).cpu().numpy()[rows]
-    rgr, _ = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T, sigma=sig[rows])
-    en, e = norm_err(gr, rgr), grad_err(gr, rgr, g[rows], c, T)
-    print(f"low-T sigma grad T={T}: {en:.2e} normwise, {e:.2e} elementwise", flush=True)
-    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG
+    gr, ws = dba.soft_codeword_grad(wt, ct, _t(g, dev), wl.L, wl.k, T, st_, return_w_soft=True)
+    print(f"low-T sigma grad T={T}:", flush=True)
+    ok &= _golden_grad(G, gr, ws, g, c, T, sigma=True)
+    assert ok
 
 
 @pytest.mark.slow
-def test_whole_decoder_layer_sampled(oracle_mod, dev):
+def test_whole_decoder_layer_sampled(dev):
     """All seven Llama-3.2-1B projection shapes as one batch of 237,568 sequences, T = 0.05."""
     wl = workloads.WORKLOADS[5]
+    G = parity.load_golden(5)
     c, w, g = wl.codebook(), wl.weights(), wl.upstream_grad()
-    rows = wl.sample_rows(4)
     T = wl.temps[0]
     wt, ct, gt = _t(w, dev), _t(c, dev), _t(g, dev)
-    ws = dba.soft_codeword(wt, ct, wl.L, wl.k, T).cpu().numpy()[rows]
-    gr = dba.soft_codeword_grad(wt, ct, gt, wl.L, wl.k, T).cpu().numpy()[rows]
-    ref, rws = oracle_mod.grad(w[rows], c, g[rows], wl.L, wl.k, T)
-    e, en, ew = grad_err(gr, ref, g[rows], c, T), norm_err(gr, ref), rel_err(ws, rws)
-    print(f"layer rows={rows.tolist()}: grad err {en:.2e} normwise, {e:.2e} elementwise; w_soft err {ew:.2e}",
-          flush=True)
-    assert en <= TOL and e <= GRAD_ELEM_TOL_LONG and ew <= TOL
+    ws = dba.soft_codeword(wt, ct, wl.L, wl.k, T)
+    gr = dba.soft_codeword_grad(wt, ct, gt, wl.L, wl.k, T)
+    print(f"decoder layer, {len(G['rows'])} rows (soft codeword from its own call):", flush=True)
+    assert _golden_grad(G, gr, ws, g, c, T)
 
 
 # ------------------------------------------------------------------------------------------------------------------
@@ -424,14 +360,13 @@ def test_random_configuration(oracle_mod, dev, i, L, B, n, T, sigma):
     w, c, g, s = _inputs(L, B, n, 5000 + i, sigma)
     wt, ct, st_ = _t(w, dev), _t(c, dev), _t(s, dev)
     got, lz = dba.soft_codeword(wt, ct, L, 2, T, st_, return_log_z=True)
-    ref, rlz = oracle_mod.soft(w, c, L, 2, T, sigma=s)
-    assert rel_err(got.cpu().numpy(), ref) <= soft_tol(T, sigma)
-    assert float(np.max(np.abs(lz.cpu().numpy() - rlz) / np.maximum(np.abs(rlz), 1.0))) <= TOL
+    ref, rlz, k_ws, k_lz = parity.soft_reference(oracle_mod, w, c, L, 2, T, sigma=s)
+    print(f"random {i}: L={L} B={B} n={n} T={T} sigma={sigma}:", flush=True)
+    ok = check("w_soft", rel_rows(got.cpu().numpy(), ref), k_ws)
+    ok &= check("ln Z", lz_rows(lz.cpu().numpy(), rlz), k_lz)
     gr, ws = dba.soft_codeword_grad(wt, ct, _t(g, dev), L, 2, T, st_, return_w_soft=True)
-    rgr, rws = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
-    assert rel_err(ws.cpu().numpy(), rws) <= soft_tol(T, sigma)
-    assert grad_err(gr.cpu().numpy(), rgr, g, c, T) <= grad_tol(T, sigma)
-    assert grad_norm_ok(gr.cpu().numpy(), rgr, T, sigma)
+    ok &= parity.grad_ok(oracle_mod, gr, ws, w, c, g, L, 2, T, s)
+    assert ok
     stt, wh, cost = dba.viterbi_hard_code(wt, ct, L, 2, st_)
     rst, rwh, rcost = oracle_mod.viterbi(w, c, L, 2, sigma=s)
     np.testing.assert_array_equal(stt.cpu().numpy(), rst)
@@ -519,8 +454,8 @@ def test_soft_quantize_autograd(oracle_mod, dev, sigma):
     wt = _t(w, dev).requires_grad_(True)
     out = dba.soft_quantize(wt, _t(c, dev), L, 2, T, _t(s, dev))
     (out * _t(g, dev)).sum().backward()
-    ref, _ = oracle_mod.soft(w, c, L, 2, T, sigma=s)
-    rgr, _ = oracle_mod.grad(w, c, g, L, 2, T, sigma=s)
-    assert rel_err(out.detach().cpu().numpy(), ref) <= TOL
-    assert grad_err(wt.grad.cpu().numpy(), rgr, g, c, T) <= grad_tol(T, sigma)
+    ref, _, k_ws, _ = parity.soft_reference(oracle_mod, w, c, L, 2, T, sigma=s)
+    ok = check("w_soft", rel_rows(out.detach().cpu().numpy(), ref), k_ws)
+    ok &= parity.grad_ok(oracle_mod, wt.grad, None, w, c, g, L, 2, T, s)
+    assert ok
     assert wt.grad.dtype == torch.float32
