@@ -10,7 +10,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libbcjr.so")
+# BCJR_LIB selects another build of the library (the host-sanitizer build of the CPU test sessions)
+LIB_PATH = os.environ.get("BCJR_LIB") or os.path.join(_PKG, "libbcjr.so")
 
 BCJR_OK = 0
 BCJR_ERR_NULL = -1

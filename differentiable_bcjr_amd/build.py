@@ -76,6 +76,43 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     return LIB
 
 
+# The host side of the C-ABI (argument checks, workspace planning, dispatch) built with AddressSanitizer and
+# UndefinedBehaviorSanitizer: host code only, each -fsanitize behind -Xarch_host so no GPU code is instrumented.  Load it
+# with clang's ASan runtime preloaded (libclang_rt.asan) and BCJR_LIB pointing at it.
+SANITIZE_HOST_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """clang's AddressSanitizer runtime, which the sanitized library needs preloaded."""
+    llvm = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm", "lib", "clang")
+    for root, _, files in os.walk(os.path.realpath(llvm)):
+        if "libclang_rt.asan-x86_64.so" in files:
+            return os.path.join(root, "libclang_rt.asan-x86_64.so")
+    raise RuntimeError("libclang_rt.asan-x86_64.so not found")
+
+
+def build_sanitized(path: str) -> str:
+    """libbcjr.so with its C-ABI translation unit (every check and workspace plan) rebuilt with the host sanitizers,
+    linked with the kernels' objects of the last build into `path`; returns path."""
+    obj = path + ".abi.o"
+    cmd = [hipcc(), "-x", "hip", *HIPCC_FLAGS, *SANITIZE_HOST_FLAGS, "-c", os.path.join(CSRC, "bcjr_abi.cpp"), "-o",
+           obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on bcjr_abi.cpp:\n{r.stdout}\n{r.stderr}")
+    objs = [obj if s == "bcjr_abi.cpp" else os.path.join(BUILD_DIR, s + ".o") for s in SOURCES]
+    missing = [o for o in objs if not os.path.exists(o)]
+    if missing:
+        raise RuntimeError(f"build() first: missing {missing}")
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+                        "-Xarch_host", "-fsanitize=undefined", *objs, "-o", path], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.remove(obj)
+    return path
+
+
 if __name__ == "__main__":
     build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

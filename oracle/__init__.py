@@ -33,6 +33,11 @@ GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=o
              "-fexcess-precision=standard"]
 
 
+# Host sanitizers (AddressSanitizer and UndefinedBehaviorSanitizer): a separate build for test sessions run with
+# gcc's libasan preloaded; any finding aborts the process.
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
 def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc; returns its path."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
@@ -40,6 +45,13 @@ def build(force: bool = True) -> str:
         subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(path: str) -> str:
+    """Compile oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer into `path` (use with
+    LD_PRELOAD=$(gcc -print-file-name=libasan.so) and ORACLE_LIB=path); returns path."""
+    subprocess.check_call(["gcc", *GCC_FLAGS, *SANITIZE_FLAGS, "-o", path, _SRC, "-lm"])
+    return path
 
 
 class _Handle:

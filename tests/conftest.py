@@ -20,7 +20,7 @@ def pytest_configure(config):
 def oracle_mod():
     import oracle
 
-    alt = os.environ.get("ORACLE_LIB")   # set only by the mutation test, which plants mistakes in copies
+    alt = os.environ.get("ORACLE_LIB")   # set by the mutation and sanitizer tests, which run other builds
     if alt:
         oracle.use_library(alt)
     else:
