@@ -31,7 +31,7 @@ are the general-trellis kernels on the same 1024x1024 matrix at 3 bits per weigh
 two weights per step (k = 4, V = 2): soft codeword, gradient and Viterbi, each against the ALU roofline of its own
 slot count (general_slots).  The soft codeword and the gradient are also timed in their checkpoint-and-recompute
 memory mode (given bcjr_workspace_bytes_min: every ceil(sqrt(n))-th message row kept, the rest rebuilt per segment),
-with the workspace that mode needs beside the full tape's.
+with the workspace that mode needs beside the full tape's (at k = 2 the tuned kernels' own checkpoint mode).
 
 ``--gpus N`` with N > 1 exits: the path runs on one GPU (sequences are independent; sharding B needs no exchange).
 """
@@ -64,6 +64,10 @@ ALU_SLOTS = {
     "viterbi": 3.5 + 2.25 * HALF_SLOTS,
 }
 DIRECTIONS = {"soft": 2, "grad": 2, "viterbi": 1}
+# The flat planning count of the same work: every VALU instruction one slot whatever its issue rate, a transcendental
+# four: soft about 11 VALU + 2.75 transcendentals, grad 17 + 3.25, Viterbi 5.5 + 0 per state-step.  The line reports
+# the fraction of the peak under both counts; the issue-rate-weighted one above is the primary (``frac``).
+FLAT_SLOTS = {"soft": 11.0 + 2.75 * TRANS_SLOTS, "grad": 17.0 + 3.25 * TRANS_SLOTS, "viterbi": 5.5}
 
 
 def general_slots(k: int, V: int) -> dict:
@@ -90,8 +94,9 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES.update({f"gen_{op}_k{k}v{V}": ["general.hip"] for op in ("soft", "grad", "viterbi")
                        for k, V in ((3, 1), (4, 2))})
 COMMON_SOURCES = ["trellis.hpp", "kernel_args.hpp"]
-KERNEL_NAMES = {"soft": "soft_kernel<16>", "grad": "grad_kernel<16, false>", "viterbi": "viterbi_kernel<16>",
-                "grad_codebook": "grad_kernel<16, true>"}
+KERNEL_NAMES = {"soft": "soft_kernel<16, false>", "grad": "grad_kernel<16, false, false>",
+                "viterbi": "viterbi_kernel<16>", "grad_codebook": "grad_kernel<16, true, false>"}
+CHECKPOINT_KERNELS = {"soft": "soft_kernel<16, true>", "grad": "grad_kernel<16, false, true>"}
 # HBM bytes per state-step of the codebook gradient: forward tape R~ and Q^ (one float per group each, i.e. 2 bytes
 # per state, written by the forward pass and read by the backward pass) + the per-state accumulator (4 bytes read
 # and 4 written per step)
@@ -357,16 +362,21 @@ def main():
         slots = ALU_SLOTS[name] * B * n * S
         per_op[name] = {"kernel": KERNEL_NAMES[name], "ms": round(ms, 4), "state_updates_per_s": upd / (ms * 1e-3),
                         "weights_per_s": B * n / (ms * 1e-3),
-                        "alu_frac": slots / (ms * 1e-3) / PEAK_SLOTS_PER_S}
+                        "alu_frac": slots / (ms * 1e-3) / PEAK_SLOTS_PER_S,
+                        "alu_frac_flat_count": FLAT_SLOTS[name] * B * n * S / (ms * 1e-3) / PEAK_SLOTS_PER_S}
     dom = max(per_op, key=lambda o: per_op[o]["ms"])
     d = per_op[dom]
     achieved = ALU_SLOTS[dom] * B * n * S / (d["ms"] * 1e-3) / 1e12
     peak = PEAK_SLOTS_PER_S / 1e12
+    flat = FLAT_SLOTS[dom] * B * n * S / (d["ms"] * 1e-3) / 1e12
     roofline = {"bound": "alu", "kernel": d["kernel"], "achieved": round(achieved, 3), "peak": round(peak, 3),
                 "unit": "T VALU-slots/s", "frac": round(achieved / peak, 4),
                 "traffic": recorded_traffic(dom, wl.name),
                 "per_unit": f"{ALU_SLOTS[dom]} fp32 VALU slots per state-step (half-rate op = 2, transcendental = 4)",
-                "units_per_launch": B * n * S}
+                "units_per_launch": B * n * S,
+                "flat_count": {"achieved": round(flat, 3), "frac": round(flat / peak, 4),
+                               "per_unit": f"{FLAT_SLOTS[dom]} slots per state-step: every VALU instruction 1, a "
+                                           "transcendental 4"}}
     # The same kernel seen from HBM: its counter-measured bytes (the message tape) over its time, against a plain
     # 1 GiB device copy (2^30 bytes read and 2^30 written) timed here, after the step, on the same stream.
     copy_rate = device_copy_rate(dev, stream)
@@ -467,8 +477,7 @@ def main():
             entry = "bcjr_soft_codeword" if name == "soft" else "bcjr_soft_codeword_grad"
             next_rows[f"{name}_checkpoint"] = {
                 "entry_point": f"{entry} with bcjr_workspace_bytes_min",
-                "kernel": f"gen_soft_kernel<{k}, 1, 64, 16>" if name == "soft"
-                else f"gen_grad_kernel<{k}, 1, 64, 16, false, true, false>",
+                "kernel": CHECKPOINT_KERNELS[name],
                 "checkpoint_interval": int(np.ceil(np.sqrt(n))), "workspace_bytes": ck_bytes,
                 "full_tape_workspace_bytes": abi.bcjr_workspace_bytes(op_id, B, n, L, k),
                 "calls": K4, "ms": round(ms4, 4), "state_updates_per_s": 2 * B * n * S / (ms4 * 1e-3),

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "trellis.hpp"
 
@@ -100,26 +101,28 @@ int check_temp(float T) {
     return BCJR_OK;
 }
 
-// Grid, slot count and per-slot workspace bytes of one entry point.  One slot per in-flight sequence.
-Plan make_plan(int op, int64_t B, int64_t n, int L) {
+// Grid, slot count and per-slot workspace bytes of one entry point.  One slot per in-flight sequence.  ckpt > 0 (soft
+// codeword and gradients): the checkpoint mode, every ckpt-th message row plus one segment's rows and the saved
+// backward message(s); the gradients also keep each step's Q input offset.
+Plan make_plan(int op, int64_t B, int64_t n, int L, int ckpt = 0) {
     const GeoRT g = geo_rt(L);
     const int64_t groups = (B + g.SPB - 1) / g.SPB;
     const int64_t cap = (int64_t)device_cus() * blocks_per_cu(L);
     Plan p{};
     p.grid = (int)(groups < cap ? groups : cap);
     p.slots = p.grid * g.SPB;
-    const size_t msgs = (size_t)(n + 1) * (size_t)g.G * 4;   // one float per group per step (+1 spare row)
+    const size_t msgs = TapeRows::rows(ckpt, (int)n) * (size_t)g.G * 4;   // one float per group per row
     const size_t nrm = (size_t)n * 4;                         // one normaliser per step
     switch (op) {
         case BCJR_OP_SOFT:   // + per-wave (S0, S1) of every step when a sequence spans several waves
-            p.slot_bytes = align256(msgs) + align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 8) : 0);
+            p.slot_bytes = align256(msgs) + align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 8) : 0) +
+                           (ckpt ? align256((size_t)g.G * 4) : 0);
             break;
-        case BCJR_OP_GRAD:   // + per-wave (S0..S3) of every step when a sequence spans several waves
-            p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0);
-            break;
-        case BCJR_OP_GRAD_CODEBOOK:   // the gradient's slot + one float accumulator per state
+        case BCJR_OP_GRAD:            // + per-wave (S0..S3) of every step when a sequence spans several waves
+        case BCJR_OP_GRAD_CODEBOOK:   // + one float accumulator per state
             p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0) +
-                           align256(((size_t)1 << L) * 4);
+                           (op == BCJR_OP_GRAD_CODEBOOK ? align256(((size_t)1 << L) * 4) : 0) +
+                           (ckpt ? align256(nrm) + align256((size_t)2 * g.G * 4) : 0);
             break;
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
     }
@@ -148,9 +151,6 @@ int checkpoint_interval(int64_t n) {
     return c;
 }
 
-// Rows of forward messages a slot holds: every step (n + 1), or with checkpoint interval c the n / c + 1 checkpoints
-// and the c - 1 rows of one segment.
-size_t tape_rows(int ckpt, int64_t n) { return ckpt == 0 ? (size_t)n + 1 : (size_t)(n / ckpt + ckpt); }
 
 // op: BCJR_OP_SOFT, BCJR_OP_GRAD, BCJR_OP_GRAD_CODEBOOK or BCJR_OP_VITERBI.  ckpt > 0 (not Viterbi): the
 // checkpoint-and-recompute mode with that interval.
@@ -187,7 +187,7 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     const int64_t cap = (int64_t)device_cus() * bpc;
     const int64_t rounds = (B + p.nsq - 1) / p.nsq;
     p.grid = (int)(rounds < cap ? rounds : cap);
-    const size_t tapes = align256(tape_rows(ckpt, n) * G * 4);
+    const size_t tapes = align256(TapeRows::rows(ckpt, (int)n) * G * 4);
     const size_t nrm = align256((size_t)n * 4);
     switch (op) {
         case BCJR_OP_SOFT:   // R~ rows, normalisers, per-wave (S0, S1[V]) of every step (+ the saved message)
@@ -331,6 +331,10 @@ size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int
     const size_t full = bcjr_workspace_bytes_v(op, B, n, L, k, V);
     // only the soft codeword and the two gradients have a checkpoint mode
     if (full == 0 || (op != BCJR_OP_SOFT && op != BCJR_OP_GRAD && op != BCJR_OP_GRAD_CODEBOOK)) return full;
+    if (tuned(k, V)) {   // the k = 2 kernels' own checkpoint mode
+        const Plan p = make_plan(op, B, n, L, checkpoint_interval(n));
+        return p.total < full ? p.total : full;
+    }
     const GenPlan p = make_gen_plan(op, B, n, L, k, V, checkpoint_interval(n));
     return p.ok && p.total < full ? p.total : full;
 }
@@ -377,8 +381,8 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     // memory: the full tape when the workspace holds it, else checkpoints with per-segment recompute
     const size_t full = tuned(k, V) ? make_plan(BCJR_OP_SOFT, B, n, L).total : make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V).total;
     const bool recompute = workspace != nullptr && workspace_bytes < full;
-    if (!tuned(k, V) || recompute) {
-        const GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
+    if (!tuned(k, V)) {
+        GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
         a.w = w;
@@ -396,7 +400,8 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
         a.ckpt = p.ckpt;
         return hip_status(launch_general(0, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
-    const Plan p = make_plan(BCJR_OP_SOFT, B, n, L);
+    const int ckpt = recompute ? checkpoint_interval(n) : 0;
+    Plan p = make_plan(BCJR_OP_SOFT, B, n, L, ckpt);
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     SoftArgs a{};
     a.w = w;
@@ -409,6 +414,7 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     a.log_z = log_z;
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
+    a.ckpt = ckpt;
     return hip_status(launch_soft(L, a, p.grid, static_cast<hipStream_t>(stream)));
 }
 
@@ -422,7 +428,7 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     const float scale = (float)std::sqrt(1.4426950408889634 / (double)T);
     const size_t full = tuned(k, V) ? make_plan(BCJR_OP_GRAD, B, n, L).total : make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V).total;
     const bool recompute = workspace != nullptr && workspace_bytes < full;
-    if (!tuned(k, V) || recompute) {
+    if (!tuned(k, V)) {
         const GenPlan p = make_gen_plan(BCJR_OP_GRAD, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
@@ -444,7 +450,8 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
         a.qg = p.qg;
         return hip_status(launch_general(1, k, V, a, p.grid, p.threads, p.lds, static_cast<hipStream_t>(stream)));
     }
-    const Plan p = make_plan(BCJR_OP_GRAD, B, n, L);
+    const int ckpt = recompute ? checkpoint_interval(n) : 0;
+    const Plan p = make_plan(BCJR_OP_GRAD, B, n, L, ckpt);
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     GradArgs a{};
     a.w = w;
@@ -459,6 +466,7 @@ int grad_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     a.w_soft = w_soft;
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
+    a.ckpt = ckpt;
     return hip_status(launch_grad(L, a, p.grid, static_cast<hipStream_t>(stream)));
 }
 
@@ -474,7 +482,7 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
     const size_t full = tuned(k, V) ? make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L).total
                                     : make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V).total;
     const bool recompute = workspace != nullptr && workspace_bytes < full;
-    if (!tuned(k, V) || recompute) {
+    if (!tuned(k, V)) {
         const GenPlan p = make_gen_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
@@ -499,7 +507,8 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
         return hip_status(launch_codebook_reduce(a.ws, p.slot_bytes, (uint32_t)p.acc_off, p.grid, (1 << L) * V,
                                                  grad_codebook, st));
     }
-    const Plan p = make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L);
+    const int ckpt = recompute ? checkpoint_interval(n) : 0;
+    const Plan p = make_plan(BCJR_OP_GRAD_CODEBOOK, B, n, L, ckpt);
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     GradArgs a{};
     a.w = w;
@@ -514,6 +523,7 @@ int grad_codebook_impl(const float* w, const float* codebook, int64_t B, int64_t
     a.w_soft = w_soft;
     a.ws = static_cast<unsigned char*>(workspace);
     a.slot_bytes = p.slot_bytes;
+    a.ckpt = ckpt;
     return hip_status(launch_grad_codebook(L, a, p.grid, st, grad_codebook));
 }
 

@@ -128,22 +128,6 @@ __device__ __forceinline__ void ld_to_lds(float* lds, int idx, rsrc_t tape, uint
     for (int i = 0; i < N; ++i) lds[idx + i] = v[i];
 }
 
-// Tape rows of the forward messages.  Without checkpoints row t sits at t * row_bytes.  With checkpoint interval c,
-// rows t = 0, c, 2c, .. (n / c + 1 of them) come first, then c - 1 rows for the steps inside one segment: row t at
-// segment position t mod c - 1.  The forward pass stores the checkpoints and row n - 1 (which the sigma end reads);
-// the backward pass recomputes each segment's other rows from its checkpoint.
-struct TapeRows {
-    int c, n;
-    uint32_t row_bytes, seg_base;
-    __device__ __forceinline__ uint32_t off(int t) const {
-        if (c == 0) return (uint32_t)t * row_bytes;
-        const int r = t % c;
-        return r == 0 ? (uint32_t)(t / c) * row_bytes : seg_base + (uint32_t)(r - 1) * row_bytes;
-    }
-    __device__ __forceinline__ bool stored(int t) const { return c == 0 || t % c == 0 || t == n - 1; }
-    __host__ __device__ static constexpr size_t rows(int c, int n) { return c == 0 ? (size_t)n + 1 : (size_t)(n / c + c); }
-};
-
 // Maximum and sum over the SEG lanes of one sequence (SEG = 64, or the whole sub-wave block).
 __device__ __forceinline__ float gseq_max(float x, int seg) {
     if (seg == 64) return wave_max64(x);

@@ -43,7 +43,7 @@ namespace bcjr {
 #define BCJR_GRAD_FWD_GROUPS 1
 #endif
 #ifndef BCJR_GRAD_BWD_GROUPS
-#define BCJR_GRAD_BWD_GROUPS 1
+#define BCJR_GRAD_BWD_GROUPS 2
 #endif
 constexpr int kGradFwdGroups = BCJR_GRAD_FWD_GROUPS;
 constexpr int kGradBwdGroups = BCJR_GRAD_BWD_GROUPS;
@@ -61,7 +61,12 @@ __device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs
 // GC: also accumulate dL/dc per state of the trellis into this slot's accumulator (read-modify-write of
 // [2^L] floats at the end of the slot, one float4 per group and step), normalising each step's posterior by the
 // previous step's exact total, with the running normaliser sums in double.
-template <int L, bool GC>
+// CK: the checkpoint mode.  The forward pass stores only rows t = 0, c, 2c, .. and row n - 1 of both messages
+// (TapeRows), and each step's Q input offset; the backward pass walks the segments from the end and, before each,
+// saves its two messages to the workspace, reloads the segment's checkpoint, reruns the forward steps of the segment
+// with the stored normalisers and offsets (the same code and numbers as the first pass, so the rows come out
+// bit-identical), and restores its messages.  A compile-time flag, so the full-tape kernels carry none of it.
+template <int L, bool GC, bool CK>
 __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     using Gm = Geo<L>;
     constexpr int G = Gm::G, Q = Gm::Q, QPT = Gm::QPT, TPS = Gm::TPS, SPB = Gm::SPB, WPS = Gm::WPS;
@@ -102,13 +107,16 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
     }
 
-    // tape of this block's sequences: slot sq at sq * slot_bytes; [n+1][G] R~, [n+1][G] Q^, then per step the
-    // normaliser N_t and the offset K_{t-1} of Q^_t (true Q_t = Q^_t + K_{t-1})
+    // tape of this block's sequences: slot sq at sq * slot_bytes; the R~ rows and the Q^ rows (TapeRows each), then
+    // per step the normaliser N_t and the offset K_{t-1} of Q^_t (true Q_t = Q^_t + K_{t-1})
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * SPB * args.slot_bytes, SPB * slot_bytes);
     const uint32_t v_quad = sq * slot_bytes + 16u * tau;
     const uint32_t v_grp = sq * slot_bytes + 4u * tau;
-    const uint32_t q_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const int ck = CK ? args.ckpt : 0;
+    constexpr uint32_t row_bytes = G * 4u;
+    const TapeRows rows{ck, n, row_bytes, ck ? (uint32_t)(n / ck + 1) * row_bytes : 0u};
+    const uint32_t q_base = (uint32_t)align256(TapeRows::rows(ck, n) * row_bytes);
     const uint32_t nrm_base = 2u * q_base;
     const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
     // with several waves per sequence, each wave's (S0, S1, S2, S3) of every step goes here and the outputs are
@@ -117,6 +125,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     // the codebook-gradient accumulator of the slot: state s at acc_base + 4 s, so the 4 states of group (m, a)
     // are the float4 at acc_base + 16 (a Q + j)
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * 16) : 0u);
+    // checkpoint mode: each step's Q input offset, then each thread's share of the two backward messages while a
+    // segment is rebuilt
+    const uint32_t kqi_base = acc_base + (GC ? (uint32_t)align256((size_t)4 << L) : 0u);
+    const uint32_t save_base = kqi_base + (uint32_t)align256((size_t)n * 4);
     using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
     const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
     if constexpr (GC) {
@@ -156,16 +168,12 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         }
         lds_barrier();
 
-        double A = 0.0;
-        float N = 0.f;
-        float kq = 0.f;       // kappa_t: Q^_t at the most likely group of R~_t, subtracted on input
-        float K = 0.f;        // K_{t-1} = sum of the kappas applied so far
-        float N_last = 0.f, K_last = 0.f;
         float4 fc[4];   // codebook rows of the next quad, when they come from memory
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-            fc[a] = !CB_REG ? cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, a) : make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int t = 0; t < n; ++t) {
+        // One forward step: R~_{t+1} and Q^_{t+1} from R~_t and Q^_t - kq (LDS, one buffer each: every input is read
+        // before a barrier, then the outputs overwrite them), normaliser N subtracted; to LDS and, when `store`, to the
+        // tape rows at roff.  lmax, lq: this thread's maximum of R~_{t+1} and the Q^ of the group attaining it.  The
+        // first pass and the checkpoint recompute both run it; fc must hold the first quad's codebook rows.
+        auto fwd_step = [&](int t, float N, float kq, bool store, uint32_t roff, float& lmax, float& lq) {
             float rin[QPT][4], qin[QPT][4];
 #pragma unroll
             for (int m = 0; m < QPT; ++m)
@@ -175,15 +183,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     qin[m][a] = mq[tau + TPS * m + Q * a] - kq;
                 }
             lds_barrier();   // every input read before any output overwrites it
-            if (tau == 0) {
-                buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
-                buf_st(K, tape, sq * slot_bytes, kq_base + 4u * t);
-            }
-            K_last = K;
-            K += kq;
             const float wt = wb[t] * scale;
             const float gt = gb[t] * inv_scale;
-            float lmax = -3.0e38f, lq = 0.f;
+            lmax = -3.0e38f;
+            lq = 0.f;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
                 const int j = tau + TPS * m;
@@ -229,9 +232,34 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
                 *reinterpret_cast<float4*>(mr + 4 * j) = r4;
                 *reinterpret_cast<float4*>(mq + 4 * j) = q4;
-                buf_st4_nt(r4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
-                buf_st4_nt(q4, tape, v_quad, q_base + (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);
+                if (store) {
+                    buf_st4_nt(r4, tape, v_quad, roff + 16u * TPS * m);
+                    buf_st4_nt(q4, tape, v_quad, q_base + roff + 16u * TPS * m);
+                }
             }
+        };
+        auto prime_fc = [&]() {
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                fc[a] = !CB_REG ? cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, a) : make_float4(0.f, 0.f, 0.f, 0.f);
+        };
+
+        double A = 0.0;
+        float N = 0.f;
+        float kq = 0.f;       // kappa_t: Q^_t at the most likely group of R~_t, subtracted on input
+        float K = 0.f;        // K_{t-1} = sum of the kappas applied so far
+        float N_last = 0.f, K_last = 0.f;
+        prime_fc();
+        for (int t = 0; t < n; ++t) {
+            if (tau == 0) {
+                buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
+                buf_st(K, tape, sq * slot_bytes, kq_base + 4u * t);
+                if constexpr (CK) buf_st(kq, tape, sq * slot_bytes, kqi_base + 4u * t);
+            }
+            K_last = K;
+            K += kq;
+            float lmax, lq;
+            fwd_step(t, N, kq, rows.stored(t + 1), rows.off(t + 1), lmax, lq);
             seg_argmax_payload<SEG>(lmax, lq);
             if constexpr (WPS > 1) {
                 if (lane == 0) {
@@ -295,8 +323,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
             __syncthreads();
             const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
-            const float r = buf_ld_nt(tape, sq * slot_bytes, (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
-            const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + (uint32_t)(n - 1) * (G * 4u) + 4u * (sig >> 2));
+            const float r = buf_ld_nt(tape, sq * slot_bytes, rows.off(n - 1) + 4u * (sig >> 2));
+            const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + rows.off(n - 1) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
             rzr = (r < 0.5f * kNeg) ? (RT)kNeg : (RT)fmaf(-d, d, r) - (RT)N_last;
             EF = fmaf(gb[n - 1] * inv_scale, d, q + K_last);   // Q^_{n-1} carries the offset K_{n-2}
@@ -358,8 +386,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
         float4 ac_n = make_float4(0.f, 0.f, 0.f, 0.f);   // the next group's accumulator (GC)
         if (t >= 0) {
-            rt_n = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u));
-            qt_n = buf_ld_nt(tape, v_grp, q_base + (uint32_t)t * (G * 4u));
+            rt_n = buf_ld_nt(tape, v_grp, rows.off(t));
+            qt_n = buf_ld_nt(tape, v_grp, q_base + rows.off(t));
             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
             if constexpr (GC) ac_n = buf_ld4(tape, v_quad, acc_base);
         }
@@ -371,7 +399,50 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * t);
             K_nx = buf_ld_nt(tape, sq * slot_bytes, kq_base + 4u * t);
         }
-        for (; t >= 0; --t) {
+        while (t >= 0) {
+        const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
+        if (CK && ck) {
+            // keep this thread's share of both backward messages (the quads it reads at step t), rebuild the
+            // segment's rows t0+1..t of R~ and Q^ from checkpoint t0 with the stored normalisers and offsets, then
+            // restore the messages
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                buf_st4(*reinterpret_cast<const float4*>(mr + 4 * j), tape, v_quad, save_base + 16u * TPS * m);
+                buf_st4(*reinterpret_cast<const float4*>(mq + 4 * j), tape, v_quad, save_base + G * 4u + 16u * TPS * m);
+            }
+            lds_barrier();   // every share read before the recompute overwrites the buffers
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                *reinterpret_cast<float4*>(mr + 4 * j) = buf_ld4(tape, v_quad, rows.off(t0) + 16u * TPS * m);
+                *reinterpret_cast<float4*>(mq + 4 * j) = buf_ld4(tape, v_quad, q_base + rows.off(t0) + 16u * TPS * m);
+            }
+            lds_barrier();
+            prime_fc();
+            for (int tt = t0; tt < t; ++tt) {
+                float Nr = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * tt);
+                float kr = buf_ld(tape, sq * slot_bytes, kqi_base + 4u * tt);
+                if constexpr (SPB == 1) {
+                    Nr = uniform_f(Nr);
+                    kr = uniform_f(kr);
+                }
+                float lm, lqr;
+                fwd_step(tt, Nr, kr, true, rows.off(tt + 1), lm, lqr);
+                lds_barrier();
+            }
+            __syncthreads();   // the rebuilt rows, written by other threads, before the backward reads them
+#pragma unroll
+            for (int m = 0; m < QPT; ++m) {
+                const int j = tau + TPS * m;
+                *reinterpret_cast<float4*>(mr + 4 * j) = buf_ld4(tape, v_quad, save_base + 16u * TPS * m);
+                *reinterpret_cast<float4*>(mq + 4 * j) = buf_ld4(tape, v_quad, save_base + G * 4u + 16u * TPS * m);
+            }
+            lds_barrier();
+            rt_n = buf_ld_nt(tape, v_grp, rows.off(t));
+            qt_n = buf_ld_nt(tape, v_grp, q_base + rows.off(t));
+        }
+        for (; t >= t0; --t) {
             float bin[QPT][4], pin[QPT][4];
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
@@ -413,12 +484,12 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const bool last = (m == QPT - 1) && (a == 3);
                     const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
                     if (!last) {
-                        const uint32_t so2 = (uint32_t)t * (G * 4u) + 4u * (TPS * m2 + Q * a2);
+                        const uint32_t so2 = rows.off(t) + 4u * (TPS * m2 + Q * a2);
                         rt_n = buf_ld_nt(tape, v_grp, so2);
                         qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
                         if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
-                    } else if (t > 0) {
-                        const uint32_t so2 = (uint32_t)(t - 1) * (G * 4u);
+                    } else if (t > 0) {   // (in checkpoint mode a row past the segment is read again once rebuilt)
+                        const uint32_t so2 = rows.off(t - 1);
                         rt_n = buf_ld_nt(tape, v_grp, so2);
                         qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
                         if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
@@ -520,6 +591,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             C += Nb;
             Nb = lmax;
         }
+        }   // segments
         if constexpr (WPS > 1) {
             // outputs of steps 0..t_out from the per-wave partial sums, one step per thread, summed over the waves
             // in wave order
@@ -600,7 +672,8 @@ __global__ void __launch_bounds__(256) codebook_reduce_kernel(const unsigned cha
 
 template <int L, bool GC>
 static hipError_t launch_grad_L(const GradArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((grad_kernel<L, GC>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    if (a.ckpt) hipLaunchKernelGGL((grad_kernel<L, GC, true>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    else hipLaunchKernelGGL((grad_kernel<L, GC, false>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
     return hipGetLastError();
 }
 
@@ -644,7 +717,7 @@ hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t 
     const int W = S < 64 ? S : 64;
     // the accumulator sits after the tape, the two scalar tracks and (several waves per sequence) the partial sums
     const size_t n = (size_t)a.n;
-    const size_t acc_off = 2 * align256((n + 1) * (size_t)g.G * 4) + 2 * align256(n * 4) +
+    const size_t acc_off = 2 * align256(TapeRows::rows(a.ckpt, (int)n) * (size_t)g.G * 4) + 2 * align256(n * 4) +
                            (g.WPS > 1 ? align256(n * (size_t)g.WPS * 16) : 0);
     hipLaunchKernelGGL(codebook_reduce_kernel, dim3(S / W), dim3(256), 0, st, a.ws, a.slot_bytes * g.SPB,
                        (uint32_t)acc_off, grid, S, grad_codebook);

@@ -17,6 +17,7 @@ struct SoftArgs {
     unsigned char* ws;
     size_t slot_bytes;
     int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
+    int32_t ckpt;          // 0: every forward message row on the tape; c > 0: every c-th row (checkpoint kernels)
 };
 
 struct GradArgs {
@@ -33,6 +34,7 @@ struct GradArgs {
     unsigned char* ws;
     size_t slot_bytes;
     int32_t sigma_enum;    // nonzero: sequence v decodes row v >> L with sigma = v mod 2^L (sigma ignored)
+    int32_t ckpt;          // 0: every forward message row on the tape; c > 0: every c-th row (checkpoint kernels)
 };
 
 struct ViterbiArgs {

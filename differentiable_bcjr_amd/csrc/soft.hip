@@ -29,15 +29,20 @@ namespace bcjr {
 
 // Groups of 4 states whose work the scheduler may interleave between two scheduling barriers (forward, backward).
 #ifndef BCJR_SOFT_FWD_GROUPS
-#define BCJR_SOFT_FWD_GROUPS 1
+#define BCJR_SOFT_FWD_GROUPS 2
 #endif
 #ifndef BCJR_SOFT_BWD_GROUPS
-#define BCJR_SOFT_BWD_GROUPS 1
+#define BCJR_SOFT_BWD_GROUPS 2
 #endif
 constexpr int kSoftFwdGroups = BCJR_SOFT_FWD_GROUPS;
 constexpr int kSoftBwdGroups = BCJR_SOFT_BWD_GROUPS;
 
-template <int L>
+// CK: the checkpoint mode.  The forward pass stores only rows t = 0, c, 2c, .. and row n - 1 (TapeRows); the
+// backward pass walks the segments from the end and, before each, saves its message to the workspace, reloads the
+// segment's checkpoint into LDS, reruns the forward steps of the segment with the stored normalisers (the same code
+// and numbers as the first pass, so the rows come out bit-identical), and restores its message.  A compile-time flag,
+// so the full-tape kernel carries none of it.
+template <int L, bool CK>
 __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
     using Gm = Geo<L>;
     constexpr int G = Gm::G, Q = Gm::Q, QPT = Gm::QPT, TPS = Gm::TPS, SPB = Gm::SPB, WPS = Gm::WPS;
@@ -74,15 +79,53 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
         }
     }
 
-    // tape of this block's sequences: slot sq at sq * slot_bytes; [n+1][G] messages, then [n] normalisers
+    // tape of this block's sequences: slot sq at sq * slot_bytes; the message rows (TapeRows), then [n] normalisers
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * SPB * args.slot_bytes, SPB * slot_bytes);
     const uint32_t v_quad = sq * slot_bytes + 16u * tau;   // float4 at group 4j, j = tau + TPS m
     const uint32_t v_grp = sq * slot_bytes + 4u * tau;     // float at group j + Q a
-    const uint32_t nrm_base = (uint32_t)align256((size_t)(n + 1) * G * 4);
+    const int ck = CK ? args.ckpt : 0;
+    constexpr uint32_t row_bytes = G * 4u;
+    const TapeRows rows{ck, n, row_bytes, ck ? (uint32_t)(n / ck + 1) * row_bytes : 0u};
+    const uint32_t nrm_base = (uint32_t)align256(TapeRows::rows(ck, n) * row_bytes);
     // with several waves per sequence, each wave's (S0, S1) of every step goes here and the soft codeword is formed
     // after the backward pass, so no wave waits on a serial per-step reduction
     const uint32_t part_base = nrm_base + (uint32_t)align256((size_t)n * 4);
+    // checkpoint mode: each thread's share of the backward message while a segment is rebuilt
+    const uint32_t save_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * 8) : 0u);
+
+    // One forward step: R~_{t+1} = logsumexp over the 4 predecessors of theta_t + R~_t (read from mc) minus the
+    // normaliser N, written to mn and, when `store`, to the tape row at row_off.  Returns this thread's maximum of
+    // the outputs.  The first pass and the checkpoint recompute both run it.
+    auto fwd_step = [&](const float* mc, float* mn, float wt, float N, bool store, uint32_t row_off) -> float {
+        float lmax = -3.0e38f;
+#pragma unroll
+        for (int m = 0; m < QPT; ++m) {
+            const int j = tau + TPS * m;
+            float r[4];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) r[a] = mc[j + Q * a];
+            float o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float x[4];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const float d = fmaf(cb[m][a][i], scale, -wt);
+                    x[a] = fmaf(-d, d, r[a]);
+                }
+                const float mx = max4(x[0], x[1], x[2], x[3]);
+                const float s = (ex2(x[0] - mx) + ex2(x[1] - mx)) + (ex2(x[2] - mx) + ex2(x[3] - mx));
+                o[i] = (mx - N) + lg2(s);
+                if ((i + 1) % kSoftFwdGroups == 0) __builtin_amdgcn_sched_barrier(0);
+            }
+            lmax = run_max(lmax, max4(o[0], o[1], o[2], o[3]));
+            const float4 o4 = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4*>(mn + 4 * j) = o4;
+            if (store) buf_st4_nt(o4, tape, v_quad, row_off + 16u * TPS * m);
+        }
+        return lmax;
+    };
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
     for (int64_t gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
@@ -106,7 +149,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             r.z = (!has_sigma || (uint32_t)(4 * j + 2) == (sig & (G - 1))) ? 0.f : kNeg;
             r.w = (!has_sigma || (uint32_t)(4 * j + 3) == (sig & (G - 1))) ? 0.f : kNeg;
             *reinterpret_cast<float4*>(msg0 + 4 * j) = r;
-            buf_st4_nt(r, tape, v_quad, 16u * TPS * m);
+            buf_st4_nt(r, tape, v_quad, 16u * TPS * m);   // row 0
         }
         lds_barrier();
 
@@ -119,32 +162,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             float* mn = (t & 1) ? msg0 : msg1;
             const float wt = w_nx * scale;
             if (t + 1 < n) w_nx = wb[t + 1];
-            float lmax = -3.0e38f;
-#pragma unroll
-            for (int m = 0; m < QPT; ++m) {
-                const int j = tau + TPS * m;
-                float r[4];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) r[a] = mc[j + Q * a];
-                float o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float x[4];
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const float d = fmaf(cb[m][a][i], scale, -wt);
-                        x[a] = fmaf(-d, d, r[a]);
-                    }
-                    const float mx = max4(x[0], x[1], x[2], x[3]);
-                    const float s = (ex2(x[0] - mx) + ex2(x[1] - mx)) + (ex2(x[2] - mx) + ex2(x[3] - mx));
-                    o[i] = (mx - N) + lg2(s);
-                    if ((i + 1) % kSoftFwdGroups == 0) __builtin_amdgcn_sched_barrier(0);
-                }
-                lmax = run_max(lmax, max4(o[0], o[1], o[2], o[3]));
-                const float4 o4 = make_float4(o[0], o[1], o[2], o[3]);
-                *reinterpret_cast<float4*>(mn + 4 * j) = o4;
-                buf_st4_nt(o4, tape, v_quad, (uint32_t)(t + 1) * (G * 4u) + 16u * TPS * m);   // row n is spare
-            }
+            // row n is a spare the full tape keeps; in checkpoint mode only the checkpoints and row n - 1 go out
+            float lmax = fwd_step(mc, mn, wt, N, rows.stored(t + 1), rows.off(t + 1));
             if (tau == 0) buf_st(N, tape, sq * slot_bytes, nrm_base + 4u * t);
             lmax = seg_max_fast<SEG>(lmax);
             if constexpr (WPS > 1) {
@@ -230,7 +249,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
         float rq[4], rn[4];
         if (t >= 0) {
 #pragma unroll
-            for (int a = 0; a < 4; ++a) rq[a] = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * Q * a);
+            for (int a = 0; a < 4; ++a) rq[a] = buf_ld_nt(tape, v_grp, rows.off(t) + 4u * Q * a);
         }
         const int t_out = t;   // last step whose soft codeword the loop below produces
         float N_nx = 0.f;
@@ -238,74 +257,110 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
             w_nx = wb[t];
             N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * t);
         }
-        for (; t >= 0; --t) {
-            const float* mc = (t & 1) ? msg1 : msg0;
-            float* mn = (t & 1) ? msg0 : msg1;
-            const float wt = w_nx * scale;
-            float Nt = N_nx;
-            if (t > 0) {   // the next step's weight and forward normaliser, one step ahead
-                w_nx = wb[t - 1];
-                N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
-            }
-            if constexpr (SPB == 1) Nt = uniform_f(Nt);
-            D += Nt;
-            const float ref = (rz + D) - C;
-            float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f;
+        while (t >= 0) {
+            const int t0 = ck ? (t / ck) * ck : 0;   // first step of this segment
+            if (CK && ck) {
+                // keep this thread's share of the backward message (the quads it reads at step t), rebuild the
+                // segment's rows t0+1..t from checkpoint t0 with the stored normalisers, then restore the message
+                const float* mb = (t & 1) ? msg1 : msg0;
 #pragma unroll
-            for (int m = 0; m < QPT; ++m) {
-                const int j = tau + TPS * m;
-                // prefetch the forward messages of the next quad (or of the next step's first quad)
-                if (m + 1 < QPT) {
+                for (int m = 0; m < QPT; ++m)
+                    buf_st4(*reinterpret_cast<const float4*>(mb + 4 * (tau + TPS * m)), tape, v_quad,
+                            save_base + 16u * TPS * m);
+                lds_barrier();   // every share read before the recompute overwrites the buffers
+                float* m0 = (t0 & 1) ? msg1 : msg0;
 #pragma unroll
-                    for (int a = 0; a < 4; ++a)
-                        rn[a] = buf_ld_nt(tape, v_grp, (uint32_t)t * (G * 4u) + 4u * (TPS * (m + 1) + Q * a));
-                } else if (t > 0) {
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) rn[a] = buf_ld_nt(tape, v_grp, (uint32_t)(t - 1) * (G * 4u) + 4u * Q * a);
+                for (int m = 0; m < QPT; ++m)
+                    *reinterpret_cast<float4*>(m0 + 4 * (tau + TPS * m)) =
+                        buf_ld4(tape, v_quad, rows.off(t0) + 16u * TPS * m);
+                lds_barrier();
+                for (int tt = t0; tt < t; ++tt) {
+                    const float* mc = (tt & 1) ? msg1 : msg0;
+                    float* mn = (tt & 1) ? msg0 : msg1;
+                    float Nr = buf_ld(tape, sq * slot_bytes, nrm_base + 4u * tt);
+                    if constexpr (SPB == 1) Nr = uniform_f(Nr);
+                    fwd_step(mc, mn, wb[tt] * scale, Nr, true, rows.off(tt + 1));
+                    lds_barrier();
                 }
-                const float4 bq = *reinterpret_cast<const float4*>(mc + 4 * j);
+                __syncthreads();   // the rebuilt rows, written by other threads, before the backward reads them
+                float* mr = (t & 1) ? msg1 : msg0;
 #pragma unroll
-                for (int a = 0; a < 4; ++a) {
-                    const float d0 = fmaf(cb[m][a][0], scale, -wt), d1 = fmaf(cb[m][a][1], scale, -wt);
-                    const float d2 = fmaf(cb[m][a][2], scale, -wt), d3 = fmaf(cb[m][a][3], scale, -wt);
-                    const float y0 = fmaf(-d0, d0, bq.x), y1 = fmaf(-d1, d1, bq.y);
-                    const float y2 = fmaf(-d2, d2, bq.z), y3 = fmaf(-d3, d3, bq.w);
-                    const float mx = max4(y0, y1, y2, y3);
-                    const float e0 = ex2(y0 - mx), e1 = ex2(y1 - mx), e2 = ex2(y2 - mx), e3 = ex2(y3 - mx);
-                    const float s = (e0 + e1) + (e2 + e3);
-                    const float out = (mx - Nb) + lg2(s);
-                    const float f = ex2((mx + rq[a]) - ref);
-                    S0 = fmaf(f, s, S0);
-                    S1 = fmaf(f, fmaf(e0, d0, fmaf(e1, d1, fmaf(e2, d2, e3 * d3))), S1);
-                    lmax = run_max(lmax, out);
-                    mn[j + Q * a] = out;   // at t = 0 this lands in a buffer nobody reads
-                    if ((a + 1) % kSoftBwdGroups == 0) {
-                        pin_order(S0, S1, lmax);
-                        __builtin_amdgcn_sched_barrier(0);
+                for (int m = 0; m < QPT; ++m)
+                    *reinterpret_cast<float4*>(mr + 4 * (tau + TPS * m)) = buf_ld4(tape, v_quad, save_base + 16u * TPS * m);
+                lds_barrier();
+#pragma unroll
+                for (int a = 0; a < 4; ++a) rq[a] = buf_ld_nt(tape, v_grp, rows.off(t) + 4u * Q * a);
+            }
+            for (; t >= t0; --t) {
+                const float* mc = (t & 1) ? msg1 : msg0;
+                float* mn = (t & 1) ? msg0 : msg1;
+                const float wt = w_nx * scale;
+                float Nt = N_nx;
+                if (t > 0) {   // the next step's weight and forward normaliser, one step ahead
+                    w_nx = wb[t - 1];
+                    N_nx = buf_ld_nt(tape, sq * slot_bytes, nrm_base + 4u * (t - 1));
+                }
+                if constexpr (SPB == 1) Nt = uniform_f(Nt);
+                D += Nt;
+                const float ref = (rz + D) - C;
+                float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f;
+#pragma unroll
+                for (int m = 0; m < QPT; ++m) {
+                    const int j = tau + TPS * m;
+                    // prefetch the forward messages of the next quad (or of the next step's first quad; in
+                    // checkpoint mode a row past the segment is read again once it has been rebuilt)
+                    if (m + 1 < QPT) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a)
+                            rn[a] = buf_ld_nt(tape, v_grp, rows.off(t) + 4u * (TPS * (m + 1) + Q * a));
+                    } else if (t > 0) {
+#pragma unroll
+                        for (int a = 0; a < 4; ++a) rn[a] = buf_ld_nt(tape, v_grp, rows.off(t - 1) + 4u * Q * a);
+                    }
+                    const float4 bq = *reinterpret_cast<const float4*>(mc + 4 * j);
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const float d0 = fmaf(cb[m][a][0], scale, -wt), d1 = fmaf(cb[m][a][1], scale, -wt);
+                        const float d2 = fmaf(cb[m][a][2], scale, -wt), d3 = fmaf(cb[m][a][3], scale, -wt);
+                        const float y0 = fmaf(-d0, d0, bq.x), y1 = fmaf(-d1, d1, bq.y);
+                        const float y2 = fmaf(-d2, d2, bq.z), y3 = fmaf(-d3, d3, bq.w);
+                        const float mx = max4(y0, y1, y2, y3);
+                        const float e0 = ex2(y0 - mx), e1 = ex2(y1 - mx), e2 = ex2(y2 - mx), e3 = ex2(y3 - mx);
+                        const float s = (e0 + e1) + (e2 + e3);
+                        const float out = (mx - Nb) + lg2(s);
+                        const float f = ex2((mx + rq[a]) - ref);
+                        S0 = fmaf(f, s, S0);
+                        S1 = fmaf(f, fmaf(e0, d0, fmaf(e1, d1, fmaf(e2, d2, e3 * d3))), S1);
+                        lmax = run_max(lmax, out);
+                        mn[j + Q * a] = out;   // at t = 0 this lands in a buffer nobody reads
+                        if ((a + 1) % kSoftBwdGroups == 0) {
+                            pin_order(S0, S1, lmax);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) rq[a] = rn[a];
+                }
+                lmax = seg_max_fast<SEG>(lmax);
+                S0 = seg_sum_fast<SEG>(S0);
+                S1 = seg_sum_fast<SEG>(S1);
+                if constexpr (WPS > 1) {
+                    if (lane == 0) {
+                        redmax[t & 1][sq][wv] = lmax;
+                        buf_st2(make_float2(S0, S1), tape, sq * slot_bytes, part_base + 8u * (uint32_t)(t * WPS + wv));
                     }
                 }
-#pragma unroll
-                for (int a = 0; a < 4; ++a) rq[a] = rn[a];
-            }
-            lmax = seg_max_fast<SEG>(lmax);
-            S0 = seg_sum_fast<SEG>(S0);
-            S1 = seg_sum_fast<SEG>(S1);
-            if constexpr (WPS > 1) {
-                if (lane == 0) {
-                    redmax[t & 1][sq][wv] = lmax;
-                    buf_st2(make_float2(S0, S1), tape, sq * slot_bytes, part_base + 8u * (uint32_t)(t * WPS + wv));
+                lds_barrier();
+                if constexpr (WPS > 1) {
+                    lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][sq][lane & 15] : -3.0e38f);
+                } else {
+                    if (tau == 0 && active)
+                        args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");
                 }
+                if constexpr (SPB == 1) lmax = uniform_f(lmax);
+                C += Nb;
+                Nb = lmax;
             }
-            lds_barrier();
-            if constexpr (WPS > 1) {
-                lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][sq][lane & 15] : -3.0e38f);
-            } else {
-                if (tau == 0 && active)
-                    args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");
-            }
-            if constexpr (SPB == 1) lmax = uniform_f(lmax);
-            C += Nb;
-            Nb = lmax;
         }
         if constexpr (WPS > 1) {
             // soft codewords of steps 0..t_out from the per-wave partial sums, one step per thread, summed over the
@@ -332,7 +387,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
 
 template <int L>
 static hipError_t launch_soft_L(const SoftArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL(soft_kernel<L>, dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    if (a.ckpt) hipLaunchKernelGGL((soft_kernel<L, true>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    else hipLaunchKernelGGL((soft_kernel<L, false>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
     return hipGetLastError();
 }
 

@@ -59,11 +59,13 @@ __host__ __device__ constexpr int blocks_per_cu(int L) { return L >= 15 ? 1 : (L
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-__device__ __forceinline__ float max4(float a, float b, float c, float d) { return fmaxf(fmaxf(a, b), fmaxf(c, d)); }
-// Running maximum over finite values (v_maximum3_f32).  fmaxf must quiet signalling NaNs, so the compiler re-canonicalises
-// an operand it cannot prove canonical (one that left an asm ordering point) with an extra half-rate v_max per use; the
-// IEEE-2019 maximum has no such requirement, and the two agree on the finite values and sentinels used here.
-__device__ __forceinline__ float run_max(float acc, float x) { return __builtin_elementwise_maximum(acc, x); }
+// Maxima over finite values use the IEEE-2019 maximum (v_maximum3_f32).  fmaxf must quiet signalling NaNs, so the
+// compiler re-canonicalises every operand it cannot prove canonical (a DPP or LDS result, one that left an asm ordering
+// point) with an extra half-rate v_max per use; the maximum has no such requirement, and the two agree on the finite
+// values and sentinels used here.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max4(float a, float b, float c, float d) { return vmax(vmax(a, b), vmax(c, d)); }
+__device__ __forceinline__ float run_max(float acc, float x) { return vmax(acc, x); }
 
 // Keeps the compiler from deferring the accumulation of these values past this point (which would keep every
 // group's temporaries alive at once): an empty volatile asm that claims to read and rewrite them.
@@ -85,7 +87,7 @@ __device__ __forceinline__ void lds_barrier() {
 template <int SEG>
 __device__ __forceinline__ float seg_max(float x) {
 #pragma unroll
-    for (int o = 1; o < SEG; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+    for (int o = 1; o < SEG; o <<= 1) x = vmax(x, __shfl_xor(x, o));
     return x;
 }
 
@@ -122,15 +124,15 @@ __device__ __forceinline__ float dpp(float x) {
 }
 
 __device__ __forceinline__ float wave_max64(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
-    x = fmaxf(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
-    x = fmaxf(x, dpp<0x141>(x));   // row_half_mirror
-    x = fmaxf(x, dpp<0x140>(x));   // row_mirror: every lane of a row holds the row max
+    x = vmax(x, dpp<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = vmax(x, dpp<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = vmax(x, dpp<0x141>(x));   // row_half_mirror
+    x = vmax(x, dpp<0x140>(x));   // row_mirror: every lane of a row holds the row max
     const float a = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
     const float b = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 16));
     const float c = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 32));
     const float d = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 48));
-    return fmaxf(fmaxf(a, b), fmaxf(c, d));
+    return max4(a, b, c, d);
 }
 
 __device__ __forceinline__ float wave_sum64(float x) {
@@ -162,10 +164,10 @@ __device__ __forceinline__ float seg_sum_fast(float x) {
 // rows read the same slots, so the result is wave-uniform.  Max and first-max are exact, so they match a serial
 // scan over the slots; a sum is added in tree order.
 __device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp<0xB1>(x));
-    x = fmaxf(x, dpp<0x4E>(x));
-    x = fmaxf(x, dpp<0x141>(x));
-    return fmaxf(x, dpp<0x140>(x));
+    x = vmax(x, dpp<0xB1>(x));
+    x = vmax(x, dpp<0x4E>(x));
+    x = vmax(x, dpp<0x141>(x));
+    return vmax(x, dpp<0x140>(x));
 }
 __device__ __forceinline__ float row16_sum(float x) {
     x += dpp<0xB1>(x);
@@ -256,6 +258,22 @@ __device__ __forceinline__ void buf_st4_nt(float4 v, rsrc_t r, uint32_t voff, ui
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
                                            voff + soff, 0, kStreamPolicy);
 }
+
+// Tape rows of the forward messages.  Without checkpoints row t sits at t * row_bytes.  With checkpoint interval c,
+// rows t = 0, c, 2c, .. (n / c + 1 of them) come first, then c - 1 rows for the steps inside one segment: row t at
+// segment position t mod c - 1.  The forward pass stores the checkpoints and row n - 1 (which the sigma end reads);
+// the backward pass recomputes each segment's other rows from its checkpoint.
+struct TapeRows {
+    int c, n;
+    uint32_t row_bytes, seg_base;
+    __device__ __forceinline__ uint32_t off(int t) const {
+        if (c == 0) return (uint32_t)t * row_bytes;
+        const int r = t % c;
+        return r == 0 ? (uint32_t)(t / c) * row_bytes : seg_base + (uint32_t)(r - 1) * row_bytes;
+    }
+    __device__ __forceinline__ bool stored(int t) const { return c == 0 || t % c == 0 || t == n - 1; }
+    __host__ __device__ static constexpr size_t rows(int c, int n) { return c == 0 ? (size_t)n + 1 : (size_t)(n / c + c); }
+};
 
 // Per-slot workspace layout (bytes), shared by the host planner and the kernels.
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

@@ -144,6 +144,23 @@ def test_general_trellis_workspace_formula(L, k, V, B, n):
             assert abi.bcjr_workspace_bytes(op, B, n, L, k) == _gen_bytes(op, B, n, L, k, V)
 
 
+def _tuned_ck_bytes(op, B, n, L, c):
+    """The k = 2 kernels in checkpoint mode: their slots (SPB sequences per block) hold n / c + c rows of each forward
+    message, the [n] normalisers (and for the gradients the [n] Q offset sums), the per-wave partial sums of every
+    step, (codebook gradient) one float accumulator per state, and then the checkpoint mode's own: the gradients' [n]
+    Q input offsets, and each thread's share of the saved backward message(s)."""
+    G, TPS, SPB = _geo(L)
+    bpc = 1 if L >= 15 else (2 if L == 14 else 8)
+    slots = min((B + SPB - 1) // SPB, 256 * bpc) * SPB
+    rows, nrm = _a256((n // c + c) * G * 4), _a256(n * 4)
+    if op == abi.BCJR_OP_SOFT:
+        part = _a256(n * _wps(L) * 8) if _wps(L) > 1 else 0
+        return slots * (rows + nrm + part + _a256(G * 4))
+    part = _a256(n * _wps(L) * 16) if _wps(L) > 1 else 0
+    acc = _a256((1 << L) * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
+    return slots * (2 * rows + 2 * nrm + part + acc + nrm + _a256(2 * G * 4))
+
+
 @pytest.mark.parametrize("L,k,V", [(16, 2, 1), (16, 3, 1), (16, 4, 2), (16, 1, 1), (16, 1, 2), (12, 1, 2), (8, 2, 1),
                                    (4, 1, 1)])
 @pytest.mark.parametrize("B,n", [(1, 1), (16, 2), (4096, 256), (100, 4096), (3, 17)])
@@ -155,7 +172,11 @@ def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
         c += 1
     for op in (abi.BCJR_OP_SOFT, abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):
         full = abi.bcjr_workspace_bytes_v(op, B, n, L, k, V)
-        want = min(full, _gen_bytes(op, B, n, L, k, V, ckpt=c)) if full else 0
+        if (k, V) == (2, 1):
+            ckb = _tuned_ck_bytes(op, B, n, L, c)   # the k = 2 kernels' own checkpoint mode
+        else:
+            ckb = _gen_bytes(op, B, n, L, k, V, ckpt=c)
+        want = min(full, ckb) if full else 0
         assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == want
         if n >= 256 and L == 16 and full:   # the codebook gradient's [2^L][V] accumulator is not reduced
             factor = 6 if op != abi.BCJR_OP_GRAD_CODEBOOK else 4
