@@ -4,7 +4,8 @@ Three operations, each a hand-written HIP kernel behind the C-ABI of ``include/b
 
 * ``soft_codeword``      -- w_soft[b, t] = E_p[c(s_t)], the Boltzmann expectation of the codebook value over all
   bitshift-trellis paths at temperature T, and ln Z (BCJR-QAT, arXiv 2605.10655; gist.science Technical Summary,
-  "Core Mechanism");
+  "Core Mechanism"); ``soft_codeword_noalloc`` is the same in the library's static scratch, for callers that cannot
+  allocate;
 * ``soft_codeword_grad`` -- dL/dw from an upstream dL/dw_soft, the exact derivative of the soft codeword;
 * ``soft_codeword_grad_codebook`` -- dL/dc [2^L], the exact derivative in the codebook values (the trellis
   parameters), summed over the batch, together with dL/dw;
@@ -35,7 +36,7 @@ import torch
 from . import abi
 from .anneal import temperature_schedule
 
-__all__ = ["soft_codeword", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code",
+__all__ = ["soft_codeword", "soft_codeword_noalloc", "soft_codeword_grad", "soft_codeword_grad_codebook", "viterbi_hard_code",
            "viterbi_tail_biting", "soft_codeword_tail_biting", "soft_codeword_grad_tail_biting", "soft_quantize",
            "temperature_schedule", "workspace_bytes", "BCJRError", "abi"]
 
@@ -141,6 +142,29 @@ def soft_codeword(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T
         _check(abi.bcjr_soft_codeword_v(w.data_ptr(), codebook.data_ptr(), B, n, L, k, V, float(T), _ptr(sig),
                                         out.data_ptr(), _ptr(lz), ws.data_ptr(), _nbytes(ws), _stream(w.device)))
     return (out, lz) if return_log_z else out
+
+
+def soft_codeword_noalloc(w: torch.Tensor, codebook: torch.Tensor, L: int, k: int = 2, T: float = 1.0,
+                          boundary_state: torch.Tensor | None = None, *, out: torch.Tensor | None = None,
+                          log_z: torch.Tensor | None = None) -> torch.Tensor:
+    """``soft_codeword`` for a codebook [2^L] through ``bcjr_soft_codeword_noalloc``, which works in the library's
+    static device scratch and allocates nothing.  Pass ``out`` (w's shape) and optionally ``log_z`` ([B]) to keep this
+    call free of allocations too.  Calls that overlap in time on one device race on that scratch."""
+    w = _f32(w, "w")
+    codebook = _f32(codebook, "codebook")
+    B, n, V = _steps(w, codebook, L)
+    if V != 1:
+        raise ValueError("soft_codeword_noalloc takes a codebook [2^L] (one weight per step)")
+    sig = _sigma(boundary_state, B, w.device)
+    if out is None:
+        out = torch.empty_like(w)
+    for t, shape in ((out, w.shape), (log_z, (B,))):
+        if t is not None and (not t.is_cuda or t.device != w.device or t.dtype != torch.float32
+                              or tuple(t.shape) != tuple(shape) or not t.is_contiguous()):
+            raise TypeError(f"outputs must be contiguous float32 tensors of shape {tuple(shape)} on w's device")
+    _check(abi.bcjr_soft_codeword_noalloc(w.data_ptr(), codebook.data_ptr(), B, n, L, k, float(T), _ptr(sig),
+                                          out.data_ptr(), _ptr(log_z), _stream(w.device)))
+    return out
 
 
 def soft_codeword_grad(w: torch.Tensor, codebook: torch.Tensor, grad_w_soft: torch.Tensor, L: int, k: int = 2,

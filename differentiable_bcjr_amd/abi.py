@@ -33,6 +33,8 @@ BCJR_OP_GRAD_TAIL_BITING = 7
 BCJR_TB_EXACT = 0
 BCJR_TB_ROTATE = 1
 
+BCJR_NOALLOC_SCRATCH_BYTES = 256 << 20
+
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _int = ctypes.c_int
 
@@ -62,6 +64,7 @@ _SIGNATURES = {
     "bcjr_workspace_bytes": ([_i32, _i64, _i64, _i32, _i32], _sz),
     "bcjr_workspace_bytes_v": ([_i32, _i64, _i64, _i32, _i32, _i32], _sz),
     "bcjr_workspace_bytes_min": ([_i32, _i64, _i64, _i32, _i32, _i32], _sz),
+    "bcjr_soft_codeword_noalloc": ([_vp, _vp, _i64, _i64, _i32, _i32, _f32, _vp, _vp, _vp, _vp], _int),
     "bcjr_status_string": ([_i32], ctypes.c_char_p),
 }
 

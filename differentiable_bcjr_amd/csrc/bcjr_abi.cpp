@@ -209,6 +209,26 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
     return p;
 }
 
+// Fewer persistent workgroups, each looping over more sequences, so that the plan's slots fit in `bytes` (the static
+// scratch of bcjr_soft_codeword_noalloc).  False when the slots of one workgroup alone exceed it.
+bool fit_grid(Plan& p, int spb, size_t bytes) {
+    const size_t per_block = (size_t)spb * p.slot_bytes;
+    if (per_block > bytes) return false;
+    const size_t most = bytes / per_block;
+    if ((size_t)p.grid > most) p.grid = (int)most;
+    p.slots = p.grid * spb;
+    p.total = (size_t)p.slots * p.slot_bytes;
+    return true;
+}
+
+bool fit_grid(GenPlan& p, size_t bytes) {
+    if (p.slot_bytes > bytes) return false;
+    const size_t most = bytes / p.slot_bytes;
+    if ((size_t)p.grid > most) p.grid = (int)most;
+    p.total = (size_t)p.grid * p.slot_bytes;
+    return true;
+}
+
 int check_workspace(const void* ws, size_t bytes, const Plan& p) {
     if (ws == nullptr || bytes < p.total) return BCJR_ERR_WORKSPACE;
     if (((uintptr_t)ws & 255u) != 0) return BCJR_ERR_WORKSPACE;
@@ -354,7 +374,8 @@ const char* bcjr_status_string(int32_t status) {
             return "BCJR_ERR_UNSUPPORTED: kernels exist for k <= 4 and V <= 2; exact tail-biting and the "
                    "tail-biting soft codeword and gradient need L <= 10";
         case BCJR_ERR_WORKSPACE:
-            return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes()";
+            return "BCJR_ERR_WORKSPACE: workspace NULL, misaligned or smaller than bcjr_workspace_bytes(); or, for "
+                   "bcjr_soft_codeword_noalloc, one sequence needs more than the library's static scratch holds";
         case BCJR_ERR_HIP: return "BCJR_ERR_HIP: the HIP runtime reported a launch error";
         default: return "BCJR: unknown status";
     }
@@ -370,9 +391,11 @@ int gen_workspace(void* workspace, size_t bytes, const GenPlan& p) {
     return BCJR_OK;
 }
 
+// fit: `workspace` is a fixed buffer of workspace_bytes (the static scratch), and the grid shrinks until the plan
+// fits in it rather than the call failing when it is smaller than the plan.
 int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V, float T,
               const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace, size_t workspace_bytes,
-              void* stream) {
+              void* stream, bool fit = false) {
     if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
     int rc = check_shape_v(B, n, L, k, V);
     if (rc) return rc;
@@ -383,6 +406,7 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     const bool recompute = workspace != nullptr && workspace_bytes < full;
     if (!tuned(k, V)) {
         GenPlan p = make_gen_plan(BCJR_OP_SOFT, B, n, L, k, V, recompute ? checkpoint_interval(n) : 0);
+        if (fit && p.ok && !fit_grid(p, workspace_bytes)) return BCJR_ERR_WORKSPACE;
         if ((rc = gen_workspace(workspace, workspace_bytes, p))) return rc;
         GenArgs a{};
         a.w = w;
@@ -402,6 +426,7 @@ int soft_impl(const float* w, const float* codebook, int64_t B, int64_t n, int32
     }
     const int ckpt = recompute ? checkpoint_interval(n) : 0;
     Plan p = make_plan(BCJR_OP_SOFT, B, n, L, ckpt);
+    if (fit && !fit_grid(p, geo_rt(L).SPB, workspace_bytes)) return BCJR_ERR_WORKSPACE;
     if ((rc = check_workspace(workspace, workspace_bytes, p))) return rc;
     SoftArgs a{};
     a.w = w;
@@ -822,9 +847,48 @@ int viterbi_tb_impl(const float* w, const float* codebook, int64_t B, int64_t n,
     return hip_status(launch_viterbi(L, a, tp.rows.grid, st));
 }
 
+// ---------------------------------------------------------------------------------------------------------------
+// The static scratch of bcjr_soft_codeword_noalloc: the workspace of callers that cannot allocate.  Each device that
+// runs the library holds its own copy, at its own address, until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels and copies get the address hipGetSymbolAddress returns for the
+// current device, looked up once per device with that device current.
+
+static __device__ __align__(256) unsigned char scratch[BCJR_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddress {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchAddress g_scratch[kMaxDevices];
+
+int scratch_address(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return BCJR_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return BCJR_ERR_UNSUPPORTED;
+    ScratchAddress& s = g_scratch[dev];
+    std::call_once(s.once, [&s] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    if (s.err != hipSuccess || s.ptr == nullptr) return BCJR_ERR_HIP;
+    *out = s.ptr;
+    return BCJR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int bcjr_soft_codeword_noalloc(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                               float T, const int32_t* boundary_state, float* w_soft, float* log_z, void* stream) {
+    // the host checks first, so that a bad call needs no device
+    if (!w || !codebook || !w_soft) return BCJR_ERR_NULL;
+    int rc = check_shape_v(B, n, L, k, 1);
+    if (rc) return rc;
+    if ((rc = check_temp(T))) return rc;
+    void* ws = nullptr;
+    if ((rc = scratch_address(&ws))) return rc;
+    return soft_impl(w, codebook, B, n, L, k, 1, T, boundary_state, w_soft, log_z, ws, BCJR_NOALLOC_SCRATCH_BYTES,
+                     stream, true);
+}
 
 int bcjr_soft_codeword(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k, float T,
                        const int32_t* boundary_state, float* w_soft, float* log_z, void* workspace,

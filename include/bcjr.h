@@ -60,7 +60,8 @@ enum {
     BCJR_ERR_UNSUPPORTED = -4, /* valid shape without a kernel: k > 4 or V > 2; exact tail-biting (choice of
                                   sigma, soft codeword or gradient under the tail-biting measure) with L > 10;
                                   unknown mode */
-    BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes() */
+    BCJR_ERR_WORKSPACE = -5,   /* workspace NULL, not 256-byte aligned, or smaller than bcjr_workspace_bytes();
+                                  bcjr_soft_codeword_noalloc: one sequence needs more than the static scratch */
     BCJR_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
 };
 
@@ -245,6 +246,28 @@ size_t bcjr_workspace_bytes_v(int32_t op, int64_t B, int64_t n, int32_t L, int32
  * For Viterbi and the tail-biting ops this is bcjr_workspace_bytes_v.  0 when the shapes are invalid or unsupported.
  */
 size_t bcjr_workspace_bytes_min(int32_t op, int64_t B, int64_t n, int32_t L, int32_t k, int32_t V);
+
+/* Bytes of the static device scratch that bcjr_soft_codeword_noalloc works in (per device). */
+#define BCJR_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/*
+ * bcjr_soft_codeword without a workspace argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It computes what bcjr_soft_codeword computes,
+ * with the same arguments minus workspace and workspace_bytes, in a static device array of
+ * BCJR_NOALLOC_SCRATCH_BYTES (256 MiB) that the library holds on each device it runs on until the process ends; it
+ * calls no allocating routine.  The scratch's address is looked up on the first call on each device.
+ *   - When the full message tape of every workgroup fits in the scratch it is used; otherwise the checkpoint mode of
+ *     bcjr_workspace_bytes_min, with the persistent grid cut to the workgroups whose slots fit (each then decodes
+ *     more sequences in turn).  At L = 16, k = 2, n = 256 that is the checkpoint mode on 122 workgroups.  The results
+ *     are those bcjr_soft_codeword gives with a workspace of the same mode.
+ *   - BCJR_ERR_WORKSPACE when one workgroup's slots alone exceed the scratch (no shape within the limits above does
+ *     at L <= 16 with checkpoints; the error exists for the rule's sake).
+ *   - Every call on one device shares that device's scratch, so calls that overlap in time on one device race and
+ *     give wrong results: serialize them (one stream, or events).  The scratch keeps the last call's contents; the
+ *     kernels need none of it on entry.
+ */
+int bcjr_soft_codeword_noalloc(const float* w, const float* codebook, int64_t B, int64_t n, int32_t L, int32_t k,
+                               float T, const int32_t* boundary_state, float* w_soft, float* log_z, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* bcjr_status_string(int32_t status);

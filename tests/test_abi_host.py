@@ -452,11 +452,35 @@ def test_trellis_below_four_state_bits_rejected(L, k):
     a = [FAKE, FAKE, 4, 8, L, k, 0.5]
     assert abi.bcjr_soft_codeword_tail_biting(*a, FAKE, None, FAKE, 1 << 30, None) == abi.BCJR_ERR_SHAPE
     assert abi.bcjr_soft_codeword_grad_tail_biting(*a, FAKE, FAKE, None, FAKE, 1 << 30, None) == abi.BCJR_ERR_SHAPE
+    assert abi.bcjr_soft_codeword_noalloc(*a, None, FAKE, None, None) == abi.BCJR_ERR_SHAPE
     for op in range(8):
         for V in (1, 2):
             assert abi.bcjr_workspace_bytes_v(op, 4, 8, L, k, V) == 0
             assert abi.bcjr_workspace_bytes_min(op, 4, 8, L, k, V) == 0
         assert abi.bcjr_workspace_bytes(op, 4, 8, L, k) == 0
+
+
+def _noalloc(**kw):
+    a = dict(w=FAKE, codebook=FAKE, B=4, n=8, L=8, k=2, T=0.5, boundary_state=None, w_soft=FAKE, log_z=None,
+             stream=None)
+    a.update(kw)
+    return abi.bcjr_soft_codeword_noalloc(*a.values())
+
+
+def test_noalloc_entry_point_checks_on_the_host():
+    """The allocation-free soft codeword runs the soft codeword's checks, in the same order, before it touches the
+    device (the scratch address is looked up only for a valid call)."""
+    assert abi.BCJR_NOALLOC_SCRATCH_BYTES == 256 << 20
+    assert _noalloc(w=None) == abi.BCJR_ERR_NULL
+    assert _noalloc(codebook=None) == abi.BCJR_ERR_NULL
+    assert _noalloc(w_soft=None) == abi.BCJR_ERR_NULL
+    for kw in (dict(B=0), dict(n=4097), dict(L=17), dict(L=3), dict(k=0)):
+        assert _noalloc(**kw) == abi.BCJR_ERR_SHAPE
+    assert _noalloc(L=10, k=5) == abi.BCJR_ERR_UNSUPPORTED
+    for T in (0.0, float("nan"), 1e-13):
+        assert _noalloc(T=T) == abi.BCJR_ERR_TEMP
+    assert _noalloc(w=None, B=0, T=-1.0) == abi.BCJR_ERR_NULL
+    assert _noalloc(B=0, T=-1.0) == abi.BCJR_ERR_SHAPE
 
 
 def test_python_wrapper_checks_a_callers_workspace():
