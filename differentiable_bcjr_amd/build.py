@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # a multiply and an add are fused only where one expression holds both (or fmaf says so), never across statements:
+    # the rounding of every result is then fixed by the source alone, so kernels that share code (the full-tape and the
+    # checkpoint forms, the codebook-gradient forms) give bit-identical shared outputs
+    "-ffp-contract=on",
     "-Wno-unused-command-line-argument",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -119,9 +119,9 @@ Plan make_plan(int op, int64_t B, int64_t n, int L, int ckpt = 0) {
                            (ckpt ? align256((size_t)g.G * 4) : 0);
             break;
         case BCJR_OP_GRAD:            // + per-wave (S0..S3) of every step when a sequence spans several waves
-        case BCJR_OP_GRAD_CODEBOOK:   // + one float accumulator per state
+        case BCJR_OP_GRAD_CODEBOOK:   // + per state one float accumulator and two pending contributions
             p.slot_bytes = 2 * align256(msgs) + 2 * align256(nrm) + (g.WPS > 1 ? align256((size_t)n * g.WPS * 16) : 0) +
-                           (op == BCJR_OP_GRAD_CODEBOOK ? align256(((size_t)1 << L) * 4) : 0) +
+                           (op == BCJR_OP_GRAD_CODEBOOK ? 3 * align256(((size_t)1 << L) * 4) : 0) +
                            (ckpt ? align256(nrm) + align256((size_t)2 * g.G * 4) : 0);
             break;
         default: p.slot_bytes = align256(2 * (size_t)n * (size_t)g.TPS * 4); break;   // 2 back-pointer buffers
@@ -195,9 +195,9 @@ GenPlan make_gen_plan(int op, int64_t B, int64_t n, int32_t L, int32_t k, int32_
                            (ckpt ? align256(G * 4) : 0);
             break;
         case BCJR_OP_GRAD:   // R~ and Q^ tapes, normalisers and Q offsets, per-wave (S0, S1[V], S2, S3[V])
-        case BCJR_OP_GRAD_CODEBOOK:   // + one float accumulator per state and component
+        case BCJR_OP_GRAD_CODEBOOK:   // + per state and component a float accumulator and two pending contributions
             p.acc_off = 2 * tapes + 2 * nrm + (wps > 1 ? align256((size_t)n * wps * (2 + 2 * V) * 4) : 0);
-            p.slot_bytes = p.acc_off + (op == BCJR_OP_GRAD_CODEBOOK ? align256((size_t)S * V * 4) : 0) +
+            p.slot_bytes = p.acc_off + (op == BCJR_OP_GRAD_CODEBOOK ? 3 * align256((size_t)S * V * 4) : 0) +
                            (ckpt ? nrm + align256(2 * G * 4) : 0) +   // + the Q input offsets, the saved messages
                            (p.qg ? align256(G * 4) : 0);              // + the Q^ message
             break;

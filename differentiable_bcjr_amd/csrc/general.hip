@@ -716,7 +716,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             } else if (tau == 0) {
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    args.w_soft[(b * n + t) * V + v] = valid ? wb[t * V + v] + (S1[v] / S0) * inv_scale
+                    args.w_soft[(b * n + t) * V + v] = valid ? fmaf(S1[v] / S0, inv_scale, wb[t * V + v])
                                                              : __builtin_nanf("");
             }
             lds_barrier();
@@ -740,7 +740,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                 }
 #pragma unroll
                 for (int v = 0; v < V; ++v)
-                    args.w_soft[(b * n + tt) * V + v] = valid ? wb[tt * V + v] + (S1[v] / S0) * inv_scale
+                    args.w_soft[(b * n + tt) * V + v] = valid ? fmaf(S1[v] / S0, inv_scale, wb[tt * V + v])
                                                               : __builtin_nanf("");
             }
         }
@@ -1040,7 +1040,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     extern __shared__ float lds[];
     __shared__ float redmax[2][16];
     __shared__ float redq[2][16];
-    __shared__ float reds[2][16][1 + V];
+    __shared__ float reds[2][16][2 + V];
 
     const int L = LT ? LT : args.L, n = args.n, TPS = LT ? (1 << LT) / SPT : (int)blockDim.x, tau = threadIdx.x;
     const int lane = tau & 63, wv = tau >> 6;
@@ -1081,7 +1081,17 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
     // the codebook-gradient accumulator of the slot: c(s, v) at acc_base + 4 (s V + v), so a tile row's entries are
     // contiguous like its codebook values
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * NS * 4) : 0u);
-    const uint32_t kin_base = acc_base + (GC ? (uint32_t)align256(((size_t)V * 4) << L) : 0u);
+    // and (boundary-state mode) each state's two pending contributions of the last step, P1 = f e [g + (2/T)(w - c)
+    // (E[F | s] - E[F])] and P2 = f e (2/T)(c - w), folded in during the next step as (P1 + m2 P2) / S0: there the
+    // posterior is nearly frozen, each step is divided by its own exact total (the forced steps near the boundary give
+    // log-weights of a hundred or more, whose roundings differ between the two passes and would make the previous
+    // step's total misweight the step by up to ~1e-5), and E[F | s] - E[F] is centred by its posterior mean m2 (zero
+    // exactly; numerically the rounding its O(1) parts share, which dL/dc would multiply by (2/T)(w - c)), as the
+    // weights' gradient is through its covariance
+    const uint32_t pend_base = acc_base + (uint32_t)align256(((size_t)V * 4) << L);
+    const uint32_t pend2_base = pend_base + (uint32_t)align256(((size_t)V * 4) << L);
+    const uint32_t kin_base = acc_base + (GC ? 3u * (uint32_t)align256(((size_t)V * 4) << L) : 0u);
+    const bool exact = GC && (args.sigma_enum || args.sigma != nullptr);
     const uint32_t save_base = kin_base + (uint32_t)align256((size_t)n * 4);
     float* mq;
     if constexpr (QG) {
@@ -1105,7 +1115,13 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
             for (int a = 0; a < P; ++a)
 #pragma unroll
-                for (int q = 0; q < NI; ++q) st_row<ROW>(z, tape, acc_base + own.row_bytes(m, a, q));
+                for (int q = 0; q < NI; ++q) {
+                    st_row<ROW>(z, tape, acc_base + own.row_bytes(m, a, q));
+                    if (exact) {
+                        st_row<ROW>(z, tape, pend_base + own.row_bytes(m, a, q));
+                        st_row<ROW>(z, tape, pend2_base + own.row_bytes(m, a, q));
+                    }
+                }
     }
 
     for (int64_t b = blockIdx.x; b < args.B; b += gridDim.x) {
@@ -1250,10 +1266,10 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             A += (double)N;
             N_last = N;
             N = lmax;
-            kq = lq;
+            kq = grid_offset(lq);
         }
         // rz = log2 Z - A_n, and E[F], which centres the covariance of the backward pass
-        float rz, EF;
+        float rz, EF, Kfin;   // E[F] = Kfin + EF: the offsets' exact sum, and the centred rest
         RT rzr;   // rz in the precision of the running sums
         if (!has_sigma) {
             float z0 = 0.f, z1 = 0.f;
@@ -1285,14 +1301,16 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             }
             rz = N + lg2(z0);
             rzr = (RT)N + (RT)lg2(z0);
-            EF = z1 / z0 + Kq;   // the final Q^_n carries the offset K_{n-1}
+            EF = z1 / z0;   // the final Q^_n carries the offset K_{n-1}
+            Kfin = Kq;
             __syncthreads();
         } else {
             __syncthreads();   // R~_{n-1} and Q^_{n-1} are on the tape, written by other threads
             const float r = buf_ld_nt(tape, 0u, rows.off(n - 1) + 4u * own.tpos(sig >> K, G));
             const float qv = buf_ld_nt(tape, 0u, q_base + rows.off(n - 1) + 4u * own.tpos(sig >> K, G));
             float x = r;
-            EF = qv + K_last;   // Q^_{n-1} carries the offset K_{n-2}
+            EF = qv;   // Q^_{n-1} carries the offset K_{n-2}
+            Kfin = K_last;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
                 const float d = fmaf(args.cb[sig * V + v], scale, -(wb[(n - 1) * V + v] * scale));
@@ -1308,6 +1326,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         float Nb = 0.f;
         RT C_ = 0, D = 0;
         float lam = 1.f;  // 1 / (posterior total of the previous step), GC only
+        float m2p = 0.f;  // E[E[F | s] - E[F]] of the previous step, boundary-state GC only
         float kb = 0.f;   // kappa_{t+1}, subtracted from the P inputs
         float H = 0.f;    // sum of the kappas of the steps after t
         int t = n - 1;
@@ -1366,22 +1385,27 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             }
             D = N_last;
             Nb = th;
-            kb = pz;
-            H = pz;
+            kb = grid_offset(pz);
+            H = kb;
             t = n - 2;
         }
         bar();
 
         const int t_out = t;
         // the accumulator row of the next unit (GC), one unit ahead, wrapping to the next step's first
-        float acn[GC ? ROW : 1];
-        auto acc_next = [&](int idx, float* nx) {
+        float acn[GC ? ROW : 1], pen[GC ? ROW : 1], pfn[GC ? ROW : 1];
+        auto acc_next = [&](int idx, float* nx, float* np, float* nf) {
             if constexpr (GC) {
                 const int x = (idx + 1) % (BPT * P * NI);
-                ld_floats<ROW>(tape, acc_base + own.row_bytes(x / (NI * P), (x / NI) % P, x % NI), nx);
+                const uint32_t o = own.row_bytes(x / (NI * P), (x / NI) % P, x % NI);
+                ld_floats<ROW>(tape, acc_base + o, nx);
+                if (exact) {
+                    ld_floats<ROW>(tape, pend_base + o, np);
+                    ld_floats<ROW>(tape, pend2_base + o, nf);
+                }
             }
         };
-        acc_next(-1, acn);
+        acc_next(-1, acn, pen, pfn);
         float N_nx = 0.f, K_nx = 0.f, rt_nx = 0.f, qt_nx = 0.f;
         if (t >= 0) {
             N_nx = buf_ld_nt(tape, 0u, nrm_base + 4u * t);
@@ -1464,7 +1488,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             D += (RT)Nt;
             const float ref = (float)(((RT)rzr + D) - C_);
             // E[F | s_t = s] - E[F] = Q^_t(s >> k) + cst + <g_t, c(s) - w_t> + P''_t(s & (G-1)), cst per step
-            const float cst = (Kt - EF) + H;
+            const float brk = (Kt - Kfin) + H;   // exact (offsets on the 2^-6 grid)
+            const float cst = brk - EF;
             float lmax = -3.0e38f, S0 = 0.f, S2 = 0.f, S1[V], S3[V];
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -1479,6 +1504,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     // R~_t and Q^_t of this group; the next group's (or the next step's first) one row ahead
                     const float rt = rt_nx;
                     const float qt = qt_nx + cst;
+                    const float qs = qt_nx - EF;   // GC: the small parts of E[F | s] - E[F]
                     if (m * P + a + 1 < BPT * P) {
                         const int m2 = (m * P + a + 1) / P, a2 = (m * P + a + 1) % P;
                         const uint32_t so = row_t + grp_soff(m2, a2);
@@ -1522,7 +1548,23 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                             e[ii] = ex2(y[ii] - cm);
                             // E[F | s] - E[F], formed before any product: its parts nearly cancel at the likely
                             // states, and multiplying them separately would keep their rounding
-                            r[ii] = z[ii] + qt;
+                            if constexpr (GC) {
+                                // dL/dc weighs it by (2/T)(w - c) state by state, so at a frozen posterior the
+                                // roundings of its O(1) parts (<g_t, c - w> at the likely state and the offsets'
+                                // bracket, which cancel there) would survive: join them before any rounding (one
+                                // fma; for V > 1 a float64 chain, exact for these products) and add the small parts
+                                const float small = pin[m][TI * q + ii] + qs;
+                                if constexpr (V == 1) {
+                                    r[ii] = fmaf(gt[0], d[ii][0], brk) + small;
+                                } else {
+                                    double rr = (double)brk;
+#pragma unroll
+                                    for (int v = 0; v < V; ++v) rr = __builtin_fma((double)gt[v], (double)d[ii][v], rr);
+                                    r[ii] = (float)(rr + (double)small);
+                                }
+                            } else {
+                                r[ii] = z[ii] + qt;
+                            }
                             cs += e[ii];
                             ez = fmaf(e[ii], z[ii], ez);
                             er = fmaf(e[ii], r[ii], er);
@@ -1536,18 +1578,41 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         const float f = ex2((cm + rt) - ref);
                         if constexpr (GC) {
                             // p_t(s) [g_{t,v} + (2/T)(w_{t,v} - c(s, v)) (E[F | s] - E[F])] with p_t(s) = lam f e
-                            float ac[ROW];
+                            float ac[ROW], pe[ROW], pf[ROW];
 #pragma unroll
-                            for (int x = 0; x < ROW; ++x) ac[x] = acn[x];
-                            acc_next((m * P + a) * NI + q, acn);
-                            const float fa = lam * f, ka = fa * kap;
+                            for (int x = 0; x < ROW; ++x) {
+                                ac[x] = acn[x];
+                                pe[x] = pen[x];
+                                pf[x] = pfn[x];
+                            }
+                            acc_next((m * P + a) * NI + q, acn, pen, pfn);
+                            if (exact) {
+                                // the previous step's pending sums join the accumulator, centred by that step's m2 and
+                                // divided by its total (lam); this step's wait
+                                const float ka = f * kap;
 #pragma unroll
-                            for (int ii = 0; ii < TI; ++ii)
+                                for (int ii = 0; ii < TI; ++ii)
 #pragma unroll
-                                for (int v = 0; v < V; ++v)
-                                    ac[ii * V + v] = fmaf(fa * gnat[v], e[ii],
-                                                          fmaf(-ka, e[ii] * d[ii][v] * r[ii], ac[ii * V + v]));
-                            st_row<ROW>(ac, tape, acc_base + own.row_bytes(m, a, q));
+                                    for (int v = 0; v < V; ++v) {
+                                        const int x = ii * V + v;
+                                        ac[x] = fmaf(lam, fmaf(m2p, pf[x], pe[x]), ac[x]);
+                                        const float ed = e[ii] * d[ii][v];
+                                        pe[x] = fmaf(f * gnat[v], e[ii], -ka * (ed * r[ii]));
+                                        pf[x] = ka * ed;
+                                    }
+                                st_row<ROW>(ac, tape, acc_base + own.row_bytes(m, a, q));
+                                st_row<ROW>(pe, tape, pend_base + own.row_bytes(m, a, q));
+                                st_row<ROW>(pf, tape, pend2_base + own.row_bytes(m, a, q));
+                            } else {
+                                const float fa = lam * f, ka = fa * kap;
+#pragma unroll
+                                for (int ii = 0; ii < TI; ++ii)
+#pragma unroll
+                                    for (int v = 0; v < V; ++v)
+                                        ac[ii * V + v] = fmaf(fa * gnat[v], e[ii],
+                                                              fmaf(-ka, e[ii] * d[ii][v] * r[ii], ac[ii * V + v]));
+                                st_row<ROW>(ac, tape, acc_base + own.row_bytes(m, a, q));
+                            }
                         }
                         S0 = fmaf(f, cs, S0);
                         S2 = fmaf(f, er, S2);
@@ -1590,7 +1655,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             if (WPS > 1 && lane == 0) {
                 redmax[t & 1][wv] = lmax;
 #pragma unroll
-                for (int x = 0; x <= V; ++x) reds[t & 1][wv][x] = Sv[x];
+                for (int x = 0; x <= V + 1; ++x) reds[t & 1][wv][x] = Sv[x];   // S0, S1[V], S2
                 const uint32_t po = part_base + 4u * (uint32_t)((t * WPS + wv) * NS);
 #pragma unroll
                 for (int x = 0; x < NS; ++x) buf_st(Sv[x], tape, 0u, po + 4u * x);
@@ -1605,10 +1670,12 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                 for (int v = 0; v < V; ++v) m1[v] = row16_sum(qs < WPS ? reds[t & 1][qs][1 + v] : 0.f) * rcp(s0b);
                 if constexpr (GC) lam = uniform_f(rcp(s0b));
+                if constexpr (GC) m2p = uniform_f(row16_sum(qs < WPS ? reds[t & 1][qs][1 + V] : 0.f) * rcp(s0b));
             } else {
 #pragma unroll
                 for (int v = 0; v < V; ++v) m1[v] = Sv[1 + v] * (1.0f / Sv[0]);
                 if constexpr (GC) lam = uniform_f(1.0f / Sv[0]);
+                if constexpr (GC) m2p = uniform_f(Sv[1 + V] * (1.0f / Sv[0]));
                 if (tau == 0) {
                     const float i0 = 1.0f / Sv[0];
                     const float m2 = Sv[1 + V] * i0;
@@ -1619,7 +1686,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                             args.grad[(b * n + t) * V + v] = valid ? args.two_over_T * cov * inv_scale
                                                                    : __builtin_nanf("");
                         if (args.w_soft)
-                            args.w_soft[(b * n + t) * V + v] = valid ? wb[t * V + v] + m1[v] * inv_scale
+                            args.w_soft[(b * n + t) * V + v] = valid ? fmaf(m1[v], inv_scale, wb[t * V + v])
                                                                      : __builtin_nanf("");
                     }
                 }
@@ -1627,7 +1694,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             float kap = 0.f;
 #pragma unroll
             for (int v = 0; v < V; ++v) kap = fmaf(gt[v], m1[v], kap);
-            kb = uniform_f(kap);
+            kb = grid_offset(uniform_f(kap));
             lmax = uniform_f(lmax);
             H += kb;
             C_ += (RT)Nb;
@@ -1655,11 +1722,33 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         args.grad[(b * n + tt) * V + v] = valid ? args.two_over_T * cov * inv_scale
                                                                 : __builtin_nanf("");
                     if (args.w_soft)
-                        args.w_soft[(b * n + tt) * V + v] = valid ? wb[tt * V + v] + m1 * inv_scale : __builtin_nanf("");
+                        args.w_soft[(b * n + tt) * V + v] = valid ? fmaf(m1, inv_scale, wb[tt * V + v]) : __builtin_nanf("");
                 }
             }
         }
         if constexpr (GC) {
+            if (exact) {   // the last step's pending sums; the pending arrays left at zero
+                float z[ROW];
+#pragma unroll
+                for (int i = 0; i < ROW; ++i) z[i] = 0.f;
+#pragma unroll
+                for (int m = 0; m < BPT; ++m)
+#pragma unroll
+                    for (int a = 0; a < P; ++a)
+#pragma unroll
+                        for (int q = 0; q < NI; ++q) {
+                            const uint32_t o = own.row_bytes(m, a, q);
+                            float ac[ROW], pe[ROW], pf[ROW];
+                            ld_floats<ROW>(tape, acc_base + o, ac);
+                            ld_floats<ROW>(tape, pend_base + o, pe);
+                            ld_floats<ROW>(tape, pend2_base + o, pf);
+#pragma unroll
+                            for (int i = 0; i < ROW; ++i) ac[i] = fmaf(lam, fmaf(m2p, pf[i], pe[i]), ac[i]);
+                            st_row<ROW>(ac, tape, acc_base + o);
+                            st_row<ROW>(z, tape, pend_base + o);
+                            st_row<ROW>(z, tape, pend2_base + o);
+                        }
+            }
             if (!valid) {   // no admissible path: the loss, hence its gradient, is undefined
                 float x[ROW];
 #pragma unroll

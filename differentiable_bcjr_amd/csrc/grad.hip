@@ -45,6 +45,11 @@ namespace bcjr {
 #ifndef BCJR_GRAD_BWD_GROUPS
 #define BCJR_GRAD_BWD_GROUPS 2
 #endif
+// How many groups ahead the backward pass issues its tape loads (R~ and Q^ of one group): the tape is the kernel's
+// one stream from HBM, and deeper prefetch keeps more of it in flight.  Must divide the groups per step (4 QPT).
+#ifndef BCJR_GRAD_TAPE_DEPTH
+#define BCJR_GRAD_TAPE_DEPTH 1
+#endif
 constexpr int kGradFwdGroups = BCJR_GRAD_FWD_GROUPS;
 constexpr int kGradBwdGroups = BCJR_GRAD_BWD_GROUPS;
 
@@ -58,16 +63,30 @@ __device__ __forceinline__ float4 cb_row(const float (&cbr)[M][4][4], rsrc_t cbs
     }
 }
 
-// GC: also accumulate dL/dc per state of the trellis into this slot's accumulator (read-modify-write of
+// GCM = 1: also accumulate dL/dc per state of the trellis into this slot's accumulator (read-modify-write of
 // [2^L] floats at the end of the slot, one float4 per group and step), normalising each step's posterior by the
 // previous step's exact total, with the running normaliser sums in double.
+// GCM = 2 (boundary-state mode): there the last ~L/2 steps are forced through far codewords, the posterior is nearly
+// frozen, and two roundings that cancel in the weights' gradient survive in dL/dc:
+//   * the messages carry log-weights of a hundred or more, whose roundings differ between the forward and the
+//     backward pass, so consecutive steps' totals differ by up to ~1e-5 and the previous step's total misweights
+//     the step; here every step is divided by its own exact total;
+//   * E[F | s] - E[F] at the likely state, a small difference of O(1) expectation messages, carries their
+//     roundings, which dL/dc multiplies by (2/T)(w - c); the weights' gradient is a covariance, centred by
+//     m2 = E[E[F | s] - E[F]] (zero exactly, the step's common rounding numerically), and here dL/dc is centred
+//     the same way: p(s) (2/T)(w - c(s)) (E[F | s] - E[F] - m2).
+// Both need the step's totals, known after its loop, so each step's contribution is kept in two further [2^L]
+// arrays, P1 = f e [g + (2/T)(w - c)(E[F | s] - E[F])] and P2 = f e (2/T)(c - w) (f the step's posterior factor),
+// and folded in during the next step (and after the last) as A += (P1 + m2 P2) / S0: two more reads and writes per
+// state and step in this mode.
 // CK: the checkpoint mode.  The forward pass stores only rows t = 0, c, 2c, .. and row n - 1 of both messages
 // (TapeRows), and each step's Q input offset; the backward pass walks the segments from the end and, before each,
 // saves its two messages to the workspace, reloads the segment's checkpoint, reruns the forward steps of the segment
 // with the stored normalisers and offsets (the same code and numbers as the first pass, so the rows come out
 // bit-identical), and restores its messages.  A compile-time flag, so the full-tape kernels carry none of it.
-template <int L, bool GC, bool CK>
+template <int L, int GCM, bool CK>
 __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
+    constexpr bool GC = GCM != 0, EXACT = GCM == 2;
     using Gm = Geo<L>;
     constexpr int G = Gm::G, Q = Gm::Q, QPT = Gm::QPT, TPS = Gm::TPS, SPB = Gm::SPB, WPS = Gm::WPS;
     constexpr int SEG = Gm::SEG;
@@ -77,7 +96,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     __shared__ float redmax[2][SPB][WPS];
     __shared__ float redq[2][SPB][WPS];
     __shared__ float4 redsum[2][SPB][WPS];
-    __shared__ float2 redsum2[2][SPB][WPS];
+    __shared__ float4 redsum2[2][SPB][WPS];
 
     const int tid = threadIdx.x;
     const int sq = tid / TPS;
@@ -127,7 +146,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
     const uint32_t acc_base = part_base + (WPS > 1 ? (uint32_t)align256((size_t)n * WPS * 16) : 0u);
     // checkpoint mode: each step's Q input offset, then each thread's share of the two backward messages while a
     // segment is rebuilt
-    const uint32_t kqi_base = acc_base + (GC ? (uint32_t)align256((size_t)4 << L) : 0u);
+    // GCM = 2: the pending contributions P1 and P2
+    const uint32_t pend_base = acc_base + (uint32_t)align256((size_t)4 << L);
+    const uint32_t pend2_base = pend_base + (uint32_t)align256((size_t)4 << L);
+    const uint32_t kqi_base = acc_base + (GC ? 3u * (uint32_t)align256((size_t)4 << L) : 0u);
     const uint32_t save_base = kqi_base + (uint32_t)align256((size_t)n * 4);
     using RT = typename std::conditional<GC, double, float>::type;   // running normaliser sums
     const float kap = args.two_over_T * inv_scale;   // (2/T) (w - c) = -kap d with d in scaled units
@@ -135,8 +157,13 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
         for (int m = 0; m < QPT; ++m)
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
+            for (int a = 0; a < 4; ++a) {
                 buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+                if constexpr (EXACT) {
+                    buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, pend_base + 16u * (TPS * m + Q * a));
+                    buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, pend2_base + 16u * (TPS * m + Q * a));
+                }
+            }
     }
 
     const int64_t ngroups = (args.B + SPB - 1) / SPB;
@@ -284,10 +311,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             A += (double)N;
             N_last = N;
             N = lmax;
-            kq = lq;
+            kq = grid_offset(lq);
         }
         // rz = log2 Z - A_n and E[F] (which centres the covariance of the backward pass)
-        float rz, EF;
+        float rz, EF, Kfin;   // E[F] = Kfin + EF: the offsets' exact sum, and the centred rest
         RT rzr;   // rz in the precision of the running sums
         if (!has_sigma) {
             float z0 = 0.f, z1 = 0.f;
@@ -317,7 +344,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
             rz = N + lg2(z0);
             rzr = (RT)N + (RT)lg2(z0);
-            EF = z1 / z0 + K;   // the final outputs Q^_n carry the offset K_{n-1}
+            EF = z1 / z0;   // the final outputs Q^_n carry the offset K_{n-1}
+            Kfin = K;
             __syncthreads();   // tape writes of the forward pass visible to every thread of the block
         } else {
             // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
@@ -327,7 +355,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + rows.off(n - 1) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
             rzr = (r < 0.5f * kNeg) ? (RT)kNeg : (RT)fmaf(-d, d, r) - (RT)N_last;
-            EF = fmaf(gb[n - 1] * inv_scale, d, q + K_last);   // Q^_{n-1} carries the offset K_{n-2}
+            EF = fmaf(gb[n - 1] * inv_scale, d, q);   // Q^_{n-1} carries the offset K_{n-2}
+            Kfin = K_last;
         }
         const bool valid = rz > 0.5f * kNeg;
 
@@ -336,6 +365,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         RT C = 0;
         RT D = 0;
         float lam = 1.f;   // 1 / (posterior total of the previous step), GC only
+        float m2p = 0.f;   // E[E[F | s] - E[F]] of the previous step, GCM = 2
         float kb = 0.f;   // kappa_{t+1} = g_{t+1} (w_soft_{t+1} - w_{t+1}), subtracted from the P^ inputs
         float H = 0.f;    // sum of the kappas of the steps after t
         int t = n - 1;
@@ -368,8 +398,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
             D = N_last;
             Nb = th;
-            kb = pz;
-            H = pz;
+            kb = grid_offset(pz);
+            H = kb;
             t = n - 2;
             if constexpr (GC) {   // p_{n-1} is the indicator of sigma and E[F | s_{n-1}] = E[F]: dL/dc(sigma) += g_{n-1}
                 const uint32_t js = (sig >> 2) & (uint32_t)(Q - 1);
@@ -382,14 +412,30 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         lds_barrier();
 
         // loads of the next group (forward messages R~, Q^ of this step, codebook row) are issued one group ahead
-        float rt_n = 0.f, qt_n = 0.f;
+        constexpr int TD = BCJR_GRAD_TAPE_DEPTH, NGS = 4 * QPT;   // tape prefetch depth, groups per step
+        static_assert(NGS % TD == 0, "the tape prefetch ring must divide the groups of a step");
+        float rt_q[TD], qt_q[TD];   // R~_t and Q^_t of the next TD groups, group gi in slot gi % TD
+        // the first TD groups of step tt into the ring
+        auto prefetch_row = [&](int tt) {
+#pragma unroll
+            for (int q = 0; q < TD; ++q) {
+                const uint32_t so = rows.off(tt) + 4u * (TPS * (q >> 2) + Q * (q & 3));
+                rt_q[q] = buf_ld_nt(tape, v_grp, so);
+                qt_q[q] = buf_ld_nt(tape, v_grp, q_base + so);
+            }
+        };
         float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
         float4 ac_n = make_float4(0.f, 0.f, 0.f, 0.f);   // the next group's accumulator (GC)
+        float4 pe_n = make_float4(0.f, 0.f, 0.f, 0.f);   // and its pending contributions (GCM = 2)
+        float4 pf_n = make_float4(0.f, 0.f, 0.f, 0.f);
         if (t >= 0) {
-            rt_n = buf_ld_nt(tape, v_grp, rows.off(t));
-            qt_n = buf_ld_nt(tape, v_grp, q_base + rows.off(t));
+            prefetch_row(t);
             if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
             if constexpr (GC) ac_n = buf_ld4(tape, v_quad, acc_base);
+            if constexpr (EXACT) {
+                pe_n = buf_ld4(tape, v_quad, pend_base);
+                pf_n = buf_ld4(tape, v_quad, pend2_base);
+            }
         }
         const int t_out = t;   // last step whose outputs the loop below produces
         float w_nx = 0.f, g_nx = 0.f, N_nx = 0.f, K_nx = 0.f;
@@ -439,8 +485,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 *reinterpret_cast<float4*>(mq + 4 * j) = buf_ld4(tape, v_quad, save_base + G * 4u + 16u * TPS * m);
             }
             lds_barrier();
-            rt_n = buf_ld_nt(tape, v_grp, rows.off(t));
-            qt_n = buf_ld_nt(tape, v_grp, q_base + rows.off(t));
+            prefetch_row(t);
         }
         for (; t >= t0; --t) {
             float bin[QPT][4], pin[QPT][4];
@@ -469,35 +514,55 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             D += Nt;
             const float ref = (float)((rzr + D) - C);
             // E[F | s_t = s] - E[F] = Q^_t(s >> 2) + cst + g_t (c(s) - w_t) + P''_t(s & (G-1)), cst per step
-            const float cst = (Kt - EF) + H;
+            const float brk = (Kt - Kfin) + H;   // exact (offsets on the 2^-6 grid)
+            const float cst = brk - EF;
             float lmax = -3.0e38f, S0 = 0.f, S1 = 0.f, S2 = 0.f, S3 = 0.f;
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
-                    const float rt = rt_n;
-                    const float qt = qt_n + cst;
+                    const int gi = 4 * m + a, slot = gi % TD;
+                    const float rt = rt_q[slot];
+                    const float qt = qt_q[slot] + cst;
+                    const float qs = qt_q[slot] - EF;   // GC: the small parts of E[F | s] - E[F]
                     float4 cr;
                     if constexpr (CB_REG) cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
                     else cr = cr_n;
-                    // issue the next group's loads (or the next step's first group's) before this group's math
+                    // issue the loads of the group TD ahead (of the next step once past this one's last) and the next
+                    // group's codebook row before this group's math; in checkpoint mode a row past the segment is
+                    // read again once rebuilt
                     const bool last = (m == QPT - 1) && (a == 3);
                     const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
-                    if (!last) {
-                        const uint32_t so2 = rows.off(t) + 4u * (TPS * m2 + Q * a2);
-                        rt_n = buf_ld_nt(tape, v_grp, so2);
-                        qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
-                        if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
-                    } else if (t > 0) {   // (in checkpoint mode a row past the segment is read again once rebuilt)
-                        const uint32_t so2 = rows.off(t - 1);
-                        rt_n = buf_ld_nt(tape, v_grp, so2);
-                        qt_n = buf_ld_nt(tape, v_grp, q_base + so2);
-                        if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+                    {
+                        const int gn = gi + TD;
+                        if (gn < NGS) {
+                            const uint32_t so2 = rows.off(t) + 4u * (TPS * (gn >> 2) + Q * (gn & 3));
+                            rt_q[slot] = buf_ld_nt(tape, v_grp, so2);
+                            qt_q[slot] = buf_ld_nt(tape, v_grp, q_base + so2);
+                        } else if (t > 0) {
+                            const int g2 = gn - NGS;
+                            const uint32_t so2 = rows.off(t - 1) + 4u * (TPS * (g2 >> 2) + Q * (g2 & 3));
+                            rt_q[slot] = buf_ld_nt(tape, v_grp, so2);
+                            qt_q[slot] = buf_ld_nt(tape, v_grp, q_base + so2);
+                        }
                     }
-                    float4 ac = ac_n;
+                    if constexpr (!CB_REG) {
+                        if (!last) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
+                        else if (t > 0) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+                    }
+                    float4 ac = ac_n, pe = pe_n, pf = pf_n;
                     if constexpr (GC) {
                         if (!last) ac_n = buf_ld4(tape, v_quad, acc_base + 16u * (TPS * m2 + Q * a2));
                         else if (t > 0) ac_n = buf_ld4(tape, v_quad, acc_base);
+                    }
+                    if constexpr (EXACT) {
+                        if (!last) {
+                            pe_n = buf_ld4(tape, v_quad, pend_base + 16u * (TPS * m2 + Q * a2));
+                            pf_n = buf_ld4(tape, v_quad, pend2_base + 16u * (TPS * m2 + Q * a2));
+                        } else if (t > 0) {
+                            pe_n = buf_ld4(tape, v_quad, pend_base);
+                            pf_n = buf_ld4(tape, v_quad, pend2_base);
+                        }
                     }
                     const float d0 = fmaf(cr.x, scale, -wt), d1 = fmaf(cr.y, scale, -wt);
                     const float d2 = fmaf(cr.z, scale, -wt), d3 = fmaf(cr.w, scale, -wt);
@@ -513,7 +578,22 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const float ed = (ed0 + ed1) + (ed2 + ed3);
                     // E[F | s] - E[F] per state, formed before any product: its two parts nearly cancel at the
                     // likely states, and multiplying them separately would keep their rounding
-                    const float r0 = z0 + qt, r1 = z1 + qt, r2 = z2 + qt, r3 = z3 + qt;
+                    float r0, r1, r2, r3;
+                    if constexpr (GC) {
+                        // dL/dc weighs it by (2/T)(w - c) state by state, so at a frozen posterior the roundings of
+                        // its two O(1) parts (g_t (c - w) at the likely state and the offsets' bracket, which cancel
+                        // there) would survive: join them inside one fma, exact before its single rounding, and add
+                        // the small parts after
+                        r0 = fmaf(gt, d0, brk) + (pin[m][0] + qs);
+                        r1 = fmaf(gt, d1, brk) + (pin[m][1] + qs);
+                        r2 = fmaf(gt, d2, brk) + (pin[m][2] + qs);
+                        r3 = fmaf(gt, d3, brk) + (pin[m][3] + qs);
+                    } else {
+                        r0 = z0 + qt;
+                        r1 = z1 + qt;
+                        r2 = z2 + qt;
+                        r3 = z3 + qt;
+                    }
                     const float er = fmaf(e0, r0, fmaf(e1, r1, fmaf(e2, r2, e3 * r3)));
                     const float edr = fmaf(ed0, r0, fmaf(ed1, r1, fmaf(ed2, r2, ed3 * r3)));
                     const float out = (mx - Nb) + lg2(s);
@@ -524,14 +604,37 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     S3 = fmaf(f, edr, S3);
                     lmax = run_max(lmax, out);
                     if constexpr (GC) {
-                        // p_t(s) [g_t + (2/T)(w_t - c(s))(E[F | s] - E[F])] with p_t(s) = lam f e_i
-                        const float fa = lam * f;
-                        const float ga = fa * gnat, ka = fa * kap;
-                        ac.x = fmaf(ga, e0, fmaf(-ka, ed0 * r0, ac.x));
-                        ac.y = fmaf(ga, e1, fmaf(-ka, ed1 * r1, ac.y));
-                        ac.z = fmaf(ga, e2, fmaf(-ka, ed2 * r2, ac.z));
-                        ac.w = fmaf(ga, e3, fmaf(-ka, ed3 * r3, ac.w));
-                        if (active) buf_st4(ac, tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+                        if constexpr (EXACT) {
+                            // the previous step's pending contributions join the accumulator, centred by that step's
+                            // m2 and divided by its total (lam); this step's wait
+                            ac.x = fmaf(lam, fmaf(m2p, pf.x, pe.x), ac.x);
+                            ac.y = fmaf(lam, fmaf(m2p, pf.y, pe.y), ac.y);
+                            ac.z = fmaf(lam, fmaf(m2p, pf.z, pe.z), ac.z);
+                            ac.w = fmaf(lam, fmaf(m2p, pf.w, pe.w), ac.w);
+                            const float ga = f * gnat, ka = f * kap;
+                            pe.x = fmaf(ga, e0, -ka * (ed0 * r0));
+                            pe.y = fmaf(ga, e1, -ka * (ed1 * r1));
+                            pe.z = fmaf(ga, e2, -ka * (ed2 * r2));
+                            pe.w = fmaf(ga, e3, -ka * (ed3 * r3));
+                            pf.x = ka * ed0;
+                            pf.y = ka * ed1;
+                            pf.z = ka * ed2;
+                            pf.w = ka * ed3;
+                            if (active) {
+                                buf_st4(ac, tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+                                buf_st4(pe, tape, v_quad, pend_base + 16u * (TPS * m + Q * a));
+                                buf_st4(pf, tape, v_quad, pend2_base + 16u * (TPS * m + Q * a));
+                            }
+                        } else {
+                            // p_t(s) [g_t + (2/T)(w_t - c(s))(E[F | s] - E[F])] with p_t(s) = lam f e_i
+                            const float fa = lam * f;
+                            const float ga = fa * gnat, ka = fa * kap;
+                            ac.x = fmaf(ga, e0, fmaf(-ka, ed0 * r0, ac.x));
+                            ac.y = fmaf(ga, e1, fmaf(-ka, ed1 * r1, ac.y));
+                            ac.z = fmaf(ga, e2, fmaf(-ka, ed2 * r2, ac.z));
+                            ac.w = fmaf(ga, e3, fmaf(-ka, ed3 * r3, ac.w));
+                            if (active) buf_st4(ac, tape, v_quad, acc_base + 16u * (TPS * m + Q * a));
+                        }
                     }
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
                     mr[u] = out;            // at t = 0 these land in buffers nobody reads
@@ -550,7 +653,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             S3 = seg_sum_fast<SEG>(S3);
             if constexpr (WPS > 1) {
                 if (lane == 0) {
-                    redsum2[t & 1][sq][wv] = make_float2(S0, S1);
+                    redsum2[t & 1][sq][wv] = make_float4(S0, S1, S2, 0.f);
                     redmax[t & 1][sq][wv] = lmax;
                     buf_st4(make_float4(S0, S1, S2, S3), tape, sq * slot_bytes,
                             part_base + 16u * (uint32_t)(t * WPS + wv));
@@ -560,16 +663,18 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             float m1;   // w_soft_t - w_t in scaled codebook units
             if constexpr (WPS > 1) {
                 const int qs = lane & 15;
-                const float2 p = qs < WPS ? redsum2[t & 1][sq][qs] : make_float2(0.f, 0.f);
+                const float4 p = qs < WPS ? redsum2[t & 1][sq][qs] : make_float4(0.f, 0.f, 0.f, 0.f);
                 lmax = row16_max(qs < WPS ? redmax[t & 1][sq][qs] : -3.0e38f);
                 // only the P offset uses m1 here, and any value common to the block serves: the approximate
                 // reciprocal keeps the division off the step's critical path
                 const float s0b = row16_sum(p.x);
                 m1 = row16_sum(p.y) * rcp(s0b);
                 if constexpr (GC) lam = rcp(s0b);
+                if constexpr (EXACT) m2p = row16_sum(p.z) * rcp(s0b);
             } else {
                 m1 = S1 * (1.0f / S0);
                 if constexpr (GC) lam = 1.0f / S0;
+                if constexpr (EXACT) m2p = S2 * (1.0f / S0);
             }
             if constexpr (WPS == 1) {
                 if (tau == 0 && active) {
@@ -578,14 +683,15 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const float cov = fmaf(-m1, m2, S3 * i0);   // Cov(c' - w', E[F | s] - E[F]), c' scaled
                     if (!GC || args.grad)
                         args.grad[b * n + t] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
-                    if (args.w_soft) args.w_soft[b * n + t] = valid ? wb[t] + m1 * inv_scale : __builtin_nanf("");
+                    if (args.w_soft) args.w_soft[b * n + t] = valid ? fmaf(m1, inv_scale, wb[t]) : __builtin_nanf("");
                 }
             }
-            kb = gt * m1;
+            kb = grid_offset(gt * m1);
             if constexpr (SPB == 1) {
                 lmax = uniform_f(lmax);
                 kb = uniform_f(kb);
                 if constexpr (GC) lam = uniform_f(lam);
+                if constexpr (EXACT) m2p = uniform_f(m2p);
             }
             H += kb;
             C += Nb;
@@ -613,8 +719,28 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 if (active) {
                     if (!GC || args.grad)
                         args.grad[b * n + tt] = valid ? args.two_over_T * cov * inv_scale : __builtin_nanf("");
-                    if (args.w_soft) args.w_soft[b * n + tt] = valid ? wb[tt] + m1 * inv_scale : __builtin_nanf("");
+                    if (args.w_soft) args.w_soft[b * n + tt] = valid ? fmaf(m1, inv_scale, wb[tt]) : __builtin_nanf("");
                 }
+            }
+        }
+        if constexpr (EXACT) {   // the last step's pending contributions; the arrays left at zero
+            if (active) {
+#pragma unroll
+                for (int m = 0; m < QPT; ++m)
+#pragma unroll
+                    for (int a = 0; a < 4; ++a) {
+                        const uint32_t o = 16u * (TPS * m + Q * a);
+                        float4 ac = buf_ld4(tape, v_quad, acc_base + o);
+                        const float4 pe = buf_ld4(tape, v_quad, pend_base + o);
+                        const float4 pf = buf_ld4(tape, v_quad, pend2_base + o);
+                        ac.x = fmaf(lam, fmaf(m2p, pf.x, pe.x), ac.x);
+                        ac.y = fmaf(lam, fmaf(m2p, pf.y, pe.y), ac.y);
+                        ac.z = fmaf(lam, fmaf(m2p, pf.z, pe.z), ac.z);
+                        ac.w = fmaf(lam, fmaf(m2p, pf.w, pe.w), ac.w);
+                        buf_st4(ac, tape, v_quad, acc_base + o);
+                        buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, pend_base + o);
+                        buf_st4(make_float4(0.f, 0.f, 0.f, 0.f), tape, v_quad, pend2_base + o);
+                    }
             }
         }
         if constexpr (GC) {
@@ -670,35 +796,35 @@ __global__ void __launch_bounds__(256) codebook_reduce_kernel(const unsigned cha
     }
 }
 
-template <int L, bool GC>
+template <int L, int GCM>
 static hipError_t launch_grad_L(const GradArgs& a, int grid, hipStream_t st) {
-    if (a.ckpt) hipLaunchKernelGGL((grad_kernel<L, GC, true>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
-    else hipLaunchKernelGGL((grad_kernel<L, GC, false>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    if (a.ckpt) hipLaunchKernelGGL((grad_kernel<L, GCM, true>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
+    else hipLaunchKernelGGL((grad_kernel<L, GCM, false>), dim3(grid), dim3(Geo<L>::NT), 0, st, a);
     return hipGetLastError();
 }
 
-template <bool GC>
+template <int GCM>
 static hipError_t launch_grad_any(int L, const GradArgs& a, int grid, hipStream_t st) {
     switch (L) {
-        case 4: return launch_grad_L<4, GC>(a, grid, st);
-        case 5: return launch_grad_L<5, GC>(a, grid, st);
-        case 6: return launch_grad_L<6, GC>(a, grid, st);
-        case 7: return launch_grad_L<7, GC>(a, grid, st);
-        case 8: return launch_grad_L<8, GC>(a, grid, st);
-        case 9: return launch_grad_L<9, GC>(a, grid, st);
-        case 10: return launch_grad_L<10, GC>(a, grid, st);
-        case 11: return launch_grad_L<11, GC>(a, grid, st);
-        case 12: return launch_grad_L<12, GC>(a, grid, st);
-        case 13: return launch_grad_L<13, GC>(a, grid, st);
-        case 14: return launch_grad_L<14, GC>(a, grid, st);
-        case 15: return launch_grad_L<15, GC>(a, grid, st);
-        case 16: return launch_grad_L<16, GC>(a, grid, st);
+        case 4: return launch_grad_L<4, GCM>(a, grid, st);
+        case 5: return launch_grad_L<5, GCM>(a, grid, st);
+        case 6: return launch_grad_L<6, GCM>(a, grid, st);
+        case 7: return launch_grad_L<7, GCM>(a, grid, st);
+        case 8: return launch_grad_L<8, GCM>(a, grid, st);
+        case 9: return launch_grad_L<9, GCM>(a, grid, st);
+        case 10: return launch_grad_L<10, GCM>(a, grid, st);
+        case 11: return launch_grad_L<11, GCM>(a, grid, st);
+        case 12: return launch_grad_L<12, GCM>(a, grid, st);
+        case 13: return launch_grad_L<13, GCM>(a, grid, st);
+        case 14: return launch_grad_L<14, GCM>(a, grid, st);
+        case 15: return launch_grad_L<15, GCM>(a, grid, st);
+        case 16: return launch_grad_L<16, GCM>(a, grid, st);
         default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_grad(int L, const GradArgs& a, int grid, hipStream_t st) {
-    return launch_grad_any<false>(L, a, grid, st);
+    return launch_grad_any<0>(L, a, grid, st);
 }
 
 // dL/dc from `count` per-slot accumulators of S floats each, `stride` bytes apart starting at ws + acc_off.
@@ -710,7 +836,9 @@ hipError_t launch_codebook_reduce(const unsigned char* ws, size_t stride, uint32
 }
 
 hipError_t launch_grad_codebook(int L, const GradArgs& a, int grid, hipStream_t st, float* grad_codebook) {
-    const hipError_t e = launch_grad_any<true>(L, a, grid, st);
+    // boundary-state mode normalises each step by its own total (GCM = 2)
+    const bool exact = a.sigma != nullptr || a.sigma_enum;
+    const hipError_t e = exact ? launch_grad_any<2>(L, a, grid, st) : launch_grad_any<1>(L, a, grid, st);
     if (e != hipSuccess) return e;
     const GeoRT g = geo_rt(L);
     const int S = 1 << L;

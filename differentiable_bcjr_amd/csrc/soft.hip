@@ -355,7 +355,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     lmax = row16_max((lane & 15) < WPS ? redmax[t & 1][sq][lane & 15] : -3.0e38f);
                 } else {
                     if (tau == 0 && active)
-                        args.w_soft[b * n + t] = valid ? wb[t] + (S1 / S0) * inv_scale : __builtin_nanf("");
+                        args.w_soft[b * n + t] = valid ? fmaf(S1 / S0, inv_scale, wb[t]) : __builtin_nanf("");
                 }
                 if constexpr (SPB == 1) lmax = uniform_f(lmax);
                 C += Nb;
@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                     S0 += p.x;
                     S1 += p.y;
                 }
-                if (active) args.w_soft[b * n + tt] = valid ? wb[tt] + (S1 / S0) * inv_scale : __builtin_nanf("");
+                if (active) args.w_soft[b * n + tt] = valid ? fmaf(S1 / S0, inv_scale, wb[tt]) : __builtin_nanf("");
             }
         }
         // the next sequence reuses the tape and the LDS buffers

@@ -59,6 +59,12 @@ __host__ __device__ constexpr int blocks_per_cu(int L) { return L >= 15 ? 1 : (L
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float lg2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+// The per-step offsets that keep the expectation messages centred are rounded to multiples of 2^-6.  Any offset
+// serves (the true message is the stored one plus the sum of the offsets applied), and on this grid every running
+// sum of offsets, and every difference of two such sums, is exact in float32 while it stays below 2^18 in
+// magnitude; E[F | s_t = s] - E[F] then carries only roundings at the size of the centred messages, not at the size
+// of F itself.
+__device__ __forceinline__ float grid_offset(float x) { return __builtin_rintf(x * 64.f) * 0.015625f; }
 // Maxima over finite values use the IEEE-2019 maximum (v_maximum3_f32).  fmaxf must quiet signalling NaNs, so the
 // compiler re-canonicalises every operand it cannot prove canonical (a DPP or LDS result, one that left an asm ordering
 // point) with an extra half-rate v_max per use; the maximum has no such requirement, and the two agree on the finite

@@ -76,7 +76,7 @@ def test_workspace_bytes_formula(L, B, n):
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_SOFT, B, n, L, 2) == slots * (msgs + nrm + part)
     part4 = _a256(n * _wps(L) * 16) if _wps(L) > 1 else 0
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD, B, n, L, 2) == slots * (2 * msgs + 2 * nrm + part4)
-    acc = _a256((1 << L) * 4)   # one float accumulator per state
+    acc = 3 * _a256((1 << L) * 4)   # per state one float accumulator and two pending contributions
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_GRAD_CODEBOOK, B, n, L, 2) == slots * (2 * msgs + 2 * nrm + part4 + acc)
     assert abi.bcjr_workspace_bytes(abi.BCJR_OP_VITERBI, B, n, L, 2) == slots * _a256(2 * n * TPS * 4)
 
@@ -122,9 +122,9 @@ def _gen_bytes(op, B, n, L, k, V, ckpt=0):
     tapes, nrm = _a256(((n + 1) if ckpt == 0 else (n // ckpt + ckpt)) * G * 4), _a256(n * 4)
     if op == abi.BCJR_OP_SOFT:
         slot = tapes + nrm + (_a256(n * wps * (1 + V) * 4) if wps > 1 else 0) + (_a256(G * 4) if ckpt else 0)
-    elif op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):   # GC: + one float accumulator per state, component
-        slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)
-        slot += _a256(S * V * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
+    elif op in (abi.BCJR_OP_GRAD, abi.BCJR_OP_GRAD_CODEBOOK):   # GC: + per state and component one float
+        slot = 2 * tapes + 2 * nrm + (_a256(n * wps * (2 + 2 * V) * 4) if wps > 1 else 0)   # accumulator, two pending
+        slot += 3 * _a256(S * V * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
         slot += nrm + _a256(2 * G * 4) if ckpt else 0
         slot += _a256(G * 4) if qg else 0
     else:
@@ -157,7 +157,7 @@ def _tuned_ck_bytes(op, B, n, L, c):
         part = _a256(n * _wps(L) * 8) if _wps(L) > 1 else 0
         return slots * (rows + nrm + part + _a256(G * 4))
     part = _a256(n * _wps(L) * 16) if _wps(L) > 1 else 0
-    acc = _a256((1 << L) * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
+    acc = 3 * _a256((1 << L) * 4) if op == abi.BCJR_OP_GRAD_CODEBOOK else 0
     return slots * (2 * rows + 2 * nrm + part + acc + nrm + _a256(2 * G * 4))
 
 
@@ -178,8 +178,8 @@ def test_workspace_min_is_the_checkpoint_mode(L, k, V, B, n):
             ckb = _gen_bytes(op, B, n, L, k, V, ckpt=c)
         want = min(full, ckb) if full else 0
         assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) == want
-        if n >= 256 and L == 16 and full:   # the codebook gradient's [2^L][V] accumulator is not reduced
-            factor = 6 if op != abi.BCJR_OP_GRAD_CODEBOOK else 4
+        if n >= 256 and L == 16 and full:   # the codebook gradient's three [2^L][V] arrays are not reduced
+            factor = 6 if op != abi.BCJR_OP_GRAD_CODEBOOK else 3
             assert abi.bcjr_workspace_bytes_min(op, B, n, L, k, V) * factor < full
     # Viterbi and the tail-biting ops have one memory mode: their smallest workspace is the full one
     for op in (abi.BCJR_OP_VITERBI, abi.BCJR_OP_VITERBI_TB_EXACT, abi.BCJR_OP_VITERBI_TB_ROTATE,
