@@ -94,9 +94,11 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES.update({f"gen_{op}_k{k}v{V}": ["general.hip"] for op in ("soft", "grad", "viterbi")
                        for k, V in ((3, 1), (4, 2))})
 COMMON_SOURCES = ["trellis.hpp", "kernel_args.hpp"]
-KERNEL_NAMES = {"soft": "soft_kernel<16, false>", "grad": "grad_kernel<16, false, false>",
-                "viterbi": "viterbi_kernel<16>", "grad_codebook": "grad_kernel<16, true, false>"}
-CHECKPOINT_KERNELS = {"soft": "soft_kernel<16, true>", "grad": "grad_kernel<16, false, true>"}
+# the kernels' template names as the profiler lists them: soft_kernel<L, checkpoint>, grad_kernel<L, codebook-gradient
+# mode, checkpoint>, viterbi_kernel<L>
+KERNEL_NAMES = {"soft": "soft_kernel<16, false>", "grad": "grad_kernel<16, 0, false>",
+                "viterbi": "viterbi_kernel<16>", "grad_codebook": "grad_kernel<16, 1, false>"}
+CHECKPOINT_KERNELS = {"soft": "soft_kernel<16, true>", "grad": "grad_kernel<16, 0, true>"}
 # HBM bytes per state-step of the codebook gradient: forward tape R~ and Q^ (one float per group each, i.e. 2 bytes
 # per state, written by the forward pass and read by the backward pass) + the per-state accumulator (4 bytes read
 # and 4 written per step)

@@ -22,8 +22,8 @@
 // buffer: each step loads its inputs into registers, barriers, then writes its outputs.  Both forward messages go to
 // the workspace tape (non-temporal: written once, read once a pass later).  At L = 16 the codebook is read through
 // L1/L2 each step (a thread has no registers left for it); at smaller L it stays in registers.  Memory latency is
-// covered by issuing each load one group (backward tape and codebook) or one quad (forward codebook) ahead, and the
-// next step's scalars (w, g, normaliser, Q offset) one step ahead.  With several waves per sequence only (S0, S1) is
+// covered by issuing the backward's tape loads and codebook rows several groups ahead, the forward's codebook rows one
+// quad ahead, and the next step's scalars (w, g, normaliser, Q offset) one step ahead.  With several waves per sequence only (S0, S1) is
 // combined across waves inside the step loop; every wave's (S0..S3) goes to the workspace and the outputs are formed
 // after the backward pass.
 //
@@ -45,10 +45,17 @@ namespace bcjr {
 #ifndef BCJR_GRAD_BWD_GROUPS
 #define BCJR_GRAD_BWD_GROUPS 2
 #endif
-// How many groups ahead the backward pass issues its tape loads (R~ and Q^ of one group): the tape is the kernel's
-// one stream from HBM, and deeper prefetch keeps more of it in flight.  Must divide the groups per step (4 QPT).
+// How many groups ahead the backward pass issues its tape loads (R~ and Q^ of one group) and its codebook rows (read
+// through L1/L2 at L = 16), each a power of two; at most the groups of a step are used.  Vector-memory loads complete
+// in issue order under one counter, so waiting for a codebook row also waits for every tape load issued before it:
+// the codebook row of a group is issued before that group's tape loads, and a tape load's lead is then the smaller of
+// the tape depth and the codebook depth plus one group.  Measured on the 1024x1024 workload (T = 0.1): tape/codebook
+// depth 1/1 (codebook after the tape) 76.6 ms, 2/1 77.0, 4/2 76.2, 4/4 74.0, 8/4 75.0, 8/8 92.0 (the rings spill).
 #ifndef BCJR_GRAD_TAPE_DEPTH
-#define BCJR_GRAD_TAPE_DEPTH 1
+#define BCJR_GRAD_TAPE_DEPTH 4
+#endif
+#ifndef BCJR_GRAD_CB_DEPTH
+#define BCJR_GRAD_CB_DEPTH 4
 #endif
 constexpr int kGradFwdGroups = BCJR_GRAD_FWD_GROUPS;
 constexpr int kGradBwdGroups = BCJR_GRAD_BWD_GROUPS;
@@ -411,9 +418,11 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         }
         lds_barrier();
 
-        // loads of the next group (forward messages R~, Q^ of this step, codebook row) are issued one group ahead
-        constexpr int TD = BCJR_GRAD_TAPE_DEPTH, NGS = 4 * QPT;   // tape prefetch depth, groups per step
-        static_assert(NGS % TD == 0, "the tape prefetch ring must divide the groups of a step");
+        // loads of later groups (forward messages R~, Q^ of this step, codebook rows) are issued ahead, in rings
+        constexpr int NGS = 4 * QPT;   // groups per step
+        constexpr int TD = BCJR_GRAD_TAPE_DEPTH < NGS ? BCJR_GRAD_TAPE_DEPTH : NGS;   // tape prefetch depth
+        constexpr int CBD = BCJR_GRAD_CB_DEPTH < NGS ? BCJR_GRAD_CB_DEPTH : NGS;      // codebook prefetch depth
+        static_assert(NGS % TD == 0 && NGS % CBD == 0, "the prefetch rings must divide the groups of a step");
         float rt_q[TD], qt_q[TD];   // R~_t and Q^_t of the next TD groups, group gi in slot gi % TD
         // the first TD groups of step tt into the ring
         auto prefetch_row = [&](int tt) {
@@ -424,13 +433,18 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 qt_q[q] = buf_ld_nt(tape, v_grp, q_base + so);
             }
         };
-        float4 cr_n = make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 cr_q[CBD];   // codebook rows of the next CBD groups, group gi in slot gi % CBD
+#pragma unroll
+        for (int q = 0; q < CBD; ++q) cr_q[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         float4 ac_n = make_float4(0.f, 0.f, 0.f, 0.f);   // the next group's accumulator (GC)
         float4 pe_n = make_float4(0.f, 0.f, 0.f, 0.f);   // and its pending contributions (GCM = 2)
         float4 pf_n = make_float4(0.f, 0.f, 0.f, 0.f);
         if (t >= 0) {
             prefetch_row(t);
-            if constexpr (!CB_REG) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
+            if constexpr (!CB_REG) {
+#pragma unroll
+                for (int q = 0; q < CBD; ++q) cr_q[q] = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, q >> 2, q & 3);
+            }
             if constexpr (GC) ac_n = buf_ld4(tape, v_quad, acc_base);
             if constexpr (EXACT) {
                 pe_n = buf_ld4(tape, v_quad, pend_base);
@@ -527,12 +541,18 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     const float qs = qt_q[slot] - EF;   // GC: the small parts of E[F | s] - E[F]
                     float4 cr;
                     if constexpr (CB_REG) cr = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m, a);
-                    else cr = cr_n;
-                    // issue the loads of the group TD ahead (of the next step once past this one's last) and the next
-                    // group's codebook row before this group's math; in checkpoint mode a row past the segment is
-                    // read again once rebuilt
+                    else cr = cr_q[gi % CBD];
+                    // before this group's math, issue the codebook row CBD groups ahead, then the tape loads of the
+                    // group TD ahead (of the next step's groups once past this one's last); in checkpoint mode a row
+                    // past the segment is read again once rebuilt
                     const bool last = (m == QPT - 1) && (a == 3);
                     const int m2 = (a == 3) ? m + 1 : m, a2 = (a + 1) & 3;
+                    if constexpr (!CB_REG) {
+                        const int gc = gi + CBD;
+                        if (gc < NGS) cr_q[gi % CBD] = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, gc >> 2, gc & 3);
+                        else if (t > 0)
+                            cr_q[gi % CBD] = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, (gc - NGS) >> 2, (gc - NGS) & 3);
+                    }
                     {
                         const int gn = gi + TD;
                         if (gn < NGS) {
@@ -545,10 +565,6 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                             rt_q[slot] = buf_ld_nt(tape, v_grp, so2);
                             qt_q[slot] = buf_ld_nt(tape, v_grp, q_base + so2);
                         }
-                    }
-                    if constexpr (!CB_REG) {
-                        if (!last) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, m2, a2);
-                        else if (t > 0) cr_n = cb_row<L, TPS, CB_REG>(cbr, cbs, v_cb, 0, 0);
                     }
                     float4 ac = ac_n, pe = pe_n, pf = pf_n;
                     if constexpr (GC) {
