@@ -119,6 +119,19 @@ __device__ __forceinline__ void st_floats(const float* v, float* lds, int idx, r
     }
 }
 
+// N floats (1, 2 or 4) to LDS at an N-aligned element offset, as one store.
+template <int N>
+__device__ __forceinline__ void lds_st(float* lds, int idx, const float* v) {
+    if constexpr (N == 4) {
+        *reinterpret_cast<float4*>(lds + idx) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(lds + idx) = make_float2(v[0], v[1]);
+    } else {
+        static_assert(N == 1, "1, 2 or 4 floats");
+        lds[idx] = v[0];
+    }
+}
+
 // N floats from the tape at one element offset into LDS (restoring a checkpoint row).
 template <int N>
 __device__ __forceinline__ void ld_to_lds(float* lds, int idx, rsrc_t tape, uint32_t voff, uint32_t soff) {
@@ -206,6 +219,18 @@ __device__ __forceinline__ float vmetric(const float* wt, const float* c, float 
         e = e + ev;
     }
     return e + vin;
+}
+
+// LDS position of message group u.  At k = 3 a thread reads and writes its block's 8 consecutive groups as two 16-byte
+// accesses 32 bytes apart across the lanes, which puts lanes 4 apart on the same banks.  Flipping bit 2 of u in every
+// 32-group row of odd index (bit 5 set) spreads them over distinct banks; a 16-byte access keeps its 4 groups together
+// (they share bit 5), and the lane-contiguous accesses of the other direction stay conflict-free.  It is a
+// permutation inside each 64 groups.  It is applied where the J = 2^(L-2k) blocks number at least 64 (L >= 12), so
+// that j + J a has the bits 2 and 5 of j and the position of j + J a is that of j plus J a.  Other k: the identity.
+template <int K>
+__device__ __forceinline__ int mpos(int u, int J) {
+    if constexpr (K == 3) return J >= 64 ? u ^ ((u >> 3) & 4) : u;
+    else return u;
 }
 
 // Per-thread view of the trellis: which blocks and groups it owns, and its codebook values.
@@ -394,7 +419,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                 for (int ii = 0; ii < TI; ++ii)
                     r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
-                st_floats<TI>(r, msg0, u0, tape, 4u * own.tpos(u0, G), 0u);
+                st_floats<TI>(r, msg0, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), 0u);
             }
         lds_barrier();
 
@@ -407,7 +432,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
-                for (int a = 0; a < P; ++a) rin[m][a] = mc[own.j(m) + J * a];
+                for (int a = 0; a < P; ++a) rin[m][a] = mc[mpos<K>(own.j(m), J) + J * a];
             if (!args.dbl) lds_barrier();   // every input read before any output overwrites it
             float lmax = -3.0e38f;
 #pragma unroll
@@ -458,7 +483,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                         lmax = run_max(lmax, o[ii]);
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(o, mn, u0, tape, 4u * own.tpos(u0, G), row_soff, store);
+                    st_floats<TI>(o, mn, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), row_soff, store);
                 }
             return lmax;
         };
@@ -500,7 +525,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q)
 #pragma unroll
-                    for (int ii = 0; ii < TI; ++ii) part += ex2(mf[own.fgroup(m, q) + ii] - N);
+                    for (int ii = 0; ii < TI; ++ii) part += ex2(mf[mpos<K>(own.fgroup(m, q), J) + ii] - N);
             part = gseq_sum(part, SEG);
             if (WPS > 1 && lane == 0) redsum[n & 1][wv] = part;
             lds_barrier();
@@ -535,7 +560,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q)
 #pragma unroll
-                    for (int ii = 0; ii < TI; ++ii) mi[own.fgroup(m, q) + ii] = 0.f;
+                    for (int ii = 0; ii < TI; ++ii) mi[mpos<K>(own.fgroup(m, q), J) + ii] = 0.f;
         } else {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma; the one finite message left is
             // B_{n-2}(sigma >> k) = theta_{n-1}(sigma)
@@ -554,7 +579,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                         for (int ii = 0; ii < TI; ++ii) {
                             const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
-                            mi[u] = (u == (sig >> K)) ? th : kNeg;
+                            mi[mpos<K>((int)u, J)] = (u == (sig >> K)) ? th : kNeg;
                         }
             }
             if (tau == 0) {
@@ -585,13 +610,13 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
-                for (int q = 0; q < NI; ++q) st_row<TI>(msg0 + own.fgroup(m, q), tape, save_base + 4u * own.fgroup(m, q));
+                for (int q = 0; q < NI; ++q) st_row<TI>(msg0 + mpos<K>(own.fgroup(m, q), J), tape, save_base + 4u * own.fgroup(m, q));
             lds_barrier();   // every share read before the recompute overwrites the buffer
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
                 for (int q = 0; q < NI; ++q)
-                    ld_to_lds<TI>(msg0, own.fgroup(m, q), tape, 4u * own.tpos(own.fgroup(m, q), G), rows.off(t0));
+                    ld_to_lds<TI>(msg0, mpos<K>(own.fgroup(m, q), J), tape, 4u * own.tpos(own.fgroup(m, q), G), rows.off(t0));
             lds_barrier();
             own.fwd_prime(cnx);
             for (int tt = t0; tt < t; ++tt) {
@@ -608,7 +633,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
                 for (int q = 0; q < NI; ++q)
-                    ld_to_lds<TI>(msg0, own.fgroup(m, q), tape, save_base + 4u * own.fgroup(m, q), 0u);
+                    ld_to_lds<TI>(msg0, mpos<K>(own.fgroup(m, q), J), tape, save_base + 4u * own.fgroup(m, q), 0u);
             lds_barrier();
             rq_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
         }
@@ -630,7 +655,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q)
 #pragma unroll
-                    for (int ii = 0; ii < TI; ++ii) bin[m][TI * q + ii] = mc[own.fgroup(m, q) + ii];
+                    for (int ii = 0; ii < TI; ++ii) bin[m][TI * q + ii] = mc[mpos<K>(own.fgroup(m, q), J) + ii];
             if (!args.dbl) lds_barrier();
             D += Nt;
             const float ref = (rz + D) - C_;
@@ -695,7 +720,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     }
                     const float out = (mx - Nb) + lg2(s);
                     lmax = run_max(lmax, out);
-                    mn[vg] = out;   // the lanes of a quad store the same value; at t = 0 nobody reads it
+                    mn[mpos<K>(own.j(m), J) + J * a] = out;   // the lanes of a quad store the same value; at t = 0 nobody reads it
                     pin_order(S0, lmax);
 #pragma unroll
                     for (int v = 0; v < V; ++v) pin_one(S1[v]);
@@ -854,7 +879,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
                         const int u = own.fgroup(m, q) + ii;
-                        lds[z * MB + u] = (!has_sigma || (uint32_t)u == (sig[z] & (uint32_t)(G - 1))) ? 0.f : kInf;
+                        lds[z * MB + mpos<K>(u, J)] = (!has_sigma || (uint32_t)u == (sig[z] & (uint32_t)(G - 1))) ? 0.f : kInf;
                     }
         lds_barrier();
 
@@ -871,7 +896,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 #pragma unroll
                 for (int m = 0; m < BPT; ++m)
 #pragma unroll
-                    for (int a = 0; a < P; ++a) vin[z][m][a] = lds[z * MB + oc + own.j(m) + J * a];
+                    for (int a = 0; a < P; ++a) vin[z][m][a] = lds[z * MB + oc + mpos<K>(own.j(m), J) + J * a];
             if (!args.dbl) lds_barrier();
             uint32_t word[NSQ];
 #pragma unroll
@@ -905,12 +930,12 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
                         if constexpr (NSQ > 1) GEN_SCHED_BARRIER();   // one row at a time: bounds the live values
                     }
 #pragma unroll
-                    for (int z = 0; z < NSQ; ++z)
+                    for (int z = 0; z < NSQ; ++z) {
 #pragma unroll
-                        for (int ii = 0; ii < TI; ++ii) {
-                            word[z] |= arg[z][ii] << ((m * I + TI * q + ii) * K);
-                            lds[z * MB + on + own.fgroup(m, q) + ii] = best[z][ii];
-                        }
+                        for (int ii = 0; ii < TI; ++ii) word[z] |= arg[z][ii] << ((m * I + TI * q + ii) * K);
+                        // the tile's metrics as one 16-byte (8-byte at k = 1) store: the position is TI-aligned
+                        lds_st<TI>(lds + z * MB + on, mpos<K>(own.fgroup(m, q), J), best[z]);
+                    }
                     GEN_SCHED_BARRIER();
                 }
 #pragma unroll
@@ -942,7 +967,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
                 for (int a = 0; a < P; ++a) {
                     float vl[NSQ];
 #pragma unroll
-                    for (int z = 0; z < NSQ; ++z) vl[z] = lds[z * MB + ol + own.j(m) + J * a];
+                    for (int z = 0; z < NSQ; ++z) vl[z] = lds[z * MB + ol + mpos<K>(own.j(m), J) + J * a];
 #pragma unroll
                     for (int q = 0; q < NI; ++q) {
                         float c[ROW];
@@ -974,7 +999,7 @@ __global__ void __launch_bounds__(1024) gen_viterbi_kernel(GenArgs args) {
 #pragma unroll
             for (int z = 0; z < NSQ; ++z) {
                 bidx[z] = sig[z];
-                best[z] = vmetric<V>(wl[z], args.cb + (size_t)sig[z] * V, lds[z * MB + ol + (sig[z] >> K)]);
+                best[z] = vmetric<V>(wl[z], args.cb + (size_t)sig[z] * V, lds[z * MB + ol + mpos<K>((int)(sig[z] >> K), J)]);
             }
         }
         if (tau == 0 && args.cost) {
@@ -1145,8 +1170,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     r[ii] = (!has_sigma || (uint32_t)(u0 + ii) == (sig & (uint32_t)(G - 1))) ? 0.f : kNeg;
                     z[ii] = 0.f;
                 }
-                st_floats<TI>(r, mr, u0, tape, 4u * own.tpos(u0, G), 0u);
-                st_floats<TI>(z, mq, u0, tape, 4u * own.tpos(u0, G), q_base);
+                st_floats<TI>(r, mr, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), 0u);
+                st_floats<TI>(z, mq, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), q_base);
             }
         bar();
 
@@ -1160,8 +1185,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
             for (int m = 0; m < BPT; ++m)
 #pragma unroll
                 for (int a = 0; a < P; ++a) {
-                    rin[m][a] = mr[own.j(m) + J * a];
-                    qin[m][a] = mq[own.j(m) + J * a] - kqt;
+                    rin[m][a] = mr[mpos<K>(own.j(m), J) + J * a];
+                    qin[m][a] = mq[mpos<K>(own.j(m), J) + J * a] - kqt;
                 }
             bar();   // every input read before any output overwrites it
             float wt[V], gt[V];
@@ -1230,8 +1255,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                         lq = up ? qo[ii] : lq;
                     }
                     const int u0 = own.fgroup(m, q);
-                    st_floats<TI>(ro, mr, u0, tape, 4u * own.tpos(u0, G), row_soff, store);
-                    st_floats<TI>(qo, mq, u0, tape, 4u * own.tpos(u0, G), q_base + row_soff, store);
+                    st_floats<TI>(ro, mr, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), row_soff, store);
+                    st_floats<TI>(qo, mq, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), q_base + row_soff, store);
                 }
         };
 
@@ -1280,9 +1305,9 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
                         const int u = own.fgroup(m, q) + ii;
-                        const float p = ex2(mr[u] - N);
+                        const float p = ex2(mr[mpos<K>(u, J)] - N);
                         z0 += p;
-                        z1 = fmaf(p, mq[u], z1);
+                        z1 = fmaf(p, mq[mpos<K>(u, J)], z1);
                     }
             z0 = gseq_sum(z0, SEG);
             z1 = gseq_sum(z1, SEG);
@@ -1338,8 +1363,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
                         const int u = own.fgroup(m, q) + ii;
-                        mr[u] = 0.f;
-                        mq[u] = 0.f;
+                        mr[mpos<K>(u, J)] = 0.f;
+                        mq[mpos<K>(u, J)] = 0.f;
                     }
         } else {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma (grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
@@ -1359,8 +1384,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
                         const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
-                        mr[u] = (u == (sig >> K)) ? th : kNeg;
-                        mq[u] = (u == (sig >> K)) ? pz : 0.f;
+                        mr[mpos<K>((int)u, J)] = (u == (sig >> K)) ? th : kNeg;
+                        mq[mpos<K>((int)u, J)] = (u == (sig >> K)) ? pz : 0.f;
                     }
             if (tau == 0) {
 #pragma unroll
@@ -1424,8 +1449,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q) {
                     const int u0 = own.fgroup(m, q);
-                    st_row<TI>(mr + u0, tape, save_base + 4u * u0);
-                    st_row<TI>(mq + u0, tape, save_base + row_bytes + 4u * u0);
+                    st_row<TI>(mr + mpos<K>(u0, J), tape, save_base + 4u * u0);
+                    st_row<TI>(mq + mpos<K>(u0, J), tape, save_base + row_bytes + 4u * u0);
                 }
             bar();   // every share read before the recompute overwrites the buffers
 #pragma unroll
@@ -1433,8 +1458,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q) {
                     const int u0 = own.fgroup(m, q);
-                    ld_to_lds<TI>(mr, u0, tape, 4u * own.tpos(u0, G), rows.off(t0));
-                    ld_to_lds<TI>(mq, u0, tape, 4u * own.tpos(u0, G), q_base + rows.off(t0));
+                    ld_to_lds<TI>(mr, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), rows.off(t0));
+                    ld_to_lds<TI>(mq, mpos<K>(u0, J), tape, 4u * own.tpos(u0, G), q_base + rows.off(t0));
                 }
             bar();
             own.fwd_prime(cnx);
@@ -1452,8 +1477,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                 for (int q = 0; q < NI; ++q) {
                     const int u0 = own.fgroup(m, q);
-                    ld_to_lds<TI>(mr, u0, tape, save_base + 4u * u0, 0u);
-                    ld_to_lds<TI>(mq, u0, tape, save_base + row_bytes + 4u * u0, 0u);
+                    ld_to_lds<TI>(mr, mpos<K>(u0, J), tape, save_base + 4u * u0, 0u);
+                    ld_to_lds<TI>(mq, mpos<K>(u0, J), tape, save_base + row_bytes + 4u * u0, 0u);
                 }
             bar();
             rt_nx = buf_ld_nt(tape, grp_voff(0, 0), rows.off(t) + grp_soff(0, 0));
@@ -1467,7 +1492,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 for (int q = 0; q < NI; ++q)
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
-                        const int u = own.fgroup(m, q) + ii;
+                        const int u = mpos<K>(own.fgroup(m, q), J) + ii;
                         bin[m][TI * q + ii] = mr[u];
                         pin[m][TI * q + ii] = mq[u] - kb;
                     }
@@ -1636,8 +1661,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                     const float out = (mx - Nb) + lg2(s);
                     lmax = run_max(lmax, out);
                     // the lanes of a quad store the same values; at t = 0 nobody reads them
-                    mr[vg] = out;
-                    mq[vg] = sez * rcp(s);
+                    mr[mpos<K>(own.j(m), J) + J * a] = out;
+                    mq[mpos<K>(own.j(m), J) + J * a] = sez * rcp(s);
                     pin_order(S0, S2, lmax);
 #pragma unroll
                     for (int v = 0; v < V; ++v) pin_order(S1[v], S3[v]);
