@@ -16,6 +16,13 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: takes more than a few seconds on the CPU")
 
 
+def pytest_terminal_summary(terminalreporter):
+    parity = sys.modules.get("parity")
+    if parity is not None and sum(parity.REF_STATS.values()):
+        terminalreporter.write_line(f"oracle references: {parity.REF_STATS['stored']} stored, "
+                                    f"{parity.REF_STATS['computed']} computed on the spot")
+
+
 @pytest.fixture(scope="session")
 def oracle_mod():
     import oracle

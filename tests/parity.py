@@ -36,6 +36,10 @@ references (mixtures over every boundary state) use the random moves only.
 """
 from __future__ import annotations
 
+import functools
+import hashlib
+import inspect
+import json
 import os
 
 import numpy as np
@@ -298,9 +302,120 @@ def _k_grad_norm_rows(K, ref, floor):
     return np.linalg.norm(K, axis=-1) / np.maximum(np.linalg.norm(ref, axis=-1), floor * np.sqrt(ref.shape[-1]))
 
 
+# ---------------------------------------------------------------------------------------------------------------
+# stored references: the answers and kappas above, for the GPU tests' own inputs, computed ahead of time by
+# tests/golden/make_ref_cache.py (the oracle alone, on the CPU).  An entry is found by a digest of everything the
+# computation reads: the function, every input array's bytes, the scalar arguments, the oracle's source and
+# REF_VERSION.  A test whose inputs have no entry computes its reference on the spot, as before.
+
+REF_CACHE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "refcache")
+REF_VERSION = 1   # raised whenever the reference computations here change what they return
+_ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "oracle.c")
+
+
+@functools.lru_cache(maxsize=1)
+def _oracle_digest() -> str:
+    with open(_ORACLE_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def ref_key(name: str, arguments: dict) -> str:
+    """Digest of one reference computation: name, oracle source, REF_VERSION and every argument but the oracle (by
+    name, defaults filled in, so positional and keyword calls agree)."""
+    h = hashlib.sha256(f"{name}|{REF_VERSION}|{_oracle_digest()}".encode())
+
+    def feed(tag, v):
+        h.update(tag.encode())
+        if v is None:
+            h.update(b"|None")
+        elif isinstance(v, np.ndarray):
+            a = np.ascontiguousarray(v)
+            h.update(f"|{a.dtype.str}|{a.shape}|".encode())
+            h.update(a.tobytes())
+        elif isinstance(v, (bool, int, float, np.integer, np.floating)):
+            h.update(f"|{type(v).__name__}|{v!r}".encode())
+        else:
+            raise TypeError(f"reference argument {tag} of type {type(v).__name__} has no digest")
+
+    for key in sorted(arguments):
+        feed(key, arguments[key])
+    return h.hexdigest()[:32]
+
+
+def _flatten(x, leaves):
+    if isinstance(x, (tuple, list)):
+        return [type(x).__name__, [_flatten(v, leaves) for v in x]]
+    leaves.append(np.asarray(x))
+    return len(leaves) - 1
+
+
+def _unflatten(tree, leaves):
+    if isinstance(tree, list):
+        items = [_unflatten(v, leaves) for v in tree[1]]
+        return tuple(items) if tree[0] == "tuple" else items
+    a = leaves[tree]
+    return a[()] if a.ndim == 0 else a
+
+
+def store_ref(key: str, value) -> None:
+    os.makedirs(REF_CACHE_DIR, exist_ok=True)
+    leaves = []
+    tree = _flatten(value, leaves)
+    tmp = os.path.join(REF_CACHE_DIR, key + ".tmp.npz")
+    np.savez_compressed(tmp, __tree__=np.array(json.dumps(tree)), **{f"l{i}": a for i, a in enumerate(leaves)})
+    os.replace(tmp, os.path.join(REF_CACHE_DIR, key + ".npz"))
+
+
+def load_ref(key: str):
+    path = os.path.join(REF_CACHE_DIR, key + ".npz")
+    if not os.path.exists(path):
+        return None
+    with np.load(path, allow_pickle=False) as z:
+        tree = json.loads(str(z["__tree__"]))
+        leaves = [z[f"l{i}"] for i in range(len(z.files) - 1)]
+    return _unflatten(tree, leaves)
+
+
+REF_STATS = {"stored": 0, "computed": 0}   # how the session's references were answered
+
+
+def stored_reference(fn):
+    """fn(oracle, ...) answered from the stored references when its inputs have an entry (with
+    PARITY_REF_CACHE_WRITE set, computed and stored when they do not)."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(oracle, *args, **kwargs):
+        bound = sig.bind(oracle, *args, **kwargs)
+        bound.apply_defaults()
+        arguments = {name: v for name, v in bound.arguments.items() if name != "oracle"}
+        key = ref_key(fn.__name__, arguments)
+        hit = load_ref(key)
+        if hit is not None:
+            REF_STATS["stored"] += 1
+            return hit
+        REF_STATS["computed"] += 1
+        out = fn(oracle, *args, **kwargs)
+        if os.environ.get("PARITY_REF_CACHE_WRITE"):
+            store_ref(key, out)
+        return out
+
+    wrapper.uncached = fn
+    return wrapper
+
+
 def soft_reference(oracle, w, c, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, rows=None, first_order=True):
     """(w_soft, ln Z) from the oracle at the float32 T and their one-ulp conditioning per sequence (kappa_w_soft,
     kappa_log_z): the larger of the first-order worst case (w_soft only) and the random moves."""
+    s = sigma if (sigma is None or rows is None) else sigma[rows]
+    ws, lz = oracle.soft(w if rows is None else w[rows], c, L, k, t32(T), sigma=s)
+    k_ws, k_lz = soft_kappas(oracle, w, c, L, k, T, sigma, trials, seed, rows, first_order)
+    return ws, lz, k_ws, k_lz
+
+
+@stored_reference
+def soft_kappas(oracle, w, c, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, rows=None, first_order=True):
+    """The kappas of soft_reference."""
     T = t32(T)
     s = sigma if (sigma is None or rows is None) else sigma[rows]
     (ws, lz), kap = one_ulp_conditioning(lambda w_, c_, g_, T_: oracle.soft(w_, c_, L, k, T_, sigma=s), w, c,
@@ -309,7 +424,7 @@ def soft_reference(oracle, w, c, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=
     if first_order and _fo_affordable(w if rows is None else w[rows], L, k):
         K = soft_first_order(oracle, w if rows is None else w[rows], c, L, k, T, sigma=s)
         k_ws = np.maximum(k_ws, _k_rel_rows(K, ws))
-    return ws, lz, k_ws, kap[1]
+    return k_ws, kap[1]
 
 
 def grad_reference(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, rows=None, floor=None,
@@ -317,6 +432,16 @@ def grad_reference(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, se
     """(grad, w_soft) from the oracle at the float32 T and their one-ulp conditioning per sequence: (kappa_grad
     elementwise, kappa_grad normwise, kappa_w_soft).  ``floor`` fixes the gradient measures' floor (that of the whole
     batch when only some rows are computed); by default it is the computed rows' own."""
+    s = sigma if (sigma is None or rows is None) else sigma[rows]
+    gr, ws = oracle.grad(w if rows is None else w[rows], c, g if rows is None else g[rows], L, k, t32(T), sigma=s)
+    k_g, k_n, k_ws = grad_kappas(oracle, w, c, g, L, k, T, sigma, trials, seed, rows, floor, first_order)
+    return gr, ws, k_g, k_n, k_ws
+
+
+@stored_reference
+def grad_kappas(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, rows=None, floor=None,
+                first_order=True):
+    """The kappas of grad_reference."""
     T = t32(T)
     s = sigma if (sigma is None or rows is None) else sigma[rows]
     gs = g if rows is None else g[rows]
@@ -338,12 +463,19 @@ def grad_reference(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, se
         k_g = np.maximum(k_g, _k_grad_rows(Kg, gr, f))
         k_n = np.maximum(k_n, _k_grad_norm_rows(Kg, gr, f))
         k_ws = np.maximum(k_ws, _k_rel_rows(Kw, ws))
-    return gr, ws, k_g, k_n, k_ws
+    return k_g, k_n, k_ws
 
 
 def codebook_grad_reference(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, first_order=True):
     """(dL/dc, dL/dw, w_soft) from the oracle at the float32 T and the one-ulp conditioning of dL/dc (normwise, of the
     max; one value each) and of dL/dw (elementwise, normwise) and w_soft (per sequence)."""
+    ref = oracle.grad_codebook(w, c, g, L, k, t32(T), sigma=sigma)
+    return ref, codebook_grad_kappas(oracle, w, c, g, L, k, T, sigma, trials, seed, first_order)
+
+
+@stored_reference
+def codebook_grad_kappas(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_TRIALS, seed=0, first_order=True):
+    """The kappas of codebook_grad_reference."""
     T = t32(T)
     (gc, gw, ws), kap = one_ulp_conditioning(
         lambda w_, c_, g_, T_: oracle.grad_codebook(w_, c_, g_, L, k, T_, sigma=sigma), w, c,
@@ -358,7 +490,7 @@ def codebook_grad_reference(oracle, w, c, g, L, k, T, sigma=None, trials=KAPPA_T
         kap[2] = np.maximum(kap[2], _k_grad_rows(Kg, gw, f))
         kap[3] = np.maximum(kap[3], _k_grad_norm_rows(Kg, gw, f))
         kap[4] = np.maximum(kap[4], _k_rel_rows(Kw, ws))
-    return (gc, gw, ws), kap
+    return kap
 
 
 def check(name, err, kappa) -> bool:
@@ -420,9 +552,17 @@ def codebook_grad_ok(oracle, gc, gw, ws, w, c, g, L, k, T, sigma=None, label="")
     return ok
 
 
-def tail_biting_ok(oracle, ws, lz, gr, ws2, w, c, g, L, k, T, label="") -> bool:
-    """The soft codeword and ln Z under the tail-biting measure, and that measure's gradient with its pass's soft
-    codeword, against the oracle's mixture of sigma-mode passes, within their conditioning bars."""
+def tail_biting_reference(oracle, w, c, g, L, k, T):
+    """The oracle's soft codeword, ln Z, gradient and the gradient pass's soft codeword under the tail-biting measure
+    at the float32 T, with their random one-ulp kappas."""
+    rws, rlz = oracle.soft_tail_biting(w, c, L, k, t32(T))
+    rgr, rws2 = oracle.grad_tail_biting(w, c, g, L, k, t32(T))
+    return (rws, rlz, rgr, rws2), tail_biting_kappas(oracle, w, c, g, L, k, T)
+
+
+@stored_reference
+def tail_biting_kappas(oracle, w, c, g, L, k, T):
+    """The kappas of tail_biting_reference."""
     T = t32(T)
     (rws, rlz), (k_ws, k_lz) = one_ulp_conditioning(
         lambda w_, c_, g_, T_: oracle.soft_tail_biting(w_, c_, L, k, T_), w, c, [(0, rel_rows), (1, lz_rows)], T=T)
@@ -430,6 +570,14 @@ def tail_biting_ok(oracle, ws, lz, gr, ws2, w, c, g, L, k, T, label="") -> bool:
         lambda w_, c_, g_, T_: oracle.grad_tail_biting(w_, c_, g_, L, k, T_), w, c,
         [(0, lambda x, r: grad_rows(x, r, g, c, T)), (0, lambda x, r: grad_norm_rows(x, r, g, c, T)),
          (1, rel_rows)], g=g, T=T)
+    return k_ws, k_lz, k_g, k_n, k_ws2
+
+
+def tail_biting_ok(oracle, ws, lz, gr, ws2, w, c, g, L, k, T, label="") -> bool:
+    """The soft codeword and ln Z under the tail-biting measure, and that measure's gradient with its pass's soft
+    codeword, against the oracle's mixture of sigma-mode passes, within their conditioning bars."""
+    (rws, rlz, rgr, rws2), (k_ws, k_lz, k_g, k_n, k_ws2) = tail_biting_reference(oracle, w, c, g, L, k, T)
+    T = t32(T)
     ok = check(f"{label}w_soft", rel_rows(_np(ws), rws), k_ws)
     ok &= check(f"{label}ln Z", lz_rows(_np(lz), rlz), k_lz)
     ok &= check(f"{label}grad", grad_rows(_np(gr), rgr, g, c, T), k_g)

@@ -19,10 +19,11 @@ import pytest
 import torch
 
 import differentiable_bcjr_amd as dba
+import cases
 import parity
 import workloads
 from differentiable_bcjr_amd import abi
-from test_gpu_general_trellis import _sigma_n, _vin
+from cases import sigma_n as _sigma_n, vin as _vin
 from test_gpu_parity import _golden_grad, _golden_soft, _t
 
 pytestmark = pytest.mark.gpu
@@ -39,8 +40,7 @@ def _soft(w, c, L, k, T, s, dev, checkpoint):
 
 
 # (L, k, V, B, n)
-CASES = [(8, 2, 1, 5, 37), (8, 2, 1, 4, 40), (9, 3, 2, 3, 50), (6, 3, 1, 4, 1), (8, 1, 2, 4, 2), (12, 1, 1, 3, 100),
-         (13, 4, 1, 2, 26), (16, 2, 1, 2, 40), (16, 3, 1, 2, 33), (16, 4, 2, 2, 20), (16, 1, 1, 1, 17)]
+CASES = cases.CHECKPOINT
 
 
 @pytest.mark.parametrize("L,k,V,B,n", CASES, ids=[f"L{c[0]}k{c[1]}V{c[2]}B{c[3]}n{c[4]}" for c in CASES])
@@ -64,7 +64,7 @@ def test_checkpoint_mode_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     assert ok
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [(8, 3, 2, 4300, 9), (16, 2, 1, 270, 5)])
+@pytest.mark.parametrize("L,k,V,B,n", cases.CHECKPOINT_SOFT_SEVERAL)
 def test_checkpoint_mode_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n):
     w, c, _, _ = _vin(L, V, B, n, 6200 + L)
     T = 0.1
@@ -150,7 +150,7 @@ def test_codebook_grad_checkpoint_mode_matches_oracle(oracle_mod, dev, L, k, V, 
     assert ok
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [(8, 3, 2, 4300, 9), (16, 2, 1, 270, 5), (8, 1, 1, 4200, 10)])
+@pytest.mark.parametrize("L,k,V,B,n", cases.CHECKPOINT_GRAD_SEVERAL)
 def test_grad_checkpoint_mode_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n):
     """Each workgroup's slot, its checkpoint rows, offsets and saved messages, reused by the next sequence."""
     w, c, g, _ = _vin(L, V, B, n, 6600 + L + k)

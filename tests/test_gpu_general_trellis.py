@@ -27,6 +27,7 @@ import torch
 
 import differentiable_bcjr_amd as dba
 import parity
+import cases
 import workloads
 from parity import norm_err
 from test_gpu_parity import _t
@@ -40,31 +41,10 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _vin(L, V, B, n, seed, sigma=False):
-    """Codebook ([2^L] for V = 1, else [2^L, V], unit variance), weights and upstream gradient [B, n V], sigma [B]."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    c = rng.standard_normal((1 << L, V))
-    c = (c / c.std()).astype(np.float32)
-    if V == 1:
-        c = c[:, 0].copy()
-    w = rng.standard_normal((B, n * V)).astype(np.float32)
-    g = rng.standard_normal((B, n * V)).astype(np.float32)
-    s = rng.integers(0, 1 << L, size=B).astype(np.int32) if sigma else None
-    return w, c, g, s
-
-
-# (L, k, V, B, n steps)
-CASES = [(4, 1, 1, 16, 6), (4, 1, 2, 7, 5), (5, 1, 1, 5, 8), (5, 2, 2, 9, 9), (6, 3, 1, 5, 4), (6, 3, 2, 3, 7),
-         (7, 3, 1, 4, 9), (8, 1, 1, 6, 33), (8, 4, 1, 4, 5), (8, 4, 2, 3, 6), (9, 1, 2, 5, 17), (9, 3, 2, 4, 12),
-         (10, 4, 1, 3, 10), (11, 1, 1, 2, 20), (12, 3, 1, 2, 16), (12, 4, 2, 2, 9), (13, 1, 2, 2, 7), (14, 3, 2, 2, 6),
-         (15, 1, 1, 2, 6), (16, 1, 1, 2, 4), (16, 1, 2, 1, 4), (16, 2, 2, 2, 5), (16, 3, 1, 2, 5), (16, 3, 2, 2, 4),
-         (16, 4, 1, 2, 4), (16, 4, 2, 2, 5)]
-IDS = [f"L{L}k{k}V{V}B{B}n{n}" for L, k, V, B, n in CASES]
-
-
-def _sigma_n(L, k, n):
-    """Enough steps for every sigma to be reachable: the constraint needs at least L/k steps."""
-    return max(n, -(-L // k) + 1)
+_vin = cases.vin
+_sigma_n = cases.sigma_n
+CASES = cases.GENERAL
+IDS = cases.ids(CASES)
 
 
 @pytest.mark.parametrize("L,k,V,B,n", CASES, ids=IDS)
@@ -128,8 +108,7 @@ def test_gradient_k1_at_L16_keeps_q_in_the_workspace(oracle_mod, dev):
 # ------------------------------------------------------------------------ batches larger than the persistent grid
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [(8, 1, 2, 4600, 5), (9, 3, 1, 4200, 4), (16, 3, 1, 260, 3),
-                                       (16, 4, 2, 258, 3), (16, 1, 1, 260, 3), (16, 1, 2, 258, 3)])
+@pytest.mark.parametrize("L,k,V,B,n", cases.GENERAL_SEVERAL)
 @pytest.mark.parametrize("ck", [False, True], ids=["full-tape", "checkpoint"])
 def test_several_sequences_per_workgroup(oracle_mod, dev, L, k, V, B, n, ck):
     """More sequences than the grid has workgroups (4096 at L <= 11, 256 at L = 16): every workgroup reuses its slot
@@ -357,8 +336,7 @@ def test_general_trellis_random_configuration(oracle_mod, dev, i, L, k, V, B, n,
     np.testing.assert_array_equal(cost.view(np.uint32), rcost.view(np.uint32))
 
 
-@pytest.mark.parametrize("L,k,V,B,n", [(9, 3, 2, 4200, 3), (8, 1, 1, 4400, 4), (16, 4, 2, 300, 2),
-                                       (16, 1, 1, 260, 3), (16, 1, 2, 258, 3)])
+@pytest.mark.parametrize("L,k,V,B,n", cases.GENERAL_GC_SEVERAL)
 @pytest.mark.parametrize("ck", [False, True], ids=["full-tape", "checkpoint"])
 def test_codebook_grad_several_sequences_per_slot(oracle_mod, dev, L, k, V, B, n, ck):
     """More sequences than the grid has workgroups: each slot's accumulator sums several sequences before the
@@ -372,7 +350,7 @@ def test_codebook_grad_several_sequences_per_slot(oracle_mod, dev, L, k, V, B, n
     assert parity.codebook_grad_ok(oracle_mod, gc, None, None, w, c, g, L, k, T)
 
 
-@pytest.mark.parametrize("L,k,V", [(10, 3, 2), (8, 1, 1), (12, 4, 1)])
+@pytest.mark.parametrize("L,k,V", cases.GENERAL_LONGEST)
 def test_longest_sequences(oracle_mod, dev, L, k, V):
     """n = 4096 steps, the largest the boundary accepts (the workspace offsets of the longest tapes)."""
     n, B, T = 4096, 2, 0.3

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 import torch
 
+import cases
 import differentiable_bcjr_amd as dba
 import parity
 import workloads
@@ -30,14 +31,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _inputs(L, B, n, seed, sigma=False):
-    rng = np.random.Generator(np.random.PCG64(seed))
-    c = rng.standard_normal(1 << L)
-    c = (c / c.std()).astype(np.float32)
-    w = rng.standard_normal((B, n)).astype(np.float32)
-    g = rng.standard_normal((B, n)).astype(np.float32)
-    s = rng.integers(0, 1 << L, size=B).astype(np.int32) if sigma else None
-    return w, c, g, s
+_inputs = cases.inputs
 
 
 def _t(a, dev):
@@ -267,12 +261,7 @@ def test_longest_sequences(oracle_mod, dev, sigma):
     np.testing.assert_array_equal(cost.cpu().numpy().view(np.uint32), rcost.view(np.uint32))
 
 
-@pytest.mark.parametrize("L,B,n,rows", [
-    (16, 1, 64, [0]),                    # one sequence on the 2^16-state trellis
-    (16, 260, 8, [0, 3, 255, 256, 259]),  # blocks 0..3 take a second sequence (grid = 256)
-    (8, 8200, 4, [0, 8191, 8192, 8199]),  # 4 sequences per block, 2048 blocks: rows past 8191 come back round
-    (4, 65, 5, [0, 63, 64]),              # 64 sequences per block: the second block has one active sequence
-])
+@pytest.mark.parametrize("L,B,n,rows", cases.BATCH_EDGES)
 def test_batch_edges(oracle_mod, dev, L, B, n, rows):
     T = 0.1
     w, c, g, _ = _inputs(L, B, n, 900 + L)

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import cases
 import differentiable_bcjr_amd as dba
 import workloads
 from test_gpu_parity import _inputs, _t
@@ -106,7 +107,7 @@ def test_tail_biting_random_configuration(oracle_mod, dev, i, mode, L, B, n):
 # ---------------------------------------------------------------- soft codeword and gradient under the measure
 # Bars: max(1e-5, kappa) per quantity, kappa its one-ulp conditioning under the measure (tests/parity.py).
 
-MEASURE = [(4, 16, 6), (4, 37, 5), (5, 9, 1), (6, 5, 2), (6, 7, 33), (8, 16, 64), (9, 5, 17), (10, 3, 40)]
+MEASURE = cases.TAIL_BITING_MEASURE
 
 
 @pytest.mark.parametrize("L,B,n", MEASURE)

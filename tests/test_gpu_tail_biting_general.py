@@ -9,9 +9,10 @@ import numpy as np
 import pytest
 import torch
 
+import cases
 import differentiable_bcjr_amd as dba
 import parity
-from test_gpu_general_trellis import _vin
+from cases import vin as _vin
 from test_gpu_parity import _t
 
 pytestmark = pytest.mark.gpu
@@ -100,8 +101,7 @@ def test_general_tail_biting_random_configuration(oracle_mod, dev, i, mode, L, k
 
 # ---------------------------------------------------------------- soft codeword and gradient under the measure
 
-MEASURE = [(4, 1, 1, 9, 6), (4, 1, 2, 5, 5), (6, 3, 1, 5, 2), (6, 3, 2, 4, 9), (8, 4, 1, 3, 2), (8, 4, 2, 3, 12),
-           (8, 2, 2, 4, 10), (9, 1, 2, 2, 13), (10, 3, 1, 2, 24), (10, 4, 2, 2, 16)]
+MEASURE = cases.TAIL_BITING_MEASURE_GENERAL
 
 
 @pytest.mark.parametrize("L,k,V,B,n", MEASURE, ids=_ids(MEASURE))
