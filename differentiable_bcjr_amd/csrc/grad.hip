@@ -133,17 +133,47 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             }
     }
 
-    // tape of this block's sequences: slot sq at sq * slot_bytes; the R~ rows and the Q^ rows (TapeRows each), then
-    // per step the normaliser N_t and the offset K_{t-1} of Q^_t (true Q_t = Q^_t + K_{t-1})
+    // tape of this block's sequences: slot sq at sq * slot_bytes; the R~ rows and the Q^ rows (TapeRows each; with
+    // the codebook gradient's full tape, one row of (R~, Q^) pairs per step instead), then per step the normaliser
+    // N_t and the offset K_{t-1} of Q^_t (true Q_t = Q^_t + K_{t-1})
     const uint32_t slot_bytes = (uint32_t)args.slot_bytes;
     const rsrc_t tape = make_rsrc(args.ws + (size_t)blockIdx.x * SPB * args.slot_bytes, SPB * slot_bytes);
     const uint32_t v_quad = sq * slot_bytes + 16u * tau;
     const uint32_t v_grp = sq * slot_bytes + 4u * tau;
     const int ck = CK ? args.ckpt : 0;
-    constexpr uint32_t row_bytes = G * 4u;
+    // The codebook gradient's full tape holds (R~, Q^) pairs, group u's two messages side by side, so its backward
+    // reads both with one 8-byte load next to its accumulator traffic (measured 2-3% faster there, while in the
+    // weights-only gradient the forward's extra register moves for the interleaved stores cost more than the loads
+    // save).  Otherwise the R~ rows and the Q^ rows are two tapes, R~ first.  Both layouts span the same bytes.
+    constexpr bool PAIR = GC && !CK;
+    constexpr uint32_t row_bytes = G * (PAIR ? 8u : 4u);
     const TapeRows rows{ck, n, row_bytes, ck ? (uint32_t)(n / ck + 1) * row_bytes : 0u};
-    const uint32_t q_base = (uint32_t)align256(TapeRows::rows(ck, n) * row_bytes);
+    const uint32_t q_base = (uint32_t)align256(TapeRows::rows(ck, n) * G * 4u);
     const uint32_t nrm_base = 2u * q_base;
+    const uint32_t v_pair = sq * slot_bytes + 32u * tau;   // pair rows: the 4 pairs of groups 4j..4j+3
+    const uint32_t v_grp2 = sq * slot_bytes + 8u * tau;    // pair rows: the pair of group j + Q a
+    // stores the forward messages of quad j (groups 4j..4j+3) into the tape row at roff
+    auto store_quad = [&](float4 r, float4 q, uint32_t roff, int m) {
+        if constexpr (PAIR) {
+            buf_st4_nt(make_float4(r.x, q.x, r.y, q.y), tape, v_pair, roff + 32u * TPS * m);
+            buf_st4_nt(make_float4(r.z, q.z, r.w, q.w), tape, v_pair, roff + 32u * TPS * m + 16u);
+        } else {
+            buf_st4_nt(r, tape, v_quad, roff + 16u * TPS * m);
+            buf_st4_nt(q, tape, v_quad, q_base + roff + 16u * TPS * m);
+        }
+    };
+    // R~_t and Q^_t of group (m, a) of this thread from the tape row at roff
+    auto load_group = [&](float& r, float& q, uint32_t roff, int m, int a) {
+        if constexpr (PAIR) {
+            const float2 v = buf_ld2_nt(tape, v_grp2, roff + 8u * (TPS * m + Q * a));
+            r = v.x;
+            q = v.y;
+        } else {
+            const uint32_t so = roff + 4u * (TPS * m + Q * a);
+            r = buf_ld_nt(tape, v_grp, so);
+            q = buf_ld_nt(tape, v_grp, q_base + so);
+        }
+    };
     const uint32_t kq_base = nrm_base + (uint32_t)align256((size_t)n * 4);
     // with several waves per sequence, each wave's (S0, S1, S2, S3) of every step goes here and the outputs are
     // formed after the backward pass; only (S0, S1) is reduced across waves inside the loop (for the P offset)
@@ -197,8 +227,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4*>(mr + 4 * j) = r;
             *reinterpret_cast<float4*>(mq + 4 * j) = z;
-            buf_st4_nt(r, tape, v_quad, 16u * TPS * m);
-            buf_st4_nt(z, tape, v_quad, q_base + 16u * TPS * m);
+            store_quad(r, z, 0u, m);
         }
         lds_barrier();
 
@@ -266,10 +295,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 const float4 q4 = make_float4(qo[0], qo[1], qo[2], qo[3]);
                 *reinterpret_cast<float4*>(mr + 4 * j) = r4;
                 *reinterpret_cast<float4*>(mq + 4 * j) = q4;
-                if (store) {
-                    buf_st4_nt(r4, tape, v_quad, roff + 16u * TPS * m);
-                    buf_st4_nt(q4, tape, v_quad, q_base + roff + 16u * TPS * m);
-                }
+                if (store) store_quad(r4, q4, roff, m);
             }
         };
         auto prime_fc = [&]() {
@@ -358,8 +384,9 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
             // R~_{n-1}, Q_{n-1} are on the tape (the last step overwrote LDS), written by other threads
             __syncthreads();
             const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
-            const float r = buf_ld_nt(tape, sq * slot_bytes, rows.off(n - 1) + 4u * (sig >> 2));
-            const float q = buf_ld_nt(tape, sq * slot_bytes, q_base + rows.off(n - 1) + 4u * (sig >> 2));
+            const float r = buf_ld_nt(tape, sq * slot_bytes, rows.off(n - 1) + (PAIR ? 8u : 4u) * (sig >> 2));
+            const float q = PAIR ? buf_ld_nt(tape, sq * slot_bytes, rows.off(n - 1) + 8u * (sig >> 2) + 4u)
+                                      : buf_ld_nt(tape, sq * slot_bytes, q_base + rows.off(n - 1) + 4u * (sig >> 2));
             rz = (r < 0.5f * kNeg) ? kNeg : fmaf(-d, d, r) - N_last;
             rzr = (r < 0.5f * kNeg) ? (RT)kNeg : (RT)fmaf(-d, d, r) - (RT)N_last;
             EF = fmaf(gb[n - 1] * inv_scale, d, q);   // Q^_{n-1} carries the offset K_{n-2}
@@ -427,11 +454,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         // the first TD groups of step tt into the ring
         auto prefetch_row = [&](int tt) {
 #pragma unroll
-            for (int q = 0; q < TD; ++q) {
-                const uint32_t so = rows.off(tt) + 4u * (TPS * (q >> 2) + Q * (q & 3));
-                rt_q[q] = buf_ld_nt(tape, v_grp, so);
-                qt_q[q] = buf_ld_nt(tape, v_grp, q_base + so);
-            }
+            for (int q = 0; q < TD; ++q) load_group(rt_q[q], qt_q[q], rows.off(tt), q >> 2, q & 3);
         };
         float4 cr_q[CBD];   // codebook rows of the next CBD groups, group gi in slot gi % CBD
 #pragma unroll
@@ -475,8 +498,16 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
             for (int m = 0; m < QPT; ++m) {
                 const int j = tau + TPS * m;
-                *reinterpret_cast<float4*>(mr + 4 * j) = buf_ld4(tape, v_quad, rows.off(t0) + 16u * TPS * m);
-                *reinterpret_cast<float4*>(mq + 4 * j) = buf_ld4(tape, v_quad, q_base + rows.off(t0) + 16u * TPS * m);
+                if constexpr (PAIR) {
+                    const float4 p0 = buf_ld4(tape, v_pair, rows.off(t0) + 32u * TPS * m);
+                    const float4 p1 = buf_ld4(tape, v_pair, rows.off(t0) + 32u * TPS * m + 16u);
+                    *reinterpret_cast<float4*>(mr + 4 * j) = make_float4(p0.x, p0.z, p1.x, p1.z);
+                    *reinterpret_cast<float4*>(mq + 4 * j) = make_float4(p0.y, p0.w, p1.y, p1.w);
+                } else {
+                    *reinterpret_cast<float4*>(mr + 4 * j) = buf_ld4(tape, v_quad, rows.off(t0) + 16u * TPS * m);
+                    *reinterpret_cast<float4*>(mq + 4 * j) =
+                        buf_ld4(tape, v_quad, q_base + rows.off(t0) + 16u * TPS * m);
+                }
             }
             lds_barrier();
             prime_fc();
@@ -556,14 +587,10 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                     {
                         const int gn = gi + TD;
                         if (gn < NGS) {
-                            const uint32_t so2 = rows.off(t) + 4u * (TPS * (gn >> 2) + Q * (gn & 3));
-                            rt_q[slot] = buf_ld_nt(tape, v_grp, so2);
-                            qt_q[slot] = buf_ld_nt(tape, v_grp, q_base + so2);
+                            load_group(rt_q[slot], qt_q[slot], rows.off(t), gn >> 2, gn & 3);
                         } else if (t > 0) {
                             const int g2 = gn - NGS;
-                            const uint32_t so2 = rows.off(t - 1) + 4u * (TPS * (g2 >> 2) + Q * (g2 & 3));
-                            rt_q[slot] = buf_ld_nt(tape, v_grp, so2);
-                            qt_q[slot] = buf_ld_nt(tape, v_grp, q_base + so2);
+                            load_group(rt_q[slot], qt_q[slot], rows.off(t - 1), g2 >> 2, g2 & 3);
                         }
                     }
                     float4 ac = ac_n, pe = pe_n, pf = pf_n;

@@ -259,6 +259,9 @@ constexpr int kStreamPolicy = 2;   // nt on gfx950
 __device__ __forceinline__ float buf_ld_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamPolicy));
 }
+__device__ __forceinline__ float2 buf_ld2_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamPolicy));
+}
 // Same store form as buf_st4 (whole offset in the VGPR, so the compiler adds the wait state after it).
 __device__ __forceinline__ void buf_st4_nt(float4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, v), r,
