@@ -563,7 +563,8 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     for (int ii = 0; ii < TI; ++ii) mi[mpos<K>(own.fgroup(m, q), J) + ii] = 0.f;
         } else {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma; the one finite message left is
-            // B_{n-2}(sigma >> k) = theta_{n-1}(sigma)
+            // B_{n-2}(sigma >> k) = theta_{n-1}(sigma).  It goes into the offset C_ and the message starts at 0, so
+            // the next step's branch terms are not rounded at theta's magnitude (a hundred or more in log2 units)
             float* mi = args.dbl && ((n - 2) & 1) ? msg1 : msg0;
             float th = 0.f;
 #pragma unroll
@@ -579,7 +580,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
 #pragma unroll
                         for (int ii = 0; ii < TI; ++ii) {
                             const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
-                            mi[mpos<K>((int)u, J)] = (u == (sig >> K)) ? th : kNeg;
+                            mi[mpos<K>((int)u, J)] = (u == (sig >> K)) ? 0.f : kNeg;
                         }
             }
             if (tau == 0) {
@@ -588,7 +589,7 @@ __global__ void __launch_bounds__(1024) gen_soft_kernel(GenArgs args) {
                     args.w_soft[(b * n + n - 1) * V + v] = valid ? args.cb[sig * V + v] : __builtin_nanf("");
             }
             D = N_last;
-            Nb = th;
+            C_ = th;
             t = n - 2;
         }
         lds_barrier();
@@ -1369,7 +1370,8 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
         } else {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma (grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
             // the messages left are B_{n-2}(sigma >> k) = theta_{n-1}(sigma) and P_{n-2}(sigma >> k) = <g, c - w>,
-            // which is kappa_{n-1} as well
+            // which is kappa_{n-1} as well.  theta goes into the offset C_ and the message starts at 0, so the next
+            // step's branch terms are not rounded at theta's magnitude (a hundred or more in log2 units)
             float th = 0.f, pz = 0.f;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
@@ -1384,7 +1386,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
 #pragma unroll
                     for (int ii = 0; ii < TI; ++ii) {
                         const uint32_t u = (uint32_t)(own.fgroup(m, q) + ii);
-                        mr[mpos<K>((int)u, J)] = (u == (sig >> K)) ? th : kNeg;
+                        mr[mpos<K>((int)u, J)] = (u == (sig >> K)) ? 0.f : kNeg;
                         mq[mpos<K>((int)u, J)] = (u == (sig >> K)) ? pz : 0.f;
                     }
             if (tau == 0) {
@@ -1409,7 +1411,7 @@ __global__ void __launch_bounds__(1024) gen_grad_kernel(GenArgs args) {
                 }
             }
             D = N_last;
-            Nb = th;
+            C_ = (RT)th;
             kb = grid_offset(pz);
             H = kb;
             t = n - 2;

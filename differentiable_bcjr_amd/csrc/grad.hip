@@ -414,7 +414,8 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
         } else {
             // s_n = sigma: posterior at n-1 is the indicator of sigma (so grad_{n-1} = 0, w_soft_{n-1} = c(sigma));
             // the messages left are B_{n-2}(sigma >> 2) = theta_{n-1}(sigma), P^_{n-2}(sigma >> 2) = g (c(sigma) - w),
-            // and kappa_{n-1} = g (c(sigma) - w) as well
+            // and kappa_{n-1} = g (c(sigma) - w) as well.  theta goes into the offset C and the message starts at 0,
+            // so the next step's branch terms are not rounded at theta's magnitude (a hundred or more in log2 units)
             const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float th = -d * d;
             const float pz = gb[n - 1] * inv_scale * d;
@@ -423,7 +424,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
                     const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
-                    mr[u] = (u == (sig >> 2)) ? th : kNeg;
+                    mr[u] = (u == (sig >> 2)) ? 0.f : kNeg;
                     mq[u] = (u == (sig >> 2)) ? pz : 0.f;
                 }
             if (tau == 0 && active) {
@@ -431,7 +432,7 @@ __global__ void __launch_bounds__(Geo<L>::NT) grad_kernel(GradArgs args) {
                 if (args.w_soft) args.w_soft[b * n + n - 1] = valid ? args.cb[sig] : __builtin_nanf("");
             }
             D = N_last;
-            Nb = th;
+            C = (RT)th;
             kb = grid_offset(pz);
             H = kb;
             t = n - 2;

@@ -226,7 +226,9 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
                 *reinterpret_cast<float4*>(mi + 4 * (tau + TPS * m)) = make_float4(0.f, 0.f, 0.f, 0.f);
         } else {
             // s_n = sigma: the posterior at n-1 is the indicator of sigma, and the only finite message left is
-            // B_{n-2}(sigma >> 2) = theta_{n-1}(sigma)
+            // B_{n-2}(sigma >> 2) = theta_{n-1}(sigma).  It goes into the offset C, and the message starts at 0:
+            // theta can be a hundred or more in log2 units, and the next step's branch terms, added to it, would
+            // keep only its absolute precision (each state's weight off by ~1e-5)
             float* mi = ((n - 2) & 1) ? msg1 : msg0;
             const float d = fmaf(args.cb[sig], scale, -(wb[n - 1] * scale));
             const float th = -d * d;
@@ -236,12 +238,12 @@ __global__ void __launch_bounds__(Geo<L>::NT) soft_kernel(SoftArgs args) {
 #pragma unroll
                     for (int a = 0; a < 4; ++a) {
                         const uint32_t u = (uint32_t)(tau + TPS * m + Q * a);
-                        mi[u] = (u == (sig >> 2)) ? th : kNeg;
+                        mi[u] = (u == (sig >> 2)) ? 0.f : kNeg;
                     }
             }
             if (tau == 0 && active) args.w_soft[b * n + n - 1] = valid ? args.cb[sig] : __builtin_nanf("");
             D = N_last;
-            Nb = th;
+            C = th;
             t = n - 2;
         }
         lds_barrier();

@@ -60,15 +60,6 @@ def _fo_affordable(w, L, k) -> bool:
 _WORKERS = max(1, min(8, os.cpu_count() or 1))
 
 
-# The known exceedances: boundary-state mode at T <= 0.1 on a short sequence (n close to L/k), where the boundary
-# forces the last L/k states through far codewords.  Their log-weights, ~1e2 in log2 units, enter the messages, and a
-# float32 rounding of such a value is worth several ulps of w: the weights' gradient then moves by up to 3x its
-# one-ulp input conditioning.  Removing it needs the log-weights centred step by step (on the best path's), which the
-# kernels do not do.  The tests that hit it are marked expected to fail (not strict) and still run.
-SIGMA_FORCED_LOG_WEIGHTS = ("boundary-state mode, T <= 0.1, n near L/k: float32 roundings of forced log-weights "
-                            "(~1e2) exceed the one-ulp conditioning of dL/dw by up to 3x")
-
-
 def t32(T) -> float:
     """The temperature as the C-ABI receives it (float32)."""
     return float(np.float32(T))

@@ -228,11 +228,9 @@ GC_IDS = IDS
 
 @pytest.mark.parametrize("L,k,V,B,n", GC_CASES, ids=GC_IDS)
 @pytest.mark.parametrize("sigma", [False, True])
-def test_codebook_grad_matches_oracle(request, oracle_mod, dev, L, k, V, B, n, sigma):
+def test_codebook_grad_matches_oracle(oracle_mod, dev, L, k, V, B, n, sigma):
     if sigma:
         n = _sigma_n(L, k, n)
-    if sigma and (L, k, V, B, n) == (8, 4, 2, 3, 6):
-        request.applymarker(pytest.mark.xfail(reason=parity.SIGMA_FORCED_LOG_WEIGHTS, strict=False))
     w, c, g, s = _vin(L, V, B, n, 7700 + 31 * L + 7 * k + V + n, sigma)
     ok = True
     for T in [1.0, 0.1, 0.05]:
